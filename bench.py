@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Throughput of the batched speculative-sampling verification step on one MI355X.
+
+A step is one call of spec_verify_run over one batch: B = 256 sequences, gamma = 4
+drafts each, V = 128256, bf16 target logits, fp32 draft distributions, T = 1
+(the full hot path: row statistics + accept test, first-rejection scan,
+residual / bonus draw). Inputs are seeded synthetic data (see synth/), resident
+in HBM before timing starts; several input sets rotate so that no step re-reads
+the previous step's data from the 256 MB last-level cache.
+
+Prints one JSON line on stdout:
+  value       verified positions/s (sum gamma_b per step / seconds per step)
+  roofline    the dominant kernel (the row-statistics pass) against HBM peak:
+              algorithmic bytes per launch / mean launch duration from HIP events
+              recorded on the launch stream during the timed loop
+  cpu_baseline the CPU oracle timed on a bounded sample of the same inputs
+Diagnostics go to stderr.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified positions/s + achieved HBM GB/s (% of peak), B=256 gamma=4 V=128256"
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def step_bytes(w, n):
+    """Algorithmic bytes of one step from this run's accepted counts n (the two-pass
+    method's minimum: every judged row once, the drawn row once, the rejected
+    position's q row once, plus the small per-position reads and outputs)."""
+    import numpy as np
+    sl = 2 if w.dtype == "bf16" else 4
+    g = w.gammas.astype(np.int64)
+    n = n.astype(np.int64)
+    if w.T == 0.0:
+        per = g * w.V * sl + (n == g) * w.V * sl + g * 4 + 4 + (g + 1) * 4 + 4
+    else:
+        per = (g * w.V * sl + w.V * sl + (n < g) * w.V * 4 + g * (4 + 4) + (g + 1) * 4
+               + 4 + (g + 1) * 4 + 4)
+    return int(per.sum())
+
+
+def cpu_baseline(w, seconds):
+    """The oracle as it stands, single process, on the first sequences of one input set."""
+    import numpy as np
+    import oracle as O
+    cu = w.cu_gamma.astype(np.int64)
+    t0 = time.perf_counter()
+    done = positions = 0
+    while done < w.B:
+        b = done
+        g = int(cu[b + 1] - cu[b])
+        base = int(cu[b])
+        O.verify_sequence(w.logits_f64(slice(base + b, base + b + g + 1)),
+                          None if w.T == 0 else w.q[base:base + g], w.draft_ids[base:base + g],
+                          None if w.T == 0 else w.uniforms[base + b:base + b + g + 1], w.T)
+        done += 1
+        positions += g
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return dict(value=positions / dt, unit="verified positions/s", cores=1, kind="oracle",
+                sample=f"first {done} sequences ({positions} positions) of input set 0, "
+                       f"float64 NumPy oracle in one process, {dt:.1f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--config", default="C3", help="workload (C3 is the measured one; others for development)")
+    ap.add_argument("--sets", type=int, default=2, help="input sets rotated across steps")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the verification step shards by sequence with no "
+              "exchange, so there is no multi-GPU path to time here. Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import speculative_sampling_verification_03_amd as sv
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    sv.load_library()
+    dev = torch.device("cuda", 0)
+
+    log(f"[bench] generating {args.sets} input set(s) of {args.config}")
+    sets = []
+    for s in range(args.sets):
+        w = synth.make_config(args.config, seed=s)
+        d = {}
+        if w.dtype == "bf16":
+            d["logits"] = torch.from_numpy(w.logits.view(np.int16)).view(torch.bfloat16).to(dev)
+        else:
+            d["logits"] = torch.from_numpy(w.logits).to(dev)
+        d["q"] = torch.from_numpy(w.q).to(dev) if w.q is not None else None
+        d["ids"] = torch.from_numpy(w.draft_ids).to(dev)
+        d["u"] = torch.from_numpy(w.uniforms).to(dev) if w.uniforms is not None else None
+        d["cu"] = torch.from_numpy(w.cu_gamma).to(dev)
+        sets.append((w, d))
+    w0 = sets[0][0]
+    ragged = w0.uniform_gamma is None
+    code = sv.SV_BF16 if w0.dtype == "bf16" else sv.SV_F32
+    ver = sv.Verifier(w0.V, code, w0.B, max(w.draft_rows for w, _ in sets), 16)
+
+    outs = []
+    for w, d in sets:
+        outs.append(sv.VerifyOutputs(
+            torch.empty(w.B, dtype=torch.int32, device=dev),
+            torch.empty(w.target_rows, dtype=torch.int32, device=dev),
+            torch.empty(w.B, dtype=torch.float32, device=dev), None))
+
+    def step(k):
+        w, d = sets[k % len(sets)]
+        if ragged:
+            ver.run(d["logits"], d["ids"], temperature=w.T, q=d["q"], uniforms=d["u"],
+                    cu_gamma=d["cu"], total_draft_rows=w.draft_rows, out=outs[k % len(sets)])
+        else:
+            ver.run(d["logits"], d["ids"], temperature=w.T, q=d["q"], uniforms=d["u"],
+                    gamma=w.uniform_gamma, out=outs[k % len(sets)])
+
+    # untimed: outputs of each set fix the algorithmic bytes of its steps
+    nb = []
+    for k in range(len(sets)):
+        step(k)
+        torch.cuda.synchronize()
+        assert ver.status() == sv.SV_OK, ver.last_error()
+        nb.append(outs[k].accepted_count.cpu().numpy())
+    bytes_per_set = [step_bytes(w, n) for (w, _), n in zip(sets, nb)]
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+
+    # timed loop: per-kernel HIP events recorded on the launch stream for every step
+    ver.set_timing(args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(k)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ktimes, kruns = ver.kernel_times()
+    ver.set_timing(0)
+    assert ver.status() == sv.SV_OK, ver.last_error()
+    assert kruns == args.steps
+
+    ms = (t1 - t0) * 1e3 / args.steps
+    pos_per_step = np.mean([w.draft_rows for w, _ in sets])
+    value = pos_per_step / (ms * 1e-3)
+    path_bytes = float(np.mean([bytes_per_set[k % len(sets)] for k in range(args.steps)]))
+    path_gbps = path_bytes / (ms * 1e-3) / 1e9
+
+    kt = dict(ktimes)
+    k1 = ktimes[0][0]
+    sl = 2 if w0.dtype == "bf16" else 4
+    k1_bytes = float(np.mean([w.draft_rows * (w.V * sl + 8) for w, _ in sets]))
+    k1_gbps = k1_bytes / (kt[k1] * 1e-3) / 1e9
+
+    # acceptance metrics of the measured inputs
+    acc = np.concatenate(nb)
+    gam = np.concatenate([w.gammas for w, _ in sets]).astype(np.int64)
+    alpha_hat = acc.sum() / (acc + (acc < gam)).sum()
+    log(f"[bench] {args.config}: {ms * 1e3:.2f} us/step, {value / 1e6:.2f} M positions/s, "
+        f"path {path_gbps:.0f} GB/s ({path_gbps / HBM_PEAK_GBPS:.1%} of peak) over "
+        f"{path_bytes / 1e6:.1f} MB/step")
+    for name, t in ktimes:
+        log(f"[bench]   {name:20s} {t * 1e3:8.2f} us")
+    log(f"[bench] acceptance: alpha_hat={alpha_hat:.4f} tokens/round={np.mean(acc + 1):.4f} "
+        f"accepted/drafted={acc.sum() / gam.sum():.4f}")
+
+    cfgd = synth.CONFIGS[args.config]
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "verified positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32/f64",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{args.config}: B={w0.B} gamma={cfgd['gamma']} V={w0.V} {w0.dtype} logits"
+                         + (", fp32 q" if w0.T > 0 else ", greedy") + f", T={w0.T:g}"),
+            "B": w0.B, "gamma": cfgd["gamma"] if not ragged else "ragged 1..8", "V": w0.V,
+            "logits": w0.dtype, "T": w0.T, "input_sets": len(sets),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": k1,
+            "achieved": k1_gbps,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": k1_gbps / HBM_PEAK_GBPS,
+            "traffic": None,
+        },
+        "path": {
+            "algorithmic_bytes_per_step": path_bytes,
+            "achieved_GBps": path_gbps,
+            "frac_of_peak": path_gbps / HBM_PEAK_GBPS,
+            "kernel_us": {n: t * 1e3 for n, t in ktimes},
+        },
+        "acceptance": {"alpha_hat": float(alpha_hat), "tokens_per_round": float(np.mean(acc + 1)),
+                       "accepted_per_drafted": float(acc.sum() / gam.sum())},
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] timing the CPU oracle for ~{args.cpu_seconds:.0f} s")
+        line["cpu_baseline"] = cpu_baseline(w0, args.cpu_seconds)
+    ver.close()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

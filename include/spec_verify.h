@@ -1,0 +1,182 @@
+/*
+ * spec_verify.h — C ABI of libspecverify.so: the batched verification step of
+ * speculative sampling on AMD Instinct MI355X (gfx950).
+ *
+ * Sources for what each call computes:
+ *   [P1] "Speculative Decoding" (atonlee.tistory.com/330), ch.2 "propose와 verify가 한
+ *        round를 만드는 방식" and ch.3 "target distribution을 보존하는 acceptance rule";
+ *   [P2] "Speculative Decoding으로 LLM 추론 속도 높이기" (donmain.dev), sections
+ *        "미리 그려놓고 한 번에 검증한다" and "품질은 rejection sampling이 지킨다";
+ *   [P3] "Fast Inference from Transformers via Speculative Decoding" (notes page),
+ *        방법론 상세: 문제 설정 and 단계 1-3;
+ *   [P4] "투기적 디코딩 — 초안 모델을 무엇으로 세울 것인가" (ailab.paldyn.com), section
+ *        "출력이 변하지 않는다는 것이 핵심이다".
+ *
+ * Problem statement ([P3] 문제 설정, 단계 1-3): for each of B sequences the draft
+ * proposed gamma_b tokens x_i ~ q_i, and one target forward produced gamma_b + 1
+ * target rows. Verification computes p_i = softmax(l_i / T), judges the drafts
+ * left to right, accepting x_i when u_i < min(1, p_i(x_i) / q_i(x_i)), stops at
+ * the first rejection and draws the replacement there from
+ * norm(max(0, p - q)); if all gamma_b drafts are accepted it draws a bonus
+ * token from p at position gamma_b + 1 ([P1] ch.2-3; [P3] 단계 3). At T = 0 it
+ * is greedy: accept iff the draft equals the target argmax (lowest index on
+ * ties), and emit the target argmax at the first mismatch or at the bonus row
+ * ([P1] ch.3 greedy paragraph; [P4]).
+ *
+ * Every draw is an inverse CDF over ascending token ids: with weights w and the
+ * uniform u, t = u * sum(w) and the token is the first v whose inclusive prefix
+ * sum exceeds t (the last positive-weight v if rounding leaves none). The
+ * sampled row's arithmetic runs in float64 on the device; the pass over the
+ * judged rows runs in float32 with a float64 accept test.
+ *
+ * Packing (ragged gamma_b, "cu_gamma" = exclusive prefix of gamma_b, length B+1):
+ *   logits row of (b, i), i <= gamma_b : cu_gamma[b] + b + i
+ *   q row / draft id of (b, i), i < gamma_b : cu_gamma[b] + i
+ *   uniform of (b, i), i <= gamma_b   : cu_gamma[b] + b + i
+ *   uniform slot i < gamma_b is the accept test of draft position i; slot
+ *   gamma_b drives the single final draw (residual or bonus).
+ * With a uniform gamma (cu_gamma == NULL) cu_gamma[b] = b * gamma.
+ *
+ * Ownership: the caller owns every input and output buffer. Pointers passed to
+ * spec_verify_run are DEVICE pointers on the context's device and must stay
+ * valid until the enqueued work has passed on the stream. The context owns its
+ * device workspace, allocated once in spec_verify_create and freed in
+ * spec_verify_destroy. spec_verify_run allocates nothing, never synchronizes and
+ * returns once the kernels are enqueued. A context allows one run in flight at a
+ * time (the workspace is shared) and is not thread-safe.
+ *
+ * Errors: functions return SV_* codes; nothing is thrown across the ABI.
+ * Argument errors found on the host return SV_EINVAL and launch nothing. HIP
+ * failures return SV_EHIP. Data errors are found on the device and raise a
+ * sticky flag read by spec_verify_status (SV_EDATA), with defined fallbacks:
+ *   - a draft id outside [0, V): that position is rejected (and its residual
+ *     uses q as given);
+ *   - a uniform outside [0, 1): used as is (u >= 1 rejects every judged
+ *     position with thr <= 1 and makes a draw take the last positive weight);
+ *   - a judged or sampled row whose softmax normaliser is not finite or not
+ *     positive (NaN / +inf logits, or a row of -inf): flagged; outputs for that
+ *     sequence are unspecified but in range;
+ *   - malformed cu_gamma (decreasing, gamma_b > max_gamma, cu_gamma[B] !=
+ *     total_draft_rows): flagged; that sequence's accepted_count is -1 and its
+ *     other outputs are not written.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct spec_verify_ctx spec_verify_ctx; /* opaque; owns the workspace */
+
+enum {
+  SV_OK = 0,     /* success */
+  SV_EINVAL = 1, /* bad argument found on the host; nothing launched */
+  SV_ENOMEM = 2, /* workspace allocation failed in create */
+  SV_EHIP = 3,   /* a HIP runtime call or launch failed */
+  SV_EDATA = 4   /* (status only) the device flagged a data error since the last status call */
+};
+
+enum { SV_F32 = 0, SV_BF16 = 1 }; /* logits element type */
+
+/* Data-error bits reported by spec_verify_status through spec_verify_last_error. */
+enum {
+  SV_DATA_DRAFT_ID = 1,   /* a draft id outside [0, V) */
+  SV_DATA_NONFINITE = 2,  /* a row normaliser not finite / not positive */
+  SV_DATA_UNIFORM = 4,    /* a uniform outside [0, 1) */
+  SV_DATA_CU_GAMMA = 8    /* malformed cu_gamma */
+};
+
+/*
+ * Create a context on HIP device `device` for vocabulary size `vocab` (V >= 1)
+ * and logits element type `logits_dtype` (SV_F32 or SV_BF16). The workspace is
+ * sized for at most `max_batch` sequences (<= 2^24; ragged runs <= 65536), `max_draft_rows` packed draft rows
+ * (>= sum gamma_b of any run) and gamma_b <= `max_gamma` (<= 1024).
+ * On success *out holds the context and SV_OK is returned; on failure *out is
+ * NULL. Errors: SV_EINVAL (out NULL, vocab < 1, max_* < 0, max_gamma > 1024,
+ * unknown dtype, or sizes whose packed tensors would not be addressable with
+ * 64-bit offsets), SV_EHIP (bad device), SV_ENOMEM.
+ */
+int spec_verify_create(spec_verify_ctx **out, int device, int vocab, int logits_dtype,
+                       int max_batch, int max_draft_rows, int max_gamma);
+
+/*
+ * Enqueue one verification step on `hip_stream` (a hipStream_t; NULL = the
+ * default stream) of the context's device.
+ *
+ *   batch            B >= 0 sequences (B == 0: nothing is enqueued; returns SV_OK).
+ *   gamma            uniform draft length (>= 0) when cu_gamma is NULL; must be -1
+ *                    when cu_gamma is given.
+ *   cu_gamma         device int32 [B+1] exclusive prefix of gamma_b, or NULL.
+ *   total_draft_rows host copy of sum gamma_b (= B * gamma when uniform).
+ *   temperature      T >= 0 and finite; T == 0 selects the greedy rule.
+ *   logits           [sum(gamma_b + 1), V] row-major, element type from create.
+ *   q                fp32 [sum gamma_b, V] draft distributions; required iff T > 0
+ *                    (ignored when T == 0).
+ *   draft_ids        int32 [sum gamma_b].
+ *   uniforms         fp32 [sum(gamma_b + 1)] in [0, 1); required iff T > 0
+ *                    (ignored when T == 0).
+ * Outputs (device buffers, written completely for valid sequences):
+ *   accepted_count   int32 [B]: n_b, the number of accepted drafts.
+ *   emitted_tokens   int32 [sum(gamma_b + 1)]: per sequence, slots 0..n_b hold the
+ *                    n_b accepted drafts and the drawn token; slots after are -1.
+ *   residual_sum     fp32 [B]: S = sum max(0, p - q) at the rejected row; 0.0 when
+ *                    every draft was accepted, and in greedy mode.
+ *   p_draft          fp32 [sum gamma_b] or NULL: p_i(x_i) for every draft
+ *                    position (NaN for an out-of-range id); not written when T == 0.
+ * Errors: SV_EINVAL (ctx / required pointer NULL, B > max_batch,
+ * total_draft_rows > max_draft_rows or inconsistent with B * gamma, gamma out of
+ * range, T < 0 or not finite), SV_EHIP (launch failure). Data errors: see top.
+ */
+int spec_verify_run(spec_verify_ctx *ctx, void *hip_stream, int batch, int gamma,
+                    const int32_t *cu_gamma, int total_draft_rows, float temperature,
+                    const void *logits, const float *q, const int32_t *draft_ids,
+                    const float *uniforms, int32_t *accepted_count, int32_t *emitted_tokens,
+                    float *residual_sum, float *p_draft);
+
+/*
+ * Synchronize the stream of the last run, read and clear the device's sticky
+ * data-error flag. Returns SV_OK, SV_EDATA (details in spec_verify_last_error),
+ * SV_EHIP, or SV_EINVAL for a NULL ctx.
+ */
+int spec_verify_status(spec_verify_ctx *ctx);
+
+/* Text of the last error on this context ("" if none). Owned by the context. */
+const char *spec_verify_last_error(const spec_verify_ctx *ctx);
+
+/* Free the workspace and the context. NULL-safe. Synchronizes the device first. */
+void spec_verify_destroy(spec_verify_ctx *ctx);
+
+/*
+ * Measurement hook. spec_verify_set_timing(ctx, runs) with runs > 0 makes the
+ * next `runs` calls of spec_verify_run record HIP events on their stream around
+ * each kernel they launch (runs == 0 switches recording off). It waits for the
+ * device and allocates the events, so call it outside timed or captured code.
+ * spec_verify_kernel_times waits for the last recorded run, writes up to `cap`
+ * per-kernel mean durations in ms over the recorded runs and the kernels' names
+ * (launch order; `names` may be NULL), stores the number of recorded runs in
+ * *runs (may be NULL), restarts the recording and returns the number of kernels
+ * per run (0 if nothing was recorded) or a negative SV_* code.
+ */
+int spec_verify_set_timing(spec_verify_ctx *ctx, int runs);
+int spec_verify_kernel_times(spec_verify_ctx *ctx, float *ms, const char **names, int cap,
+                             int *runs);
+
+/*
+ * Host-side argument check: the checks spec_verify_run performs before any
+ * launch, without a context or a device. Returns SV_OK or SV_EINVAL (with the
+ * reason copied into `msg`, NUL-terminated, when msg_cap > 0).
+ */
+int spec_verify_check_args(int vocab, int logits_dtype, int max_batch, int max_draft_rows,
+                           int max_gamma, int batch, int gamma, int has_cu_gamma,
+                           int total_draft_rows, float temperature, int has_logits, int has_q,
+                           int has_draft_ids, int has_uniforms, int has_accepted_count,
+                           int has_emitted_tokens, int has_residual_sum, char *msg, int msg_cap);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

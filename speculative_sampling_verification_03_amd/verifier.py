@@ -1,0 +1,140 @@
+"""Torch-facing wrapper over the C ABI: checks tensors, allocates outputs, passes the stream.
+
+Torch supplies device memory and the current HIP stream only; the computation
+is the library's.
+"""
+from __future__ import annotations
+
+from typing import NamedTuple, Optional
+
+from .binding import (SV_BF16, SV_EDATA, SV_F32, spec_verify_create, spec_verify_destroy,
+                      spec_verify_kernel_times, spec_verify_last_error, spec_verify_run,
+                      spec_verify_set_timing, spec_verify_status)
+
+
+class VerifyOutputs(NamedTuple):
+    accepted_count: "torch.Tensor"   # int32 [B]
+    emitted_tokens: "torch.Tensor"   # int32 [sum(gamma_b + 1)]
+    residual_sum: "torch.Tensor"     # float32 [B]
+    p_draft: Optional["torch.Tensor"]  # float32 [sum gamma_b] or None
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return SV_BF16
+    if t.dtype == torch.float32:
+        return SV_F32
+    raise TypeError(f"logits must be bfloat16 or float32, got {t.dtype}")
+
+
+class Verifier:
+    """One library context on one device, sized by the max_* arguments."""
+
+    def __init__(self, vocab: int, logits_dtype, max_batch: int, max_draft_rows: int,
+                 max_gamma: int, device: int = 0):
+        import torch
+        self.device = torch.device("cuda", device)
+        code = logits_dtype if isinstance(logits_dtype, int) else (
+            SV_BF16 if logits_dtype == torch.bfloat16 else SV_F32)
+        self.vocab, self.dtype_code = vocab, code
+        self.max_batch, self.max_draft_rows, self.max_gamma = max_batch, max_draft_rows, max_gamma
+        self.ctx = spec_verify_create(device, vocab, code, max_batch, max_draft_rows, max_gamma)
+
+    # ------------------------------------------------------------------
+    def _check(self, name, t, dtype, numel=None):
+        import torch
+        if t is None:
+            return
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch tensor")
+        if t.device != self.device:
+            raise ValueError(f"{name} is on {t.device}, expected {self.device}")
+        if dtype is not None and t.dtype != dtype:
+            raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if numel is not None and t.numel() != numel:
+            raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+
+    def run(self, logits, draft_ids, *, temperature: float, q=None, uniforms=None,
+            gamma: Optional[int] = None, cu_gamma=None, total_draft_rows: Optional[int] = None,
+            out: Optional[VerifyOutputs] = None, want_p_draft: bool = True,
+            stream=None) -> VerifyOutputs:
+        """Enqueue one verification step on `stream` (default: torch's current stream).
+
+        Uniform gamma: pass `gamma`. Ragged: pass `cu_gamma` (int32 [B+1] on the device)
+        and the host value `total_draft_rows` (defaults to draft_ids.numel()).
+        """
+        import torch
+        if _dtype_code(logits) != self.dtype_code:
+            raise TypeError("logits dtype differs from the context's")
+        V = self.vocab
+        if cu_gamma is not None:
+            self._check("cu_gamma", cu_gamma, torch.int32)
+            B = cu_gamma.numel() - 1
+            R = int(total_draft_rows if total_draft_rows is not None else draft_ids.numel())
+            g_arg = -1
+        else:
+            if gamma is None:
+                raise ValueError("pass gamma or cu_gamma")
+            B = logits.shape[0] // (gamma + 1) if logits.numel() else 0
+            R = B * gamma
+            g_arg = gamma
+        self._check("logits", logits, None, (R + B) * V)
+        self._check("draft_ids", draft_ids, torch.int32, R)
+        greedy = float(temperature) == 0.0
+        if not greedy:
+            self._check("q", q, torch.float32, R * V)
+            self._check("uniforms", uniforms, torch.float32, R + B)
+        if out is None:
+            dev = self.device
+            out = VerifyOutputs(
+                torch.empty(B, dtype=torch.int32, device=dev),
+                torch.empty(R + B, dtype=torch.int32, device=dev),
+                torch.empty(B, dtype=torch.float32, device=dev),
+                torch.empty(R, dtype=torch.float32, device=dev) if (want_p_draft and not greedy) else None)
+        self._check("accepted_count", out.accepted_count, torch.int32, B)
+        self._check("emitted_tokens", out.emitted_tokens, torch.int32, R + B)
+        self._check("residual_sum", out.residual_sum, torch.float32, B)
+        self._check("p_draft", out.p_draft, torch.float32, R)
+        st = stream if stream is not None else torch.cuda.current_stream(self.device)
+        spec_verify_run(self.ctx, st, B, g_arg, cu_gamma, R, float(temperature), logits,
+                        None if greedy else q, draft_ids, None if greedy else uniforms,
+                        out.accepted_count, out.emitted_tokens, out.residual_sum, out.p_draft)
+        return out
+
+    def status(self) -> int:
+        """SV_OK, or SV_EDATA when the device flagged a data error (see last_error)."""
+        return spec_verify_status(self.ctx)
+
+    def data_error(self) -> Optional[str]:
+        return spec_verify_last_error(self.ctx) if self.status() == SV_EDATA else None
+
+    def last_error(self) -> str:
+        return spec_verify_last_error(self.ctx)
+
+    def set_timing(self, runs: int):
+        """Record per-kernel events for the next `runs` runs (0: off)."""
+        spec_verify_set_timing(self.ctx, runs)
+
+    def kernel_times(self):
+        """([(kernel, mean ms), ...], runs) over the recorded runs."""
+        return spec_verify_kernel_times(self.ctx)
+
+    def close(self):
+        if getattr(self, "ctx", None):
+            spec_verify_destroy(self.ctx)
+            self.ctx = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

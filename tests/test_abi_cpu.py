@@ -1,0 +1,108 @@
+"""C-ABI library checks that need no GPU: it loads, exports every symbol the
+header declares, and its host-side argument checks return the documented codes."""
+import os
+import re
+import subprocess
+
+import pytest
+
+from conftest import ROOT
+
+import speculative_sampling_verification_03_amd as sv
+
+HEADER = os.path.join(ROOT, "include", "spec_verify.h")
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spec_verify_\w+)\s*\(", text)))
+
+
+def test_library_built():
+    assert os.path.exists(sv.LIB_PATH), "build libspecverify.so first (python -m speculative_sampling_verification_03_amd.build)"
+
+
+def test_exports_every_declared_symbol():
+    lib = sv.load_library()
+    decl = declared_functions()
+    assert len(decl) >= 8
+    for name in decl:
+        assert hasattr(lib, name), name
+    assert sorted(sv.EXPORTED) == decl
+    out = subprocess.run(["nm", "-D", "--defined-only", sv.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (spec_verify_\w+)", out))
+    assert exported == set(decl)
+
+
+def test_library_links_no_torch():
+    out = subprocess.run(["ldd", sv.LIB_PATH], capture_output=True, text=True).stdout
+    assert "torch" not in out and "c10" not in out
+    assert "amdhip64" in out
+
+
+BASE = dict(vocab=1000, logits_dtype=sv.SV_BF16, max_batch=64, max_draft_rows=512, max_gamma=8,
+            batch=16, gamma=4, has_cu_gamma=False, total_draft_rows=64, temperature=1.0)
+
+
+def check(**kw):
+    a = dict(BASE)
+    a.update(kw)
+    return sv.spec_verify_check_args(**a)
+
+
+def test_check_args_accepts_valid():
+    assert check() == (sv.SV_OK, "")
+    assert check(temperature=0.0, has_q=False, has_uniforms=False)[0] == sv.SV_OK
+    assert check(gamma=-1, has_cu_gamma=True, total_draft_rows=100)[0] == sv.SV_OK
+    assert check(batch=0, total_draft_rows=0)[0] == sv.SV_OK
+    assert check(gamma=0, total_draft_rows=0)[0] == sv.SV_OK
+
+
+@pytest.mark.parametrize("kw,frag", [
+    (dict(vocab=0), "vocab"),
+    (dict(logits_dtype=7), "dtype"),
+    (dict(batch=-1), "batch"),
+    (dict(batch=65, total_draft_rows=260), "max_batch"),
+    (dict(total_draft_rows=513, batch=64, gamma=8, max_gamma=8), "max_draft_rows"),
+    (dict(gamma=9), "max_gamma"),
+    (dict(gamma=-2), "gamma"),
+    (dict(total_draft_rows=63), "batch * gamma"),
+    (dict(has_cu_gamma=True), "gamma must be -1"),
+    (dict(temperature=-0.5), "temperature"),
+    (dict(temperature=float("nan")), "temperature"),
+    (dict(temperature=float("inf")), "temperature"),
+    (dict(has_logits=False), "logits"),
+    (dict(has_q=False), "q is NULL"),
+    (dict(has_uniforms=False), "uniforms"),
+    (dict(has_draft_ids=False), "draft_ids"),
+    (dict(has_accepted_count=False), "output"),
+    (dict(has_emitted_tokens=False), "output"),
+    (dict(has_residual_sum=False), "output"),
+])
+def test_check_args_rejects(kw, frag):
+    rc, msg = check(**kw)
+    assert rc == sv.SV_EINVAL
+    assert frag in msg
+
+
+def test_null_context_calls():
+    lib = sv.load_library()
+    assert lib.spec_verify_status(None) == sv.SV_EINVAL
+    assert lib.spec_verify_set_timing(None, 1) == sv.SV_EINVAL
+    assert lib.spec_verify_kernel_times(None, None, None, 0, None) == -sv.SV_EINVAL
+    assert lib.spec_verify_last_error(None) == b""
+    lib.spec_verify_destroy(None)  # NULL-safe
+    rc = lib.spec_verify_run(None, None, 1, 1, None, 1, 1.0, None, None, None, None, None, None, None, None)
+    assert rc == sv.SV_EINVAL
+
+
+def test_create_rejects_bad_arguments_before_touching_a_device():
+    import ctypes
+    lib = sv.load_library()
+    out = ctypes.c_void_p(123)
+    assert lib.spec_verify_create(None, 0, 10, sv.SV_F32, 1, 1, 1) == sv.SV_EINVAL
+    assert lib.spec_verify_create(ctypes.byref(out), 0, 0, sv.SV_F32, 1, 1, 1) == sv.SV_EINVAL
+    assert out.value is None
+    assert lib.spec_verify_create(ctypes.byref(out), 0, 10, 5, 1, 1, 1) == sv.SV_EINVAL
+    assert lib.spec_verify_create(ctypes.byref(out), 0, 10, sv.SV_F32, 1, 1, 2000) == sv.SV_EINVAL
