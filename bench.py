@@ -50,14 +50,15 @@ def step_bytes(w, n):
 
 
 def cpu_baseline(w, seconds):
-    """The oracle as it stands, single process, on the first sequences of one input set."""
+    """The oracle as it stands, single process, cycling over the sequences of one input
+    set until about `seconds` of CPU work have been done."""
     import numpy as np
     import oracle as O
     cu = w.cu_gamma.astype(np.int64)
     t0 = time.perf_counter()
     done = positions = 0
-    while done < w.B:
-        b = done
+    while True:
+        b = done % w.B
         g = int(cu[b + 1] - cu[b])
         base = int(cu[b])
         O.verify_sequence(w.logits_f64(slice(base + b, base + b + g + 1)),
@@ -69,8 +70,8 @@ def cpu_baseline(w, seconds):
             break
     dt = time.perf_counter() - t0
     return dict(value=positions / dt, unit="verified positions/s", cores=1, kind="oracle",
-                sample=f"first {done} sequences ({positions} positions) of input set 0, "
-                       f"float64 NumPy oracle in one process, {dt:.1f} s")
+                sample=f"{done} sequences ({positions} positions) cycling over input set 0 "
+                       f"({w.B} sequences), float64 NumPy oracle in one process, {dt:.1f} s")
 
 
 def main():

@@ -78,7 +78,7 @@ class Verifier:
         else:
             if gamma is None:
                 raise ValueError("pass gamma or cu_gamma")
-            B = logits.shape[0] // (gamma + 1) if logits.numel() else 0
+            B = logits.numel() // ((gamma + 1) * V)
             R = B * gamma
             g_arg = gamma
         self._check("logits", logits, None, (R + B) * V)

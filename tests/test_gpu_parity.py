@@ -138,7 +138,10 @@ def test_q_equals_p_always_accepts(lib):
     for b in range(B):
         for i in range(g):
             Q[b * g + i] = O.target_distribution(L[b * (g + 1) + i], 1.0)
-    ids = np.array([rng.choice(V, p=Q[r] / Q[r].sum()) for r in range(B * g)], np.int32)
+    ids = np.empty(B * g, np.int32)
+    for r in range(B * g):
+        pr = Q[r].astype(np.float64)
+        ids[r] = rng.choice(V, p=pr / pr.sum())
     u = rng.random(B * (g + 1), dtype=np.float32)
     w = _custom("q=p", L, Q, ids, u, [g] * B, 1.0)
     gpu, ora, rep = check_parity(lib, w, "q=p")
@@ -186,7 +189,10 @@ def test_ragged_extremes(lib):
             x = L[cu[b] + b + i] + rng.normal(0, 0.7, V)
             e = np.exp(x - x.max())
             Q[cu[b] + i] = e / e.sum()
-    ids = np.array([rng.choice(V, p=Q[r].astype(np.float64) / Q[r].sum()) for r in range(R)], np.int32)
+    ids = np.empty(R, np.int32)
+    for r in range(R):
+        pr = Q[r].astype(np.float64)
+        ids[r] = rng.choice(V, p=pr / pr.sum())
     u = rng.random(R + B, dtype=np.float32)
     check_parity(lib, _custom("ragged 0/1/8", L, Q, ids, u, gammas, 1.0, dtype="bf16"), "ragged 0/1/8")
 
