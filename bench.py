@@ -83,6 +83,8 @@ def main():
     ap.add_argument("--sets", type=int, default=2, help="input sets rotated across steps")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run plain device copies of MIB MiB (calibrates the HBM byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -98,8 +100,21 @@ def main():
     import synth
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    sv.load_library()
     dev = torch.device("cuda", 0)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / 5
+        log(f"[bench] copy of {args.copy_calibration} MiB: {dt * 1e6:.1f} us, "
+            f"{2 * n / dt / 1e9:.0f} GB/s (read + write); each copy reads {n} B and writes {n} B")
+        return
+    sv.load_library()
 
     log(f"[bench] generating {args.sets} input set(s) of {args.config}")
     sets = []

@@ -90,12 +90,12 @@ enum {
 };
 
 /*
- * Create a context on HIP device `device` for vocabulary size `vocab` (V >= 1)
+ * Create a context on HIP device `device` for vocabulary size `vocab` (1 <= V <= 2^24)
  * and logits element type `logits_dtype` (SV_F32 or SV_BF16). The workspace is
  * sized for at most `max_batch` sequences (<= 2^24; ragged runs <= 65536), `max_draft_rows` packed draft rows
  * (>= sum gamma_b of any run) and gamma_b <= `max_gamma` (<= 1024).
  * On success *out holds the context and SV_OK is returned; on failure *out is
- * NULL. Errors: SV_EINVAL (out NULL, vocab < 1, max_* < 0, max_gamma > 1024,
+ * NULL. Errors: SV_EINVAL (out NULL, vocab outside [1, 2^24], max_* < 0, max_gamma > 1024,
  * unknown dtype, or sizes whose packed tensors would not be addressable with
  * 64-bit offsets), SV_EHIP (bad device), SV_ENOMEM.
  */

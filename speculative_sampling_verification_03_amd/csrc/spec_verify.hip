@@ -11,25 +11,29 @@
 //   [P4] "투기적 디코딩 — 초안 모델을 무엇으로 세울 것인가" (ailab.paldyn.com), "출력이
 //        변하지 않는다는 것이 핵심이다" (greedy reduces to argmax equality).
 //
-// Pipeline per call (three launches on the caller's stream, no host sync):
-//   1. k_rowstats / k_rowargmax: one read of every judged (draft) target row,
-//      split over `split` workgroups per row. Sampling: online max and
-//      sum exp((l - m)/T) in fp32 (p = softmax(l / T)). Greedy: max and its
-//      lowest index. Partials go to the workspace.
-//   2. k_sample_chunks / k_greedy_chunks, grid = B x nc (4096-element chunks of
-//      the vocabulary). Prologue: merge the partials of the sequence's rows, run
-//      the accept test of every draft position (p(x) in fp64), find the first
-//      rejection n_b. Body: one fp64 sweep of this chunk of the single row that
-//      will be drawn from: the rejected row (residual) or row gamma_b (bonus).
-//      The residual sweep defers normalisation: with e(v) = exp((l(v) - m)/T),
-//      v is positive iff e(v) > q(v) * Z32 (Z32 from step 1) and the chunk
-//      keeps E = sum_pos e, Q = sum_pos q, Zc = sum e. The bonus sweep keeps a
-//      chunk max and sum exp((l - m_c)/T). Greedy keeps the chunk argmax of row
-//      gamma_b only when every draft was accepted.
-//   3. k_sample_finalize / k_greedy_finalize, grid = B: combine chunk sums
-//      (Z64 = sum Zc, R_c = E_c / Z64 - Q_c, S = sum R_c), locate the chunk where
-//      the prefix crosses t = u * S, re-sweep that chunk with an fp64 block scan
-//      and emit the first token whose inclusive prefix exceeds t.
+// Two launches per call on the caller's stream, no host sync:
+//   1. k_rowstats / k_rowargmax, grid = (draft rows) x split, 256 threads: one read
+//      of every judged target row. Sampling keeps, in base 2 with k2 = log2(e)/T,
+//      the scaled row max c = max(l) * k2 and z = sum 2^(l * k2 - c), i.e. the
+//      softmax normaliser of l / T, in fp32; greedy keeps the max and its lowest
+//      index. When a row is not split, the same workgroup also runs the accept test
+//      of its draft position (p(x) in fp64) and records the decision.
+//   2. k_sample_seq / k_greedy_seq, grid = B, 1024 threads: find the first rejection
+//      n_b, then one fp64 sweep of the single row the sequence draws from: the
+//      rejected row (residual) or row gamma_b (bonus), its exponentials good to
+//      1.5e-13 relative. Each wave owns a contiguous
+//      region of the row. The residual sweep defers normalisation: with
+//      e(v) = 2^(l(v) k2 - c) and Z32 from step 1, w(v) = e(v) - q(v) Z32 and a region
+//      keeps D = sum max(w, 0), Q = sum_{w > 0} q, Zr = sum e. Since
+//      e/Z64 - q = w/Z64 - q (Z64 - Z32)/Z64, the region's residual mass is
+//      D/Z64 - Q (Z64 - Z32)/Z64 with Z64 = sum Zr. The region where the prefix
+//      crosses t = u * S is re-swept with an fp64 block scan and the first token
+//      whose inclusive prefix exceeds t is emitted. The bonus sweep keeps a running
+//      region max instead. Greedy reads row gamma_b only when every draft was accepted.
+//
+// Cross-workgroup hand-off inside one launch is avoided on purpose: the per-XCD L2
+// caches are not coherent for plain stores, and a device-scope fence (L2 write-back
+// and invalidate) per workgroup costs far more than the kernel boundary.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -47,17 +51,26 @@ using namespace sv;
 
 namespace {
 
-constexpr int kChunkGroups = 2;                            // groups per thread per chunk
-constexpr int kChunk = kThreads * kGroup * kChunkGroups;   // 4096 vocabulary entries
+// Tuning defaults (compile-time; -D overrides exist for sweeps).
+#ifndef SV_UNROLL
+#define SV_UNROLL 4
+#endif
+#ifndef SV_SPLIT_TARGET
+#define SV_SPLIT_TARGET 1024
+#endif
+#ifndef SV_SPLIT_MIN_SPAN
+#define SV_SPLIT_MIN_SPAN 2048
+#endif
 constexpr int kMaxSplit = 16;
 constexpr int kMaxGamma = 1024;
 constexpr int kMaxRaggedBatch = 65536;  // row -> sequence search limit
 constexpr int kMaxBatch = 1 << 24;
-constexpr int kUnroll = 4;  // groups in flight per thread in the row-stats loop
+constexpr int kMaxVocab = 1 << 24;
+constexpr int kUnroll = SV_UNROLL;      // groups in flight per thread in the row-stats loop
 
-struct RowStat { float m; float z; };  // sampling: max raw logit, sum exp((l - m)/T); greedy: max, index bits
-struct SeqInfo { int n; int mode; float m; float z; int tok; int g; int base; int pad; };
-enum { MODE_RESIDUAL = 0, MODE_BONUS = 1, MODE_GREEDY = 2, MODE_INVALID = 3 };
+// Row statistics of one split. Sampling: c = max(l) * k2 (clamped to fp32 range) and
+// z = sum 2^(l * k2 - c). Greedy: c = max(l), z = bits of its lowest index.
+struct RowStat { float c; float z; };
 
 struct Args {
   const void* logits;
@@ -69,18 +82,18 @@ struct Args {
   int32_t* emitted;
   float* rsum;
   float* pdraft;
-  RowStat* p1;
-  double* csum;   // [B][nc][3]
-  SeqInfo* info;  // [B]
+  RowStat* p1;     // [rows][split]
+  int32_t* accept; // [rows] decisions of step 1 (rows that are not split)
   int* err;
-  int B, gamma, V, R, split, span, nc, max_gamma;
-  float k2;       // log2(e) / T
-  double invT;    // 1 / T
+  int B, gamma, V, R, split, span, max_gamma;
+  float k2;        // log2(e) / T, fp32
+  double k2d;      // log2(e) / T, fp64
 };
 
 __device__ __forceinline__ bool finite_pos(float z) { return z > 0.f && z <= FLT_MAX; }
+__device__ __forceinline__ bool finite_f(float v) { return v >= -FLT_MAX && v <= FLT_MAX; }
 
-// Geometry of sequence b; false (and the data flag) when cu_gamma is malformed.
+// Geometry of sequence b; false when cu_gamma is malformed.
 template <bool RAGGED>
 __device__ __forceinline__ bool seq_geom(const Args& a, int b, int& base, int& g) {
   if (!RAGGED) {
@@ -97,96 +110,139 @@ __device__ __forceinline__ bool seq_geom(const Args& a, int b, int& base, int& g
   return ok;
 }
 
+// Merge (c, z) partial softmax states kept in base 2.
+__device__ __forceinline__ void lse2_merge(float& c, float& z, float c2, float z2) {
+  const float C = fmaxf(c, c2);
+  z = z * fast_exp2(c - C) + z2 * fast_exp2(c2 - C);
+  c = C;
+}
+
+// Accept test of one draft position ([P1] ch.3; [P2] "품질은 rejection sampling이
+// 지킨다"; [P3] 단계 3): p(x) = 2^(l_x k2 - c) / z in fp64 (the same normaliser as
+// the row statistics), thr = 1 if p(x) >= q(x) else p(x) / q(x), accept iff u < thr.
+// An id outside [0, V) rejects; data errors raise the sticky flag.
+__device__ __forceinline__ bool accept_test(int x, float lx, float qx, float uu, float c, float z,
+                                            const Args& a, double& px) {
+  px = __builtin_nan("");
+  bool acc = false;
+  if (x >= 0 && x < a.V) {
+    px = exp2(static_cast<double>(lx) * static_cast<double>(a.k2) - static_cast<double>(c)) /
+         static_cast<double>(z);
+    const double qd = qx;
+    const double thr = px >= qd ? 1.0 : px / qd;  // no division when p >= q
+    acc = static_cast<double>(uu) < thr;         // strict
+    if (!(uu >= 0.f && uu < 1.f)) atomicOr(a.err, SV_DATA_UNIFORM);
+  } else {
+    atomicOr(a.err, SV_DATA_DRAFT_ID);
+  }
+  if (!(finite_pos(z) && finite_f(c))) atomicOr(a.err, SV_DATA_NONFINITE);
+  return acc;
+}
+
 // ============================================================== step 1
-// Row statistics of one split of one draft row: m = max l, z = sum exp2((l - m) * k2).
-template <typename T, bool ALIGNED, bool RAGGED>
+template <typename T, bool ALIGNED, bool RAGGED, bool ACCEPT>
 __global__ __launch_bounds__(kThreads) void k_rowstats(Args a) {
-  __shared__ float s_m[kWaves], s_z[kWaves];
+  __shared__ float s_c[kWaves], s_z[kWaves];
   const int d = blockIdx.x / a.split, k = blockIdx.x - d * a.split;
   const int b = RAGGED ? seq_of_row(a.cu, a.B, d) : d / a.gamma;
   const T* row = static_cast<const T*>(a.logits) + static_cast<size_t>(d + b) * a.V;
+  // operands of the accept test, issued first so their latency hides under the stream
+  int x = -1;
+  float lx = 0.f, qx = 0.f, uu = 0.f;
+  if (ACCEPT && threadIdx.x == 0) {
+    x = a.ids[d];
+    uu = a.u[d + b];
+    if (x >= 0 && x < a.V) {
+      lx = load_one(row, x);
+      qx = a.q[static_cast<size_t>(d) * a.V + x];
+    }
+  }
   const int lo = k * a.span, hi = min(a.V, lo + a.span);
   const float k2 = a.k2;
-  float m = -FLT_MAX;
+  float m = -FLT_MAX, c = -FLT_MAX;  // running max of l and its scaled value
   float s[kGroup];
 #pragma unroll
   for (int j = 0; j < kGroup; ++j) s[j] = 0.f;
-
+  auto rebase = [&](float bm) {
+    if (bm > m) {
+      const float cn = fmaxf(bm * k2, -FLT_MAX);
+      const float sc = fast_exp2(c - cn);
+#pragma unroll
+      for (int j = 0; j < kGroup; ++j) s[j] *= sc;
+      m = bm;
+      c = cn;
+    }
+  };
   if (ALIGNED) {
     const int g1 = hi >> 3;
     int g = (lo >> 3) + threadIdx.x;
     for (; g + (kUnroll - 1) * kThreads < g1; g += kUnroll * kThreads) {
-      float x[kUnroll][kGroup];
+      float xv[kUnroll][kGroup];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) load_group(row, static_cast<size_t>(g + u * kThreads) * kGroup, x[u]);
-      float bm = x[0][0];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u)
-#pragma unroll
-        for (int j = 0; j < kGroup; ++j) bm = fmaxf(bm, x[u][j]);
-      if (bm > m) {
-        const float sc = fast_exp2((m - bm) * k2);
-#pragma unroll
-        for (int j = 0; j < kGroup; ++j) s[j] *= sc;
-        m = bm;
-      }
+      for (int u = 0; u < kUnroll; ++u) load_group(row, static_cast<size_t>(g + u * kThreads) * kGroup, xv[u]);
+      float bm = xv[0][0];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u)
 #pragma unroll
-        for (int j = 0; j < kGroup; ++j) s[j] += fast_exp2((x[u][j] - m) * k2);
+        for (int j = 0; j < kGroup; ++j) bm = fmaxf(bm, xv[u][j]);
+      rebase(bm);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j) s[j] += fast_exp2(fmaf(xv[u][j], k2, -c));
     }
     for (; g < g1; g += kThreads) {
-      float x[kGroup];
-      load_group(row, static_cast<size_t>(g) * kGroup, x);
-      float bm = x[0];
+      float xv[kGroup];
+      load_group(row, static_cast<size_t>(g) * kGroup, xv);
+      float bm = xv[0];
 #pragma unroll
-      for (int j = 1; j < kGroup; ++j) bm = fmaxf(bm, x[j]);
-      if (bm > m) {
-        const float sc = fast_exp2((m - bm) * k2);
+      for (int j = 1; j < kGroup; ++j) bm = fmaxf(bm, xv[j]);
+      rebase(bm);
 #pragma unroll
-        for (int j = 0; j < kGroup; ++j) s[j] *= sc;
-        m = bm;
-      }
-#pragma unroll
-      for (int j = 0; j < kGroup; ++j) s[j] += fast_exp2((x[j] - m) * k2);
+      for (int j = 0; j < kGroup; ++j) s[j] += fast_exp2(fmaf(xv[j], k2, -c));
     }
   } else {
     for (int e = lo + threadIdx.x; e < hi; e += kThreads) {
-      const float x = load_one(row, e);
-      if (x > m) {
-        s[0] *= fast_exp2((m - x) * k2);
-        m = x;
-      }
-      s[0] += fast_exp2((x - m) * k2);
+      const float xv = load_one(row, e);
+      rebase(xv);
+      s[0] += fast_exp2(fmaf(xv, k2, -c));
     }
   }
   float z = ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
-    const float m2 = __shfl_xor(m, o), z2 = __shfl_xor(z, o);
-    lse_merge(m, z, m2, z2, k2);
+    const float c2 = __shfl_xor(c, o), z2 = __shfl_xor(z, o);
+    lse2_merge(c, z, c2, z2);
   }
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   if (lane == 0) {
-    s_m[w] = m;
+    s_c[w] = c;
     s_z[w] = z;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    float M = s_m[0], Z = s_z[0];
-    for (int i = 1; i < kWaves; ++i) lse_merge(M, Z, s_m[i], s_z[i], k2);
-    a.p1[blockIdx.x] = RowStat{M, Z};
+    float C = s_c[0], Z = s_z[0];
+    for (int i = 1; i < kWaves; ++i) lse2_merge(C, Z, s_c[i], s_z[i]);
+    a.p1[blockIdx.x] = RowStat{C, Z};
+    if (ACCEPT) {
+      double px;
+      a.accept[d] = accept_test(x, lx, qx, uu, C, Z, a, px) ? 1 : 0;
+      if (a.pdraft) a.pdraft[d] = static_cast<float>(px);
+    }
   }
 }
 
-// Greedy twin: max raw logit of one split of one draft row and its lowest index.
-template <typename T, bool ALIGNED, bool RAGGED>
+// Greedy twin: max raw logit of one split of one draft row and its lowest index; an
+// unsplit row also records whether its draft equals that argmax.
+template <typename T, bool ALIGNED, bool RAGGED, bool ACCEPT>
 __global__ __launch_bounds__(kThreads) void k_rowargmax(Args a) {
   __shared__ float s_v[kWaves];
   __shared__ int s_i[kWaves];
   const int d = blockIdx.x / a.split, k = blockIdx.x - d * a.split;
   const int b = RAGGED ? seq_of_row(a.cu, a.B, d) : d / a.gamma;
   const T* row = static_cast<const T*>(a.logits) + static_cast<size_t>(d + b) * a.V;
+  int x = -1;
+  if (ACCEPT && threadIdx.x == 0) x = a.ids[d];
   const int lo = k * a.span, hi = min(a.V, lo + a.span);
   float bv = -INFINITY;
   int bi = INT_MAX;
@@ -195,25 +251,25 @@ __global__ __launch_bounds__(kThreads) void k_rowargmax(Args a) {
     int g = (lo >> 3) + threadIdx.x;
     if (g < g1) bi = g * kGroup;  // seed: a row of -inf still yields its first index
     for (; g + (kUnroll - 1) * kThreads < g1; g += kUnroll * kThreads) {
-      float x[kUnroll][kGroup];
+      float xv[kUnroll][kGroup];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) load_group(row, static_cast<size_t>(g + u * kThreads) * kGroup, x[u]);
+      for (int u = 0; u < kUnroll; ++u) load_group(row, static_cast<size_t>(g + u * kThreads) * kGroup, xv[u]);
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u)
 #pragma unroll
         for (int j = 0; j < kGroup; ++j)
-          if (x[u][j] > bv) {
-            bv = x[u][j];
+          if (xv[u][j] > bv) {
+            bv = xv[u][j];
             bi = (g + u * kThreads) * kGroup + j;
           }
     }
     for (; g < g1; g += kThreads) {
-      float x[kGroup];
-      load_group(row, static_cast<size_t>(g) * kGroup, x);
+      float xv[kGroup];
+      load_group(row, static_cast<size_t>(g) * kGroup, xv);
 #pragma unroll
       for (int j = 0; j < kGroup; ++j)
-        if (x[j] > bv) {
-          bv = x[j];
+        if (xv[j] > bv) {
+          bv = xv[j];
           bi = g * kGroup + j;
         }
     }
@@ -221,9 +277,9 @@ __global__ __launch_bounds__(kThreads) void k_rowargmax(Args a) {
     int e = lo + threadIdx.x;
     if (e < hi) bi = e;
     for (; e < hi; e += kThreads) {
-      const float x = load_one(row, e);
-      if (x > bv) {
-        bv = x;
+      const float xv = load_one(row, e);
+      if (xv > bv) {
+        bv = xv;
         bi = e;
       }
     }
@@ -245,406 +301,532 @@ __global__ __launch_bounds__(kThreads) void k_rowargmax(Args a) {
     int I = s_i[0];
     for (int i = 1; i < kWaves; ++i) argmax_merge(V, I, s_v[i], s_i[i]);
     a.p1[blockIdx.x] = RowStat{V, __int_as_float(I)};
-  }
-}
-
-// ============================================================== step 2 (sampling)
-// Load this thread's part of chunk c of a row: groups (tid + k * kThreads), k < 2.
-// Entries past V read as `fill`.
-template <typename T, bool ALIGNED>
-__device__ __forceinline__ void load_chunk(const T* row, int V, int c, float (&x)[kChunkGroups][kGroup], float fill) {
-#pragma unroll
-  for (int k = 0; k < kChunkGroups; ++k) {
-    const int e = c * kChunk + (threadIdx.x + k * kThreads) * kGroup;
-    if (ALIGNED) {
-      if (e < V) {
-        load_group(row, e, x[k]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < kGroup; ++j) x[k][j] = fill;
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < kGroup; ++j) x[k][j] = (e + j < V) ? load_one(row, e + j) : fill;
+    if (ACCEPT) {
+      // accept iff the draft equals the target argmax ([P1] ch.3 greedy; [P4])
+      a.accept[d] = x == I ? 1 : 0;
+      if (!(x >= 0 && x < a.V)) atomicOr(a.err, SV_DATA_DRAFT_ID);
     }
   }
 }
 
-template <typename T, bool ALIGNED, bool RAGGED>
-__global__ __launch_bounds__(kThreads) void k_sample_chunks(Args a) {
+// ============================================================== step 2: one workgroup per sequence
+#ifndef SV_SEQ_WAVES
+#define SV_SEQ_WAVES 16
+#endif
+#ifndef SV_RING
+#define SV_RING 4
+#endif
+constexpr int kSeqWaves = SV_SEQ_WAVES;
+constexpr int kSeqThreads = 64 * kSeqWaves;
+constexpr int kIter = 64 * kGroup;          // entries a wave covers per sweep iteration (1 group per lane)
+constexpr int kRing = SV_RING;              // sweep iterations held in registers (kRing - 1 in flight)
+constexpr int kPass = kSeqWaves * kIter;    // entries the block covers per re-sweep pass
+
+// Raw bits of one group of 8 entries: one 16-byte vector for bf16, two for fp32.
+template <typename T>
+struct Raw {
+  static constexpr int N = sizeof(T) / 2;
+  uint4 v[N];
+};
+
+template <typename T> __device__ __forceinline__ uint32_t neg_inf_word();
+template <> __device__ __forceinline__ uint32_t neg_inf_word<uint16_t>() { return 0xFF80FF80u; }
+template <> __device__ __forceinline__ uint32_t neg_inf_word<float>() { return 0xFF800000u; }
+__device__ __forceinline__ uint32_t elem_bits(const uint16_t* p, int e) { return p[e]; }
+__device__ __forceinline__ uint32_t elem_bits(const float* p, int e) { return __float_as_uint(p[e]); }
+
+// Group starting at entry e of `row`, known to lie inside the row (no check, so a
+// loop of these keeps a fixed number of loads in flight).
+template <typename T>
+__device__ __forceinline__ void load_raw_in(const T* __restrict__ row, int e, Raw<T>& r) {
+  const uint4* p = reinterpret_cast<const uint4*>(row + e);
+#pragma unroll
+  for (int i = 0; i < Raw<T>::N; ++i) r.v[i] = p[i];
+}
+
+// Group starting at entry e of `row`; entries at or past `lim` read as `fill`.
+template <typename T, bool ALIGNED>
+__device__ __forceinline__ void load_raw(const T* __restrict__ row, int e, int lim, Raw<T>& r, uint32_t fill) {
+  if (ALIGNED) {
+    if (e < lim) {
+      const uint4* p = reinterpret_cast<const uint4*>(row + e);
+#pragma unroll
+      for (int i = 0; i < Raw<T>::N; ++i) r.v[i] = p[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < Raw<T>::N; ++i) r.v[i] = make_uint4(fill, fill, fill, fill);
+    }
+  } else {
+    uint32_t w[8];
+    if (sizeof(T) == 2) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t lo = (e + 2 * k < lim) ? elem_bits(row, e + 2 * k) : (fill & 0xFFFFu);
+        const uint32_t hi = (e + 2 * k + 1 < lim) ? elem_bits(row, e + 2 * k + 1) : (fill & 0xFFFFu);
+        w[k] = lo | (hi << 16);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) w[k] = (e + k < lim) ? elem_bits(row, e + k) : fill;
+    }
+#pragma unroll
+    for (int i = 0; i < Raw<T>::N; ++i) r.v[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+  }
+}
+
+__device__ __forceinline__ void unpack(const Raw<uint16_t>& r, float x[8]) {
+  x[0] = bf16_lo(r.v[0].x); x[1] = bf16_hi(r.v[0].x); x[2] = bf16_lo(r.v[0].y); x[3] = bf16_hi(r.v[0].y);
+  x[4] = bf16_lo(r.v[0].z); x[5] = bf16_hi(r.v[0].z); x[6] = bf16_lo(r.v[0].w); x[7] = bf16_hi(r.v[0].w);
+}
+__device__ __forceinline__ void unpack(const Raw<float>& r, float x[8]) {
+  x[0] = __uint_as_float(r.v[0].x); x[1] = __uint_as_float(r.v[0].y);
+  x[2] = __uint_as_float(r.v[0].z); x[3] = __uint_as_float(r.v[0].w);
+  x[4] = __uint_as_float(r.v[1].x); x[5] = __uint_as_float(r.v[1].y);
+  x[6] = __uint_as_float(r.v[1].z); x[7] = __uint_as_float(r.v[1].w);
+}
+
+// The per-sequence prologue shared by the sampling and greedy kernels: the first
+// rejection n (g when every draft was accepted). Sampling also leaves each row's
+// (c, z) in s_cz; greedy leaves each row's argmax in s_tok.
+template <typename T, bool ACCEPT, bool GREEDY>
+__device__ __forceinline__ int first_rejection(const Args& a, int b, int base, int g, float2* s_cz, int* s_tok,
+                                               int* s_n) {
+  if (threadIdx.x == 0) *s_n = g;
+  __syncthreads();
+  const T* L = static_cast<const T*>(a.logits);
+  for (int i = threadIdx.x; i < g; i += kSeqThreads) {
+    const int d = base + i;
+    bool acc;
+    if (ACCEPT) {
+      const RowStat r = a.p1[d];
+      if (GREEDY) s_tok[i] = __float_as_int(r.z);
+      else s_cz[i] = make_float2(r.c, r.z);
+      acc = a.accept[d] != 0;
+    } else if (GREEDY) {
+      float V = -INFINITY;
+      int I = INT_MAX;
+      for (int k = 0; k < a.split; ++k) {
+        const RowStat r = a.p1[static_cast<size_t>(d) * a.split + k];
+        argmax_merge(V, I, r.c, __float_as_int(r.z));
+      }
+      s_tok[i] = I;
+      const int x = a.ids[d];
+      acc = x == I;
+      if (!(x >= 0 && x < a.V)) atomicOr(a.err, SV_DATA_DRAFT_ID);
+    } else {
+      float C = -FLT_MAX, Z = 0.f;
+      for (int k = 0; k < a.split; ++k) {
+        const RowStat r = a.p1[static_cast<size_t>(d) * a.split + k];
+        lse2_merge(C, Z, r.c, r.z);
+      }
+      s_cz[i] = make_float2(C, Z);
+      const int x = a.ids[d];
+      const bool valid = x >= 0 && x < a.V;
+      const float lx = valid ? load_one(L, static_cast<size_t>(d + b) * a.V + x) : 0.f;
+      const float qx = valid ? a.q[static_cast<size_t>(d) * a.V + x] : 0.f;
+      double px;
+      acc = accept_test(x, lx, qx, a.u[d + b], C, Z, a, px);
+      if (a.pdraft) a.pdraft[d] = static_cast<float>(px);
+    }
+    if (!acc) atomicMin(s_n, i);
+  }
+  __syncthreads();
+  return *s_n;
+}
+
+// Keeps the compiler from reordering memory operations across this point.
+__device__ __forceinline__ void issue_order_fence() { asm volatile("" ::: "memory"); }
+
+// Region geometry: wave w owns [w * rw, min(V, (w + 1) * rw)); rw is a multiple of
+// kRing * kIter so that every region but the last holds whole rings of iterations.
+__device__ __forceinline__ int region_width(int V) {
+  const int per = (V + kSeqWaves - 1) / kSeqWaves;
+  return (per + kRing * kIter - 1) / (kRing * kIter) * (kRing * kIter);
+}
+
+template <typename T, bool ALIGNED, bool RAGGED, bool ACCEPT>
+__global__ __launch_bounds__(kSeqThreads) void k_sample_seq(Args a) {
+  __shared__ double s_tab[kExpN];
+  __shared__ float2 s_cz[kMaxGamma];
+  __shared__ double s_reg[kSeqWaves][3];  // residual: (D, Q, Zr); bonus: (m, s, -)
+  __shared__ double s_wt[kSeqWaves];      // re-sweep: per-wave totals of a pass
+  __shared__ int s_wc[kSeqWaves], s_wl[kSeqWaves];
   __shared__ int s_n;
-  __shared__ float2 s_mz[kMaxGamma];
-  __shared__ double s_red[kWaves * 3];
-  __shared__ float s_f[kWaves];
-  const int b = blockIdx.x / a.nc, c = blockIdx.x - b * a.nc;
+  __shared__ double s_bc[6];  // search result: t, P (prefix before the region), Z64, delta, S, ref
+  __shared__ int s_bi[3];     // search result: region r*, kind, take_last
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar
   int base, g;
   if (!seq_geom<RAGGED>(a, b, base, g)) {
-    if (c == 0 && threadIdx.x == 0) {
+    if (threadIdx.x == 0) {
       atomicOr(a.err, SV_DATA_CU_GAMMA);
-      SeqInfo si{};
-      si.mode = MODE_INVALID;
-      a.info[b] = si;
       a.acc[b] = -1;
     }
     return;
   }
-  if (threadIdx.x == 0) s_n = g;
-  __syncthreads();
-  const T* L = static_cast<const T*>(a.logits);
+  exp_table_init(s_tab);
+  const int n = first_rejection<T, ACCEPT, false>(a, b, base, g, s_cz, nullptr, &s_n);
+  for (int i = threadIdx.x; i < n; i += kSeqThreads) a.emitted[base + b + i] = a.ids[base + i];
+  if (threadIdx.x == 0) a.acc[b] = n;
 
-  // ---- prologue: accept test of every draft position ([P1] ch.3; [P3] 단계 3)
-  for (int i = threadIdx.x; i < g; i += kThreads) {
-    const int d = base + i;
-    float M = -FLT_MAX, Z = 0.f;
-    for (int k = 0; k < a.split; ++k) {
-      const RowStat r = a.p1[static_cast<size_t>(d) * a.split + k];
-      lse_merge(M, Z, r.m, r.z, a.k2);
-    }
-    s_mz[i] = make_float2(M, Z);
-    const int x = a.ids[d];
-    const bool valid = x >= 0 && x < a.V;
-    double px = __builtin_nan("");
-    bool accept = false;
-    if (valid) {
-      const float lx = load_one(L, static_cast<size_t>(d + b) * a.V + x);
-      px = exp((static_cast<double>(lx) - static_cast<double>(M)) * a.invT) / static_cast<double>(Z);
-      const double qx = a.q[static_cast<size_t>(d) * a.V + x];
-      const double thr = px >= qx ? 1.0 : px / qx;  // min(1, p/q) without dividing when p >= q
-      const float uu = a.u[base + b + i];
-      accept = static_cast<double>(uu) < thr;      // strict
-      if (c == 0 && !(uu >= 0.f && uu < 1.f)) atomicOr(a.err, SV_DATA_UNIFORM);
-    }
-    if (!accept) atomicMin(&s_n, i);
-    if (c == 0) {
-      if (!valid) atomicOr(a.err, SV_DATA_DRAFT_ID);
-      if (!(finite_pos(Z) && M <= FLT_MAX)) atomicOr(a.err, SV_DATA_NONFINITE);
-      if (a.pdraft) a.pdraft[d] = static_cast<float>(px);
-    }
-  }
-  __syncthreads();
-  const int n = s_n;  // first rejection, or g when all accepted ([P1] ch.2)
+  const int V = a.V;
+  const bool residual = n < g;
+  const T* lrow = static_cast<const T*>(a.logits) + static_cast<size_t>(base + b + (residual ? n : g)) * V;
+  const float* qrow = residual ? a.q + static_cast<size_t>(base + n) * V : nullptr;
+  const double KN = kExpScale * a.k2d;  // exp2_tab(l KN - N c) = 2^(l k2 - c)
+  const float cr = residual ? s_cz[n].x : 0.f;
+  const double Zq = residual ? static_cast<double>(s_cz[n].y) : 0.0;
+  const int rw = region_width(V);
+  const int r0 = min(V, wave * rw), r1 = min(V, r0 + rw);
+  // whole iterations are read without checks (only possible when aligned); the rest, masked
+  const int nfull = ALIGNED ? (r1 - r0) / kIter : 0;
+  const int mstart = r0 + nfull * kIter;
+  const uint32_t linf = neg_inf_word<T>();
 
-  if (c == 0) {
-    for (int i = threadIdx.x; i < n; i += kThreads) a.emitted[base + b + i] = a.ids[base + i];
-    if (threadIdx.x == 0) {
-      SeqInfo si{};
-      si.n = n;
-      si.mode = n < g ? MODE_RESIDUAL : MODE_BONUS;
-      si.m = n < g ? s_mz[n].x : 0.f;
-      si.z = n < g ? s_mz[n].y : 0.f;
-      si.g = g;
-      si.base = base;
-      a.info[b] = si;
-      a.acc[b] = n;
-    }
-  }
-
-  double acc[3] = {0.0, 0.0, 0.0};
-  float mc = -INFINITY;  // bonus: chunk max of the raw logits
-  if (n < g) {
-    // ---- residual sweep of chunk c of row n ([P1] ch.3 residual; [P3] 단계 3 x')
-    const float M = s_mz[n].x;
-    const double Zq = static_cast<double>(s_mz[n].y);
-    const T* lrow = L + static_cast<size_t>(base + b + n) * a.V;
-    const float* qrow = a.q + static_cast<size_t>(base + n) * a.V;
-    float lx[kChunkGroups][kGroup], qx[kChunkGroups][kGroup];
-    load_chunk<T, ALIGNED>(lrow, a.V, c, lx, -INFINITY);
-    load_chunk<float, ALIGNED>(qrow, a.V, c, qx, 0.f);
-#pragma unroll
-    for (int k = 0; k < kChunkGroups; ++k)
+  // ---- one fp64 sweep of this wave's region through a ring of kRing register buffers
+  if (residual) {
+    // residual max(0, p - q) ([P1] ch.3; [P3] 단계 3), normalisation deferred
+    const double CN = kExpScale * static_cast<double>(cr);
+    double D = 0.0, Zr = 0.0;
+    float Q = 0.f;
+    auto step = [&](const Raw<T>& lr, const Raw<float>& qr) {
+      float x[kGroup], qv[kGroup];
+      unpack(lr, x);
+      unpack(qr, qv);
 #pragma unroll
       for (int j = 0; j < kGroup; ++j) {
-        const double ev = exp((static_cast<double>(lx[k][j]) - static_cast<double>(M)) * a.invT);
-        const double qv = static_cast<double>(qx[k][j]);
-        const bool pos = ev > qv * Zq;
-        acc[0] += pos ? ev : 0.0;
-        acc[1] += pos ? qv : 0.0;
-        acc[2] += ev;
+        const double e = exp2_tab(fma(static_cast<double>(x[j]), KN, -CN), s_tab);
+        const double w = fma(-static_cast<double>(qv[j]), Zq, e);
+        D += fmax(w, 0.0);
+        Q += w > 0.0 ? qv[j] : 0.f;
+        Zr += e;
       }
+    };
+    if (nfull > 0) {
+      Raw<T> Lb[kRing];
+      Raw<float> Qb[kRing];
+      const int eb = r0 + lane * kGroup, last = nfull - 1;
+      auto at = [&](int it) { return eb + min(it, last) * kIter; };  // clamped: always in range
+      // issue order pinned: the ring's wait counts assume the oldest buffer lands first
+#pragma unroll
+      for (int k = 0; k < kRing - 1; ++k) {
+        load_raw_in(lrow, at(k), Lb[k]);
+        load_raw_in(qrow, at(k), Qb[k]);
+        issue_order_fence();
+      }
+      for (int it = 0; it < nfull; it += kRing) {
+#pragma unroll
+        for (int k = 0; k < kRing; ++k) {
+          const int nb = (k + kRing - 1) % kRing;
+          load_raw_in(lrow, at(it + k + kRing - 1), Lb[nb]);
+          load_raw_in(qrow, at(it + k + kRing - 1), Qb[nb]);
+          if (k == 0 || it + k < nfull) step(Lb[k], Qb[k]);
+        }
+      }
+    }
+    // the rest of the region, masked per lane (fills contribute nothing); the trip count
+    // is the same for every lane of the wave
+    for (int e0 = mstart; e0 < r1; e0 += kIter) {
+      Raw<T> lr;
+      Raw<float> qr;
+      load_raw<T, ALIGNED>(lrow, e0 + lane * kGroup, r1, lr, linf);
+      load_raw<float, ALIGNED>(qrow, e0 + lane * kGroup, r1, qr, 0u);
+      step(lr, qr);
+    }
+    D = wave_sum(D);
+    Zr = wave_sum(Zr);
+    Q = wave_sum(Q);
+    if (lane == 0) {
+      s_reg[wave][0] = D;
+      s_reg[wave][1] = Q;
+      s_reg[wave][2] = Zr;
+    }
   } else {
-    // ---- bonus sweep of chunk c of row g ([P1] ch.2 bonus; [P3] 단계 3)
-    const T* lrow = L + static_cast<size_t>(base + b + g) * a.V;
-    float lx[kChunkGroups][kGroup];
-    load_chunk<T, ALIGNED>(lrow, a.V, c, lx, -INFINITY);
+    // bonus row ([P1] ch.2; [P3] 단계 3): running region max mw, sum 2^((l - mw) k2)
+    float mw = -INFINITY;
+    double mK = 0.0, sacc = 0.0;
+    auto step = [&](const Raw<T>& lr) {
+      float x[kGroup];
+      unpack(lr, x);
+      float bm = x[0];
 #pragma unroll
-    for (int k = 0; k < kChunkGroups; ++k)
+      for (int j = 1; j < kGroup; ++j) bm = fmaxf(bm, x[j]);
+      bm = wave_max_dpp(bm);
+      if (bm > mw) {  // wave-uniform
+        const double nK = static_cast<double>(bm) * KN;
+        sacc *= mw > -INFINITY ? exp2_tab(mK - nK, s_tab) : 0.0;
+        mw = bm;
+        mK = nK;
+      }
+      if (mw > -INFINITY) {
 #pragma unroll
-      for (int j = 0; j < kGroup; ++j) mc = fmaxf(mc, lx[k][j]);
-    mc = block_max(mc, s_f);
-    if (mc > -INFINITY) {
+        for (int j = 0; j < kGroup; ++j) sacc += exp2_tab(fma(static_cast<double>(x[j]), KN, -mK), s_tab);
+      }
+    };
+    if (nfull > 0) {
+      Raw<T> Lb[kRing];
+      const int eb = r0 + lane * kGroup, last = nfull - 1;
+      auto at = [&](int it) { return eb + min(it, last) * kIter; };
 #pragma unroll
-      for (int k = 0; k < kChunkGroups; ++k)
+      for (int k = 0; k < kRing - 1; ++k) {
+        load_raw_in(lrow, at(k), Lb[k]);
+        issue_order_fence();
+      }
+      for (int it = 0; it < nfull; it += kRing) {
 #pragma unroll
-        for (int j = 0; j < kGroup; ++j)
-          acc[1] += exp((static_cast<double>(lx[k][j]) - static_cast<double>(mc)) * a.invT);
+        for (int k = 0; k < kRing; ++k) {
+          load_raw_in(lrow, at(it + k + kRing - 1), Lb[(k + kRing - 1) % kRing]);
+          if (k == 0 || it + k < nfull) step(Lb[k]);
+        }
+      }
+    }
+    for (int e0 = mstart; e0 < r1; e0 += kIter) {  // wave-uniform trip count (step shuffles)
+      Raw<T> lr;
+      load_raw<T, ALIGNED>(lrow, e0 + lane * kGroup, r1, lr, linf);
+      step(lr);
+    }
+    sacc = wave_sum(sacc);
+    if (lane == 0) {
+      s_reg[wave][0] = mw;
+      s_reg[wave][1] = sacc;
+      s_reg[wave][2] = 0.0;
     }
   }
-  block_sum<3>(acc, s_red);
-  if (threadIdx.x == 0) {
-    double* o = a.csum + (static_cast<size_t>(b) * a.nc + c) * 3;
-    o[0] = n < g ? acc[0] : static_cast<double>(mc);
-    o[1] = acc[1];
-    o[2] = acc[2];
-  }
-}
+  __syncthreads();
 
-// ============================================================== step 3 (sampling)
-template <typename T, bool ALIGNED, bool RAGGED>
-__global__ __launch_bounds__(kThreads) void k_sample_finalize(Args a) {
-  __shared__ double s_d[kWaves];
-  __shared__ int s_i[kWaves];
-  const int b = blockIdx.x;
-  const SeqInfo si = a.info[b];
-  if (si.mode == MODE_INVALID) return;
-  const int n = si.n, g = si.g, base = si.base;
+  // ---- totals and the region where the inclusive prefix first exceeds t (wave 0,
+  // lane r holding region r)
   const float uf = a.u[base + b + g];
-  const double u = uf;
-  const double* cs = a.csum + static_cast<size_t>(b) * a.nc * 3;
-  const int nc = a.nc;
-
-  // kind 0: residual max(0, p - q); 1: degenerate residual, draw from p; 2: bonus from p
-  int kind;
-  double Zs = 0.0, S = 0.0, invZ = 0.0, Mb = -INFINITY, t;
-  if (si.mode == MODE_RESIDUAL) {
-    for (int c = 0; c < nc; ++c) Zs += cs[c * 3 + 2];
-    invZ = 1.0 / Zs;
-    for (int c = 0; c < nc; ++c) S += cs[c * 3 + 0] * invZ - cs[c * 3 + 1];
-    if (S > 0.0) {
-      kind = 0;
-      t = u * S;
+  if (wave == 0) {
+    const double u = uf;
+    const int r = lane < kSeqWaves ? lane : 0;
+    const bool live = lane < kSeqWaves;
+    int kind;  // 0: residual; 1: degenerate residual (S <= 0), draw from p; 2: bonus from p
+    double Z64, S = 0.0, delta = 0.0, ref, t, wgt;
+    if (residual) {
+      Z64 = wave_sum(live ? s_reg[r][2] : 0.0);
+      delta = (Z64 - Zq) / Z64;
+      wgt = live ? s_reg[r][0] / Z64 - s_reg[r][1] * delta : 0.0;
+      S = wave_sum(wgt);
+      kind = S > 0.0 ? 0 : 1;
+      if (kind == 1) wgt = live ? s_reg[r][2] : 0.0;
+      t = kind == 0 ? u * S : u * Z64;
+      ref = kExpScale * static_cast<double>(cr);
     } else {
-      kind = 1;
-      t = u * Zs;
+      double M = live ? s_reg[r][0] : -INFINITY;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) M = fmax(M, __shfl_xor(M, o));
+      ref = M * KN;
+      const double mr = live ? s_reg[r][0] : -INFINITY;
+      wgt = mr > -INFINITY ? s_reg[r][1] * exp2_tab(mr * KN - ref, s_tab) : 0.0;
+      Z64 = wave_sum(wgt);
+      kind = 2;
+      t = u * Z64;
     }
-  } else {
-    for (int c = 0; c < nc; ++c) Mb = fmax(Mb, cs[c * 3 + 0]);
-    for (int c = 0; c < nc; ++c) {
-      const double mc = cs[c * 3 + 0];
-      if (mc > -INFINITY) Zs += cs[c * 3 + 1] * exp((mc - Mb) * a.invT);
+    const double ex = wave_excl_scan(wgt);
+    const unsigned long long cross = __ballot(live && ex + wgt > t);
+    int rs = cross ? __ffsll(cross) - 1 : -1;
+    double P = __shfl(ex, rs < 0 ? 0 : rs);
+    int take_last = 0;
+    if (rs < 0) {  // no crossing (rounding, or u >= 1): last positive-weight token
+      take_last = 1;
+      const unsigned long long pos = __ballot(live && wgt > 0.0);
+      rs = pos ? 63 - __clzll(pos) : -1;
+      P = 0.0;
     }
-    kind = 2;
-    t = u * Zs;
-  }
-  if (threadIdx.x == 0) {
-    if (!(Zs > 0.0 && Zs <= DBL_MAX)) atomicOr(a.err, SV_DATA_NONFINITE);
-    if (!(uf >= 0.f && uf < 1.f)) atomicOr(a.err, SV_DATA_UNIFORM);
-  }
-  auto weight = [&](int c) -> double {
-    if (kind == 0) return cs[c * 3 + 0] * invZ - cs[c * 3 + 1];
-    if (kind == 1) return cs[c * 3 + 2];
-    const double mc = cs[c * 3 + 0];
-    return mc > -INFINITY ? cs[c * 3 + 1] * exp((mc - Mb) * a.invT) : 0.0;
-  };
-  // chunk where the inclusive prefix first exceeds t
-  double P = 0.0;
-  int cstar = -1;
-  for (int c = 0; c < nc; ++c) {
-    const double w = weight(c);
-    if (P + w > t) {
-      cstar = c;
-      break;
+    if (lane == 0) {
+      if (!(Z64 > 0.0 && Z64 <= DBL_MAX)) atomicOr(a.err, SV_DATA_NONFINITE);
+      if (!(uf >= 0.f && uf < 1.f)) atomicOr(a.err, SV_DATA_UNIFORM);
+      s_bc[0] = t;
+      s_bc[1] = P;
+      s_bc[2] = Z64;
+      s_bc[3] = delta;
+      s_bc[4] = S;
+      s_bc[5] = ref;
+      s_bi[0] = rs;
+      s_bi[1] = kind;
+      s_bi[2] = take_last;
     }
-    P += w;
   }
-  bool take_last = false;
-  if (cstar < 0) {  // no crossing (rounding, or u >= 1): last positive-weight token
-    take_last = true;
-    for (int c = nc - 1; c >= 0; --c)
-      if (weight(c) > 0.0) {
-        cstar = c;
-        break;
+  __syncthreads();
+  const double t = s_bc[0], Z64 = s_bc[2], delta = s_bc[3], S = s_bc[4], ref = s_bc[5];
+  const int rs = s_bi[0], kind = s_bi[1];
+  const bool take_last = s_bi[2] != 0;
+
+  // ---- re-sweep of region r* in passes of kPass entries: wave w scans the w-th kIter
+  // entries of a pass, lane l owns 8 consecutive entries
+  int tok = V - 1;
+  if (rs >= 0) {
+    const int R0 = min(V, rs * rw), R1 = min(V, R0 + rw);
+    const double invZ = 1.0 / Z64;
+    double run = s_bc[1];
+    int cand = INT_MAX, lastpos = -1;
+    for (int p0 = R0; p0 < R1 && cand == INT_MAX; p0 += kPass) {
+      const int e = p0 + wave * kIter + lane * kGroup;
+      Raw<T> lr;
+      float x[kGroup], qv[kGroup];
+      load_raw<T, ALIGNED>(lrow, e, R1, lr, linf);
+      unpack(lr, x);
+      if (kind == 0) {
+        Raw<float> qr;
+        load_raw<float, ALIGNED>(qrow, e, R1, qr, 0u);
+        unpack(qr, qv);
       }
-  }
-  int tok = a.V - 1;
-  if (cstar >= 0) {
-    const T* L = static_cast<const T*>(a.logits);
-    const int row_off = kind == 2 ? g : n;
-    const T* lrow = L + static_cast<size_t>(base + b + row_off) * a.V;
-    const int e0 = cstar * kChunk + threadIdx.x * (kGroup * kChunkGroups);
-    float lx[kChunkGroups][kGroup], qx[kChunkGroups][kGroup];
-#pragma unroll
-    for (int k = 0; k < kChunkGroups; ++k) {
-      const int e = e0 + k * kGroup;
-      if (ALIGNED && e < a.V) {
-        load_group(lrow, e, lx[k]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < kGroup; ++j) lx[k][j] = (e + j < a.V) ? load_one(lrow, e + j) : -INFINITY;
-      }
-    }
-    if (kind == 0) {
-      const float* qrow = a.q + static_cast<size_t>(base + n) * a.V;
-#pragma unroll
-      for (int k = 0; k < kChunkGroups; ++k) {
-        const int e = e0 + k * kGroup;
-        if (ALIGNED && e < a.V) {
-          load_group(qrow, e, qx[k]);
-        } else {
-#pragma unroll
-          for (int j = 0; j < kGroup; ++j) qx[k][j] = (e + j < a.V) ? qrow[e + j] : 0.f;
-        }
-      }
-    }
-    const double ref = kind == 2 ? Mb : static_cast<double>(si.m);
-    const double Zq = static_cast<double>(si.z);
-    double r[kChunkGroups * kGroup];
-    double tot = 0.0;
-#pragma unroll
-    for (int k = 0; k < kChunkGroups; ++k)
+      double rv[kGroup];
+      double tot = 0.0;
 #pragma unroll
       for (int j = 0; j < kGroup; ++j) {
-        const double ev = exp((static_cast<double>(lx[k][j]) - ref) * a.invT);
-        double w = ev;
+        const double ev = exp2_tab(fma(static_cast<double>(x[j]), KN, -ref), s_tab);
+        double wv = ev;
         if (kind == 0) {
-          const double qv = static_cast<double>(qx[k][j]);
-          w = ev > qv * Zq ? ev * invZ - qv : 0.0;
+          const double w = fma(-static_cast<double>(qv[j]), Zq, ev);
+          wv = w > 0.0 ? w * invZ - static_cast<double>(qv[j]) * delta : 0.0;
         }
-        r[k * kGroup + j] = w;
-        tot += w;
+        rv[j] = wv;
+        tot += wv;
       }
-    double run = P + block_excl_scan(tot, s_d);
-    int cand = INT_MAX, lastpos = -1;
+      const double lex = wave_excl_scan(tot);
+      if (lane == 63) s_wt[wave] = lex + tot;
+      __syncthreads();
+      double acc = run;
+      for (int w = 0; w < wave; ++w) acc += s_wt[w];
+      acc += lex;
+      int c2 = INT_MAX, lp = -1;
 #pragma unroll
-    for (int j = 0; j < kChunkGroups * kGroup; ++j) {
-      run += r[j];
-      if (!take_last && cand == INT_MAX && run > t) cand = e0 + j;
-      if (r[j] > 0.0) lastpos = e0 + j;
+      for (int j = 0; j < kGroup; ++j) {
+        acc += rv[j];
+        if (!take_last && c2 == INT_MAX && acc > t) c2 = e + j;
+        if (rv[j] > 0.0) lp = e + j;
+      }
+      c2 = wave_min_int(c2);
+      lp = wave_max_int(lp);
+      if (lane == 0) {
+        s_wc[wave] = c2;
+        s_wl[wave] = lp;
+      }
+      __syncthreads();
+      int cm = INT_MAX, lm = -1;
+      double tsum = run;
+      for (int w = 0; w < kSeqWaves; ++w) {
+        cm = min(cm, s_wc[w]);
+        lm = max(lm, s_wl[w]);
+        tsum += s_wt[w];
+      }
+      cand = cm;
+      lastpos = max(lastpos, lm);
+      run = tsum;
+      __syncthreads();  // s_wt / s_wc / s_wl are rewritten by the next pass
     }
-    cand = block_min_int(cand, s_i);
-    lastpos = block_max_int(lastpos, s_i);
-    tok = cand != INT_MAX ? cand : (lastpos >= 0 ? lastpos : a.V - 1);
+    tok = cand != INT_MAX ? cand : (lastpos >= 0 ? lastpos : V - 1);
   }
   if (threadIdx.x == 0) {
     a.emitted[base + b + n] = tok;
     a.rsum[b] = kind == 2 ? 0.f : static_cast<float>(S);
   }
-  for (int i = n + 1 + threadIdx.x; i <= g; i += kThreads) a.emitted[base + b + i] = -1;
+  for (int i = n + 1 + threadIdx.x; i <= g; i += kSeqThreads) a.emitted[base + b + i] = -1;
 }
 
-// ============================================================== steps 2-3 (greedy)
-template <typename T, bool ALIGNED, bool RAGGED>
-__global__ __launch_bounds__(kThreads) void k_greedy_chunks(Args a) {
-  __shared__ int s_n;
+// Greedy: the argmax of row g is computed only when every draft was accepted.
+template <typename T, bool ALIGNED, bool RAGGED, bool ACCEPT>
+__global__ __launch_bounds__(kSeqThreads) void k_greedy_seq(Args a) {
   __shared__ int s_tok[kMaxGamma];
-  __shared__ float s_v[kWaves];
-  __shared__ int s_i[kWaves];
-  const int b = blockIdx.x / a.nc, c = blockIdx.x - b * a.nc;
+  __shared__ float s_v[kSeqWaves];
+  __shared__ int s_i[kSeqWaves];
+  __shared__ int s_n;
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int base, g;
   if (!seq_geom<RAGGED>(a, b, base, g)) {
-    if (c == 0 && threadIdx.x == 0) {
+    if (threadIdx.x == 0) {
       atomicOr(a.err, SV_DATA_CU_GAMMA);
-      SeqInfo si{};
-      si.mode = MODE_INVALID;
-      a.info[b] = si;
       a.acc[b] = -1;
     }
     return;
   }
-  if (threadIdx.x == 0) s_n = g;
-  __syncthreads();
-  // accept iff the draft equals the target argmax ([P1] ch.3 greedy; [P4])
-  for (int i = threadIdx.x; i < g; i += kThreads) {
-    const int d = base + i;
-    float V = -INFINITY;
-    int I = INT_MAX;
-    for (int k = 0; k < a.split; ++k) {
-      const RowStat r = a.p1[static_cast<size_t>(d) * a.split + k];
-      argmax_merge(V, I, r.m, __float_as_int(r.z));
-    }
-    s_tok[i] = I;
-    const int x = a.ids[d];
-    if (x != I) atomicMin(&s_n, i);
-    if (c == 0 && !(x >= 0 && x < a.V)) atomicOr(a.err, SV_DATA_DRAFT_ID);
-  }
-  __syncthreads();
-  const int n = s_n;
-  if (c == 0) {
-    for (int i = threadIdx.x; i < n; i += kThreads) a.emitted[base + b + i] = a.ids[base + i];
-    if (threadIdx.x == 0) {
-      SeqInfo si{};
-      si.n = n;
-      si.mode = MODE_GREEDY;
-      si.tok = n < g ? s_tok[n] : -1;
-      si.g = g;
-      si.base = base;
-      a.info[b] = si;
-      a.acc[b] = n;
-    }
-  }
-  if (n < g) return;  // the bonus row is read only when every draft was accepted
-  const T* lrow = static_cast<const T*>(a.logits) + static_cast<size_t>(base + b + g) * a.V;
-  float lx[kChunkGroups][kGroup];
-  load_chunk<T, ALIGNED>(lrow, a.V, c, lx, -INFINITY);
-  float bv = -INFINITY;
-  int bi = INT_MAX;
+  const int n = first_rejection<T, ACCEPT, true>(a, b, base, g, nullptr, s_tok, &s_n);
+  for (int i = threadIdx.x; i < n; i += kSeqThreads) a.emitted[base + b + i] = a.ids[base + i];
+  int tok = n < g ? s_tok[n] : -1;
+  if (n == g) {  // the bonus row is read only when every draft was accepted
+    const T* row = static_cast<const T*>(a.logits) + static_cast<size_t>(base + b + g) * a.V;
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+    if (ALIGNED) {
+      const int g1 = a.V >> 3;
+      int gi = threadIdx.x;
+      if (gi < g1) bi = gi * kGroup;
+      for (; gi + (kUnroll - 1) * kSeqThreads < g1; gi += kUnroll * kSeqThreads) {
+        float xv[kUnroll][kGroup];
 #pragma unroll
-  for (int k = 0; k < kChunkGroups; ++k) {
-    const int e = c * kChunk + (threadIdx.x + k * kThreads) * kGroup;
+        for (int u = 0; u < kUnroll; ++u) load_group(row, static_cast<size_t>(gi + u * kSeqThreads) * kGroup, xv[u]);
 #pragma unroll
-    for (int j = 0; j < kGroup; ++j) {
-      if (e + j < a.V && bi == INT_MAX) bi = e + j;  // seed with the first in-range entry
-      if (lx[k][j] > bv) {
-        bv = lx[k][j];
-        bi = e + j;
+        for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+          for (int j = 0; j < kGroup; ++j)
+            if (xv[u][j] > bv) {
+              bv = xv[u][j];
+              bi = (gi + u * kSeqThreads) * kGroup + j;
+            }
+      }
+      for (; gi < g1; gi += kSeqThreads) {
+        float xv[kGroup];
+        load_group(row, static_cast<size_t>(gi) * kGroup, xv);
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j)
+          if (xv[j] > bv) {
+            bv = xv[j];
+            bi = gi * kGroup + j;
+          }
+      }
+    } else {
+      int e = threadIdx.x;
+      if (e < a.V) bi = e;
+      for (; e < a.V; e += kSeqThreads) {
+        const float xv = load_one(row, e);
+        if (xv > bv) {
+          bv = xv;
+          bi = e;
+        }
       }
     }
-  }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float v2 = __shfl_xor(bv, o);
-    const int i2 = __shfl_xor(bi, o);
-    argmax_merge(bv, bi, v2, i2);
-  }
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  if (lane == 0) {
-    s_v[w] = bv;
-    s_i[w] = bi;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
+    for (int o = 32; o > 0; o >>= 1) {
+      const float v2 = __shfl_xor(bv, o);
+      const int i2 = __shfl_xor(bi, o);
+      argmax_merge(bv, bi, v2, i2);
+    }
+    if (lane == 0) {
+      s_v[wave] = bv;
+      s_i[wave] = bi;
+    }
+    __syncthreads();
     float V = s_v[0];
     int I = s_i[0];
-    for (int i = 1; i < kWaves; ++i) argmax_merge(V, I, s_v[i], s_i[i]);
-    double* o = a.csum + (static_cast<size_t>(b) * a.nc + c) * 3;
-    o[0] = V;
-    o[1] = static_cast<double>(I);
-  }
-}
-
-__global__ __launch_bounds__(64) void k_greedy_finalize(Args a) {
-  const int b = blockIdx.x;
-  const SeqInfo si = a.info[b];
-  if (si.mode == MODE_INVALID) return;
-  const int n = si.n, g = si.g, base = si.base;
-  int tok = si.tok;
-  if (n == g) {
-    const double* cs = a.csum + static_cast<size_t>(b) * a.nc * 3;
-    float V = -INFINITY;
-    int I = INT_MAX;
-    for (int c = 0; c < a.nc; ++c) argmax_merge(V, I, static_cast<float>(cs[c * 3]), static_cast<int>(cs[c * 3 + 1]));
+    for (int w = 1; w < kSeqWaves; ++w) argmax_merge(V, I, s_v[w], s_i[w]);
     tok = I;
   }
   if (threadIdx.x == 0) {
+    a.acc[b] = n;
     a.emitted[base + b + n] = tok;
     a.rsum[b] = 0.f;
   }
-  for (int i = n + 1 + threadIdx.x; i <= g; i += 64) a.emitted[base + b + i] = -1;
+  for (int i = n + 1 + threadIdx.x; i <= g; i += kSeqThreads) a.emitted[base + b + i] = -1;
 }
 
 // ============================================================== host side
-const char* kKernelNames[2][3] = {
-    {"k_rowstats", "k_sample_chunks", "k_sample_finalize"},
-    {"k_rowargmax", "k_greedy_chunks", "k_greedy_finalize"},
+constexpr int kKernels = 2;
+const char* kKernelNames[2][kKernels] = {
+    {"k_rowstats", "k_sample_seq"},
+    {"k_rowargmax", "k_greedy_seq"},
 };
 
 }  // namespace
 
 struct spec_verify_ctx {
-  int device = 0, V = 0, dtype = 0, max_batch = 0, max_rows = 0, max_gamma = 0, nc = 0, cus = 0;
+  int device = 0, V = 0, dtype = 0, max_batch = 0, max_rows = 0, max_gamma = 0, cus = 0;
   void* ws = nullptr;
   RowStat* p1 = nullptr;
-  double* csum = nullptr;
-  SeqInfo* info = nullptr;
+  int32_t* accept = nullptr;
   int* err = nullptr;
   hipStream_t last_stream = nullptr;
   bool ran = false;
@@ -652,7 +834,7 @@ struct spec_verify_ctx {
   int timing_cap = 0, timing_runs = 0;
   hipEvent_t* ev = nullptr;
   int nk = 0;
-  const char* kname[3] = {nullptr, nullptr, nullptr};
+  const char* kname[kKernels] = {nullptr, nullptr};
   char msg[512] = {0};
 };
 
@@ -681,11 +863,8 @@ struct DeviceGuard {
   }
 };
 
-constexpr int kKernels = 3;
-
-template <typename T, bool AL, bool RG>
+template <typename T, bool AL, bool RG, bool AC>
 hipError_t launch_path(spec_verify_ctx* ctx, const Args& a, hipStream_t st, bool greedy) {
-  const dim3 blk(kThreads);
   const bool rec = ctx->timing_runs < ctx->timing_cap;
   hipEvent_t* ev = rec ? ctx->ev + static_cast<size_t>(ctx->timing_runs) * (kKernels + 1) : nullptr;
   auto mark = [&](int i) {
@@ -695,31 +874,32 @@ hipError_t launch_path(spec_verify_ctx* ctx, const Args& a, hipStream_t st, bool
   if (a.R > 0) {
     const dim3 grid(static_cast<unsigned>(a.R) * a.split);
     if (greedy)
-      hipLaunchKernelGGL((k_rowargmax<T, AL, RG>), grid, blk, 0, st, a);
+      hipLaunchKernelGGL((k_rowargmax<T, AL, RG, AC>), grid, dim3(kThreads), 0, st, a);
     else
-      hipLaunchKernelGGL((k_rowstats<T, AL, RG>), grid, blk, 0, st, a);
+      hipLaunchKernelGGL((k_rowstats<T, AL, RG, AC>), grid, dim3(kThreads), 0, st, a);
   }
   mark(1);
-  const dim3 grid2(static_cast<unsigned>(a.B) * a.nc);
   if (greedy)
-    hipLaunchKernelGGL((k_greedy_chunks<T, AL, RG>), grid2, blk, 0, st, a);
+    hipLaunchKernelGGL((k_greedy_seq<T, AL, RG, AC>), dim3(a.B), dim3(kSeqThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((k_sample_chunks<T, AL, RG>), grid2, blk, 0, st, a);
+    hipLaunchKernelGGL((k_sample_seq<T, AL, RG, AC>), dim3(a.B), dim3(kSeqThreads), 0, st, a);
   mark(2);
-  if (greedy)
-    hipLaunchKernelGGL(k_greedy_finalize, dim3(a.B), dim3(64), 0, st, a);
-  else
-    hipLaunchKernelGGL((k_sample_finalize<T, AL, RG>), dim3(a.B), blk, 0, st, a);
-  mark(3);
   if (rec) ++ctx->timing_runs;
   return hipGetLastError();
+}
+
+template <typename T, bool AL, bool RG>
+hipError_t launch_ac(spec_verify_ctx* ctx, const Args& a, hipStream_t st, bool greedy) {
+  // rows that are not split run their accept test inside the row-statistics kernel
+  return a.split == 1 ? launch_path<T, AL, RG, true>(ctx, a, st, greedy)
+                      : launch_path<T, AL, RG, false>(ctx, a, st, greedy);
 }
 
 template <typename T>
 hipError_t launch_dt(spec_verify_ctx* ctx, const Args& a, hipStream_t st, bool greedy, bool aligned, bool ragged) {
   if (aligned)
-    return ragged ? launch_path<T, true, true>(ctx, a, st, greedy) : launch_path<T, true, false>(ctx, a, st, greedy);
-  return ragged ? launch_path<T, false, true>(ctx, a, st, greedy) : launch_path<T, false, false>(ctx, a, st, greedy);
+    return ragged ? launch_ac<T, true, true>(ctx, a, st, greedy) : launch_ac<T, true, false>(ctx, a, st, greedy);
+  return ragged ? launch_ac<T, false, true>(ctx, a, st, greedy) : launch_ac<T, false, false>(ctx, a, st, greedy);
 }
 
 void free_events(spec_verify_ctx* ctx) {
@@ -733,11 +913,12 @@ void free_events(spec_verify_ctx* ctx) {
   ctx->timing_cap = ctx->timing_runs = 0;
 }
 
-// Row-stats split: aim for >= 2048 workgroups, >= 2048 entries per split.
+// Row-stats split: aim for >= SV_SPLIT_TARGET workgroups with >= SV_SPLIT_MIN_SPAN
+// entries per split.
 void choose_split(int R, int V, int& split, int& span) {
-  int s = R > 0 ? (2048 + R - 1) / R : 1;
+  int s = R > 0 ? (SV_SPLIT_TARGET + R - 1) / R : 1;
   s = s < 1 ? 1 : (s > kMaxSplit ? kMaxSplit : s);
-  const int by_len = (V + 2047) / 2048;
+  const int by_len = (V + SV_SPLIT_MIN_SPAN - 1) / SV_SPLIT_MIN_SPAN;
   if (s > by_len) s = by_len < 1 ? 1 : by_len;
   int sp = (V + s - 1) / s;
   sp = (sp + kGroup - 1) / kGroup * kGroup;
@@ -792,7 +973,8 @@ int spec_verify_create(spec_verify_ctx** out, int device, int vocab, int logits_
                        int max_draft_rows, int max_gamma) {
   if (!out) return SV_EINVAL;
   *out = nullptr;
-  if (vocab < 1 || max_batch < 0 || max_draft_rows < 0 || max_gamma < 0 || max_gamma > kMaxGamma ||
+  if (vocab < 1 || vocab > kMaxVocab || max_batch < 0 || max_draft_rows < 0 || max_gamma < 0 ||
+      max_gamma > kMaxGamma ||
       max_batch > kMaxBatch || (logits_dtype != SV_F32 && logits_dtype != SV_BF16))
     return SV_EINVAL;
   int ndev = 0;
@@ -806,24 +988,22 @@ int spec_verify_create(spec_verify_ctx** out, int device, int vocab, int logits_
   ctx->max_batch = max_batch;
   ctx->max_rows = max_draft_rows;
   ctx->max_gamma = max_gamma;
-  ctx->nc = (vocab + kChunk - 1) / kChunk;
   if (hipDeviceGetAttribute(&ctx->cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) ctx->cus = 256;
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-  const int max_split = (vocab + 2047) / 2048 < kMaxSplit ? (vocab + 2047) / 2048 : kMaxSplit;
+  const int by_len = (vocab + SV_SPLIT_MIN_SPAN - 1) / SV_SPLIT_MIN_SPAN;
+  const int max_split = by_len < kMaxSplit ? by_len : kMaxSplit;
   const size_t n_p1 =
       up(sizeof(RowStat) * static_cast<size_t>(max_draft_rows > 0 ? max_draft_rows : 1) * max_split);
-  const size_t n_cs = up(sizeof(double) * 3 * static_cast<size_t>(max_batch > 0 ? max_batch : 1) * ctx->nc);
-  const size_t n_in = up(sizeof(SeqInfo) * static_cast<size_t>(max_batch > 0 ? max_batch : 1));
+  const size_t n_ac = up(sizeof(int32_t) * static_cast<size_t>(max_draft_rows > 0 ? max_draft_rows : 1));
   const size_t n_er = 256;
-  if (hipMalloc(&ctx->ws, n_p1 + n_cs + n_in + n_er) != hipSuccess) {
+  if (hipMalloc(&ctx->ws, n_p1 + n_ac + n_er) != hipSuccess) {
     delete ctx;
     return SV_ENOMEM;
   }
   char* p = static_cast<char*>(ctx->ws);
   ctx->p1 = reinterpret_cast<RowStat*>(p);
-  ctx->csum = reinterpret_cast<double*>(p + n_p1);
-  ctx->info = reinterpret_cast<SeqInfo*>(p + n_p1 + n_cs);
-  ctx->err = reinterpret_cast<int*>(p + n_p1 + n_cs + n_in);
+  ctx->accept = reinterpret_cast<int32_t*>(p + n_p1);
+  ctx->err = reinterpret_cast<int*>(p + n_p1 + n_ac);
   if (hipMemset(ctx->err, 0, n_er) != hipSuccess) {
     (void)hipFree(ctx->ws);
     delete ctx;
@@ -867,28 +1047,26 @@ int spec_verify_run(spec_verify_ctx* ctx, void* hip_stream, int batch, int gamma
   a.rsum = residual_sum;
   a.pdraft = greedy ? nullptr : p_draft;
   a.p1 = ctx->p1;
-  a.csum = ctx->csum;
-  a.info = ctx->info;
+  a.accept = ctx->accept;
   a.err = ctx->err;
   a.B = batch;
   a.gamma = cu_gamma ? -1 : gamma;
   a.V = ctx->V;
   a.R = total_draft_rows;
-  a.nc = ctx->nc;
   a.max_gamma = ctx->max_gamma;
   choose_split(a.R, a.V, a.split, a.span);
   const unsigned long long max_threads = 1ull << 32;
   if (static_cast<unsigned long long>(a.R) * a.split * kThreads >= max_threads ||
-      static_cast<unsigned long long>(a.B) * a.nc * kThreads >= max_threads) {
+      static_cast<unsigned long long>(a.B) * kSeqThreads >= max_threads) {
     set_msg(ctx->msg, sizeof(ctx->msg), "launch grid too large: reduce the batch");
     return SV_EINVAL;
   }
   if (greedy) {
     a.k2 = 0.f;
-    a.invT = 0.0;
+    a.k2d = 0.0;
   } else {
-    a.invT = 1.0 / static_cast<double>(temperature);
-    a.k2 = static_cast<float>(1.4426950408889634 * a.invT);
+    a.k2d = 1.4426950408889634 / static_cast<double>(temperature);
+    a.k2 = static_cast<float>(a.k2d);
   }
   DeviceGuard guard(ctx->device);
   hipStream_t st = static_cast<hipStream_t>(hip_stream);

@@ -47,6 +47,59 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
   m = M;
 }
 
+// 2^(Z/N) in float64 for Z in units of 1/N octave, N = 2^SV_EXP_LOG2N table entries.
+// With n = rint(Z) = N k + j (0 <= j < N) and f = Z - n (exact, |f| <= 1/2):
+// 2^(Z/N) = 2^k * 2^(j/N) * e^(f c), c = ln2/N, e^(f c) from a short Taylor
+// polynomial: degree 3 for N = 256 (relative error below 1.5e-13), degree 2 for
+// N = 2048 (below 1e-12). rint comes from adding 1.5 * 2^52, whose sum keeps n in
+// its low 32 bits. `tab` holds 2^(j/N). Arguments below -3e8 (and -inf) give 0;
+// results below 2^-1022 come out subnormal.
+#ifndef SV_EXP_LOG2N
+#define SV_EXP_LOG2N 8
+#endif
+constexpr int kExpN = 1 << SV_EXP_LOG2N;
+constexpr double kExpScale = static_cast<double>(kExpN);  // Z = kExpScale * octaves
+
+__device__ __forceinline__ double exp2_tab(double Z, const double* tab) {
+  Z = fmax(Z, -3.0e8);
+  const double t = Z + 6755399441055744.0;
+  const double n = t - 6755399441055744.0;
+  const double f = Z - n;
+#if SV_EXP_LOG2N == 8
+  double p = fma(f, 3.3083026805413713e-09, 3.6655655969101062e-06);  // c^3/6, c^2/2
+  p = fma(f, p, 2.7076061740622863e-03);                              // c
+  p = fma(f, p, 1.0);
+#elif SV_EXP_LOG2N == 11
+  double p = fma(f, 5.7274462451720440e-08, 3.3845077175778579e-04);  // c^2/2, c
+  p = fma(f, p, 1.0);
+#else
+#error "SV_EXP_LOG2N must be 8 or 11"
+#endif
+  const int ni = __double2loint(t);
+  return ldexp(tab[ni & (kExpN - 1)] * p, ni >> SV_EXP_LOG2N);
+}
+
+// Fill tab[0..N-1] with 2^(j/N) (all threads of the block); caller syncs.
+__device__ __forceinline__ void exp_table_init(double* tab) {
+  for (int j = threadIdx.x; j < kExpN; j += blockDim.x) tab[j] = exp2(static_cast<double>(j) / kExpScale);
+}
+
+// Wave-wide max of a float through DPP row permutations and four lane reads (no LDS
+// traffic); the result is wave-uniform.
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  int x = __float_as_int(v);
+  // within rows of 16 lanes: quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false))));
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false))));
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false))));
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x140, 0xF, 0xF, false))));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(x, 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(x, 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(x, 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(x, 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
 // ---------------------------------------------------------------- wave / block reductions
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
@@ -66,8 +119,9 @@ __device__ __forceinline__ int wave_max_int(int v) {
   return v;
 }
 
-// Block-wide sum of N doubles; result valid in every thread. `lds` holds kWaves*N.
-template <int N>
+// Block-wide reductions over NW waves (blockDim.x == 64 * NW); the result is
+// valid in every thread. Each call ends with a barrier, so `lds` may be reused.
+template <int NW, int N>
 __device__ __forceinline__ void block_sum(double (&v)[N], double* lds) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
@@ -81,12 +135,13 @@ __device__ __forceinline__ void block_sum(double (&v)[N], double* lds) {
   for (int i = 0; i < N; ++i) {
     double t = 0.0;
 #pragma unroll
-    for (int k = 0; k < kWaves; ++k) t += lds[k * N + i];
+    for (int k = 0; k < NW; ++k) t += lds[k * N + i];
     v[i] = t;
   }
   __syncthreads();
 }
 
+template <int NW>
 __device__ __forceinline__ float block_max(float v, float* lds) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
@@ -95,11 +150,26 @@ __device__ __forceinline__ float block_max(float v, float* lds) {
   __syncthreads();
   float t = lds[0];
 #pragma unroll
-  for (int k = 1; k < kWaves; ++k) t = fmaxf(t, lds[k]);
+  for (int k = 1; k < NW; ++k) t = fmaxf(t, lds[k]);
   __syncthreads();
   return t;
 }
 
+template <int NW>
+__device__ __forceinline__ double block_max_d(double v, double* lds) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o));
+  if (lane == 0) lds[w] = v;
+  __syncthreads();
+  double t = lds[0];
+#pragma unroll
+  for (int k = 1; k < NW; ++k) t = fmax(t, lds[k]);
+  __syncthreads();
+  return t;
+}
+
+template <int NW>
 __device__ __forceinline__ int block_min_int(int v, int* lds) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   v = wave_min_int(v);
@@ -107,10 +177,12 @@ __device__ __forceinline__ int block_min_int(int v, int* lds) {
   __syncthreads();
   int t = lds[0];
 #pragma unroll
-  for (int k = 1; k < kWaves; ++k) t = min(t, lds[k]);
+  for (int k = 1; k < NW; ++k) t = min(t, lds[k]);
   __syncthreads();
   return t;
 }
+
+template <int NW>
 __device__ __forceinline__ int block_max_int(int v, int* lds) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   v = wave_max_int(v);
@@ -118,27 +190,36 @@ __device__ __forceinline__ int block_max_int(int v, int* lds) {
   __syncthreads();
   int t = lds[0];
 #pragma unroll
-  for (int k = 1; k < kWaves; ++k) t = max(t, lds[k]);
+  for (int k = 1; k < NW; ++k) t = max(t, lds[k]);
   __syncthreads();
   return t;
 }
 
-// Exclusive block scan of one double per thread (thread order); returns the
-// prefix of the threads before this one. `lds` holds kWaves doubles.
-__device__ __forceinline__ double block_excl_scan(double v, double* lds) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+// Exclusive scan of one double per lane within a wave (lane order).
+__device__ __forceinline__ double wave_excl_scan(double v) {
+  const int lane = threadIdx.x & 63;
   double inc = v;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const double n = __shfl_up(inc, o);
     if (lane >= o) inc += n;
   }
-  if (lane == 63) lds[w] = inc;
+  const double prev = __shfl_up(inc, 1);
+  return lane == 0 ? 0.0 : prev;
+}
+
+// Exclusive block scan of one double per thread (thread order); returns the
+// sum of the values of the threads before this one. `lds` holds NW doubles.
+template <int NW>
+__device__ __forceinline__ double block_excl_scan(double v, double* lds) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const double ex = wave_excl_scan(v);
+  if (lane == 63) lds[w] = ex + v;
   __syncthreads();
   double base = 0.0;
   for (int k = 0; k < w; ++k) base += lds[k];
   __syncthreads();
-  return base + inc - v;
+  return base + ex;
 }
 
 // Greedy partial: (value, index) with the larger value winning, lowest index on ties.

@@ -106,3 +106,4 @@ def test_create_rejects_bad_arguments_before_touching_a_device():
     assert out.value is None
     assert lib.spec_verify_create(ctypes.byref(out), 0, 10, 5, 1, 1, 1) == sv.SV_EINVAL
     assert lib.spec_verify_create(ctypes.byref(out), 0, 10, sv.SV_F32, 1, 1, 2000) == sv.SV_EINVAL
+    assert lib.spec_verify_create(ctypes.byref(out), 0, (1 << 24) + 1, sv.SV_F32, 1, 1, 1) == sv.SV_EINVAL
