@@ -151,8 +151,9 @@ void spec_verify_destroy(spec_verify_ctx *ctx);
 
 /*
  * Measurement hook. spec_verify_set_timing(ctx, runs) with runs > 0 makes the
- * next `runs` calls of spec_verify_run record HIP events on their stream around
- * each kernel they launch (runs == 0 switches recording off). It waits for the
+ * next `runs` calls of spec_verify_run launch each kernel with a start and a stop
+ * HIP event (hipExtLaunchKernel), which take that dispatch's own begin and end
+ * timestamps on the launch stream (runs == 0 switches recording off). It waits for the
  * device and allocates the events, so call it outside timed or captured code.
  * spec_verify_kernel_times waits for the last recorded run, writes up to `cap`
  * per-kernel mean durations in ms over the recorded runs and the kernels' names

@@ -35,6 +35,7 @@
 // caches are not coherent for plain stores, and a device-scope fence (L2 write-back
 // and invalidate) per workgroup costs far more than the kernel boundary.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <math.h>
 #include <stdio.h>
@@ -815,6 +816,7 @@ __global__ __launch_bounds__(kSeqThreads) void k_greedy_seq(Args a) {
 
 // ============================================================== host side
 constexpr int kKernels = 2;
+constexpr int kEventsPerRun = 2 * kKernels;
 const char* kKernelNames[2][kKernels] = {
     {"k_rowstats", "k_sample_seq"},
     {"k_rowargmax", "k_greedy_seq"},
@@ -830,7 +832,7 @@ struct spec_verify_ctx {
   int* err = nullptr;
   hipStream_t last_stream = nullptr;
   bool ran = false;
-  // measurement: kKernels + 1 events per recorded run, for up to timing_cap runs
+  // measurement: a start and a stop event per kernel and recorded run, for up to timing_cap runs
   int timing_cap = 0, timing_runs = 0;
   hipEvent_t* ev = nullptr;
   int nk = 0;
@@ -863,27 +865,31 @@ struct DeviceGuard {
   }
 };
 
+// With timing on, each kernel is launched through hipExtLaunchKernel with a start and
+// a stop event, which take the dispatch's own begin / end timestamps (the launch gap
+// between kernels is not counted).
 template <typename T, bool AL, bool RG, bool AC>
 hipError_t launch_path(spec_verify_ctx* ctx, const Args& a, hipStream_t st, bool greedy) {
   const bool rec = ctx->timing_runs < ctx->timing_cap;
-  hipEvent_t* ev = rec ? ctx->ev + static_cast<size_t>(ctx->timing_runs) * (kKernels + 1) : nullptr;
-  auto mark = [&](int i) {
-    if (ev) (void)hipEventRecord(ev[i], st);
+  hipEvent_t* ev = rec ? ctx->ev + static_cast<size_t>(ctx->timing_runs) * kEventsPerRun : nullptr;
+  auto go = [&](const void* fn, dim3 grid, dim3 block, int k) -> hipError_t {
+    void* args[] = {const_cast<Args*>(&a)};
+    return hipExtLaunchKernel(fn, grid, block, args, 0, st, ev ? ev[2 * k] : nullptr,
+                              ev ? ev[2 * k + 1] : nullptr, 0);
   };
-  mark(0);
+  hipError_t e = hipSuccess;
   if (a.R > 0) {
     const dim3 grid(static_cast<unsigned>(a.R) * a.split);
-    if (greedy)
-      hipLaunchKernelGGL((k_rowargmax<T, AL, RG, AC>), grid, dim3(kThreads), 0, st, a);
-    else
-      hipLaunchKernelGGL((k_rowstats<T, AL, RG, AC>), grid, dim3(kThreads), 0, st, a);
+    e = greedy ? go(reinterpret_cast<const void*>(&k_rowargmax<T, AL, RG, AC>), grid, dim3(kThreads), 0)
+               : go(reinterpret_cast<const void*>(&k_rowstats<T, AL, RG, AC>), grid, dim3(kThreads), 0);
+  } else if (ev) {
+    (void)hipEventRecord(ev[0], st);
+    (void)hipEventRecord(ev[1], st);
   }
-  mark(1);
-  if (greedy)
-    hipLaunchKernelGGL((k_greedy_seq<T, AL, RG, AC>), dim3(a.B), dim3(kSeqThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL((k_sample_seq<T, AL, RG, AC>), dim3(a.B), dim3(kSeqThreads), 0, st, a);
-  mark(2);
+  if (e != hipSuccess) return e;
+  e = greedy ? go(reinterpret_cast<const void*>(&k_greedy_seq<T, AL, RG, AC>), dim3(a.B), dim3(kSeqThreads), 1)
+             : go(reinterpret_cast<const void*>(&k_sample_seq<T, AL, RG, AC>), dim3(a.B), dim3(kSeqThreads), 1);
+  if (e != hipSuccess) return e;
   if (rec) ++ctx->timing_runs;
   return hipGetLastError();
 }
@@ -904,7 +910,7 @@ hipError_t launch_dt(spec_verify_ctx* ctx, const Args& a, hipStream_t st, bool g
 
 void free_events(spec_verify_ctx* ctx) {
   if (ctx->ev) {
-    const size_t n = static_cast<size_t>(ctx->timing_cap) * (kKernels + 1);
+    const size_t n = static_cast<size_t>(ctx->timing_cap) * kEventsPerRun;
     for (size_t i = 0; i < n; ++i)
       if (ctx->ev[i]) (void)hipEventDestroy(ctx->ev[i]);
     delete[] ctx->ev;
@@ -1120,7 +1126,7 @@ int spec_verify_set_timing(spec_verify_ctx* ctx, int runs) {
   (void)hipDeviceSynchronize();
   free_events(ctx);
   if (runs == 0) return SV_OK;
-  const size_t n = static_cast<size_t>(runs) * (kKernels + 1);
+  const size_t n = static_cast<size_t>(runs) * kEventsPerRun;
   ctx->ev = new (std::nothrow) hipEvent_t[n]();
   if (!ctx->ev) return SV_ENOMEM;
   ctx->timing_cap = runs;
@@ -1141,14 +1147,14 @@ int spec_verify_kernel_times(spec_verify_ctx* ctx, float* ms, const char** names
   if (ctx->timing_runs == 0) return 0;
   DeviceGuard guard(ctx->device);
   const int R = ctx->timing_runs;
-  hipError_t e = hipEventSynchronize(ctx->ev[static_cast<size_t>(R) * (kKernels + 1) - 1]);
+  hipError_t e = hipEventSynchronize(ctx->ev[static_cast<size_t>(R) * kEventsPerRun - 1]);
   if (e != hipSuccess) return -hip_fail(ctx, "hipEventSynchronize", e);
   for (int k = 0; k < ctx->nk && k < cap; ++k) {
     double sum = 0.0;
     for (int r = 0; r < R; ++r) {
       float t = 0.f;
-      hipEvent_t* ev = ctx->ev + static_cast<size_t>(r) * (kKernels + 1);
-      e = hipEventElapsedTime(&t, ev[k], ev[k + 1]);
+      hipEvent_t* ev = ctx->ev + static_cast<size_t>(r) * kEventsPerRun;
+      e = hipEventElapsedTime(&t, ev[2 * k], ev[2 * k + 1]);
       if (e != hipSuccess) return -hip_fail(ctx, "hipEventElapsedTime", e);
       sum += t;
     }
