@@ -33,19 +33,22 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def step_bytes(w, n):
-    """Algorithmic bytes of one step from this run's accepted counts n (the two-pass
-    method's minimum: every judged row once, the drawn row once, the rejected
-    position's q row once, plus the small per-position reads and outputs)."""
+def step_bytes(w, n, stop_at_rejection):
+    """Algorithmic bytes of one step from this run's accepted counts n: the judged
+    rows once (with `stop_at_rejection`, rows 0..min(n, gamma - 1) of each sequence,
+    the rows the left-to-right verification looks at; otherwise all gamma rows), the
+    drawn row once, the rejected position's q row once, plus the per-position reads
+    (id, uniform, q(x)) and the outputs."""
     import numpy as np
     sl = 2 if w.dtype == "bf16" else 4
     g = w.gammas.astype(np.int64)
     n = n.astype(np.int64)
+    rows = np.minimum(n + 1, g) if stop_at_rejection else g
+    outputs = 4 + (g + 1) * 4 + (4 if w.T > 0 else 0)
     if w.T == 0.0:
-        per = g * w.V * sl + (n == g) * w.V * sl + g * 4 + 4 + (g + 1) * 4 + 4
+        per = rows * w.V * sl + (n == g) * w.V * sl + g * 4 + outputs
     else:
-        per = (g * w.V * sl + w.V * sl + (n < g) * w.V * 4 + g * (4 + 4) + (g + 1) * 4
-               + 4 + (g + 1) * 4 + 4)
+        per = rows * w.V * sl + w.V * sl + (n < g) * w.V * 4 + g * 12 + 4 + outputs
     return int(per.sum())
 
 
@@ -83,6 +86,8 @@ def main():
     ap.add_argument("--sets", type=int, default=2, help="input sets rotated across steps")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--plan", choices=("auto", "two", "one"), default="auto",
+                    help="launch plan (auto: one launch when B >= the number of compute units)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run plain device copies of MIB MiB (calibrates the HBM byte counters)")
     args = ap.parse_args()
@@ -134,6 +139,7 @@ def main():
     ragged = w0.uniform_gamma is None
     code = sv.SV_BF16 if w0.dtype == "bf16" else sv.SV_F32
     ver = sv.Verifier(w0.V, code, w0.B, max(w.draft_rows for w, _ in sets), 16)
+    ver.set_path({"auto": sv.SV_PATH_AUTO, "two": sv.SV_PATH_TWO_LAUNCH, "one": sv.SV_PATH_ONE_LAUNCH}[args.plan])
 
     outs = []
     for w, d in sets:
@@ -158,7 +164,8 @@ def main():
         torch.cuda.synchronize()
         assert ver.status() == sv.SV_OK, ver.last_error()
         nb.append(outs[k].accepted_count.cpu().numpy())
-    bytes_per_set = [step_bytes(w, n) for (w, _), n in zip(sets, nb)]
+    one_launch = ver.last_path() == sv.SV_PATH_ONE_LAUNCH  # stops reading rows at the first rejection
+    bytes_per_set = [step_bytes(w, n, one_launch) for (w, _), n in zip(sets, nb)]
 
     for k in range(args.warmup):
         step(k)
@@ -183,10 +190,15 @@ def main():
     path_bytes = float(np.mean([bytes_per_set[k % len(sets)] for k in range(args.steps)]))
     path_gbps = path_bytes / (ms * 1e-3) / 1e9
 
+    # the roofline is taken on the kernel that moves the most bytes: the whole step
+    # when it is one launch, else the row-statistics pass
     kt = dict(ktimes)
     k1 = ktimes[0][0]
     sl = 2 if w0.dtype == "bf16" else 4
-    k1_bytes = float(np.mean([w.draft_rows * (w.V * sl + 8) for w, _ in sets]))
+    if one_launch:
+        k1_bytes = path_bytes
+    else:
+        k1_bytes = float(np.mean([w.draft_rows * (w.V * sl + 8) for w, _ in sets]))
     k1_gbps = k1_bytes / (kt[k1] * 1e-3) / 1e9
 
     # acceptance metrics of the measured inputs
@@ -224,6 +236,7 @@ def main():
         "roofline": {
             "bound": "hbm",
             "kernel": k1,
+            "bytes_per_launch": k1_bytes,
             "achieved": k1_gbps,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
@@ -231,6 +244,7 @@ def main():
             "traffic": None,
         },
         "path": {
+            "plan": "one launch, stops reading rows at the first rejection" if one_launch else "two launches",
             "algorithmic_bytes_per_step": path_bytes,
             "achieved_GBps": path_gbps,
             "frac_of_peak": path_gbps / HBM_PEAK_GBPS,

@@ -137,6 +137,26 @@ int spec_verify_run(spec_verify_ctx *ctx, void *hip_stream, int batch, int gamma
                     float *residual_sum, float *p_draft);
 
 /*
+ * Launch plan. A run either takes two launches (row statistics of every draft row,
+ * then one workgroup per sequence for the first-rejection scan and the draw) or
+ * one launch (one workgroup per sequence that judges its rows left to right,
+ * stops reading at the first rejection and then draws). The one-launch plan needs
+ * T > 0, V a multiple of 8, 16-byte aligned logits and q, gamma_b <= 64 (for
+ * ragged runs: the context's max_gamma <= 64) and, under SV_PATH_AUTO, at least as
+ * many sequences as the device has compute units. With p_draft requested it still
+ * reads every row. Both plans return the same outputs.
+ *   spec_verify_set_path(ctx, mode): SV_PATH_AUTO (default), SV_PATH_TWO_LAUNCH, or
+ *     SV_PATH_ONE_LAUNCH (taken whenever the run allows it, whatever B). Returns
+ *     SV_OK or SV_EINVAL (NULL ctx, unknown mode).
+ *   spec_verify_last_path(ctx): the plan of the last successful run
+ *     (SV_PATH_TWO_LAUNCH or SV_PATH_ONE_LAUNCH), SV_PATH_AUTO if none yet, or
+ *     -SV_EINVAL for a NULL ctx.
+ */
+enum { SV_PATH_AUTO = 0, SV_PATH_TWO_LAUNCH = 1, SV_PATH_ONE_LAUNCH = 2 };
+int spec_verify_set_path(spec_verify_ctx *ctx, int mode);
+int spec_verify_last_path(const spec_verify_ctx *ctx);
+
+/*
  * Synchronize the stream of the last run, read and clear the device's sticky
  * data-error flag. Returns SV_OK, SV_EDATA (details in spec_verify_last_error),
  * SV_EHIP, or SV_EINVAL for a NULL ctx.

@@ -18,13 +18,15 @@ LIB_PATH = os.path.join(PKG, "libspecverify.so")
 SV_OK, SV_EINVAL, SV_ENOMEM, SV_EHIP, SV_EDATA = 0, 1, 2, 3, 4
 SV_F32, SV_BF16 = 0, 1
 SV_DATA_DRAFT_ID, SV_DATA_NONFINITE, SV_DATA_UNIFORM, SV_DATA_CU_GAMMA = 1, 2, 4, 8
+SV_PATH_AUTO, SV_PATH_TWO_LAUNCH, SV_PATH_ONE_LAUNCH = 0, 1, 2
 _CODE_NAMES = {SV_OK: "SV_OK", SV_EINVAL: "SV_EINVAL", SV_ENOMEM: "SV_ENOMEM",
                SV_EHIP: "SV_EHIP", SV_EDATA: "SV_EDATA"}
 
 EXPORTED = (
     "spec_verify_create", "spec_verify_run", "spec_verify_status",
     "spec_verify_last_error", "spec_verify_destroy", "spec_verify_set_timing",
-    "spec_verify_kernel_times", "spec_verify_check_args",
+    "spec_verify_kernel_times", "spec_verify_check_args", "spec_verify_set_path",
+    "spec_verify_last_path",
 )
 
 
@@ -65,6 +67,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.spec_verify_kernel_times.restype = i32
     lib.spec_verify_check_args.argtypes = [i32] * 9 + [f32] + [i32] * 7 + [ctypes.c_char_p, i32]
     lib.spec_verify_check_args.restype = i32
+    lib.spec_verify_set_path.argtypes = [vp, i32]
+    lib.spec_verify_set_path.restype = i32
+    lib.spec_verify_last_path.argtypes = [vp]
+    lib.spec_verify_last_path.restype = i32
     if path is None:
         _lib = lib
     return lib
@@ -162,3 +168,18 @@ def spec_verify_check_args(vocab, logits_dtype, max_batch, max_draft_rows, max_g
         int(bool(has_draft_ids)), int(bool(has_uniforms)), int(bool(has_accepted_count)),
         int(bool(has_emitted_tokens)), int(bool(has_residual_sum)), buf, len(buf))
     return rc, buf.value.decode()
+
+
+def spec_verify_set_path(ctx: int, mode: int) -> None:
+    """Choose the launch plan: SV_PATH_AUTO, SV_PATH_TWO_LAUNCH or SV_PATH_ONE_LAUNCH."""
+    rc = load_library().spec_verify_set_path(ctx, int(mode))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, f"unknown path mode {mode}" if ctx else "NULL context")
+
+
+def spec_verify_last_path(ctx: int) -> int:
+    """The launch plan of the last successful run (SV_PATH_AUTO if none yet)."""
+    rc = load_library().spec_verify_last_path(ctx)
+    if rc < 0:
+        raise SpecVerifyError(-rc, "NULL context")
+    return rc

@@ -89,6 +89,9 @@ struct Args {
   int B, gamma, V, R, split, span, max_gamma;
   float k2;        // log2(e) / T, fp32
   double k2d;      // log2(e) / T, fp64
+  // bf16 value table of the one-launch path: magnitudes (bit patterns without the sign)
+  // tlo..thi, thi < 0x7F80; tlo > thi when the table is not used
+  int tlo, thi;
 };
 
 __device__ __forceinline__ bool finite_pos(float z) { return z > 0.f && z <= FLT_MAX; }
@@ -122,8 +125,8 @@ __device__ __forceinline__ void lse2_merge(float& c, float& z, float c2, float z
 // 지킨다"; [P3] 단계 3): p(x) = 2^(l_x k2 - c) / z in fp64 (the same normaliser as
 // the row statistics), thr = 1 if p(x) >= q(x) else p(x) / q(x), accept iff u < thr.
 // An id outside [0, V) rejects; data errors raise the sticky flag.
-__device__ __forceinline__ bool accept_test(int x, float lx, float qx, float uu, float c, float z,
-                                            const Args& a, double& px) {
+__device__ __forceinline__ bool accept_decision(int x, float lx, float qx, float uu, float c, float z,
+                                                const Args& a, double& px, bool flag_errors) {
   px = __builtin_nan("");
   bool acc = false;
   if (x >= 0 && x < a.V) {
@@ -132,12 +135,16 @@ __device__ __forceinline__ bool accept_test(int x, float lx, float qx, float uu,
     const double qd = qx;
     const double thr = px >= qd ? 1.0 : px / qd;  // no division when p >= q
     acc = static_cast<double>(uu) < thr;         // strict
-    if (!(uu >= 0.f && uu < 1.f)) atomicOr(a.err, SV_DATA_UNIFORM);
-  } else {
+    if (flag_errors && !(uu >= 0.f && uu < 1.f)) atomicOr(a.err, SV_DATA_UNIFORM);
+  } else if (flag_errors) {
     atomicOr(a.err, SV_DATA_DRAFT_ID);
   }
-  if (!(finite_pos(z) && finite_f(c))) atomicOr(a.err, SV_DATA_NONFINITE);
+  if (flag_errors && !(finite_pos(z) && finite_f(c))) atomicOr(a.err, SV_DATA_NONFINITE);
   return acc;
+}
+__device__ __forceinline__ bool accept_test(int x, float lx, float qx, float uu, float c, float z,
+                                            const Args& a, double& px) {
+  return accept_decision(x, lx, qx, uu, c, z, a, px, true);
 }
 
 // ============================================================== step 1
@@ -445,39 +452,30 @@ __device__ __forceinline__ int region_width(int V) {
   return (per + kRing * kIter - 1) / (kRing * kIter) * (kRing * kIter);
 }
 
-template <typename T, bool ALIGNED, bool RAGGED, bool ACCEPT>
-__global__ __launch_bounds__(kSeqThreads) void k_sample_seq(Args a) {
-  __shared__ double s_tab[kExpN];
-  __shared__ float2 s_cz[kMaxGamma];
+// The draw that ends a sequence's round ([P1] ch.2-3; [P2] "미리 그려놓고 한 번에 검증한다";
+// [P3] 단계 3): after a rejection at n < g, one token from norm(max(0, p_n - q_n)); when
+// all g drafts were accepted, the bonus token from p_g. Writes emitted[n], the -1
+// padding after it and residual_sum[b]. For a residual, row n's statistics come in as
+// a reference cref (in octaves) and Zq = sum 2^(l k2 - cref) over the row, exact or
+// fp32-rounded (unused for the bonus). Every thread of the block calls it; s_tab holds
+// the exp2_tab table.
+template <typename T, bool ALIGNED>
+__device__ __forceinline__ void final_draw(const Args& a, int b, int base, int g, int n, double cref,
+                                           double Zq_in, const double* s_tab) {
   __shared__ double s_reg[kSeqWaves][3];  // residual: (D, Q, Zr); bonus: (m, s, -)
   __shared__ double s_wt[kSeqWaves];      // re-sweep: per-wave totals of a pass
   __shared__ int s_wc[kSeqWaves], s_wl[kSeqWaves];
-  __shared__ int s_n;
   __shared__ double s_bc[6];  // search result: t, P (prefix before the region), Z64, delta, S, ref
   __shared__ int s_bi[3];     // search result: region r*, kind, take_last
-  const int b = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar
-  int base, g;
-  if (!seq_geom<RAGGED>(a, b, base, g)) {
-    if (threadIdx.x == 0) {
-      atomicOr(a.err, SV_DATA_CU_GAMMA);
-      a.acc[b] = -1;
-    }
-    return;
-  }
-  exp_table_init(s_tab);
-  const int n = first_rejection<T, ACCEPT, false>(a, b, base, g, s_cz, nullptr, &s_n);
-  for (int i = threadIdx.x; i < n; i += kSeqThreads) a.emitted[base + b + i] = a.ids[base + i];
-  if (threadIdx.x == 0) a.acc[b] = n;
-
   const int V = a.V;
   const bool residual = n < g;
   const T* lrow = static_cast<const T*>(a.logits) + static_cast<size_t>(base + b + (residual ? n : g)) * V;
   const float* qrow = residual ? a.q + static_cast<size_t>(base + n) * V : nullptr;
   const double KN = kExpScale * a.k2d;  // exp2_tab(l KN - N c) = 2^(l k2 - c)
-  const float cr = residual ? s_cz[n].x : 0.f;
-  const double Zq = residual ? static_cast<double>(s_cz[n].y) : 0.0;
+  const double cr = residual ? cref : 0.0;
+  const double Zq = residual ? Zq_in : 0.0;
   const int rw = region_width(V);
   const int r0 = min(V, wave * rw), r1 = min(V, r0 + rw);
   // whole iterations are read without checks (only possible when aligned); the rest, masked
@@ -488,7 +486,7 @@ __global__ __launch_bounds__(kSeqThreads) void k_sample_seq(Args a) {
   // ---- one fp64 sweep of this wave's region through a ring of kRing register buffers
   if (residual) {
     // residual max(0, p - q) ([P1] ch.3; [P3] 단계 3), normalisation deferred
-    const double CN = kExpScale * static_cast<double>(cr);
+    const double CN = kExpScale * cr;
     double D = 0.0, Zr = 0.0;
     float Q = 0.f;
     auto step = [&](const Raw<T>& lr, const Raw<float>& qr) {
@@ -613,7 +611,7 @@ __global__ __launch_bounds__(kSeqThreads) void k_sample_seq(Args a) {
       kind = S > 0.0 ? 0 : 1;
       if (kind == 1) wgt = live ? s_reg[r][2] : 0.0;
       t = kind == 0 ? u * S : u * Z64;
-      ref = kExpScale * static_cast<double>(cr);
+      ref = kExpScale * cr;
     } else {
       double M = live ? s_reg[r][0] : -INFINITY;
 #pragma unroll
@@ -728,6 +726,533 @@ __global__ __launch_bounds__(kSeqThreads) void k_sample_seq(Args a) {
   for (int i = n + 1 + threadIdx.x; i <= g; i += kSeqThreads) a.emitted[base + b + i] = -1;
 }
 
+template <typename T, bool ALIGNED, bool RAGGED, bool ACCEPT>
+__global__ __launch_bounds__(kSeqThreads) void k_sample_seq(Args a) {
+  __shared__ double s_tab[kExpN];
+  __shared__ float2 s_cz[kMaxGamma];
+  __shared__ int s_n;
+  const int b = blockIdx.x;
+  int base, g;
+  if (!seq_geom<RAGGED>(a, b, base, g)) {
+    if (threadIdx.x == 0) {
+      atomicOr(a.err, SV_DATA_CU_GAMMA);
+      a.acc[b] = -1;
+    }
+    return;
+  }
+  exp_table_init(s_tab);
+  const int n = first_rejection<T, ACCEPT, false>(a, b, base, g, s_cz, nullptr, &s_n);
+  for (int i = threadIdx.x; i < n; i += kSeqThreads) a.emitted[base + b + i] = a.ids[base + i];
+  if (threadIdx.x == 0) a.acc[b] = n;
+  final_draw<T, ALIGNED>(a, b, base, g, n, n < g ? static_cast<double>(s_cz[n].x) : 0.0,
+                         n < g ? static_cast<double>(s_cz[n].y) : 0.0, s_tab);
+}
+
+// ============================================================== one-launch path
+// One workgroup per sequence does the whole round. Pass 1 reads the draft rows in
+// order and judges each as soon as its statistics are complete: the verification
+// runs left to right and stops at the first rejection ([P2] "미리 그려놓고 한 번에
+// 검증한다"; [P4] "이득의 크기는 두 숫자가 정한다"), so rows after it are not read
+// (all rows are, when p(x) is requested for every draft). The 16 waves walk each row
+// front to back in 512-entry chunks (wave w takes chunks w, w + 16, ...), through a
+// register ring that runs on into the next row while a row is being judged. At a row
+// end every wave merges the 16 partial (c, z) from LDS and runs the accept test itself
+// (lane i holds row i's operands), so all waves reach the same decision without a
+// second barrier. Pass 2 is final_draw.
+constexpr int kFuseMaxGamma = 64;  // lane i judges row i
+
+// One chunk of the row statistics: lanes whose group lies past the row (the partial
+// last chunk; their load was clamped onto the row's last group) count with weight 0,
+// which leaves the max unchanged too (that group is part of the row).
+template <typename T>
+__device__ __forceinline__ void stats_step(const Raw<T>& lr, float wgt, float k2, float& m, float& c,
+                                           float (&sacc)[kGroup]) {
+  float xv[kGroup];
+  unpack(lr, xv);
+  float bm = xv[0];
+#pragma unroll
+  for (int j = 1; j < kGroup; ++j) bm = fmaxf(bm, xv[j]);
+  if (bm > m) {  // new running max: rebase the partial sums
+    const float cn = fmaxf(bm * k2, -FLT_MAX);
+    const float sc = fast_exp2(c - cn);
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) sacc[j] *= sc;
+    m = bm;
+    c = cn;
+  }
+#pragma unroll
+  for (int j = 0; j < kGroup; ++j) sacc[j] = fmaf(wgt, fast_exp2(fmaf(xv[j], k2, -c)), sacc[j]);
+}
+
+// Walks the sequence's rows 0, 1, ... (row i at Lseq + i V) chunk by chunk: wave w takes
+// chunks w, w + kSeqWaves, ... of 512 entries; nitp, the chunk steps per row, is a
+// multiple of kRing so every row starts at ring slot 0, and the ring's loads run on
+// into the next row while row_end(i) judges row i. step(buf, ch, wgt) gets the chunk
+// index and weight 1 or 0 (0: the lane's group lies past the row and its load was
+// clamped onto the row's last group). after_prologue() runs once the first loads are
+// in flight. row_end(i) returns true to stop.
+template <typename T, typename Pro, typename Step, typename RowEnd>
+__device__ __forceinline__ void walk_rows(const T* Lseq, int V, int g, Pro&& after_prologue, Step&& step,
+                                          RowEnd&& row_end) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nch = (V + kIter - 1) / kIter;
+  const int nitp = ((nch + kSeqWaves - 1) / kSeqWaves + kRing - 1) / kRing * kRing;
+  const int total = g * nitp;
+  Raw<T> Lb[kRing];
+  int jl = 0, il = 0, kl = 0;  // next (flattened) iteration to load: row il, step kl
+  auto issue = [&](Raw<T>& dst) {
+    const int e = min((kl * kSeqWaves + wave) * kIter + lane * kGroup, V - kGroup);
+    load_raw_in(Lseq + static_cast<size_t>(il) * V, e, dst);
+    if (jl < total - 1) {
+      ++jl;
+      if (++kl == nitp) {
+        kl = 0;
+        ++il;
+      }
+    }
+  };
+#pragma unroll
+  for (int k = 0; k < kRing - 1; ++k) {
+    issue(Lb[k]);
+    issue_order_fence();
+  }
+  after_prologue();
+  for (int i = 0; i < g; ++i) {
+    for (int k0 = 0; k0 < nitp; k0 += kRing) {
+#pragma unroll
+      for (int r = 0; r < kRing; ++r) {
+        issue(Lb[(r + kRing - 1) % kRing]);
+        const int ch = (k0 + r) * kSeqWaves + wave;
+        if (ch < nch) step(Lb[r], ch, ch * kIter + lane * kGroup < V);
+      }
+    }
+    if (row_end(i)) break;
+  }
+}
+
+// ---- bf16 value table: 2^(x k2) in fp64 for every bf16 x whose magnitude bits lie in
+// [tlo, thi] (|x k2| < 990), both signs: entry 2 (mag - tlo) + sign. Magnitudes below tlo
+// use the tlo entry (|x| below 2^-40 of the window top: relative error under 3e-12);
+// above thi (and inf / NaN) a lookup is flagged and the exp2_tab path takes over.
+constexpr int kTabBinades = 48;
+constexpr int kTabEntries = 2 * kTabBinades * 128;
+
+__device__ __forceinline__ double tab_lookup(uint32_t mag, uint32_t sgn, const double* sT, uint32_t tlo,
+                                             uint32_t thi) {
+  return sT[2 * (min(max(mag, tlo), thi) - tlo) + sgn];
+}
+// Fills sT. Within a binade the 128 values of x form an arithmetic sequence, so their
+// 2^(x k2) form a geometric one: each of 768 threads takes 16 consecutive entries of one
+// (binade, sign), computes the first with exp2 and steps by R = 2^(dx k2) (relative error
+// under 16 * 2^-52 + the exp2 error). The caller syncs before the first lookup.
+constexpr int kTabPiece = 16;
+static_assert(2 * kTabBinades * (128 / kTabPiece) <= kSeqThreads, "one table piece per thread");
+__device__ __forceinline__ void tab_build(double* sT, const Args& a) {
+  const int t = threadIdx.x;
+  const int h = t / (128 / kTabPiece), m0 = (t % (128 / kTabPiece)) * kTabPiece;
+  const int be_lo = a.tlo >> 7, nb = ((a.thi + 1) >> 7) - be_lo;
+  if (h < 2 * nb) {
+    const int be = be_lo + (h >> 1);
+    const double sgn = (h & 1) ? -1.0 : 1.0;
+    // x = 2^(be - 127) (1 + m / 128) for be >= 1; subnormal binade: x = m 2^-133
+    const double x0 = be >= 1 ? ldexp(1.0, be - 127) : 0.0;
+    const double dx = ldexp(1.0, (be >= 1 ? be : 1) - 127 - 7);
+    double v = exp2(sgn * (x0 + m0 * dx) * a.k2d);
+    const double R = exp2(sgn * dx * a.k2d);
+    double* dst = sT + 2 * (be * 128 + m0 - a.tlo) + (h & 1);
+#pragma unroll
+    for (int m = 0; m < kTabPiece; ++m) {
+      dst[2 * m] = v;
+      v *= R;
+    }
+  }
+}
+
+// The draw through the value table (bf16 rows): the same arithmetic as final_draw with
+// e = 2^(l k2) looked up instead of computed (reference 0); the residual's Zq comes in
+// on that scale. Returns false, having written nothing, when the drawn row holds a value
+// outside the table; the caller then runs final_draw.
+__device__ __forceinline__ bool final_draw_tab(const Args& a, int b, int base, int g, int n, double Zq,
+                                               const double* sT) {
+  __shared__ double s_reg[kSeqWaves][3];  // residual: (D, Q, Zr); bonus: (s, -, -)
+  __shared__ uint32_t s_mx[kSeqWaves];
+  __shared__ double s_wt[kSeqWaves];
+  __shared__ int s_wc[kSeqWaves], s_wl[kSeqWaves];
+  __shared__ double s_bc[5];  // t, P (prefix before the region), Z64, delta, S
+  __shared__ int s_bi[4];     // region r*, kind, take_last, ok
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int V = a.V;
+  const uint32_t tlo = a.tlo, thi = a.thi;
+  const bool residual = n < g;
+  const uint16_t* lrow =
+      static_cast<const uint16_t*>(a.logits) + static_cast<size_t>(base + b + (residual ? n : g)) * V;
+  const float* qrow = residual ? a.q + static_cast<size_t>(base + n) * V : nullptr;
+  const int rw = region_width(V);
+  const int r0 = min(V, wave * rw), r1 = min(V, r0 + rw);
+  const int nfull = (r1 - r0) / kIter;
+  const int mstart = r0 + nfull * kIter;
+  uint32_t mx = 0;
+  // the 8 table values of one group of raw bf16 words
+  auto lookup8 = [&](const Raw<uint16_t>& lr, double (&e)[kGroup]) {
+    const uint32_t w[4] = {lr.v[0].x, lr.v[0].y, lr.v[0].z, lr.v[0].w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t ml = w[k] & 0x7FFFu, mh = (w[k] >> 16) & 0x7FFFu;
+      mx = max(mx, max(ml, mh));
+      e[2 * k] = tab_lookup(ml, (w[k] >> 15) & 1u, sT, tlo, thi);
+      e[2 * k + 1] = tab_lookup(mh, w[k] >> 31, sT, tlo, thi);
+    }
+  };
+  if (residual) {
+    // residual max(0, p - q) ([P1] ch.3; [P3] 단계 3), normalisation deferred as in final_draw
+    double D = 0.0, Zr = 0.0;
+    float Q = 0.f;
+    auto step = [&](const Raw<uint16_t>& lr, const Raw<float>& qr) {
+      float qv[kGroup];
+      unpack(qr, qv);
+      double e[kGroup];
+      lookup8(lr, e);
+#pragma unroll
+      for (int j = 0; j < kGroup; ++j) {
+        const double w = fma(-static_cast<double>(qv[j]), Zq, e[j]);
+        D += fmax(w, 0.0);
+        Q += w > 0.0 ? qv[j] : 0.f;
+        Zr += e[j];
+      }
+    };
+    if (nfull > 0) {
+      Raw<uint16_t> Lb[kRing];
+      Raw<float> Qb[kRing];
+      const int eb = r0 + lane * kGroup, last = nfull - 1;
+      auto at = [&](int it) { return eb + min(it, last) * kIter; };
+#pragma unroll
+      for (int k = 0; k < kRing - 1; ++k) {
+        load_raw_in(lrow, at(k), Lb[k]);
+        load_raw_in(qrow, at(k), Qb[k]);
+        issue_order_fence();
+      }
+      for (int it = 0; it < nfull; it += kRing) {
+#pragma unroll
+        for (int k = 0; k < kRing; ++k) {
+          const int nb = (k + kRing - 1) % kRing;
+          load_raw_in(lrow, at(it + k + kRing - 1), Lb[nb]);
+          load_raw_in(qrow, at(it + k + kRing - 1), Qb[nb]);
+          if (k == 0 || it + k < nfull) step(Lb[k], Qb[k]);
+        }
+      }
+    }
+    for (int e0 = mstart; e0 < r1; e0 += kIter) {  // the rest of the region; lanes past r1 idle
+      Raw<uint16_t> lr;
+      Raw<float> qr;
+      const int e = e0 + lane * kGroup;
+      load_raw_in(lrow, min(e, r1 - kGroup), lr);
+      load_raw_in(qrow, min(e, r1 - kGroup), qr);
+      if (e < r1) step(lr, qr);
+    }
+    D = wave_sum(D);
+    Zr = wave_sum(Zr);
+    Q = wave_sum(Q);
+    if (lane == 0) {
+      s_reg[wave][0] = D;
+      s_reg[wave][1] = Q;
+      s_reg[wave][2] = Zr;
+    }
+  } else {
+    // bonus row ([P1] ch.2; [P3] 단계 3): sum of 2^(l k2), no running max needed
+    double sacc = 0.0;
+    auto step = [&](const Raw<uint16_t>& lr) {
+      double e[kGroup];
+      lookup8(lr, e);
+      sacc += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+    };
+    if (nfull > 0) {
+      Raw<uint16_t> Lb[kRing];
+      const int eb = r0 + lane * kGroup, last = nfull - 1;
+      auto at = [&](int it) { return eb + min(it, last) * kIter; };
+#pragma unroll
+      for (int k = 0; k < kRing - 1; ++k) {
+        load_raw_in(lrow, at(k), Lb[k]);
+        issue_order_fence();
+      }
+      for (int it = 0; it < nfull; it += kRing) {
+#pragma unroll
+        for (int k = 0; k < kRing; ++k) {
+          load_raw_in(lrow, at(it + k + kRing - 1), Lb[(k + kRing - 1) % kRing]);
+          if (k == 0 || it + k < nfull) step(Lb[k]);
+        }
+      }
+    }
+    for (int e0 = mstart; e0 < r1; e0 += kIter) {
+      Raw<uint16_t> lr;
+      const int e = e0 + lane * kGroup;
+      load_raw_in(lrow, min(e, r1 - kGroup), lr);
+      if (e < r1) step(lr);
+    }
+    sacc = wave_sum(sacc);
+    if (lane == 0) {
+      s_reg[wave][0] = sacc;
+      s_reg[wave][1] = 0.0;
+      s_reg[wave][2] = 0.0;
+    }
+  }
+  mx = static_cast<uint32_t>(wave_max_int(static_cast<int>(mx)));
+  if (lane == 0) s_mx[wave] = mx;
+  __syncthreads();
+
+  // ---- totals and the region where the inclusive prefix first exceeds t
+  const float uf = a.u[base + b + g];
+  if (wave == 0) {
+    const double u = uf;
+    const int r = lane < kSeqWaves ? lane : 0;
+    const bool live = lane < kSeqWaves;
+    const bool ok = __ballot(live && s_mx[r] > thi) == 0;
+    int kind;  // 0: residual; 1: degenerate residual (S <= 0), draw from p; 2: bonus from p
+    double Z64, S = 0.0, delta = 0.0, t, wgt;
+    if (residual) {
+      Z64 = wave_sum(live ? s_reg[r][2] : 0.0);
+      delta = (Z64 - Zq) / Z64;
+      wgt = live ? s_reg[r][0] / Z64 - s_reg[r][1] * delta : 0.0;
+      S = wave_sum(wgt);
+      kind = S > 0.0 ? 0 : 1;
+      if (kind == 1) wgt = live ? s_reg[r][2] : 0.0;
+      t = kind == 0 ? u * S : u * Z64;
+    } else {
+      wgt = live ? s_reg[r][0] : 0.0;
+      Z64 = wave_sum(wgt);
+      kind = 2;
+      t = u * Z64;
+    }
+    const double ex = wave_excl_scan(wgt);
+    const unsigned long long cross = __ballot(live && ex + wgt > t);
+    int rs = cross ? __ffsll(cross) - 1 : -1;
+    double P = __shfl(ex, rs < 0 ? 0 : rs);
+    int take_last = 0;
+    if (rs < 0) {  // no crossing (rounding, or u >= 1): last positive-weight token
+      take_last = 1;
+      const unsigned long long pos = __ballot(live && wgt > 0.0);
+      rs = pos ? 63 - __clzll(pos) : -1;
+      P = 0.0;
+    }
+    if (lane == 0) {
+      s_bc[0] = t;
+      s_bc[1] = P;
+      s_bc[2] = Z64;
+      s_bc[3] = delta;
+      s_bc[4] = S;
+      s_bi[0] = rs;
+      s_bi[1] = kind;
+      s_bi[2] = take_last;
+      s_bi[3] = ok ? 1 : 0;
+    }
+  }
+  __syncthreads();
+  if (!s_bi[3]) return false;
+  if (threadIdx.x == 0) {
+    if (!(s_bc[2] > 0.0 && s_bc[2] <= DBL_MAX)) atomicOr(a.err, SV_DATA_NONFINITE);
+    if (!(uf >= 0.f && uf < 1.f)) atomicOr(a.err, SV_DATA_UNIFORM);
+  }
+  const double t = s_bc[0], Z64 = s_bc[2], delta = s_bc[3], S = s_bc[4];
+  const int rs = s_bi[0], kind = s_bi[1];
+  const bool take_last = s_bi[2] != 0;
+
+  // ---- re-sweep of region r* in passes of kPass entries (as in final_draw)
+  int tok = V - 1;
+  if (rs >= 0) {
+    const int R0 = min(V, rs * rw), R1 = min(V, R0 + rw);
+    const double invZ = 1.0 / Z64;
+    double run = s_bc[1];
+    int cand = INT_MAX, lastpos = -1;
+    for (int p0 = R0; p0 < R1 && cand == INT_MAX; p0 += kPass) {
+      const int e = p0 + wave * kIter + lane * kGroup;
+      const bool in = e < R1;
+      Raw<uint16_t> lr;
+      load_raw_in(lrow, min(e, R1 - kGroup), lr);
+      float qv[kGroup];
+      if (kind == 0) {
+        Raw<float> qr;
+        load_raw_in(qrow, min(e, R1 - kGroup), qr);
+        unpack(qr, qv);
+      }
+      double ev[kGroup];
+      lookup8(lr, ev);
+      double rv[kGroup];
+      double tot = 0.0;
+#pragma unroll
+      for (int j = 0; j < kGroup; ++j) {
+        double wv = ev[j];
+        if (kind == 0) {
+          const double w = fma(-static_cast<double>(qv[j]), Zq, ev[j]);
+          wv = w > 0.0 ? w * invZ - static_cast<double>(qv[j]) * delta : 0.0;
+        }
+        rv[j] = in ? wv : 0.0;
+        tot += rv[j];
+      }
+      const double lex = wave_excl_scan(tot);
+      if (lane == 63) s_wt[wave] = lex + tot;
+      __syncthreads();
+      double acc = run;
+      for (int w2 = 0; w2 < wave; ++w2) acc += s_wt[w2];
+      acc += lex;
+      int c2 = INT_MAX, lp = -1;
+#pragma unroll
+      for (int j = 0; j < kGroup; ++j) {
+        acc += rv[j];
+        if (!take_last && c2 == INT_MAX && acc > t) c2 = e + j;
+        if (rv[j] > 0.0) lp = e + j;
+      }
+      c2 = wave_min_int(c2);
+      lp = wave_max_int(lp);
+      if (lane == 0) {
+        s_wc[wave] = c2;
+        s_wl[wave] = lp;
+      }
+      __syncthreads();
+      int cm = INT_MAX, lm = -1;
+      double tsum = run;
+      for (int w2 = 0; w2 < kSeqWaves; ++w2) {
+        cm = min(cm, s_wc[w2]);
+        lm = max(lm, s_wl[w2]);
+        tsum += s_wt[w2];
+      }
+      cand = cm;
+      lastpos = max(lastpos, lm);
+      run = tsum;
+      __syncthreads();
+    }
+    tok = cand != INT_MAX ? cand : (lastpos >= 0 ? lastpos : V - 1);
+  }
+  if (threadIdx.x == 0) {
+    a.emitted[base + b + n] = tok;
+    a.rsum[b] = kind == 2 ? 0.f : static_cast<float>(S);
+  }
+  for (int i = n + 1 + threadIdx.x; i <= g; i += kSeqThreads) a.emitted[base + b + i] = -1;
+  return true;
+}
+
+// Pass 1 on the exact path: fp32 online (max, sum) per row, as the row statistics
+// kernel computes them. Returns n; s_cz[i] = (c, z) of each judged row.
+template <typename T, typename Hook>
+__device__ __forceinline__ int judge_rows_exact(const Args& a, int b, int base, int g, float2* s_cz, Hook&& hook) {
+  __shared__ float2 s_part[kSeqWaves];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int V = a.V;
+  const T* Lseq = static_cast<const T*>(a.logits) + static_cast<size_t>(base + b) * V;
+  const bool all_rows = a.pdraft != nullptr;
+  const float k2 = a.k2;
+  const int ir = min(lane, g - 1);
+  const int x = a.ids[base + ir];
+  const float uu = a.u[base + b + ir];
+  const int xc = min(max(x, 0), V - 1);
+  uint32_t lxb = 0;  // raw bits of l[x]
+  float qx = 0.f;
+  int n = g;
+  float m = -FLT_MAX, c = -FLT_MAX;  // running max of l and its scaled value
+  float sacc[kGroup];
+#pragma unroll
+  for (int j = 0; j < kGroup; ++j) sacc[j] = 0.f;
+  walk_rows<T>(
+      Lseq, V, g,
+      [&] {
+        // the 32-bit word holding l[x] (rows are 16-byte aligned on this path)
+        if constexpr (sizeof(T) == 2)
+          lxb = reinterpret_cast<const uint32_t*>(Lseq + static_cast<size_t>(ir) * V)[xc >> 1];
+        else
+          lxb = elem_bits(Lseq + static_cast<size_t>(ir) * V, xc);
+        qx = a.q[static_cast<size_t>(base + ir) * V + xc];
+        hook();
+      },
+      [&](const Raw<T>& lr, int, bool in) { stats_step<T>(lr, in ? 1.f : 0.f, k2, m, c, sacc); },
+      [&](int i) {
+        float z = ((sacc[0] + sacc[1]) + (sacc[2] + sacc[3])) + ((sacc[4] + sacc[5]) + (sacc[6] + sacc[7]));
+        float cw = c;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+          const float c2 = __shfl_xor(cw, o), z2 = __shfl_xor(z, o);
+          lse2_merge(cw, z, c2, z2);
+        }
+        if (lane == 0) s_part[wave] = make_float2(cw, z);
+        m = -FLT_MAX;
+        c = -FLT_MAX;
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j) sacc[j] = 0.f;
+        __syncthreads();
+        // every wave merges the partials in the same order and takes the same decision
+        float C = -FLT_MAX, Z = 0.f;
+        if (lane < kSeqWaves) {
+          const float2 pz = s_part[lane];
+          C = pz.x;
+          Z = pz.y;
+        }
+#pragma unroll
+        for (int o = kSeqWaves / 2; o > 0; o >>= 1) {
+          const float c2 = __shfl_xor(C, o), z2 = __shfl_xor(Z, o);
+          lse2_merge(C, Z, c2, z2);
+        }
+        C = __shfl(C, 0);
+        Z = __shfl(Z, 0);
+        // lx, qx were loaded behind the ring's first loads: keep their uses here, inside
+        // the row loop, so that waiting for them never drains the ring
+        asm volatile("" : "+v"(lxb), "+v"(qx));
+        const float lx = sizeof(T) == 2 ? bf16_word_half(lxb, xc & 1) : __uint_as_float(lxb);
+        bool acc = true;
+        double px = 0.0;
+        if (lane == i) acc = accept_decision(x, lx, qx, uu, C, Z, a, px, wave == 0);
+        if (wave == 0 && lane == i) {
+          if (a.pdraft) a.pdraft[base + i] = static_cast<float>(px);
+          s_cz[i] = make_float2(C, Z);
+        }
+        const bool rej = __ballot(!acc) != 0;
+        __syncthreads();  // s_part is rewritten by the next row
+        if (rej && n == g) {
+          n = i;
+          if (!all_rows) return true;  // with p(x) wanted, the remaining rows are still judged
+        }
+        return false;
+      });
+  return n;
+}
+
+template <typename T, bool RAGGED>
+__global__ __launch_bounds__(kSeqThreads) void k_verify_seq(Args a) {
+  __shared__ double s_tab[kExpN];
+  __shared__ float2 s_cz[kFuseMaxGamma];
+  const int b = blockIdx.x;
+  int base, g;
+  if (!seq_geom<RAGGED>(a, b, base, g)) {
+    if (threadIdx.x == 0) {
+      atomicOr(a.err, SV_DATA_CU_GAMMA);
+      a.acc[b] = -1;
+    }
+    return;
+  }
+  exp_table_init(s_tab);
+  if constexpr (sizeof(T) == 2) {
+    __shared__ double sT[kTabEntries];
+    const bool tab = a.tlo <= a.thi;
+    // the value table is built while the first loads of pass 1 are in flight
+    const int n = g > 0 ? judge_rows_exact<T>(a, b, base, g, s_cz, [&] { if (tab) tab_build(sT, a); }) : 0;
+    if (g == 0 && tab) tab_build(sT, a);
+    __syncthreads();  // s_cz of row n, s_tab, sT
+    for (int i = threadIdx.x; i < n; i += kSeqThreads) a.emitted[base + b + i] = a.ids[base + i];
+    if (threadIdx.x == 0) a.acc[b] = n;
+    const double cr = n < g ? static_cast<double>(s_cz[n].x) : 0.0;
+    const double zr = n < g ? static_cast<double>(s_cz[n].y) : 0.0;
+    // table scale: sum 2^(l k2) = z 2^c
+    if (tab && final_draw_tab(a, b, base, g, n, zr * exp2(cr), sT)) return;
+    final_draw<T, true>(a, b, base, g, n, cr, zr, s_tab);
+  } else {
+    const int n = g > 0 ? judge_rows_exact<T>(a, b, base, g, s_cz, [] {}) : 0;
+    __syncthreads();  // s_cz of row n, s_tab
+    for (int i = threadIdx.x; i < n; i += kSeqThreads) a.emitted[base + b + i] = a.ids[base + i];
+    if (threadIdx.x == 0) a.acc[b] = n;
+    final_draw<T, true>(a, b, base, g, n, n < g ? static_cast<double>(s_cz[n].x) : 0.0,
+                        n < g ? static_cast<double>(s_cz[n].y) : 0.0, s_tab);
+  }
+}
+
 // Greedy: the argmax of row g is computed only when every draft was accepted.
 template <typename T, bool ALIGNED, bool RAGGED, bool ACCEPT>
 __global__ __launch_bounds__(kSeqThreads) void k_greedy_seq(Args a) {
@@ -815,11 +1340,19 @@ __global__ __launch_bounds__(kSeqThreads) void k_greedy_seq(Args a) {
 }
 
 // ============================================================== host side
-constexpr int kKernels = 2;
+constexpr int kKernels = 2;  // most kernels one call launches
 constexpr int kEventsPerRun = 2 * kKernels;
-const char* kKernelNames[2][kKernels] = {
-    {"k_rowstats", "k_sample_seq"},
-    {"k_rowargmax", "k_greedy_seq"},
+
+// The launch sequences a call can take.
+enum Path { kPathSample2 = 0, kPathGreedy2 = 1, kPathSample1 = 2, kPaths = 3 };
+struct PathInfo {
+  int nk;
+  const char* names[kKernels];
+};
+const PathInfo kPathInfo[kPaths] = {
+    {2, {"k_rowstats", "k_sample_seq"}},
+    {2, {"k_rowargmax", "k_greedy_seq"}},
+    {1, {"k_verify_seq", nullptr}},
 };
 
 }  // namespace
@@ -835,8 +1368,8 @@ struct spec_verify_ctx {
   // measurement: a start and a stop event per kernel and recorded run, for up to timing_cap runs
   int timing_cap = 0, timing_runs = 0;
   hipEvent_t* ev = nullptr;
-  int nk = 0;
-  const char* kname[kKernels] = {nullptr, nullptr};
+  int timing_path = -1;  // the path of the recorded runs (runs on another path are not recorded)
+  int path_mode = SV_PATH_AUTO, last_path = SV_PATH_AUTO;
   char msg[512] = {0};
 };
 
@@ -868,14 +1401,37 @@ struct DeviceGuard {
 // With timing on, each kernel is launched through hipExtLaunchKernel with a start and
 // a stop event, which take the dispatch's own begin / end timestamps (the launch gap
 // between kernels is not counted).
+// Events of this run when it is recorded, else nullptr.
+hipEvent_t* timing_slot(spec_verify_ctx* ctx, int path) {
+  if (ctx->timing_runs >= ctx->timing_cap) return nullptr;
+  if (ctx->timing_runs > 0 && ctx->timing_path != path) return nullptr;
+  ctx->timing_path = path;
+  return ctx->ev + static_cast<size_t>(ctx->timing_runs) * kEventsPerRun;
+}
+
+hipError_t launch_one(const void* fn, dim3 grid, dim3 block, const Args& a, hipStream_t st, hipEvent_t* ev,
+                      int k) {
+  void* args[] = {const_cast<Args*>(&a)};
+  return hipExtLaunchKernel(fn, grid, block, args, 0, st, ev ? ev[2 * k] : nullptr, ev ? ev[2 * k + 1] : nullptr,
+                            0);
+}
+
+template <typename T, bool RG>
+hipError_t launch_fused(spec_verify_ctx* ctx, const Args& a, hipStream_t st) {
+  hipEvent_t* ev = timing_slot(ctx, kPathSample1);
+  const hipError_t e =
+      launch_one(reinterpret_cast<const void*>(&k_verify_seq<T, RG>), dim3(a.B), dim3(kSeqThreads), a, st, ev, 0);
+  if (e != hipSuccess) return e;
+  if (ev) ++ctx->timing_runs;
+  return hipGetLastError();
+}
+
 template <typename T, bool AL, bool RG, bool AC>
 hipError_t launch_path(spec_verify_ctx* ctx, const Args& a, hipStream_t st, bool greedy) {
-  const bool rec = ctx->timing_runs < ctx->timing_cap;
-  hipEvent_t* ev = rec ? ctx->ev + static_cast<size_t>(ctx->timing_runs) * kEventsPerRun : nullptr;
+  hipEvent_t* ev = timing_slot(ctx, greedy ? kPathGreedy2 : kPathSample2);
+  const bool rec = ev != nullptr;
   auto go = [&](const void* fn, dim3 grid, dim3 block, int k) -> hipError_t {
-    void* args[] = {const_cast<Args*>(&a)};
-    return hipExtLaunchKernel(fn, grid, block, args, 0, st, ev ? ev[2 * k] : nullptr,
-                              ev ? ev[2 * k + 1] : nullptr, 0);
+    return launch_one(fn, grid, block, a, st, ev, k);
   };
   hipError_t e = hipSuccess;
   if (a.R > 0) {
@@ -917,6 +1473,7 @@ void free_events(spec_verify_ctx* ctx) {
   }
   ctx->ev = nullptr;
   ctx->timing_cap = ctx->timing_runs = 0;
+  ctx->timing_path = -1;
 }
 
 // Row-stats split: aim for >= SV_SPLIT_TARGET workgroups with >= SV_SPLIT_MIN_SPAN
@@ -1067,25 +1624,51 @@ int spec_verify_run(spec_verify_ctx* ctx, void* hip_stream, int batch, int gamma
     set_msg(ctx->msg, sizeof(ctx->msg), "launch grid too large: reduce the batch");
     return SV_EINVAL;
   }
+  a.tlo = 1;
+  a.thi = 0;  // no value table
   if (greedy) {
     a.k2 = 0.f;
     a.k2d = 0.0;
   } else {
     a.k2d = 1.4426950408889634 / static_cast<double>(temperature);
     a.k2 = static_cast<float>(a.k2d);
+    // bf16 value table window: magnitudes below 2^etop, |x k2| < 990, kTabBinades octaves
+    const int etop = static_cast<int>(floor(log2(990.0 / a.k2d)));
+    const int be_hi = etop + 127 > 255 ? 255 : etop + 127;  // biased exponent, exclusive
+    const int be_lo = be_hi - kTabBinades < 0 ? 0 : be_hi - kTabBinades;
+    if (ctx->dtype == SV_BF16 && be_hi > be_lo) {
+      a.tlo = be_lo * 128;
+      a.thi = be_hi * 128 - 1;
+    }
   }
   DeviceGuard guard(ctx->device);
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
-  const hipError_t e = ctx->dtype == SV_BF16
-                           ? launch_dt<uint16_t>(ctx, a, st, greedy, aligned, cu_gamma != nullptr)
-                           : launch_dt<float>(ctx, a, st, greedy, aligned, cu_gamma != nullptr);
+  // one launch per call when there are enough sequences to give every compute unit one
+  const int gmax = cu_gamma ? ctx->max_gamma : gamma;
+  const bool fused = ctx->path_mode != SV_PATH_TWO_LAUNCH && !greedy && aligned && gmax <= kFuseMaxGamma &&
+                     (ctx->path_mode == SV_PATH_ONE_LAUNCH || batch >= ctx->cus);
+  const bool rg = cu_gamma != nullptr;
+  hipError_t e;
+  if (fused)
+    e = ctx->dtype == SV_BF16 ? (rg ? launch_fused<uint16_t, true>(ctx, a, st) : launch_fused<uint16_t, false>(ctx, a, st))
+                              : (rg ? launch_fused<float, true>(ctx, a, st) : launch_fused<float, false>(ctx, a, st));
+  else
+    e = ctx->dtype == SV_BF16 ? launch_dt<uint16_t>(ctx, a, st, greedy, aligned, rg)
+                              : launch_dt<float>(ctx, a, st, greedy, aligned, rg);
   if (e != hipSuccess) return hip_fail(ctx, "kernel launch", e);
   ctx->last_stream = st;
   ctx->ran = true;
-  ctx->nk = kKernels;
-  for (int i = 0; i < kKernels; ++i) ctx->kname[i] = kKernelNames[greedy ? 1 : 0][i];
+  ctx->last_path = fused ? SV_PATH_ONE_LAUNCH : SV_PATH_TWO_LAUNCH;
   return SV_OK;
 }
+
+int spec_verify_set_path(spec_verify_ctx* ctx, int mode) {
+  if (!ctx || (mode != SV_PATH_AUTO && mode != SV_PATH_TWO_LAUNCH && mode != SV_PATH_ONE_LAUNCH)) return SV_EINVAL;
+  ctx->path_mode = mode;
+  return SV_OK;
+}
+
+int spec_verify_last_path(const spec_verify_ctx* ctx) { return ctx ? ctx->last_path : -SV_EINVAL; }
 
 int spec_verify_status(spec_verify_ctx* ctx) {
   if (!ctx) return SV_EINVAL;
@@ -1147,9 +1730,10 @@ int spec_verify_kernel_times(spec_verify_ctx* ctx, float* ms, const char** names
   if (ctx->timing_runs == 0) return 0;
   DeviceGuard guard(ctx->device);
   const int R = ctx->timing_runs;
-  hipError_t e = hipEventSynchronize(ctx->ev[static_cast<size_t>(R) * kEventsPerRun - 1]);
+  const PathInfo& path = kPathInfo[ctx->timing_path];
+  hipError_t e = hipEventSynchronize(ctx->ev[static_cast<size_t>(R - 1) * kEventsPerRun + 2 * path.nk - 1]);
   if (e != hipSuccess) return -hip_fail(ctx, "hipEventSynchronize", e);
-  for (int k = 0; k < ctx->nk && k < cap; ++k) {
+  for (int k = 0; k < path.nk && k < cap; ++k) {
     double sum = 0.0;
     for (int r = 0; r < R; ++r) {
       float t = 0.f;
@@ -1159,10 +1743,12 @@ int spec_verify_kernel_times(spec_verify_ctx* ctx, float* ms, const char** names
       sum += t;
     }
     if (ms) ms[k] = static_cast<float>(sum / R);
-    if (names) names[k] = ctx->kname[k];
+    if (names) names[k] = path.names[k];
   }
   ctx->timing_runs = 0;  // the next runs record afresh
-  return ctx->nk;
+  const int nk = path.nk;
+  ctx->timing_path = -1;
+  return nk;
 }
 
 }  // extern "C"

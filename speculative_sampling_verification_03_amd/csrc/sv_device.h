@@ -19,6 +19,7 @@ constexpr int kGroup = 8;      // elements per group
 // ---------------------------------------------------------------- loads
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_word_half(uint32_t w, int hi) { return hi ? bf16_hi(w) : bf16_lo(w); }
 
 // One aligned group of 8 logits starting at element offset `e` of `p`.
 __device__ __forceinline__ void load_group(const uint16_t* __restrict__ p, size_t e, float x[8]) {

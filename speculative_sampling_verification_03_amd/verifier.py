@@ -8,8 +8,8 @@ from __future__ import annotations
 from typing import NamedTuple, Optional
 
 from .binding import (SV_BF16, SV_EDATA, SV_F32, spec_verify_create, spec_verify_destroy,
-                      spec_verify_kernel_times, spec_verify_last_error, spec_verify_run,
-                      spec_verify_set_timing, spec_verify_status)
+                      spec_verify_kernel_times, spec_verify_last_error, spec_verify_last_path,
+                      spec_verify_run, spec_verify_set_path, spec_verify_set_timing, spec_verify_status)
 
 
 class VerifyOutputs(NamedTuple):
@@ -121,6 +121,13 @@ class Verifier:
     def kernel_times(self):
         """([(kernel, mean ms), ...], runs) over the recorded runs."""
         return spec_verify_kernel_times(self.ctx)
+
+    def set_path(self, mode: int):
+        """Launch plan for the next runs: SV_PATH_AUTO, SV_PATH_TWO_LAUNCH or SV_PATH_ONE_LAUNCH."""
+        spec_verify_set_path(self.ctx, mode)
+
+    def last_path(self) -> int:
+        return spec_verify_last_path(self.ctx)
 
     def close(self):
         if getattr(self, "ctx", None):

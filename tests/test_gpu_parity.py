@@ -42,19 +42,37 @@ def verifier(sv, V, dtype, max_batch, max_rows, max_gamma=16):
     if key not in _CACHE:
         code = sv.SV_BF16 if dtype == "bf16" else sv.SV_F32
         _CACHE[key] = sv.Verifier(V, code, max_batch, max_rows, max_gamma)
-    return _CACHE[key]
+    v = _CACHE[key]
+    v.set_path(sv.SV_PATH_AUTO)
+    return v
 
 
-def check_parity(sv, w, label, ragged=None, max_gamma=16):
+# Every parity case runs both launch plans; the one-launch plan also without p(x), the
+# way it stops reading rows at the first rejection.
+PLANS = (("two-launch", "SV_PATH_TWO_LAUNCH", True),
+         ("one-launch", "SV_PATH_ONE_LAUNCH", True),
+         ("one-launch, stop at rejection", "SV_PATH_ONE_LAUNCH", False))
+
+
+def check_parity(sv, w, label, ragged=None, max_gamma=16, plans=PLANS):
+    """Runs w under each plan and compares each result with the oracle; returns
+    ({plan: gpu outputs}, oracle result)."""
     _say(label, f"B={w.B} V={w.V} dtype={w.dtype} T={w.T} rows={w.draft_rows}")
     v = verifier(sv, w.V, w.dtype, max(w.B, 1), max(w.draft_rows, 1), max_gamma)
-    gpu = run_gpu(v, w, ragged=ragged)
-    assert gpu["status"] == sv.SV_OK, v.last_error()
+    dev = to_device(w)
     ora = oracle_batch(w)
-    rep = compare(w, gpu, ora)
-    _say(label, rep.summary())
-    assert rep.ok(), rep.summary()
-    return gpu, ora, rep
+    runs = {}
+    for name, mode, want_p in plans:
+        v.set_path(getattr(sv, mode))
+        _say(label, name)
+        gpu = run_gpu(v, w, dev=dev, ragged=ragged, want_p_draft=want_p)
+        assert gpu["status"] == sv.SV_OK, v.last_error()
+        rep = compare(w, gpu, ora)
+        _say(label, name, f"(plan {v.last_path()})", rep.summary())
+        assert rep.ok(), (name, rep.summary())
+        runs[name] = gpu
+    v.set_path(sv.SV_PATH_AUTO)
+    return runs, ora
 
 
 # ---------------------------------------------------------------- configurations
@@ -74,7 +92,7 @@ def test_c3_more_seeds(lib):
 
 
 def test_c4_greedy_full_size(lib):
-    _, ora, _ = check_parity(lib, synth.make_config("C4", seed=0), "C4 seed=0")
+    _, ora = check_parity(lib, synth.make_config("C4", seed=0), "C4 seed=0")
     assert ora.accepted_count.mean() > 3  # agreement 0.8: the bonus path is exercised
     assert np.sum(ora.accepted_count == 8) > 20
 
@@ -97,21 +115,22 @@ def test_uniform_batch_through_ragged_entry(lib):
 def test_c1_rounds_and_slot_distributions(lib):
     """C1: fixed p and q, 10^4 rounds in one call; parity plus chi-square per slot."""
     w = synth.make_config("C1", seed=0, batch=10000)
-    gpu, ora, rep = check_parity(lib, w, "C1 B=10^4")
+    runs, ora = check_parity(lib, w, "C1 B=10^4")
     L = w.logits_f64(slice(0, 5))
     P = [O.target_distribution(L[i], 1.0) for i in range(5)]
-    em = gpu["emitted_tokens"].reshape(w.B, 5)
-    n = gpu["accepted_count"]
-    for i in range(5):
-        toks = em[n >= i, i]
-        cnt = np.bincount(toks, minlength=w.V)
-        exp = len(toks) * P[i]
-        keep = exp >= 5
-        obs = np.r_[cnt[keep], cnt[~keep].sum()]
-        ex = np.r_[exp[keep], exp[~keep].sum()]
-        if ex[-1] == 0:
-            obs, ex = obs[:-1], ex[:-1]
-        assert stats.chisquare(obs, ex).pvalue * 5 > 1e-4, i
+    for gpu in runs.values():
+        em = gpu["emitted_tokens"].reshape(w.B, 5)
+        n = gpu["accepted_count"]
+        for i in range(5):
+            toks = em[n >= i, i]
+            cnt = np.bincount(toks, minlength=w.V)
+            exp = len(toks) * P[i]
+            keep = exp >= 5
+            obs = np.r_[cnt[keep], cnt[~keep].sum()]
+            ex = np.r_[exp[keep], exp[~keep].sum()]
+            if ex[-1] == 0:
+                obs, ex = obs[:-1], ex[:-1]
+            assert stats.chisquare(obs, ex).pvalue * 15 > 1e-4, i
 
 
 # ---------------------------------------------------------------- edge cases
@@ -144,9 +163,10 @@ def test_q_equals_p_always_accepts(lib):
         ids[r] = rng.choice(V, p=pr / pr.sum())
     u = rng.random(B * (g + 1), dtype=np.float32)
     w = _custom("q=p", L, Q, ids, u, [g] * B, 1.0)
-    gpu, ora, rep = check_parity(lib, w, "q=p")
+    runs, ora = check_parity(lib, w, "q=p")
     # fp32 q vs fp64 p: p(x) < q(x) by rounding can only reject within the flag window
-    assert np.mean(gpu["accepted_count"] == g) > 0.99
+    for gpu in runs.values():
+        assert np.mean(gpu["accepted_count"] == g) > 0.99
 
 
 def test_zero_target_mass_always_rejects(lib):
@@ -160,9 +180,10 @@ def test_zero_target_mass_always_rejects(lib):
         Q[b, ids[b]] = 1.0           # one-hot draft
     u = rng.random(2 * B, dtype=np.float32)
     w = _custom("p(x)=0", L, Q, ids, u, [1] * B, 1.0)
-    gpu, ora, rep = check_parity(lib, w, "p(x)=0")
-    assert np.all(gpu["accepted_count"] == 0)
-    np.testing.assert_allclose(gpu["residual_sum"], 1.0, rtol=1e-6)
+    runs, ora = check_parity(lib, w, "p(x)=0")
+    for gpu in runs.values():
+        assert np.all(gpu["accepted_count"] == 0)
+        np.testing.assert_allclose(gpu["residual_sum"], 1.0, rtol=1e-6)
 
 
 def test_one_hot_draft(lib):
@@ -224,7 +245,9 @@ def test_misaligned_pointers(lib):
     assert dev["logits"].data_ptr() % 16 != 0
     _say("misaligned", f"B={w.B} V={w.V}")
     v = verifier(lib, w.V, w.dtype, w.B, w.draft_rows)
+    v.set_path(lib.SV_PATH_ONE_LAUNCH)  # not possible on misaligned buffers: two launches
     gpu = run_gpu(v, w, dev=dev)
+    assert v.last_path() == lib.SV_PATH_TWO_LAUNCH
     rep = compare(w, gpu, oracle_batch(w))
     _say("misaligned", rep.summary())
     assert rep.ok(), rep.summary()
@@ -291,9 +314,14 @@ def test_host_errors_launch_nothing(lib):
     assert torch.all(acc == -7) and torch.all(em == -7) and torch.all(rs == -7.0)
 
 
-def test_device_data_errors_set_flag_and_fallbacks(lib):
+PLAN_IDS = ["SV_PATH_TWO_LAUNCH", "SV_PATH_ONE_LAUNCH"]
+
+
+@pytest.mark.parametrize("plan", PLAN_IDS)
+def test_device_data_errors_set_flag_and_fallbacks(lib, plan):
     w = synth.make_config("C2", seed=11, batch=8, vocab=640)
     v = verifier(lib, 640, "f32", 8, 40)
+    v.set_path(getattr(lib, plan))
     # draft id out of range -> that position rejected, flag raised
     w.draft_ids = w.draft_ids.copy()
     w.draft_ids[5 * 3 + 2] = 640
@@ -314,11 +342,13 @@ def test_device_data_errors_set_flag_and_fallbacks(lib):
     assert rep.ok(), rep.summary()
 
 
-def test_nonfinite_logits_flagged(lib):
+@pytest.mark.parametrize("plan", PLAN_IDS)
+def test_nonfinite_logits_flagged(lib, plan):
     w = synth.make_config("C2", seed=13, batch=4, vocab=512)
     w.logits = w.logits.copy()
     w.logits[0, 7] = np.nan
     v = verifier(lib, 512, "f32", 4, 20)
+    v.set_path(getattr(lib, plan))
     gpu = run_gpu(v, w)
     assert gpu["status"] == lib.SV_EDATA
     assert "non-finite" in v.last_error()
@@ -326,13 +356,15 @@ def test_nonfinite_logits_flagged(lib):
     assert np.all((gpu["emitted_tokens"] >= -1) & (gpu["emitted_tokens"] < 512))
 
 
-def test_malformed_cu_gamma_flagged(lib):
+@pytest.mark.parametrize("plan", PLAN_IDS)
+def test_malformed_cu_gamma_flagged(lib, plan):
     w = synth.make_config("C5", seed=14, batch=8, vocab=1024)
     dev = to_device(w)
     bad = w.cu_gamma.copy()
     bad[3], bad[4] = bad[4], bad[3]  # decreasing
     dev["cu_gamma"] = torch.from_numpy(bad).cuda()
     v = verifier(lib, 1024, "bf16", 8, w.draft_rows)
+    v.set_path(getattr(lib, plan))
     gpu = run_gpu(v, w, dev=dev, ragged=True)
     assert gpu["status"] == lib.SV_EDATA
     assert "cu_gamma" in v.last_error()
@@ -341,14 +373,18 @@ def test_malformed_cu_gamma_flagged(lib):
 
 # ---------------------------------------------------------------- determinism, streams, timing
 
-def test_repeatable_bit_for_bit(lib):
+@pytest.mark.parametrize("plan", PLAN_IDS)
+def test_repeatable_bit_for_bit(lib, plan):
     w = synth.make_config("C3", seed=15, batch=64)
     v = verifier(lib, w.V, w.dtype, w.B, w.draft_rows)
+    v.set_path(getattr(lib, plan))
     dev = to_device(w)
-    a = run_gpu(v, w, dev=dev)
-    b = run_gpu(v, w, dev=dev)
-    for k in ("accepted_count", "emitted_tokens", "residual_sum", "p_draft"):
-        assert np.array_equal(a[k], b[k], equal_nan=True), k
+    for want_p in (True, False):
+        a = run_gpu(v, w, dev=dev, want_p_draft=want_p)
+        b = run_gpu(v, w, dev=dev, want_p_draft=want_p)
+        for k in ("accepted_count", "emitted_tokens", "residual_sum", "p_draft"):
+            if a[k] is not None or b[k] is not None:
+                assert np.array_equal(a[k], b[k], equal_nan=True), k
 
 
 def test_side_stream_and_timing(lib):
@@ -371,6 +407,26 @@ def test_side_stream_and_timing(lib):
     assert all(t > 0 for _, t in times)
     gpu = dict(accepted_count=out.accepted_count.cpu().numpy(), emitted_tokens=out.emitted_tokens.cpu().numpy(),
                residual_sum=out.residual_sum.cpu().numpy(), p_draft=out.p_draft.cpu().numpy())
+    rep = compare(w, gpu, oracle_batch(w))
+    assert rep.ok(), rep.summary()
+
+
+def test_one_launch_plan_chosen_and_timed(lib):
+    """B >= the number of compute units takes one launch by default; its kernel is timed."""
+    w = synth.make_config("C3", seed=17)
+    v = verifier(lib, w.V, w.dtype, w.B, w.draft_rows)
+    dev = to_device(w)
+    _say("one-launch timing", f"B={w.B}")
+    v.set_timing(2)
+    try:
+        for _ in range(2):
+            gpu = run_gpu(v, w, dev=dev, want_p_draft=False)
+        times, runs = v.kernel_times()
+    finally:
+        v.set_timing(0)
+    assert v.last_path() == lib.SV_PATH_ONE_LAUNCH
+    assert runs == 2
+    assert [n for n, _ in times] == ["k_verify_seq"] and times[0][1] > 0
     rep = compare(w, gpu, oracle_batch(w))
     assert rep.ok(), rep.summary()
 
