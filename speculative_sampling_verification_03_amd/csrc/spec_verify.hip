@@ -784,26 +784,42 @@ __device__ __forceinline__ void stats_step(const Raw<T>& lr, float wgt, float k2
   for (int j = 0; j < kGroup; ++j) sacc[j] = fmaf(wgt, fast_exp2(fmaf(xv[j], k2, -c)), sacc[j]);
 }
 
-// Walks the sequence's rows 0, 1, ... (row i at Lseq + i V) chunk by chunk: wave w takes
-// chunks w, w + kSeqWaves, ... of 512 entries; nitp, the chunk steps per row, is a
-// multiple of kRing so every row starts at ring slot 0, and the ring's loads run on
-// into the next row while row_end(i) judges row i. step(buf, ch, wgt) gets the chunk
-// index and weight 1 or 0 (0: the lane's group lies past the row and its load was
-// clamped onto the row's last group). after_prologue() runs once the first loads are
-// in flight. row_end(i) returns true to stop.
-template <typename T, typename Pro, typename Step, typename RowEnd>
+// Walks the sequence's rows 0, 1, ... (row i at Lseq + i V) span by span: a span is
+// kSeqWaves chunks of 512 entries, wave w reading chunk w of each span (so the block
+// reads every row front to back). nitp, the spans per row rounded up to a multiple of
+// kRing, keeps every row starting at ring slot 0; the ring's loads run on into the next
+// row while row_end(i) judges row i. A span's address is a scalar base plus the lane's
+// fixed byte offset. With V >= one span (WIDE), the row's last span is read from
+// V - kSpan, overlapping the one before, and lanes whose entry lies before
+// (nsp - 1) kSpan must not count it (row_weight gives the lane's weight for the last
+// span); otherwise the single span's lanes past V read the row's last group instead
+// and must not count it. Padding spans re-read the last span and are not handed to
+// step. step(buf, k) gets the span index k < nsp; after_prologue() runs once the first
+// loads are in flight; row_end(i) returns true to stop.
+template <typename T, bool WIDE, typename Pro, typename Step, typename RowEnd>
 __device__ __forceinline__ void walk_rows(const T* Lseq, int V, int g, Pro&& after_prologue, Step&& step,
                                           RowEnd&& row_end) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nch = (V + kIter - 1) / kIter;
-  const int nitp = ((nch + kSeqWaves - 1) / kSeqWaves + kRing - 1) / kRing * kRing;
+  constexpr int kSpan = kSeqWaves * kIter;
+  const int lane_off = wave * kIter + lane * kGroup;
+  const uint32_t lane_byte = static_cast<uint32_t>(lane_off) * sizeof(T);
+  const int nsp = (V + kSpan - 1) / kSpan;
+  const int nitp = (nsp + kRing - 1) / kRing * kRing;
   const int total = g * nitp;
   Raw<T> Lb[kRing];
-  int jl = 0, il = 0, kl = 0;  // next (flattened) iteration to load: row il, step kl
+  int jl = 0, il = 0, kl = 0;  // next (flattened) iteration to load: row il, span kl
   auto issue = [&](Raw<T>& dst) {
-    const int e = min((kl * kSeqWaves + wave) * kIter + lane * kGroup, V - kGroup);
-    load_raw_in(Lseq + static_cast<size_t>(il) * V, e, dst);
+    const T* rowp = Lseq + static_cast<size_t>(il) * V;
+    if (WIDE) {
+      const int e0 = kl < nsp - 1 ? kl * kSpan : V - kSpan;
+      const char* sb = reinterpret_cast<const char*>(rowp + e0);
+      const uint4* p = reinterpret_cast<const uint4*>(sb + lane_byte);
+#pragma unroll
+      for (int q = 0; q < Raw<T>::N; ++q) dst.v[q] = p[q];
+    } else {
+      load_raw_in(rowp, min(lane_off, V - kGroup), dst);
+    }
     if (jl < total - 1) {
       ++jl;
       if (++kl == nitp) {
@@ -823,12 +839,21 @@ __device__ __forceinline__ void walk_rows(const T* Lseq, int V, int g, Pro&& aft
 #pragma unroll
       for (int r = 0; r < kRing; ++r) {
         issue(Lb[(r + kRing - 1) % kRing]);
-        const int ch = (k0 + r) * kSeqWaves + wave;
-        if (ch < nch) step(Lb[r], ch, ch * kIter + lane * kGroup < V);
+        const int k = k0 + r;
+        if (k < nsp) step(Lb[r], k);
       }
     }
     if (row_end(i)) break;
   }
+}
+
+// Weight of this lane's entries in the row's last span (see walk_rows).
+template <bool WIDE>
+__device__ __forceinline__ float last_span_weight(int V) {
+  constexpr int kSpan = kSeqWaves * kIter;
+  const int lane_off = (threadIdx.x >> 6) * kIter + (threadIdx.x & 63) * kGroup;
+  const int nsp = (V + kSpan - 1) / kSpan;
+  return (WIDE ? V - kSpan + lane_off >= (nsp - 1) * kSpan : lane_off < V) ? 1.f : 0.f;
 }
 
 // ---- bf16 value table: 2^(x k2) in fp64 for every bf16 x whose magnitude bits lie in
@@ -1131,9 +1156,13 @@ __device__ __forceinline__ bool final_draw_tab(const Args& a, int b, int base, i
   return true;
 }
 
-// Pass 1 on the exact path: fp32 online (max, sum) per row, as the row statistics
-// kernel computes them. Returns n; s_cz[i] = (c, z) of each judged row.
-template <typename T, typename Hook>
+// Pass 1: per row, z = sum 2^(l k2 - c) in fp32. Each wave takes its reference c from
+// the first chunk it reads of the row (the chunk's max times k2; the row max can only be
+// larger, so no entry underflows the sum's precision) and adds plain exp2 terms after
+// that, with no running max. A wave whose sum overflows (a value more than ~100 octaves
+// above that first chunk's max) or is not finite redoes its chunks of the row with the
+// running max. Returns n; s_cz[i] = (c, z) of each judged row.
+template <typename T, bool WIDE, typename Hook>
 __device__ __forceinline__ int judge_rows_exact(const Args& a, int b, int base, int g, float2* s_cz, Hook&& hook) {
   __shared__ float2 s_part[kSeqWaves];
   const int lane = threadIdx.x & 63;
@@ -1149,11 +1178,15 @@ __device__ __forceinline__ int judge_rows_exact(const Args& a, int b, int base, 
   uint32_t lxb = 0;  // raw bits of l[x]
   float qx = 0.f;
   int n = g;
-  float m = -FLT_MAX, c = -FLT_MAX;  // running max of l and its scaled value
+  constexpr int kSpan = kSeqWaves * kIter;
+  const int lane_off = wave * kIter + lane * kGroup;
+  const int nsp = (V + kSpan - 1) / kSpan;
+  const float wlast = last_span_weight<WIDE>(V);
+  float c = -FLT_MAX;  // this wave's reference for the current row
   float sacc[kGroup];
 #pragma unroll
   for (int j = 0; j < kGroup; ++j) sacc[j] = 0.f;
-  walk_rows<T>(
+  walk_rows<T, WIDE>(
       Lseq, V, g,
       [&] {
         // the 32-bit word holding l[x] (rows are 16-byte aligned on this path)
@@ -1164,17 +1197,42 @@ __device__ __forceinline__ int judge_rows_exact(const Args& a, int b, int base, 
         qx = a.q[static_cast<size_t>(base + ir) * V + xc];
         hook();
       },
-      [&](const Raw<T>& lr, int, bool in) { stats_step<T>(lr, in ? 1.f : 0.f, k2, m, c, sacc); },
-      [&](int i) {
-        float z = ((sacc[0] + sacc[1]) + (sacc[2] + sacc[3])) + ((sacc[4] + sacc[5]) + (sacc[6] + sacc[7]));
-        float cw = c;
+      [&](const Raw<T>& lr, int k) {
+        float xv[kGroup];
+        unpack(lr, xv);
+        if (k == 0) {  // the row's first chunk sets the reference
+          float bm = xv[0];
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-          const float c2 = __shfl_xor(cw, o), z2 = __shfl_xor(z, o);
-          lse2_merge(cw, z, c2, z2);
+          for (int j = 1; j < kGroup; ++j) bm = fmaxf(bm, xv[j]);
+          c = fmaxf(wave_max_dpp(bm) * k2, -FLT_MAX);
+        }
+        const float wgt = k == nsp - 1 ? wlast : 1.f;
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j) sacc[j] = fmaf(wgt, fast_exp2(fmaf(xv[j], k2, -c)), sacc[j]);
+      },
+      [&](int i) {
+        float z = wave_sum(((sacc[0] + sacc[1]) + (sacc[2] + sacc[3])) + ((sacc[4] + sacc[5]) + (sacc[6] + sacc[7])));
+        float cw = c;
+        if (!(z <= FLT_MAX)) {  // overflow or not finite: this wave's chunks again, running max
+          const T* rowp = Lseq + static_cast<size_t>(i) * V;
+          float m = -FLT_MAX;
+          cw = -FLT_MAX;
+#pragma unroll
+          for (int j = 0; j < kGroup; ++j) sacc[j] = 0.f;
+          for (int k = 0; k < nsp; ++k) {
+            Raw<T> lr;
+            const int e = WIDE ? (k < nsp - 1 ? k * kSpan : V - kSpan) + lane_off : min(lane_off, V - kGroup);
+            load_raw_in(rowp, e, lr);
+            stats_step<T>(lr, k == nsp - 1 ? wlast : 1.f, k2, m, cw, sacc);
+          }
+          z = ((sacc[0] + sacc[1]) + (sacc[2] + sacc[3])) + ((sacc[4] + sacc[5]) + (sacc[6] + sacc[7]));
+#pragma unroll
+          for (int o = 32; o > 0; o >>= 1) {
+            const float c2 = __shfl_xor(cw, o), z2 = __shfl_xor(z, o);
+            lse2_merge(cw, z, c2, z2);
+          }
         }
         if (lane == 0) s_part[wave] = make_float2(cw, z);
-        m = -FLT_MAX;
         c = -FLT_MAX;
 #pragma unroll
         for (int j = 0; j < kGroup; ++j) sacc[j] = 0.f;
@@ -1233,7 +1291,12 @@ __global__ __launch_bounds__(kSeqThreads) void k_verify_seq(Args a) {
     __shared__ double sT[kTabEntries];
     const bool tab = a.tlo <= a.thi;
     // the value table is built while the first loads of pass 1 are in flight
-    const int n = g > 0 ? judge_rows_exact<T>(a, b, base, g, s_cz, [&] { if (tab) tab_build(sT, a); }) : 0;
+    auto hook = [&] {
+      if (tab) tab_build(sT, a);
+    };
+    const int n = g == 0 ? 0
+                  : a.V >= kSeqWaves * kIter ? judge_rows_exact<T, true>(a, b, base, g, s_cz, hook)
+                                             : judge_rows_exact<T, false>(a, b, base, g, s_cz, hook);
     if (g == 0 && tab) tab_build(sT, a);
     __syncthreads();  // s_cz of row n, s_tab, sT
     for (int i = threadIdx.x; i < n; i += kSeqThreads) a.emitted[base + b + i] = a.ids[base + i];
@@ -1244,7 +1307,9 @@ __global__ __launch_bounds__(kSeqThreads) void k_verify_seq(Args a) {
     if (tab && final_draw_tab(a, b, base, g, n, zr * exp2(cr), sT)) return;
     final_draw<T, true>(a, b, base, g, n, cr, zr, s_tab);
   } else {
-    const int n = g > 0 ? judge_rows_exact<T>(a, b, base, g, s_cz, [] {}) : 0;
+    const int n = g == 0 ? 0
+                  : a.V >= kSeqWaves * kIter ? judge_rows_exact<T, true>(a, b, base, g, s_cz, [] {})
+                                             : judge_rows_exact<T, false>(a, b, base, g, s_cz, [] {});
     __syncthreads();  // s_cz of row n, s_tab
     for (int i = threadIdx.x; i < n; i += kSeqThreads) a.emitted[base + b + i] = a.ids[base + i];
     if (threadIdx.x == 0) a.acc[b] = n;
