@@ -33,12 +33,27 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def step_bytes(w, n, stop_at_rejection):
-    """Algorithmic bytes of one step from this run's accepted counts n: the judged
-    rows once (with `stop_at_rejection`, rows 0..min(n, gamma - 1) of each sequence,
-    the rows the left-to-right verification looks at; otherwise all gamma rows), the
-    drawn row once, the rejected position's q row once, plus the per-position reads
-    (id, uniform, q(x)) and the outputs."""
+def method_bytes(w, n):
+    """Algorithmic bytes of one step by the two-pass method's per-sequence figure, from
+    this run's accepted counts n: every draft row once, the drawn row once, the rejected
+    position's q row once, the per-position id and uniform reads and the outputs.
+    Greedy drops q and u, and reads its bonus row only when all drafts were accepted."""
+    import numpy as np
+    sl = 2 if w.dtype == "bf16" else 4
+    g = w.gammas.astype(np.int64)
+    n = n.astype(np.int64)
+    if w.T == 0.0:
+        per = g * w.V * sl + (n == g) * w.V * sl + g * 4 + 4 + (g + 1) * 4
+    else:
+        per = (g * w.V * sl + w.V * sl + (n < g) * w.V * 4 + g * (4 + 4) + (g + 1) * 4
+               + 4 + (g + 1) * 4 + 4)
+    return int(per.sum())
+
+
+def needed_bytes(w, n, stop_at_rejection):
+    """Bytes this launch plan has to read and write: as method_bytes, except that with
+    `stop_at_rejection` only rows 0..min(n, gamma - 1) of each sequence are read (the rows
+    the left-to-right verification looks at) and q(x) is read for every draft."""
     import numpy as np
     sl = 2 if w.dtype == "bf16" else 4
     g = w.gammas.astype(np.int64)
@@ -50,6 +65,31 @@ def step_bytes(w, n, stop_at_rejection):
     else:
         per = rows * w.V * sl + w.V * sl + (n < g) * w.V * 4 + g * 12 + 4 + outputs
     return int(per.sum())
+
+
+def kernel_source_hash():
+    """sha256 of the kernel sources; a committed counter summary applies only to them."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("csrc/spec_verify.hip", "csrc/sv_device.h"):
+        with open(os.path.join(ROOT, "speculative_sampling_verification_03_amd", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def counter_traffic(kernel, workload_tag):
+    """HBM bytes per launch of `kernel` on `workload_tag` from a rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary under profiles/ whose kernel sources match these ones, else None.
+    A summary states it on a line: traffic <kernel> <workload> <bytes> <source sha256>."""
+    import glob
+    src = kernel_source_hash()
+    for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.txt"))):
+        for line in open(f, encoding="utf-8"):
+            parts = line.split()
+            if len(parts) == 5 and parts[0] == "traffic" and parts[1] == kernel and parts[2] == workload_tag \
+                    and parts[4] == src:
+                return float(parts[3])
+    return None
 
 
 def cpu_baseline(w, seconds):
@@ -86,6 +126,8 @@ def main():
     ap.add_argument("--sets", type=int, default=2, help="input sets rotated across steps")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-every-row", action="store_true",
+                    help="skip the second timing with p(x) requested (every draft row read)")
     ap.add_argument("--plan", choices=("auto", "two", "one"), default="auto",
                     help="launch plan (auto: one launch when B >= the number of compute units)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -165,7 +207,8 @@ def main():
         assert ver.status() == sv.SV_OK, ver.last_error()
         nb.append(outs[k].accepted_count.cpu().numpy())
     one_launch = ver.last_path() == sv.SV_PATH_ONE_LAUNCH  # stops reading rows at the first rejection
-    bytes_per_set = [step_bytes(w, n, one_launch) for (w, _), n in zip(sets, nb)]
+    method_per_set = [method_bytes(w, n) for (w, _), n in zip(sets, nb)]
+    needed_per_set = [needed_bytes(w, n, one_launch) for (w, _), n in zip(sets, nb)]
 
     for k in range(args.warmup):
         step(k)
@@ -187,27 +230,58 @@ def main():
     ms = (t1 - t0) * 1e3 / args.steps
     pos_per_step = np.mean([w.draft_rows for w, _ in sets])
     value = pos_per_step / (ms * 1e-3)
-    path_bytes = float(np.mean([bytes_per_set[k % len(sets)] for k in range(args.steps)]))
+    path_bytes = float(np.mean([method_per_set[k % len(sets)] for k in range(args.steps)]))
     path_gbps = path_bytes / (ms * 1e-3) / 1e9
+    needed = float(np.mean([needed_per_set[k % len(sets)] for k in range(args.steps)]))
 
-    # the roofline is taken on the kernel that moves the most bytes: the whole step
-    # when it is one launch, else the row-statistics pass
+    # the roofline is taken on the kernel that moves the most bytes: the whole step when
+    # it is one launch, else the row-statistics pass (every draft row once)
     kt = dict(ktimes)
     k1 = ktimes[0][0]
     sl = 2 if w0.dtype == "bf16" else 4
     if one_launch:
-        k1_bytes = path_bytes
+        k1_bytes, k1_needed = path_bytes, needed
     else:
         k1_bytes = float(np.mean([w.draft_rows * (w.V * sl + 8) for w, _ in sets]))
+        k1_needed = k1_bytes
     k1_gbps = k1_bytes / (kt[k1] * 1e-3) / 1e9
+
+    # the same steps with p(x) requested for every draft: the one-launch plan then reads
+    # every draft row, as the two-launch plan always does
+    all_rows = None
+    if one_launch and not w0.T == 0.0 and not args.no_every_row:
+        outs_p = [sv.VerifyOutputs(o.accepted_count, o.emitted_tokens, o.residual_sum,
+                                   torch.empty(w.draft_rows, dtype=torch.float32, device=dev))
+                  for o, (w, _) in zip(outs, sets)]
+        saved = list(outs)
+        outs[:] = outs_p
+        for k in range(args.warmup):
+            step(k)
+        torch.cuda.synchronize()
+        ver.set_timing(args.steps)
+        t2 = time.perf_counter()
+        for k in range(args.steps):
+            step(k)
+        torch.cuda.synchronize()
+        t3 = time.perf_counter()
+        kt_all, _ = ver.kernel_times()
+        ver.set_timing(0)
+        assert ver.status() == sv.SV_OK, ver.last_error()
+        outs[:] = saved
+        ms_all = (t3 - t2) * 1e3 / args.steps
+        all_rows = {"ms_per_step": ms_all, "value": pos_per_step / (ms_all * 1e-3),
+                    "kernel_us": {nm: t * 1e3 for nm, t in kt_all},
+                    "achieved_GBps": path_bytes / (kt_all[0][1] * 1e-3) / 1e9}
+        log(f"[bench] every row read (p(x) requested): {ms_all * 1e3:.2f} us/step, "
+            f"{all_rows['value'] / 1e6:.2f} M positions/s")
 
     # acceptance metrics of the measured inputs
     acc = np.concatenate(nb)
     gam = np.concatenate([w.gammas for w, _ in sets]).astype(np.int64)
     alpha_hat = acc.sum() / (acc + (acc < gam)).sum()
     log(f"[bench] {args.config}: {ms * 1e3:.2f} us/step, {value / 1e6:.2f} M positions/s, "
-        f"path {path_gbps:.0f} GB/s ({path_gbps / HBM_PEAK_GBPS:.1%} of peak) over "
-        f"{path_bytes / 1e6:.1f} MB/step")
+        f"{path_gbps:.0f} GB/s ({path_gbps / HBM_PEAK_GBPS:.1%} of peak) over the method's "
+        f"{path_bytes / 1e6:.1f} MB/step; this plan reads {needed / 1e6:.1f} MB/step")
     for name, t in ktimes:
         log(f"[bench]   {name:20s} {t * 1e3:8.2f} us")
     log(f"[bench] acceptance: alpha_hat={alpha_hat:.4f} tokens/round={np.mean(acc + 1):.4f} "
@@ -236,19 +310,25 @@ def main():
         "roofline": {
             "bound": "hbm",
             "kernel": k1,
-            "bytes_per_launch": k1_bytes,
             "achieved": k1_gbps,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": k1_gbps / HBM_PEAK_GBPS,
-            "traffic": None,
+            "traffic": counter_traffic(k1, f"{args.config}-{'one' if one_launch else 'two'}"),
+            "bytes_per_launch": k1_bytes,
+            "bytes_basis": ("the two-pass method's bytes per sequence (every draft row, the drawn row, "
+                            "q of the rejected row, ids, uniforms, outputs) from this run's accepted counts"),
+            "needed_bytes_per_launch": k1_needed,
+            "needed_GBps": k1_needed / (kt[k1] * 1e-3) / 1e9,
         },
         "path": {
             "plan": "one launch, stops reading rows at the first rejection" if one_launch else "two launches",
-            "algorithmic_bytes_per_step": path_bytes,
+            "method_bytes_per_step": path_bytes,
+            "needed_bytes_per_step": needed,
             "achieved_GBps": path_gbps,
             "frac_of_peak": path_gbps / HBM_PEAK_GBPS,
             "kernel_us": {n: t * 1e3 for n, t in ktimes},
+            "every_row_read": all_rows,
         },
         "acceptance": {"alpha_hat": float(alpha_hat), "tokens_per_round": float(np.mean(acc + 1)),
                        "accepted_per_drafted": float(acc.sum() / gam.sum())},
