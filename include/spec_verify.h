@@ -182,6 +182,9 @@ void spec_verify_destroy(spec_verify_ctx *ctx);
  * per run (0 if nothing was recorded) or a negative SV_* code.
  */
 int spec_verify_set_timing(spec_verify_ctx *ctx, int runs);
+/* Record only one run in every `stride` (>= 1; default 1) of the runs that follow, so
+ * that the events disturb a timed loop less. Returns SV_OK or SV_EINVAL. */
+int spec_verify_set_timing_stride(spec_verify_ctx *ctx, int stride);
 int spec_verify_kernel_times(spec_verify_ctx *ctx, float *ms, const char **names, int cap,
                              int *runs);
 

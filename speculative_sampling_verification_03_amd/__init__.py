@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     SV_PATH_AUTO, SV_PATH_ONE_LAUNCH, SV_PATH_TWO_LAUNCH,
     SpecVerifyError, load_library, spec_verify_check_args, spec_verify_create,
     spec_verify_destroy, spec_verify_kernel_times, spec_verify_last_error, spec_verify_last_path,
-    spec_verify_run, spec_verify_set_path, spec_verify_set_timing, spec_verify_status,
+    spec_verify_run, spec_verify_set_path, spec_verify_set_timing, spec_verify_set_timing_stride,
+    spec_verify_status,
 )
 from .verifier import Verifier, VerifyOutputs  # noqa: F401

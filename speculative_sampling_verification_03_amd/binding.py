@@ -25,7 +25,7 @@ _CODE_NAMES = {SV_OK: "SV_OK", SV_EINVAL: "SV_EINVAL", SV_ENOMEM: "SV_ENOMEM",
 EXPORTED = (
     "spec_verify_create", "spec_verify_run", "spec_verify_status",
     "spec_verify_last_error", "spec_verify_destroy", "spec_verify_set_timing",
-    "spec_verify_kernel_times", "spec_verify_check_args", "spec_verify_set_path",
+    "spec_verify_kernel_times", "spec_verify_check_args", "spec_verify_set_path", "spec_verify_set_timing_stride",
     "spec_verify_last_path",
 )
 
@@ -67,6 +67,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.spec_verify_kernel_times.restype = i32
     lib.spec_verify_check_args.argtypes = [i32] * 9 + [f32] + [i32] * 7 + [ctypes.c_char_p, i32]
     lib.spec_verify_check_args.restype = i32
+    lib.spec_verify_set_timing_stride.argtypes = [vp, i32]
+    lib.spec_verify_set_timing_stride.restype = i32
     lib.spec_verify_set_path.argtypes = [vp, i32]
     lib.spec_verify_set_path.restype = i32
     lib.spec_verify_last_path.argtypes = [vp]
@@ -142,6 +144,13 @@ def spec_verify_set_timing(ctx: int, runs: int) -> None:
     rc = load_library().spec_verify_set_timing(ctx, int(runs))
     if rc != SV_OK:
         raise SpecVerifyError(rc, _msg(ctx))
+
+
+def spec_verify_set_timing_stride(ctx: int, stride: int) -> None:
+    """Record one run in every `stride` of the following runs."""
+    rc = load_library().spec_verify_set_timing_stride(ctx, int(stride))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "bad stride" if ctx else "NULL context")
 
 
 def spec_verify_kernel_times(ctx: int, cap: int = 8):

@@ -328,6 +328,10 @@ constexpr int kSeqWaves = SV_SEQ_WAVES;
 constexpr int kSeqThreads = 64 * kSeqWaves;
 constexpr int kIter = 64 * kGroup;          // entries a wave covers per sweep iteration (1 group per lane)
 constexpr int kRing = SV_RING;              // sweep iterations held in registers (kRing - 1 in flight)
+#ifndef SV_RING1
+#define SV_RING1 4
+#endif
+constexpr int kRing1 = SV_RING1;            // the same for the one-launch row walk
 constexpr int kPass = kSeqWaves * kIter;    // entries the block covers per re-sweep pass
 
 // Raw bits of one group of 8 entries: one 16-byte vector for bf16, two for fp32.
@@ -787,7 +791,7 @@ __device__ __forceinline__ void stats_step(const Raw<T>& lr, float wgt, float k2
 // Walks the sequence's rows 0, 1, ... (row i at Lseq + i V) span by span: a span is
 // kSeqWaves chunks of 512 entries, wave w reading chunk w of each span (so the block
 // reads every row front to back). nitp, the spans per row rounded up to a multiple of
-// kRing, keeps every row starting at ring slot 0; the ring's loads run on into the next
+// kRing1, keeps every row starting at ring slot 0; the ring's loads run on into the next
 // row while row_end(i) judges row i. A span's address is a scalar base plus the lane's
 // fixed byte offset. With V >= one span (WIDE), the row's last span is read from
 // V - kSpan, overlapping the one before, and lanes whose entry lies before
@@ -805,9 +809,9 @@ __device__ __forceinline__ void walk_rows(const T* Lseq, int V, int g, Pro&& aft
   const int lane_off = wave * kIter + lane * kGroup;
   const uint32_t lane_byte = static_cast<uint32_t>(lane_off) * sizeof(T);
   const int nsp = (V + kSpan - 1) / kSpan;
-  const int nitp = (nsp + kRing - 1) / kRing * kRing;
+  const int nitp = (nsp + kRing1 - 1) / kRing1 * kRing1;
   const int total = g * nitp;
-  Raw<T> Lb[kRing];
+  Raw<T> Lb[kRing1];
   int jl = 0, il = 0, kl = 0;  // next (flattened) iteration to load: row il, span kl
   auto issue = [&](Raw<T>& dst) {
     const T* rowp = Lseq + static_cast<size_t>(il) * V;
@@ -829,16 +833,16 @@ __device__ __forceinline__ void walk_rows(const T* Lseq, int V, int g, Pro&& aft
     }
   };
 #pragma unroll
-  for (int k = 0; k < kRing - 1; ++k) {
+  for (int k = 0; k < kRing1 - 1; ++k) {
     issue(Lb[k]);
     issue_order_fence();
   }
   after_prologue();
   for (int i = 0; i < g; ++i) {
-    for (int k0 = 0; k0 < nitp; k0 += kRing) {
+    for (int k0 = 0; k0 < nitp; k0 += kRing1) {
 #pragma unroll
-      for (int r = 0; r < kRing; ++r) {
-        issue(Lb[(r + kRing - 1) % kRing]);
+      for (int r = 0; r < kRing1; ++r) {
+        issue(Lb[(r + kRing1 - 1) % kRing1]);
         const int k = k0 + r;
         if (k < nsp) step(Lb[r], k);
       }
@@ -1432,6 +1436,8 @@ struct spec_verify_ctx {
   bool ran = false;
   // measurement: a start and a stop event per kernel and recorded run, for up to timing_cap runs
   int timing_cap = 0, timing_runs = 0;
+  int timing_stride = 1;          // record one run in every timing_stride
+  long long timing_seen = 0;      // runs seen since recording was armed
   hipEvent_t* ev = nullptr;
   int timing_path = -1;  // the path of the recorded runs (runs on another path are not recorded)
   int path_mode = SV_PATH_AUTO, last_path = SV_PATH_AUTO;
@@ -1469,6 +1475,7 @@ struct DeviceGuard {
 // Events of this run when it is recorded, else nullptr.
 hipEvent_t* timing_slot(spec_verify_ctx* ctx, int path) {
   if (ctx->timing_runs >= ctx->timing_cap) return nullptr;
+  if (ctx->timing_seen++ % ctx->timing_stride != 0) return nullptr;
   if (ctx->timing_runs > 0 && ctx->timing_path != path) return nullptr;
   ctx->timing_path = path;
   return ctx->ev + static_cast<size_t>(ctx->timing_runs) * kEventsPerRun;
@@ -1778,6 +1785,7 @@ int spec_verify_set_timing(spec_verify_ctx* ctx, int runs) {
   ctx->ev = new (std::nothrow) hipEvent_t[n]();
   if (!ctx->ev) return SV_ENOMEM;
   ctx->timing_cap = runs;
+  ctx->timing_seen = 0;
   for (size_t i = 0; i < n; ++i) {
     const hipError_t e = hipEventCreate(&ctx->ev[i]);
     if (e != hipSuccess) {
@@ -1786,6 +1794,13 @@ int spec_verify_set_timing(spec_verify_ctx* ctx, int runs) {
     }
   }
   ctx->timing_runs = 0;
+  return SV_OK;
+}
+
+int spec_verify_set_timing_stride(spec_verify_ctx* ctx, int stride) {
+  if (!ctx || stride < 1) return SV_EINVAL;
+  ctx->timing_stride = stride;
+  ctx->timing_seen = 0;
   return SV_OK;
 }
 
@@ -1811,6 +1826,7 @@ int spec_verify_kernel_times(spec_verify_ctx* ctx, float* ms, const char** names
     if (names) names[k] = path.names[k];
   }
   ctx->timing_runs = 0;  // the next runs record afresh
+  ctx->timing_seen = 0;
   const int nk = path.nk;
   ctx->timing_path = -1;
   return nk;

@@ -9,7 +9,8 @@ from typing import NamedTuple, Optional
 
 from .binding import (SV_BF16, SV_EDATA, SV_F32, spec_verify_create, spec_verify_destroy,
                       spec_verify_kernel_times, spec_verify_last_error, spec_verify_last_path,
-                      spec_verify_run, spec_verify_set_path, spec_verify_set_timing, spec_verify_status)
+                      spec_verify_run, spec_verify_set_path, spec_verify_set_timing,
+                      spec_verify_set_timing_stride, spec_verify_status)
 
 
 class VerifyOutputs(NamedTuple):
@@ -114,9 +115,10 @@ class Verifier:
     def last_error(self) -> str:
         return spec_verify_last_error(self.ctx)
 
-    def set_timing(self, runs: int):
-        """Record per-kernel events for the next `runs` runs (0: off)."""
+    def set_timing(self, runs: int, stride: int = 1):
+        """Record per-kernel events for `runs` of the next runs, one in every `stride` (0 runs: off)."""
         spec_verify_set_timing(self.ctx, runs)
+        spec_verify_set_timing_stride(self.ctx, stride)
 
     def kernel_times(self):
         """([(kernel, mean ms), ...], runs) over the recorded runs."""

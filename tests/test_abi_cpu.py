@@ -93,6 +93,7 @@ def test_null_context_calls():
     assert lib.spec_verify_kernel_times(None, None, None, 0, None) == -sv.SV_EINVAL
     assert lib.spec_verify_last_error(None) == b""
     assert lib.spec_verify_set_path(None, sv.SV_PATH_AUTO) == sv.SV_EINVAL
+    assert lib.spec_verify_set_timing_stride(None, 2) == sv.SV_EINVAL
     assert lib.spec_verify_last_path(None) == -sv.SV_EINVAL
     lib.spec_verify_destroy(None)  # NULL-safe
     rc = lib.spec_verify_run(None, None, 1, 1, None, 1, 1.0, None, None, None, None, None, None, None, None)
