@@ -332,6 +332,10 @@ constexpr int kRing = SV_RING;              // sweep iterations held in register
 #define SV_RING1 4
 #endif
 constexpr int kRing1 = SV_RING1;            // the same for the one-launch row walk
+#ifndef SV_NT_DRAW
+#define SV_NT_DRAW 0
+#endif
+constexpr bool kNtDraw = SV_NT_DRAW;        // nontemporal loads for the table draw's sweep
 constexpr int kPass = kSeqWaves * kIter;    // entries the block covers per re-sweep pass
 
 // Raw bits of one group of 8 entries: one 16-byte vector for bf16, two for fp32.
@@ -349,11 +353,11 @@ __device__ __forceinline__ uint32_t elem_bits(const float* p, int e) { return __
 
 // Group starting at entry e of `row`, known to lie inside the row (no check, so a
 // loop of these keeps a fixed number of loads in flight).
-template <typename T>
+template <typename T, bool NT = false>
 __device__ __forceinline__ void load_raw_in(const T* __restrict__ row, int e, Raw<T>& r) {
   const uint4* p = reinterpret_cast<const uint4*>(row + e);
 #pragma unroll
-  for (int i = 0; i < Raw<T>::N; ++i) r.v[i] = p[i];
+  for (int i = 0; i < Raw<T>::N; ++i) r.v[i] = load16<NT>(p + i);
 }
 
 // Group starting at entry e of `row`; entries at or past `lim` read as `fill`.
@@ -797,10 +801,10 @@ __device__ __forceinline__ void stats_step(const Raw<T>& lr, float wgt, float k2
 // V - kSpan, overlapping the one before, and lanes whose entry lies before
 // (nsp - 1) kSpan must not count it (row_weight gives the lane's weight for the last
 // span); otherwise the single span's lanes past V read the row's last group instead
-// and must not count it. Padding spans re-read the last span and are not handed to
+// and must not count it. NT makes the loads nontemporal. Padding spans re-read the last span and are not handed to
 // step. step(buf, k) gets the span index k < nsp; after_prologue() runs once the first
 // loads are in flight; row_end(i) returns true to stop.
-template <typename T, bool WIDE, typename Pro, typename Step, typename RowEnd>
+template <typename T, bool WIDE, bool NT, typename Pro, typename Step, typename RowEnd>
 __device__ __forceinline__ void walk_rows(const T* Lseq, int V, int g, Pro&& after_prologue, Step&& step,
                                           RowEnd&& row_end) {
   const int lane = threadIdx.x & 63;
@@ -820,9 +824,9 @@ __device__ __forceinline__ void walk_rows(const T* Lseq, int V, int g, Pro&& aft
       const char* sb = reinterpret_cast<const char*>(rowp + e0);
       const uint4* p = reinterpret_cast<const uint4*>(sb + lane_byte);
 #pragma unroll
-      for (int q = 0; q < Raw<T>::N; ++q) dst.v[q] = p[q];
+      for (int q = 0; q < Raw<T>::N; ++q) dst.v[q] = load16<NT>(p + q);
     } else {
-      load_raw_in(rowp, min(lane_off, V - kGroup), dst);
+      load_raw_in<T, NT>(rowp, min(lane_off, V - kGroup), dst);
     }
     if (jl < total - 1) {
       ++jl;
@@ -906,11 +910,13 @@ __device__ __forceinline__ bool final_draw_tab(const Args& a, int b, int base, i
                                                const double* sT) {
   __shared__ double s_reg[kSeqWaves][3];  // residual: (D, Q, Zr); bonus: (s, -, -)
   __shared__ uint32_t s_mx[kSeqWaves];
-  __shared__ double s_wt[kSeqWaves];
-  __shared__ int s_wc[kSeqWaves], s_wl[kSeqWaves];
-  __shared__ double s_bc[5];  // t, P (prefix before the region), Z64, delta, S
-  __shared__ int s_bi[4];     // region r*, kind, take_last, ok
+  __shared__ double s_wt[2][kSeqWaves];   // re-sweep: per-wave totals, by pass parity
+  __shared__ int s_cand, s_last;          // re-sweep: first crossing, last positive entry
   const int lane = threadIdx.x & 63;
+  if (threadIdx.x == 0) {
+    s_cand = INT_MAX;
+    s_last = -1;
+  }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int V = a.V;
   const uint32_t tlo = a.tlo, thi = a.thi;
@@ -958,16 +964,16 @@ __device__ __forceinline__ bool final_draw_tab(const Args& a, int b, int base, i
       auto at = [&](int it) { return eb + min(it, last) * kIter; };
 #pragma unroll
       for (int k = 0; k < kRing - 1; ++k) {
-        load_raw_in(lrow, at(k), Lb[k]);
-        load_raw_in(qrow, at(k), Qb[k]);
+        load_raw_in<uint16_t, kNtDraw>(lrow, at(k), Lb[k]);
+        load_raw_in<float, kNtDraw>(qrow, at(k), Qb[k]);
         issue_order_fence();
       }
       for (int it = 0; it < nfull; it += kRing) {
 #pragma unroll
         for (int k = 0; k < kRing; ++k) {
           const int nb = (k + kRing - 1) % kRing;
-          load_raw_in(lrow, at(it + k + kRing - 1), Lb[nb]);
-          load_raw_in(qrow, at(it + k + kRing - 1), Qb[nb]);
+          load_raw_in<uint16_t, kNtDraw>(lrow, at(it + k + kRing - 1), Lb[nb]);
+          load_raw_in<float, kNtDraw>(qrow, at(it + k + kRing - 1), Qb[nb]);
           if (k == 0 || it + k < nfull) step(Lb[k], Qb[k]);
         }
       }
@@ -976,16 +982,16 @@ __device__ __forceinline__ bool final_draw_tab(const Args& a, int b, int base, i
       Raw<uint16_t> lr;
       Raw<float> qr;
       const int e = e0 + lane * kGroup;
-      load_raw_in(lrow, min(e, r1 - kGroup), lr);
-      load_raw_in(qrow, min(e, r1 - kGroup), qr);
+      load_raw_in<uint16_t, kNtDraw>(lrow, min(e, r1 - kGroup), lr);
+      load_raw_in<float, kNtDraw>(qrow, min(e, r1 - kGroup), qr);
       if (e < r1) step(lr, qr);
     }
-    D = wave_sum(D);
-    Zr = wave_sum(Zr);
-    Q = wave_sum(Q);
+    D = wave_sum_dpp(D);
+    Zr = wave_sum_dpp(Zr);
+    const double Qd = wave_sum_dpp(static_cast<double>(Q));
     if (lane == 0) {
       s_reg[wave][0] = D;
-      s_reg[wave][1] = Q;
+      s_reg[wave][1] = Qd;
       s_reg[wave][2] = Zr;
     }
   } else {
@@ -1002,13 +1008,13 @@ __device__ __forceinline__ bool final_draw_tab(const Args& a, int b, int base, i
       auto at = [&](int it) { return eb + min(it, last) * kIter; };
 #pragma unroll
       for (int k = 0; k < kRing - 1; ++k) {
-        load_raw_in(lrow, at(k), Lb[k]);
+        load_raw_in<uint16_t, kNtDraw>(lrow, at(k), Lb[k]);
         issue_order_fence();
       }
       for (int it = 0; it < nfull; it += kRing) {
 #pragma unroll
         for (int k = 0; k < kRing; ++k) {
-          load_raw_in(lrow, at(it + k + kRing - 1), Lb[(k + kRing - 1) % kRing]);
+          load_raw_in<uint16_t, kNtDraw>(lrow, at(it + k + kRing - 1), Lb[(k + kRing - 1) % kRing]);
           if (k == 0 || it + k < nfull) step(Lb[k]);
         }
       }
@@ -1016,84 +1022,67 @@ __device__ __forceinline__ bool final_draw_tab(const Args& a, int b, int base, i
     for (int e0 = mstart; e0 < r1; e0 += kIter) {
       Raw<uint16_t> lr;
       const int e = e0 + lane * kGroup;
-      load_raw_in(lrow, min(e, r1 - kGroup), lr);
+      load_raw_in<uint16_t, kNtDraw>(lrow, min(e, r1 - kGroup), lr);
       if (e < r1) step(lr);
     }
-    sacc = wave_sum(sacc);
+    sacc = wave_sum_dpp(sacc);
     if (lane == 0) {
       s_reg[wave][0] = sacc;
       s_reg[wave][1] = 0.0;
       s_reg[wave][2] = 0.0;
     }
   }
-  mx = static_cast<uint32_t>(wave_max_int(static_cast<int>(mx)));
+  mx = static_cast<uint32_t>(wave_max_int_dpp(static_cast<int>(mx)));
   if (lane == 0) s_mx[wave] = mx;
   __syncthreads();
 
-  // ---- totals and the region where the inclusive prefix first exceeds t
+  // ---- totals and the region where the inclusive prefix first exceeds t: every wave
+  // reads the 16 region sums and takes the same decision (lane r holds region r)
   const float uf = a.u[base + b + g];
-  if (wave == 0) {
-    const double u = uf;
-    const int r = lane < kSeqWaves ? lane : 0;
-    const bool live = lane < kSeqWaves;
-    const bool ok = __ballot(live && s_mx[r] > thi) == 0;
-    int kind;  // 0: residual; 1: degenerate residual (S <= 0), draw from p; 2: bonus from p
-    double Z64, S = 0.0, delta = 0.0, t, wgt;
-    if (residual) {
-      Z64 = wave_sum(live ? s_reg[r][2] : 0.0);
-      delta = (Z64 - Zq) / Z64;
-      wgt = live ? s_reg[r][0] / Z64 - s_reg[r][1] * delta : 0.0;
-      S = wave_sum(wgt);
-      kind = S > 0.0 ? 0 : 1;
-      if (kind == 1) wgt = live ? s_reg[r][2] : 0.0;
-      t = kind == 0 ? u * S : u * Z64;
-    } else {
-      wgt = live ? s_reg[r][0] : 0.0;
-      Z64 = wave_sum(wgt);
-      kind = 2;
-      t = u * Z64;
-    }
-    const double ex = wave_excl_scan(wgt);
-    const unsigned long long cross = __ballot(live && ex + wgt > t);
-    int rs = cross ? __ffsll(cross) - 1 : -1;
-    double P = __shfl(ex, rs < 0 ? 0 : rs);
-    int take_last = 0;
-    if (rs < 0) {  // no crossing (rounding, or u >= 1): last positive-weight token
-      take_last = 1;
-      const unsigned long long pos = __ballot(live && wgt > 0.0);
-      rs = pos ? 63 - __clzll(pos) : -1;
-      P = 0.0;
-    }
-    if (lane == 0) {
-      s_bc[0] = t;
-      s_bc[1] = P;
-      s_bc[2] = Z64;
-      s_bc[3] = delta;
-      s_bc[4] = S;
-      s_bi[0] = rs;
-      s_bi[1] = kind;
-      s_bi[2] = take_last;
-      s_bi[3] = ok ? 1 : 0;
-    }
+  const double u = uf;
+  const int r = lane < kSeqWaves ? lane : 0;
+  const bool live = lane < kSeqWaves;
+  if (__ballot(live && s_mx[r] > thi) != 0) return false;
+  int kind;  // 0: residual; 1: degenerate residual (S <= 0), draw from p; 2: bonus from p
+  double Z64, S = 0.0, delta = 0.0, t, wgt;
+  if (residual) {
+    Z64 = wave_sum_dpp(live ? s_reg[r][2] : 0.0);
+    delta = (Z64 - Zq) / Z64;
+    wgt = live ? s_reg[r][0] / Z64 - s_reg[r][1] * delta : 0.0;
+    S = wave_sum_dpp(wgt);
+    kind = S > 0.0 ? 0 : 1;
+    if (kind == 1) wgt = live ? s_reg[r][2] : 0.0;
+    t = kind == 0 ? u * S : u * Z64;
+  } else {
+    wgt = live ? s_reg[r][0] : 0.0;
+    Z64 = wave_sum_dpp(wgt);
+    kind = 2;
+    t = u * Z64;
   }
-  __syncthreads();
-  if (!s_bi[3]) return false;
+  const double inc = wave_incl_scan_dpp(wgt);
+  const unsigned long long cross = __ballot(live && inc > t);
+  int rs = cross ? __ffsll(cross) - 1 : -1;
+  double run = readlane_d(inc - wgt, rs < 0 ? 0 : rs);
+  bool take_last = false;
+  if (rs < 0) {  // no crossing (rounding, or u >= 1): last positive-weight token
+    take_last = true;
+    const unsigned long long pos = __ballot(live && wgt > 0.0);
+    rs = pos ? 63 - __clzll(pos) : -1;
+    run = 0.0;
+  }
   if (threadIdx.x == 0) {
-    if (!(s_bc[2] > 0.0 && s_bc[2] <= DBL_MAX)) atomicOr(a.err, SV_DATA_NONFINITE);
+    if (!(Z64 > 0.0 && Z64 <= DBL_MAX)) atomicOr(a.err, SV_DATA_NONFINITE);
     if (!(uf >= 0.f && uf < 1.f)) atomicOr(a.err, SV_DATA_UNIFORM);
   }
-  const double t = s_bc[0], Z64 = s_bc[2], delta = s_bc[3], S = s_bc[4];
-  const int rs = s_bi[0], kind = s_bi[1];
-  const bool take_last = s_bi[2] != 0;
 
-  // ---- re-sweep of region r* in passes of kPass entries (as in final_draw)
+  // ---- re-sweep of region r* in passes of kPass entries: wave w scans the w-th kIter
+  // entries of a pass, lane l owns 8 consecutive entries; two barriers per pass
   int tok = V - 1;
   if (rs >= 0) {
     const int R0 = min(V, rs * rw), R1 = min(V, R0 + rw);
     const double invZ = 1.0 / Z64;
-    double run = s_bc[1];
-    int cand = INT_MAX, lastpos = -1;
-    for (int p0 = R0; p0 < R1 && cand == INT_MAX; p0 += kPass) {
+    int parity = 0;
+    for (int p0 = R0; p0 < R1; p0 += kPass, parity ^= 1) {
       const int e = p0 + wave * kIter + lane * kGroup;
       const bool in = e < R1;
       Raw<uint16_t> lr;
@@ -1118,11 +1107,16 @@ __device__ __forceinline__ bool final_draw_tab(const Args& a, int b, int base, i
         rv[j] = in ? wv : 0.0;
         tot += rv[j];
       }
-      const double lex = wave_excl_scan(tot);
-      if (lane == 63) s_wt[wave] = lex + tot;
+      const double linc = wave_incl_scan_dpp(tot);
+      const double lex = linc - tot;
+      if (lane == 63) s_wt[parity][wave] = linc;
       __syncthreads();
-      double acc = run;
-      for (int w2 = 0; w2 < wave; ++w2) acc += s_wt[w2];
+      double acc = run, tsum = run;
+      for (int w2 = 0; w2 < kSeqWaves; ++w2) {
+        const double v2 = s_wt[parity][w2];
+        if (w2 < wave) acc += v2;
+        tsum += v2;
+      }
       acc += lex;
       int c2 = INT_MAX, lp = -1;
 #pragma unroll
@@ -1131,26 +1125,17 @@ __device__ __forceinline__ bool final_draw_tab(const Args& a, int b, int base, i
         if (!take_last && c2 == INT_MAX && acc > t) c2 = e + j;
         if (rv[j] > 0.0) lp = e + j;
       }
-      c2 = wave_min_int(c2);
-      lp = wave_max_int(lp);
+      c2 = wave_min_int_dpp(c2);
+      lp = wave_max_int_dpp(lp);
       if (lane == 0) {
-        s_wc[wave] = c2;
-        s_wl[wave] = lp;
+        if (c2 != INT_MAX) atomicMin(&s_cand, c2);
+        if (lp >= 0) atomicMax(&s_last, lp);
       }
-      __syncthreads();
-      int cm = INT_MAX, lm = -1;
-      double tsum = run;
-      for (int w2 = 0; w2 < kSeqWaves; ++w2) {
-        cm = min(cm, s_wc[w2]);
-        lm = max(lm, s_wl[w2]);
-        tsum += s_wt[w2];
-      }
-      cand = cm;
-      lastpos = max(lastpos, lm);
       run = tsum;
       __syncthreads();
+      if (s_cand != INT_MAX) break;
     }
-    tok = cand != INT_MAX ? cand : (lastpos >= 0 ? lastpos : V - 1);
+    tok = s_cand != INT_MAX ? s_cand : (s_last >= 0 ? s_last : V - 1);
   }
   if (threadIdx.x == 0) {
     a.emitted[base + b + n] = tok;
@@ -1166,7 +1151,7 @@ __device__ __forceinline__ bool final_draw_tab(const Args& a, int b, int base, i
 // that, with no running max. A wave whose sum overflows (a value more than ~100 octaves
 // above that first chunk's max) or is not finite redoes its chunks of the row with the
 // running max. Returns n; s_cz[i] = (c, z) of each judged row.
-template <typename T, bool WIDE, typename Hook>
+template <typename T, bool WIDE, bool NT, typename Hook>
 __device__ __forceinline__ int judge_rows_exact(const Args& a, int b, int base, int g, float2* s_cz, Hook&& hook) {
   __shared__ float2 s_part[kSeqWaves];
   const int lane = threadIdx.x & 63;
@@ -1190,7 +1175,7 @@ __device__ __forceinline__ int judge_rows_exact(const Args& a, int b, int base, 
   float sacc[kGroup];
 #pragma unroll
   for (int j = 0; j < kGroup; ++j) sacc[j] = 0.f;
-  walk_rows<T, WIDE>(
+  walk_rows<T, WIDE, NT>(
       Lseq, V, g,
       [&] {
         // the 32-bit word holding l[x] (rows are 16-byte aligned on this path)
@@ -1274,10 +1259,18 @@ __device__ __forceinline__ int judge_rows_exact(const Args& a, int b, int base, 
         }
         return false;
       });
+  // the accepted drafts and the count, from the operands already in wave 0's lanes
+  if (wave == 0) {
+    if (lane < n) a.emitted[base + b + lane] = x;
+    if (lane == 0) a.acc[b] = n;
+  }
   return n;
 }
 
-template <typename T, bool RAGGED>
+// NT1: the judged rows are read with nontemporal loads. Measured on MI355X this helps
+// when every sequence has its own compute unit (B <= CUs: C3, 4.6% faster) and costs
+// when workgroups run in several rounds (C5, 1.6% slower), so the host picks it by B.
+template <typename T, bool RAGGED, bool NT1>
 __global__ __launch_bounds__(kSeqThreads) void k_verify_seq(Args a) {
   __shared__ double s_tab[kExpN];
   __shared__ float2 s_cz[kFuseMaxGamma];
@@ -1299,12 +1292,13 @@ __global__ __launch_bounds__(kSeqThreads) void k_verify_seq(Args a) {
       if (tab) tab_build(sT, a);
     };
     const int n = g == 0 ? 0
-                  : a.V >= kSeqWaves * kIter ? judge_rows_exact<T, true>(a, b, base, g, s_cz, hook)
-                                             : judge_rows_exact<T, false>(a, b, base, g, s_cz, hook);
-    if (g == 0 && tab) tab_build(sT, a);
+                  : a.V >= kSeqWaves * kIter ? judge_rows_exact<T, true, NT1>(a, b, base, g, s_cz, hook)
+                                             : judge_rows_exact<T, false, NT1>(a, b, base, g, s_cz, hook);
+    if (g == 0) {
+      if (tab) tab_build(sT, a);
+      if (threadIdx.x == 0) a.acc[b] = 0;
+    }
     __syncthreads();  // s_cz of row n, s_tab, sT
-    for (int i = threadIdx.x; i < n; i += kSeqThreads) a.emitted[base + b + i] = a.ids[base + i];
-    if (threadIdx.x == 0) a.acc[b] = n;
     const double cr = n < g ? static_cast<double>(s_cz[n].x) : 0.0;
     const double zr = n < g ? static_cast<double>(s_cz[n].y) : 0.0;
     // table scale: sum 2^(l k2) = z 2^c
@@ -1312,11 +1306,10 @@ __global__ __launch_bounds__(kSeqThreads) void k_verify_seq(Args a) {
     final_draw<T, true>(a, b, base, g, n, cr, zr, s_tab);
   } else {
     const int n = g == 0 ? 0
-                  : a.V >= kSeqWaves * kIter ? judge_rows_exact<T, true>(a, b, base, g, s_cz, [] {})
-                                             : judge_rows_exact<T, false>(a, b, base, g, s_cz, [] {});
+                  : a.V >= kSeqWaves * kIter ? judge_rows_exact<T, true, NT1>(a, b, base, g, s_cz, [] {})
+                                             : judge_rows_exact<T, false, NT1>(a, b, base, g, s_cz, [] {});
+    if (g == 0 && threadIdx.x == 0) a.acc[b] = 0;
     __syncthreads();  // s_cz of row n, s_tab
-    for (int i = threadIdx.x; i < n; i += kSeqThreads) a.emitted[base + b + i] = a.ids[base + i];
-    if (threadIdx.x == 0) a.acc[b] = n;
     final_draw<T, true>(a, b, base, g, n, n < g ? static_cast<double>(s_cz[n].x) : 0.0,
                         n < g ? static_cast<double>(s_cz[n].y) : 0.0, s_tab);
   }
@@ -1491,8 +1484,9 @@ hipError_t launch_one(const void* fn, dim3 grid, dim3 block, const Args& a, hipS
 template <typename T, bool RG>
 hipError_t launch_fused(spec_verify_ctx* ctx, const Args& a, hipStream_t st) {
   hipEvent_t* ev = timing_slot(ctx, kPathSample1);
-  const hipError_t e =
-      launch_one(reinterpret_cast<const void*>(&k_verify_seq<T, RG>), dim3(a.B), dim3(kSeqThreads), a, st, ev, 0);
+  const void* fn = a.B <= ctx->cus ? reinterpret_cast<const void*>(&k_verify_seq<T, RG, true>)
+                                   : reinterpret_cast<const void*>(&k_verify_seq<T, RG, false>);
+  const hipError_t e = launch_one(fn, dim3(a.B), dim3(kSeqThreads), a, st, ev, 0);
   if (e != hipSuccess) return e;
   if (ev) ++ctx->timing_runs;
   return hipGetLastError();

@@ -21,6 +21,18 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float bf16_word_half(uint32_t w, int hi) { return hi ? bf16_hi(w) : bf16_lo(w); }
 
+// 16-byte load; NT marks it nontemporal (streamed data that is not read again soon).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+template <bool NT>
+__device__ __forceinline__ uint4 load16(const uint4* p) {
+  if constexpr (NT) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+  } else {
+    return *p;
+  }
+}
+
 // One aligned group of 8 logits starting at element offset `e` of `p`.
 __device__ __forceinline__ void load_group(const uint16_t* __restrict__ p, size_t e, float x[8]) {
   const uint4 v = *reinterpret_cast<const uint4*>(p + e);
@@ -99,6 +111,60 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
   const float r2 = __int_as_float(__builtin_amdgcn_readlane(x, 32));
   const float r3 = __int_as_float(__builtin_amdgcn_readlane(x, 48));
   return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// ---------------------------------------------------------------- DPP forms (no LDS round trip)
+// DPP controls used below: quad_perm [1,0,3,2] 0xB1, quad_perm [2,3,0,1] 0x4E,
+// row_half_mirror 0x141, row_mirror 0x140, row_shr:n 0x110 + n, row_bcast:15 0x142,
+// row_bcast:31 0x143. Lanes of disabled rows (and, with BOUND, lanes whose source lies
+// outside the row) receive `old`.
+template <int CTRL, int ROWS = 0xF, bool BOUND = false>
+__device__ __forceinline__ double dpp_d(double v, double old) {
+  const int lo = __builtin_amdgcn_update_dpp(__double2loint(old), __double2loint(v), CTRL, ROWS, 0xF, BOUND);
+  const int hi = __builtin_amdgcn_update_dpp(__double2hiint(old), __double2hiint(v), CTRL, ROWS, 0xF, BOUND);
+  return __hiloint2double(hi, lo);
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ double readlane_d(double v, int l) {
+  return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), l),
+                          __builtin_amdgcn_readlane(__double2loint(v), l));
+}
+// Sum over the wave; the result is wave-uniform.
+__device__ __forceinline__ double wave_sum_dpp(double v) {
+  v += dpp_d<0xB1>(v, 0.0);
+  v += dpp_d<0x4E>(v, 0.0);
+  v += dpp_d<0x141>(v, 0.0);
+  v += dpp_d<0x140>(v, 0.0);
+  return (readlane_d(v, 0) + readlane_d(v, 16)) + (readlane_d(v, 32) + readlane_d(v, 48));
+}
+// Inclusive prefix sum over the lanes of the wave, in lane order.
+__device__ __forceinline__ double wave_incl_scan_dpp(double v) {
+  v += dpp_d<0x111, 0xF, true>(v, 0.0);
+  v += dpp_d<0x112, 0xF, true>(v, 0.0);
+  v += dpp_d<0x114, 0xF, true>(v, 0.0);
+  v += dpp_d<0x118, 0xF, true>(v, 0.0);
+  v += dpp_d<0x142, 0xA>(v, 0.0);  // row 0's total into row 1, row 2's into row 3
+  v += dpp_d<0x143, 0xC>(v, 0.0);  // lane 31's total into rows 2 and 3
+  return v;
+}
+__device__ __forceinline__ int wave_min_int_dpp(int x) {
+  x = min(x, dpp_i<0xB1>(x));
+  x = min(x, dpp_i<0x4E>(x));
+  x = min(x, dpp_i<0x141>(x));
+  x = min(x, dpp_i<0x140>(x));
+  return min(min(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+             min(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
+}
+__device__ __forceinline__ int wave_max_int_dpp(int x) {
+  x = max(x, dpp_i<0xB1>(x));
+  x = max(x, dpp_i<0x4E>(x));
+  x = max(x, dpp_i<0x141>(x));
+  x = max(x, dpp_i<0x140>(x));
+  return max(max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+             max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
 }
 
 // ---------------------------------------------------------------- wave / block reductions
