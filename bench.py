@@ -93,6 +93,43 @@ def counter_traffic(kernel, workload_tag):
     return None
 
 
+def bench_sampling(sv, torch, sets, dev, code, args, iters=100):
+    """Tokens/s of spec_sample_run on the workload's target rows (softmax of the logits)
+    and on its draft rows (fp32 weights q), with inputs resident in HBM."""
+    import numpy as np
+    res = {}
+    w0, d0 = sets[0]
+    sl = 2 if w0.dtype == "bf16" else 4
+    for name, x, rows, per_row in (
+            ("target_rows_from_logits", [d["logits"] for _, d in sets], w0.target_rows, w0.V * sl),
+            ("draft_rows_from_q", [d["q"] for _, d in sets], w0.draft_rows, w0.V * 4)):
+        v = sv.Verifier(w0.V, code, rows, 1, 1)
+        u = torch.rand(rows, device=dev)
+        tok = torch.empty(rows, dtype=torch.int32, device=dev)
+
+        def go(k):
+            if name == "target_rows_from_logits":
+                v.sample(x[k % len(x)], uniforms=u, temperature=w0.T, tokens=tok)
+            else:
+                v.sample_weights(x[k % len(x)], uniforms=u, tokens=tok)
+        for k in range(10):
+            go(k)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(iters):
+            go(k)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / iters
+        assert v.status() == sv.SV_OK, v.last_error()
+        v.close()
+        nbytes = rows * (per_row + 8)
+        res[name] = {"rows": rows, "us_per_call": dt * 1e6, "tokens_per_s": rows / dt,
+                     "GBps": nbytes / dt / 1e9, "frac_of_peak": nbytes / dt / 1e9 / HBM_PEAK_GBPS}
+        log(f"[bench] F1 sampling {name}: {rows} rows in {dt * 1e6:.1f} us, "
+            f"{nbytes / dt / 1e9:.0f} GB/s")
+    return res
+
+
 def cpu_baseline(w, seconds):
     """The oracle as it stands, single process, cycling over the sequences of one input
     set until about `seconds` of CPU work have been done."""
@@ -127,6 +164,7 @@ def main():
     ap.add_argument("--sets", type=int, default=2, help="input sets rotated across steps")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-next", action="store_true", help="skip the follow-on measurements (F1 sampling)")
     ap.add_argument("--no-every-row", action="store_true",
                     help="skip the second timing with p(x) requested (every draft row read)")
     ap.add_argument("--plan", choices=("auto", "two", "one"), default="auto",
@@ -278,6 +316,11 @@ def main():
         log(f"[bench] every row read (p(x) requested): {ms_all * 1e3:.2f} us/step, "
             f"{all_rows['value'] / 1e6:.2f} M positions/s")
 
+    # follow-on F1: one token per row from a given distribution, on this workload's rows
+    next_rows = {}
+    if not args.no_next and w0.T > 0:
+        next_rows["F1_sample"] = bench_sampling(sv, torch, sets, dev, code, args)
+
     # acceptance metrics of the measured inputs
     acc = np.concatenate(nb)
     gam = np.concatenate([w.gammas for w, _ in sets]).astype(np.int64)
@@ -333,6 +376,7 @@ def main():
             "kernel_us": {n: t * 1e3 for n, t in ktimes},
             "every_row_read": all_rows,
         },
+        "next_rows": next_rows,
         "acceptance": {"alpha_hat": float(alpha_hat), "tokens_per_round": float(np.mean(acc + 1)),
                        "accepted_per_drafted": float(acc.sum() / gam.sum())},
     }

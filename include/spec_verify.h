@@ -157,6 +157,28 @@ int spec_verify_set_path(spec_verify_ctx *ctx, int mode);
 int spec_verify_last_path(const spec_verify_ctx *ctx);
 
 /*
+ * Sampling one token per row from a given distribution: the draw of verification on
+ * its own (decoding with the target alone, x ~ p, or drawing drafts, x ~ q), following
+ * the draw's rule: t = u * sum(w) over the row's weights w, the token is the first id
+ * whose inclusive prefix sum exceeds t, else the last id with positive weight.
+ *   rows       number of rows (0 <= rows <= the context's max_batch; 0 enqueues nothing).
+ *   mode       SV_SAMPLE_LOGITS: `x` is [rows, V] logits in the context's dtype and the
+ *              weights are softmax(l / T); T == 0 takes the argmax (lowest index on ties)
+ *              and ignores `uniforms`. This is spec_verify_run with gamma = 0.
+ *              SV_SAMPLE_WEIGHTS: `x` is [rows, V] fp32 weights >= 0 (probabilities or
+ *              any unnormalised weights; 4-byte aligned); T is ignored.
+ *   uniforms   fp32 [rows] in [0, 1), one per row.
+ *   tokens     int32 [rows] output.
+ * Errors: SV_EINVAL (NULL ctx or pointer, rows out of range, unknown mode, bad T),
+ * SV_EHIP. Data errors (sticky flag, spec_verify_status): negative or non-finite
+ * weights count as 0 and set SV_DATA_NONFINITE, as does a row whose sum is not
+ * positive (its token is then V - 1); a uniform outside [0, 1) sets SV_DATA_UNIFORM.
+ */
+enum { SV_SAMPLE_LOGITS = 0, SV_SAMPLE_WEIGHTS = 1 };
+int spec_sample_run(spec_verify_ctx *ctx, void *hip_stream, int rows, int mode, float temperature,
+                    const void *x, const float *uniforms, int32_t *tokens);
+
+/*
  * Synchronize the stream of the last run, read and clear the device's sticky
  * data-error flag. Returns SV_OK, SV_EDATA (details in spec_verify_last_error),
  * SV_EHIP, or SV_EINVAL for a NULL ctx.

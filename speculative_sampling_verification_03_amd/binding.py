@@ -19,6 +19,7 @@ SV_OK, SV_EINVAL, SV_ENOMEM, SV_EHIP, SV_EDATA = 0, 1, 2, 3, 4
 SV_F32, SV_BF16 = 0, 1
 SV_DATA_DRAFT_ID, SV_DATA_NONFINITE, SV_DATA_UNIFORM, SV_DATA_CU_GAMMA = 1, 2, 4, 8
 SV_PATH_AUTO, SV_PATH_TWO_LAUNCH, SV_PATH_ONE_LAUNCH = 0, 1, 2
+SV_SAMPLE_LOGITS, SV_SAMPLE_WEIGHTS = 0, 1
 _CODE_NAMES = {SV_OK: "SV_OK", SV_EINVAL: "SV_EINVAL", SV_ENOMEM: "SV_ENOMEM",
                SV_EHIP: "SV_EHIP", SV_EDATA: "SV_EDATA"}
 
@@ -26,7 +27,7 @@ EXPORTED = (
     "spec_verify_create", "spec_verify_run", "spec_verify_status",
     "spec_verify_last_error", "spec_verify_destroy", "spec_verify_set_timing",
     "spec_verify_kernel_times", "spec_verify_check_args", "spec_verify_set_path", "spec_verify_set_timing_stride",
-    "spec_verify_last_path",
+    "spec_verify_last_path", "spec_sample_run",
 )
 
 
@@ -67,6 +68,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.spec_verify_kernel_times.restype = i32
     lib.spec_verify_check_args.argtypes = [i32] * 9 + [f32] + [i32] * 7 + [ctypes.c_char_p, i32]
     lib.spec_verify_check_args.restype = i32
+    lib.spec_sample_run.argtypes = [vp, vp, i32, i32, f32, vp, vp, vp]
+    lib.spec_sample_run.restype = i32
     lib.spec_verify_set_timing_stride.argtypes = [vp, i32]
     lib.spec_verify_set_timing_stride.restype = i32
     lib.spec_verify_set_path.argtypes = [vp, i32]
@@ -119,6 +122,15 @@ def spec_verify_run(ctx: int, stream, batch: int, gamma: int, cu_gamma, total_dr
         ctx, _stream(stream), batch, gamma, _ptr(cu_gamma), total_draft_rows, float(temperature),
         _ptr(logits), _ptr(q), _ptr(draft_ids), _ptr(uniforms), _ptr(accepted_count),
         _ptr(emitted_tokens), _ptr(residual_sum), _ptr(p_draft))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, _msg(ctx))
+
+
+def spec_sample_run(ctx: int, stream, rows: int, mode: int, temperature: float, x, uniforms, tokens) -> None:
+    """Enqueue one token per row drawn from logits (SV_SAMPLE_LOGITS) or fp32 weights
+    (SV_SAMPLE_WEIGHTS); raises SpecVerifyError on a non-OK code."""
+    rc = load_library().spec_sample_run(ctx, _stream(stream), rows, mode, float(temperature), _ptr(x),
+                                        _ptr(uniforms), _ptr(tokens))
     if rc != SV_OK:
         raise SpecVerifyError(rc, _msg(ctx))
 

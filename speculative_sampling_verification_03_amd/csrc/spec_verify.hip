@@ -1315,6 +1315,142 @@ __global__ __launch_bounds__(kSeqThreads) void k_verify_seq(Args a) {
   }
 }
 
+// ============================================================== sampling from given weights
+// One token per row from weights w >= 0 (fp32, normalised or not): the inverse CDF of
+// the draw ([P1] ch.2; [P3] 단계 1 draws the drafts from q), t = u sum(w), the first v
+// whose inclusive prefix exceeds t, else the last v with positive weight. Negative or
+// non-finite weights count as 0 and raise the non-finite flag. One 1024-thread
+// workgroup per row: a sweep of region sums in fp64 (wave w owns region w), every
+// wave's search over the 16 sums, a re-sweep of the crossing region.
+template <bool ALIGNED>
+__global__ __launch_bounds__(kSeqThreads) void k_sample_weights(const float* __restrict__ w, const float* u,
+                                                               int32_t* tokens, int* err, int V) {
+  __shared__ double s_reg[kSeqWaves];
+  __shared__ double s_wt[2][kSeqWaves];
+  __shared__ int s_cand, s_last, s_bad;
+  const int row = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (threadIdx.x == 0) {
+    s_cand = INT_MAX;
+    s_last = -1;
+    s_bad = 0;
+  }
+  const float* wrow = w + static_cast<size_t>(row) * V;
+  const int rw = region_width(V);
+  const int r0 = min(V, wave * rw), r1 = min(V, r0 + rw);
+  const int nfull = ALIGNED ? (r1 - r0) / kIter : 0;
+  const int mstart = r0 + nfull * kIter;
+  double acc = 0.0;
+  bool bad = false;
+  auto step = [&](const Raw<float>& r) {
+    float v[kGroup];
+    unpack(r, v);
+    double s0 = 0.0, s1 = 0.0;
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+      bad |= !(v[j] >= 0.f && v[j] <= FLT_MAX);
+      const double c = fmax(static_cast<double>(v[j]), 0.0);  // NaN -> 0
+      if (j & 1) s1 += c; else s0 += c;
+    }
+    acc += s0 + s1;
+  };
+  if (nfull > 0) {
+    Raw<float> Lb[kRing];
+    const int eb = r0 + lane * kGroup, last = nfull - 1;
+    auto at = [&](int it) { return eb + min(it, last) * kIter; };
+#pragma unroll
+    for (int k = 0; k < kRing - 1; ++k) {
+      load_raw_in(wrow, at(k), Lb[k]);
+      issue_order_fence();
+    }
+    for (int it = 0; it < nfull; it += kRing) {
+#pragma unroll
+      for (int k = 0; k < kRing; ++k) {
+        load_raw_in(wrow, at(it + k + kRing - 1), Lb[(k + kRing - 1) % kRing]);
+        if (k == 0 || it + k < nfull) step(Lb[k]);
+      }
+    }
+  }
+  for (int e0 = mstart; e0 < r1; e0 += kIter) {  // the rest of the region, 0 past r1
+    Raw<float> r;
+    load_raw<float, ALIGNED>(wrow, e0 + lane * kGroup, r1, r, 0u);
+    step(r);
+  }
+  acc = wave_sum_dpp(acc);
+  if (lane == 0) s_reg[wave] = acc;
+  if (__ballot(bad) != 0 && lane == 0) atomicOr(&s_bad, 1);
+  __syncthreads();
+  const float uf = u[row];
+  const bool live = lane < kSeqWaves;
+  const double wgt = live ? s_reg[lane] : 0.0;
+  const double tot = wave_sum_dpp(wgt);
+  const double t = static_cast<double>(uf) * tot;
+  const double inc = wave_incl_scan_dpp(wgt);
+  const unsigned long long cross = __ballot(live && inc > t);
+  int rs = cross ? __ffsll(cross) - 1 : -1;
+  double run = readlane_d(inc - wgt, rs < 0 ? 0 : rs);
+  bool take_last = false;
+  if (rs < 0) {
+    take_last = true;
+    const unsigned long long pos = __ballot(live && wgt > 0.0);
+    rs = pos ? 63 - __clzll(pos) : -1;
+    run = 0.0;
+  }
+  if (threadIdx.x == 0) {
+    if (s_bad || !(tot > 0.0 && tot <= DBL_MAX)) atomicOr(err, SV_DATA_NONFINITE);
+    if (!(uf >= 0.f && uf < 1.f)) atomicOr(err, SV_DATA_UNIFORM);
+  }
+  int tok = V - 1;
+  if (rs >= 0) {
+    const int R0 = min(V, rs * rw), R1 = min(V, R0 + rw);
+    int parity = 0;
+    for (int p0 = R0; p0 < R1; p0 += kPass, parity ^= 1) {
+      const int e = p0 + wave * kIter + lane * kGroup;
+      Raw<float> r;
+      load_raw<float, ALIGNED>(wrow, e, R1, r, 0u);
+      float v[kGroup];
+      unpack(r, v);
+      double rv[kGroup];
+      double tsum_l = 0.0;
+#pragma unroll
+      for (int j = 0; j < kGroup; ++j) {
+        rv[j] = fmax(static_cast<double>(v[j]), 0.0);
+        tsum_l += rv[j];
+      }
+      const double linc = wave_incl_scan_dpp(tsum_l);
+      const double lex = linc - tsum_l;
+      if (lane == 63) s_wt[parity][wave] = linc;
+      __syncthreads();
+      double accp = run, tsum = run;
+      for (int w2 = 0; w2 < kSeqWaves; ++w2) {
+        const double v2 = s_wt[parity][w2];
+        if (w2 < wave) accp += v2;
+        tsum += v2;
+      }
+      accp += lex;
+      int c2 = INT_MAX, lp = -1;
+#pragma unroll
+      for (int j = 0; j < kGroup; ++j) {
+        accp += rv[j];
+        if (!take_last && c2 == INT_MAX && accp > t) c2 = e + j;
+        if (rv[j] > 0.0) lp = e + j;
+      }
+      c2 = wave_min_int_dpp(c2);
+      lp = wave_max_int_dpp(lp);
+      if (lane == 0) {
+        if (c2 != INT_MAX) atomicMin(&s_cand, c2);
+        if (lp >= 0) atomicMax(&s_last, lp);
+      }
+      run = tsum;
+      __syncthreads();
+      if (s_cand != INT_MAX) break;
+    }
+    tok = s_cand != INT_MAX ? s_cand : (s_last >= 0 ? s_last : V - 1);
+  }
+  if (threadIdx.x == 0) tokens[row] = tok;
+}
+
 // Greedy: the argmax of row g is computed only when every draft was accepted.
 template <typename T, bool ALIGNED, bool RAGGED, bool ACCEPT>
 __global__ __launch_bounds__(kSeqThreads) void k_greedy_seq(Args a) {
@@ -1424,6 +1560,8 @@ struct spec_verify_ctx {
   void* ws = nullptr;
   RowStat* p1 = nullptr;
   int32_t* accept = nullptr;
+  int32_t* s_acc = nullptr;  // sampling: accepted counts (all 0) of the verify launch
+  float* s_rsum = nullptr;   // sampling: residual sums (all 0)
   int* err = nullptr;
   hipStream_t last_stream = nullptr;
   bool ran = false;
@@ -1624,15 +1762,18 @@ int spec_verify_create(spec_verify_ctx** out, int device, int vocab, int logits_
   const size_t n_p1 =
       up(sizeof(RowStat) * static_cast<size_t>(max_draft_rows > 0 ? max_draft_rows : 1) * max_split);
   const size_t n_ac = up(sizeof(int32_t) * static_cast<size_t>(max_draft_rows > 0 ? max_draft_rows : 1));
+  const size_t n_sb = up(sizeof(int32_t) * static_cast<size_t>(max_batch > 0 ? max_batch : 1));
   const size_t n_er = 256;
-  if (hipMalloc(&ctx->ws, n_p1 + n_ac + n_er) != hipSuccess) {
+  if (hipMalloc(&ctx->ws, n_p1 + n_ac + 2 * n_sb + n_er) != hipSuccess) {
     delete ctx;
     return SV_ENOMEM;
   }
   char* p = static_cast<char*>(ctx->ws);
   ctx->p1 = reinterpret_cast<RowStat*>(p);
   ctx->accept = reinterpret_cast<int32_t*>(p + n_p1);
-  ctx->err = reinterpret_cast<int*>(p + n_p1 + n_ac);
+  ctx->s_acc = reinterpret_cast<int32_t*>(p + n_p1 + n_ac);
+  ctx->s_rsum = reinterpret_cast<float*>(p + n_p1 + n_ac + n_sb);
+  ctx->err = reinterpret_cast<int*>(p + n_p1 + n_ac + 2 * n_sb);
   if (hipMemset(ctx->err, 0, n_er) != hipSuccess) {
     (void)hipFree(ctx->ws);
     delete ctx;
@@ -1725,6 +1866,44 @@ int spec_verify_run(spec_verify_ctx* ctx, void* hip_stream, int batch, int gamma
   ctx->last_stream = st;
   ctx->ran = true;
   ctx->last_path = fused ? SV_PATH_ONE_LAUNCH : SV_PATH_TWO_LAUNCH;
+  return SV_OK;
+}
+
+int spec_sample_run(spec_verify_ctx* ctx, void* hip_stream, int rows, int mode, float temperature, const void* x,
+                    const float* uniforms, int32_t* tokens) {
+  if (!ctx) return SV_EINVAL;
+  auto bad = [&](const char* m) {
+    set_msg(ctx->msg, sizeof(ctx->msg), m);
+    return SV_EINVAL;
+  };
+  if (rows < 0) return bad("rows must be >= 0");
+  if (rows > ctx->max_batch) return bad("rows exceeds max_batch");
+  if (mode != SV_SAMPLE_LOGITS && mode != SV_SAMPLE_WEIGHTS) return bad("mode must be SV_SAMPLE_LOGITS or SV_SAMPLE_WEIGHTS");
+  if (mode == SV_SAMPLE_LOGITS && !(temperature >= 0.f && temperature <= FLT_MAX))
+    return bad("temperature must be finite and >= 0");
+  if (rows == 0) return SV_OK;
+  if (!x || !tokens) return bad("x or tokens is NULL");
+  const bool greedy = mode == SV_SAMPLE_LOGITS && temperature == 0.f;
+  if (!greedy && !uniforms) return bad("uniforms is NULL");
+  if (mode == SV_SAMPLE_LOGITS) {
+    // the draw of a round with no drafts: row b is the target row, slot b its uniform
+    const int rc = spec_verify_run(ctx, hip_stream, rows, 0, nullptr, 0, temperature, x, nullptr, nullptr,
+                                   uniforms, ctx->s_acc, tokens, ctx->s_rsum, nullptr);
+    return rc;
+  }
+  if (reinterpret_cast<uintptr_t>(x) % 4 != 0) return bad("weights not aligned to 4 bytes");
+  const bool aligned = ctx->V % kGroup == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0;
+  DeviceGuard guard(ctx->device);
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const float* w = static_cast<const float*>(x);
+  if (aligned)
+    hipLaunchKernelGGL((k_sample_weights<true>), dim3(rows), dim3(kSeqThreads), 0, st, w, uniforms, tokens, ctx->err, ctx->V);
+  else
+    hipLaunchKernelGGL((k_sample_weights<false>), dim3(rows), dim3(kSeqThreads), 0, st, w, uniforms, tokens, ctx->err, ctx->V);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(ctx, "kernel launch", e);
+  ctx->last_stream = st;
+  ctx->ran = true;
   return SV_OK;
 }
 

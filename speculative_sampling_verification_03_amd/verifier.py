@@ -10,7 +10,8 @@ from typing import NamedTuple, Optional
 from .binding import (SV_BF16, SV_EDATA, SV_F32, spec_verify_create, spec_verify_destroy,
                       spec_verify_kernel_times, spec_verify_last_error, spec_verify_last_path,
                       spec_verify_run, spec_verify_set_path, spec_verify_set_timing,
-                      spec_verify_set_timing_stride, spec_verify_status)
+                      spec_verify_set_timing_stride, spec_verify_status, spec_sample_run,
+                      SV_SAMPLE_LOGITS, SV_SAMPLE_WEIGHTS)
 
 
 class VerifyOutputs(NamedTuple):
@@ -104,6 +105,35 @@ class Verifier:
                         None if greedy else q, draft_ids, None if greedy else uniforms,
                         out.accepted_count, out.emitted_tokens, out.residual_sum, out.p_draft)
         return out
+
+    def sample(self, x, *, uniforms=None, temperature: float = 1.0, tokens=None, stream=None):
+        """One token per row of logits `x` ([rows, V], the context's dtype): p = softmax(l / T),
+        T = 0 takes the argmax. Returns the int32 tokens tensor."""
+        import torch
+        if _dtype_code(x) != self.dtype_code:
+            raise TypeError("logits dtype differs from the context's")
+        return self._sample(x, SV_SAMPLE_LOGITS, uniforms, temperature, tokens, stream)
+
+    def sample_weights(self, w, *, uniforms, tokens=None, stream=None):
+        """One token per row of fp32 weights `w` ([rows, V], >= 0, not necessarily normalised)."""
+        import torch
+        self._check("weights", w, torch.float32)
+        return self._sample(w, SV_SAMPLE_WEIGHTS, uniforms, 1.0, tokens, stream)
+
+    def _sample(self, x, mode, uniforms, temperature, tokens, stream):
+        import torch
+        if not x.is_contiguous() or x.numel() % self.vocab:
+            raise ValueError("x must be a contiguous [rows, V] tensor")
+        rows = x.numel() // self.vocab
+        if mode == SV_SAMPLE_WEIGHTS or float(temperature) != 0.0:
+            self._check("uniforms", uniforms, torch.float32, rows)
+        if tokens is None:
+            tokens = torch.empty(rows, dtype=torch.int32, device=self.device)
+        self._check("tokens", tokens, torch.int32, rows)
+        st = stream if stream is not None else torch.cuda.current_stream(self.device)
+        spec_sample_run(self.ctx, st, rows, mode, float(temperature), x,
+                        None if (mode == SV_SAMPLE_LOGITS and float(temperature) == 0.0) else uniforms, tokens)
+        return tokens
 
     def status(self) -> int:
         """SV_OK, or SV_EDATA when the device flagged a data error (see last_error)."""

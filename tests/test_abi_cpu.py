@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "spec_verify.h")
 def declared_functions():
     text = open(HEADER, encoding="utf-8").read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(spec_verify_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(spec_(?:verify|sample)_\w+)\s*\(", text)))
 
 
 def test_library_built():
@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
         assert hasattr(lib, name), name
     assert sorted(sv.EXPORTED) == decl
     out = subprocess.run(["nm", "-D", "--defined-only", sv.LIB_PATH], capture_output=True, text=True).stdout
-    exported = set(re.findall(r"\bT (spec_verify_\w+)", out))
+    exported = set(re.findall(r"\bT (spec_\w+)", out))
     assert exported == set(decl)
 
 
@@ -94,6 +94,7 @@ def test_null_context_calls():
     assert lib.spec_verify_last_error(None) == b""
     assert lib.spec_verify_set_path(None, sv.SV_PATH_AUTO) == sv.SV_EINVAL
     assert lib.spec_verify_set_timing_stride(None, 2) == sv.SV_EINVAL
+    assert lib.spec_sample_run(None, None, 1, sv.SV_SAMPLE_WEIGHTS, 1.0, None, None, None) == sv.SV_EINVAL
     assert lib.spec_verify_last_path(None) == -sv.SV_EINVAL
     lib.spec_verify_destroy(None)  # NULL-safe
     rc = lib.spec_verify_run(None, None, 1, 1, None, 1, 1.0, None, None, None, None, None, None, None, None)
