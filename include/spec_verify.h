@@ -137,6 +137,21 @@ int spec_verify_run(spec_verify_ctx *ctx, void *hip_stream, int batch, int gamma
                     float *residual_sum, float *p_draft);
 
 /*
+ * The same step for deterministic drafts (n-gram or prompt-lookup proposals): the draft
+ * distribution is one-hot at the proposed id, q = onehot(x), so no q is passed or read.
+ * Then the accept test is u < p(x), and after a rejection at n the draw is from
+ * max(0, p_n - onehot(x_n)) = p_n with x_n removed, S = 1 - p_n(x_n) (p_n(x_n) = 1 draws
+ * from p_n and reports S = 0). An id outside [0, V) is rejected and removes nothing.
+ * Arguments, outputs and errors as spec_verify_run without q; with T == 0 it is the
+ * greedy rule.
+ */
+int spec_verify_run_onehot(spec_verify_ctx *ctx, void *hip_stream, int batch, int gamma,
+                           const int32_t *cu_gamma, int total_draft_rows, float temperature,
+                           const void *logits, const int32_t *draft_ids, const float *uniforms,
+                           int32_t *accepted_count, int32_t *emitted_tokens, float *residual_sum,
+                           float *p_draft);
+
+/*
  * Launch plan. A run either takes two launches (row statistics of every draft row,
  * then one workgroup per sequence for the first-rejection scan and the draw) or
  * one launch (one workgroup per sequence that judges its rows left to right,

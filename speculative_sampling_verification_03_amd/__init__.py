@@ -13,6 +13,6 @@ from .binding import (  # noqa: F401
     SpecVerifyError, load_library, spec_verify_check_args, spec_verify_create,
     spec_verify_destroy, spec_verify_kernel_times, spec_verify_last_error, spec_verify_last_path,
     spec_verify_run, spec_verify_set_path, spec_verify_set_timing, spec_verify_set_timing_stride,
-    spec_verify_status, spec_sample_run,
+    spec_verify_status, spec_sample_run, spec_verify_run_onehot,
 )
 from .verifier import Verifier, VerifyOutputs  # noqa: F401

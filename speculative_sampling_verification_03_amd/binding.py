@@ -27,7 +27,7 @@ EXPORTED = (
     "spec_verify_create", "spec_verify_run", "spec_verify_status",
     "spec_verify_last_error", "spec_verify_destroy", "spec_verify_set_timing",
     "spec_verify_kernel_times", "spec_verify_check_args", "spec_verify_set_path", "spec_verify_set_timing_stride",
-    "spec_verify_last_path", "spec_sample_run",
+    "spec_verify_last_path", "spec_sample_run", "spec_verify_run_onehot",
 )
 
 
@@ -68,6 +68,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.spec_verify_kernel_times.restype = i32
     lib.spec_verify_check_args.argtypes = [i32] * 9 + [f32] + [i32] * 7 + [ctypes.c_char_p, i32]
     lib.spec_verify_check_args.restype = i32
+    lib.spec_verify_run_onehot.argtypes = [vp, vp, i32, i32, vp, i32, f32, vp, vp, vp, vp, vp, vp, vp]
+    lib.spec_verify_run_onehot.restype = i32
     lib.spec_sample_run.argtypes = [vp, vp, i32, i32, f32, vp, vp, vp]
     lib.spec_sample_run.restype = i32
     lib.spec_verify_set_timing_stride.argtypes = [vp, i32]
@@ -122,6 +124,18 @@ def spec_verify_run(ctx: int, stream, batch: int, gamma: int, cu_gamma, total_dr
         ctx, _stream(stream), batch, gamma, _ptr(cu_gamma), total_draft_rows, float(temperature),
         _ptr(logits), _ptr(q), _ptr(draft_ids), _ptr(uniforms), _ptr(accepted_count),
         _ptr(emitted_tokens), _ptr(residual_sum), _ptr(p_draft))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, _msg(ctx))
+
+
+def spec_verify_run_onehot(ctx: int, stream, batch: int, gamma: int, cu_gamma, total_draft_rows: int,
+                           temperature: float, logits, draft_ids, uniforms, accepted_count,
+                           emitted_tokens, residual_sum, p_draft=None) -> None:
+    """Enqueue one verification step of deterministic drafts (q = one-hot(draft))."""
+    rc = load_library().spec_verify_run_onehot(
+        ctx, _stream(stream), batch, gamma, _ptr(cu_gamma), total_draft_rows, float(temperature),
+        _ptr(logits), _ptr(draft_ids), _ptr(uniforms), _ptr(accepted_count), _ptr(emitted_tokens),
+        _ptr(residual_sum), _ptr(p_draft))
     if rc != SV_OK:
         raise SpecVerifyError(rc, _msg(ctx))
 

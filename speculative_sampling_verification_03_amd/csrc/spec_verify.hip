@@ -92,6 +92,7 @@ struct Args {
   // bf16 value table of the one-launch path: magnitudes (bit patterns without the sign)
   // tlo..thi, thi < 0x7F80; tlo > thi when the table is not used
   int tlo, thi;
+  int onehot;      // drafts are deterministic: q = one-hot(draft), q is not read
 };
 
 __device__ __forceinline__ bool finite_pos(float z) { return z > 0.f && z <= FLT_MAX; }
@@ -162,7 +163,7 @@ __global__ __launch_bounds__(kThreads) void k_rowstats(Args a) {
     uu = a.u[d + b];
     if (x >= 0 && x < a.V) {
       lx = load_one(row, x);
-      qx = a.q[static_cast<size_t>(d) * a.V + x];
+      qx = a.onehot ? 1.f : a.q[static_cast<size_t>(d) * a.V + x];
     }
   }
   const int lo = k * a.span, hi = min(a.V, lo + a.span);
@@ -439,7 +440,7 @@ __device__ __forceinline__ int first_rejection(const Args& a, int b, int base, i
       const int x = a.ids[d];
       const bool valid = x >= 0 && x < a.V;
       const float lx = valid ? load_one(L, static_cast<size_t>(d + b) * a.V + x) : 0.f;
-      const float qx = valid ? a.q[static_cast<size_t>(d) * a.V + x] : 0.f;
+      const float qx = !valid ? 0.f : a.onehot ? 1.f : a.q[static_cast<size_t>(d) * a.V + x];
       double px;
       acc = accept_test(x, lx, qx, a.u[d + b], C, Z, a, px);
       if (a.pdraft) a.pdraft[d] = static_cast<float>(px);
@@ -469,18 +470,24 @@ __device__ __forceinline__ int region_width(int V) {
 // the exp2_tab table.
 template <typename T, bool ALIGNED>
 __device__ __forceinline__ void final_draw(const Args& a, int b, int base, int g, int n, double cref,
-                                           double Zq_in, const double* s_tab) {
+                                           double Zq_in, const double* s_tab, int xn = -1) {
   __shared__ double s_reg[kSeqWaves][3];  // residual: (D, Q, Zr); bonus: (m, s, -)
   __shared__ double s_wt[kSeqWaves];      // re-sweep: per-wave totals of a pass
   __shared__ int s_wc[kSeqWaves], s_wl[kSeqWaves];
   __shared__ double s_bc[6];  // search result: t, P (prefix before the region), Z64, delta, S, ref
-  __shared__ int s_bi[3];     // search result: region r*, kind, take_last
+  __shared__ int s_bi[4];     // search result: region r*, kind, take_last, excluded id
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar
   const int V = a.V;
   const bool residual = n < g;
+  // one-hot drafts: max(0, p - onehot(x_n)) is p with x_n removed, drawn like a bonus row
+  const bool oh = residual && a.onehot;
+  const bool qres = residual && !oh;
   const T* lrow = static_cast<const T*>(a.logits) + static_cast<size_t>(base + b + (residual ? n : g)) * V;
-  const float* qrow = residual ? a.q + static_cast<size_t>(base + n) * V : nullptr;
+  const float* qrow = qres ? a.q + static_cast<size_t>(base + n) * V : nullptr;
+  if (oh && xn < 0) xn = a.ids[base + n];
+  const bool excl_ok = oh && xn >= 0 && xn < V;  // an invalid id removes nothing
+  const float lxn = excl_ok ? load_one(lrow, xn) : 0.f;
   const double KN = kExpScale * a.k2d;  // exp2_tab(l KN - N c) = 2^(l k2 - c)
   const double cr = residual ? cref : 0.0;
   const double Zq = residual ? Zq_in : 0.0;
@@ -492,7 +499,7 @@ __device__ __forceinline__ void final_draw(const Args& a, int b, int base, int g
   const uint32_t linf = neg_inf_word<T>();
 
   // ---- one fp64 sweep of this wave's region through a ring of kRing register buffers
-  if (residual) {
+  if (qres) {
     // residual max(0, p - q) ([P1] ch.3; [P3] 단계 3), normalisation deferred
     const double CN = kExpScale * cr;
     double D = 0.0, Zr = 0.0;
@@ -609,9 +616,10 @@ __device__ __forceinline__ void final_draw(const Args& a, int b, int base, int g
     const double u = uf;
     const int r = lane < kSeqWaves ? lane : 0;
     const bool live = lane < kSeqWaves;
-    int kind;  // 0: residual; 1: degenerate residual (S <= 0), draw from p; 2: bonus from p
+    int kind;  // 0: residual; 1: degenerate residual (S <= 0), draw from p; 2: from p; 3: p without x_n
+    int excl = -1;
     double Z64, S = 0.0, delta = 0.0, ref, t, wgt;
-    if (residual) {
+    if (qres) {
       Z64 = wave_sum(live ? s_reg[r][2] : 0.0);
       delta = (Z64 - Zq) / Z64;
       wgt = live ? s_reg[r][0] / Z64 - s_reg[r][1] * delta : 0.0;
@@ -630,6 +638,17 @@ __device__ __forceinline__ void final_draw(const Args& a, int b, int base, int g
       Z64 = wave_sum(wgt);
       kind = 2;
       t = u * Z64;
+      if (oh) {
+        // S = 1 - p(x_n); the region holding x_n loses e(x_n)
+        const double ex_n = excl_ok ? exp2_tab(fma(static_cast<double>(lxn), KN, -ref), s_tab) : 0.0;
+        S = (Z64 - ex_n) / Z64;
+        if (S > 0.0) {
+          kind = 3;
+          excl = excl_ok ? xn : -1;
+          if (excl_ok && r == xn / rw && live) wgt = fmax(wgt - ex_n, 0.0);
+          t = u * wave_sum(live ? wgt : 0.0);
+        }
+      }
     }
     const double ex = wave_excl_scan(wgt);
     const unsigned long long cross = __ballot(live && ex + wgt > t);
@@ -654,11 +673,12 @@ __device__ __forceinline__ void final_draw(const Args& a, int b, int base, int g
       s_bi[0] = rs;
       s_bi[1] = kind;
       s_bi[2] = take_last;
+      s_bi[3] = excl;
     }
   }
   __syncthreads();
   const double t = s_bc[0], Z64 = s_bc[2], delta = s_bc[3], S = s_bc[4], ref = s_bc[5];
-  const int rs = s_bi[0], kind = s_bi[1];
+  const int rs = s_bi[0], kind = s_bi[1], excl = s_bi[3];
   const bool take_last = s_bi[2] != 0;
 
   // ---- re-sweep of region r* in passes of kPass entries: wave w scans the w-th kIter
@@ -690,6 +710,7 @@ __device__ __forceinline__ void final_draw(const Args& a, int b, int base, int g
           const double w = fma(-static_cast<double>(qv[j]), Zq, ev);
           wv = w > 0.0 ? w * invZ - static_cast<double>(qv[j]) * delta : 0.0;
         }
+        if (e + j == excl) wv = 0.0;
         rv[j] = wv;
         tot += wv;
       }
@@ -729,7 +750,7 @@ __device__ __forceinline__ void final_draw(const Args& a, int b, int base, int g
   }
   if (threadIdx.x == 0) {
     a.emitted[base + b + n] = tok;
-    a.rsum[b] = kind == 2 ? 0.f : static_cast<float>(S);
+    a.rsum[b] = residual ? static_cast<float>(S) : 0.f;
   }
   for (int i = n + 1 + threadIdx.x; i <= g; i += kSeqThreads) a.emitted[base + b + i] = -1;
 }
@@ -907,7 +928,7 @@ __device__ __forceinline__ void tab_build(double* sT, const Args& a) {
 // on that scale. Returns false, having written nothing, when the drawn row holds a value
 // outside the table; the caller then runs final_draw.
 __device__ __forceinline__ bool final_draw_tab(const Args& a, int b, int base, int g, int n, double Zq,
-                                               const double* sT) {
+                                               const double* sT, int xn = -1) {
   __shared__ double s_reg[kSeqWaves][3];  // residual: (D, Q, Zr); bonus: (s, -, -)
   __shared__ uint32_t s_mx[kSeqWaves];
   __shared__ double s_wt[2][kSeqWaves];   // re-sweep: per-wave totals, by pass parity
@@ -921,9 +942,15 @@ __device__ __forceinline__ bool final_draw_tab(const Args& a, int b, int base, i
   const int V = a.V;
   const uint32_t tlo = a.tlo, thi = a.thi;
   const bool residual = n < g;
+  // one-hot drafts: max(0, p - onehot(x_n)) is p with x_n removed, drawn like a bonus row
+  const bool oh = residual && a.onehot;
+  const bool qres = residual && !oh;
   const uint16_t* lrow =
       static_cast<const uint16_t*>(a.logits) + static_cast<size_t>(base + b + (residual ? n : g)) * V;
-  const float* qrow = residual ? a.q + static_cast<size_t>(base + n) * V : nullptr;
+  const float* qrow = qres ? a.q + static_cast<size_t>(base + n) * V : nullptr;
+  if (oh && xn < 0) xn = a.ids[base + n];
+  const bool excl_ok = oh && xn >= 0 && xn < V;  // an invalid id removes nothing
+  const uint32_t lxn = excl_ok ? static_cast<uint32_t>(lrow[xn]) : 0u;
   const int rw = region_width(V);
   const int r0 = min(V, wave * rw), r1 = min(V, r0 + rw);
   const int nfull = (r1 - r0) / kIter;
@@ -940,7 +967,7 @@ __device__ __forceinline__ bool final_draw_tab(const Args& a, int b, int base, i
       e[2 * k + 1] = tab_lookup(mh, w[k] >> 31, sT, tlo, thi);
     }
   };
-  if (residual) {
+  if (qres) {
     // residual max(0, p - q) ([P1] ch.3; [P3] 단계 3), normalisation deferred as in final_draw
     double D = 0.0, Zr = 0.0;
     float Q = 0.f;
@@ -1043,9 +1070,10 @@ __device__ __forceinline__ bool final_draw_tab(const Args& a, int b, int base, i
   const int r = lane < kSeqWaves ? lane : 0;
   const bool live = lane < kSeqWaves;
   if (__ballot(live && s_mx[r] > thi) != 0) return false;
-  int kind;  // 0: residual; 1: degenerate residual (S <= 0), draw from p; 2: bonus from p
+  int kind;  // 0: residual; 1: degenerate residual (S <= 0), draw from p; 2: from p; 3: p without x_n
+  int excl = -1;
   double Z64, S = 0.0, delta = 0.0, t, wgt;
-  if (residual) {
+  if (qres) {
     Z64 = wave_sum_dpp(live ? s_reg[r][2] : 0.0);
     delta = (Z64 - Zq) / Z64;
     wgt = live ? s_reg[r][0] / Z64 - s_reg[r][1] * delta : 0.0;
@@ -1058,6 +1086,17 @@ __device__ __forceinline__ bool final_draw_tab(const Args& a, int b, int base, i
     Z64 = wave_sum_dpp(wgt);
     kind = 2;
     t = u * Z64;
+    if (oh) {
+      // S = 1 - p(x_n); the region holding x_n loses e(x_n)
+      const double ex_n = excl_ok ? tab_lookup(lxn & 0x7FFFu, lxn >> 15, sT, tlo, thi) : 0.0;
+      S = (Z64 - ex_n) / Z64;
+      if (S > 0.0) {
+        kind = 3;
+        excl = excl_ok ? xn : -1;
+        if (excl_ok && live && r == xn / rw) wgt = fmax(wgt - ex_n, 0.0);
+        t = u * wave_sum_dpp(live ? wgt : 0.0);
+      }
+    }
   }
   const double inc = wave_incl_scan_dpp(wgt);
   const unsigned long long cross = __ballot(live && inc > t);
@@ -1104,7 +1143,7 @@ __device__ __forceinline__ bool final_draw_tab(const Args& a, int b, int base, i
           const double w = fma(-static_cast<double>(qv[j]), Zq, ev[j]);
           wv = w > 0.0 ? w * invZ - static_cast<double>(qv[j]) * delta : 0.0;
         }
-        rv[j] = in ? wv : 0.0;
+        rv[j] = (in && e + j != excl) ? wv : 0.0;
         tot += rv[j];
       }
       const double linc = wave_incl_scan_dpp(tot);
@@ -1139,7 +1178,7 @@ __device__ __forceinline__ bool final_draw_tab(const Args& a, int b, int base, i
   }
   if (threadIdx.x == 0) {
     a.emitted[base + b + n] = tok;
-    a.rsum[b] = kind == 2 ? 0.f : static_cast<float>(S);
+    a.rsum[b] = residual ? static_cast<float>(S) : 0.f;
   }
   for (int i = n + 1 + threadIdx.x; i <= g; i += kSeqThreads) a.emitted[base + b + i] = -1;
   return true;
@@ -1152,7 +1191,8 @@ __device__ __forceinline__ bool final_draw_tab(const Args& a, int b, int base, i
 // above that first chunk's max) or is not finite redoes its chunks of the row with the
 // running max. Returns n; s_cz[i] = (c, z) of each judged row.
 template <typename T, bool WIDE, bool NT, typename Hook>
-__device__ __forceinline__ int judge_rows_exact(const Args& a, int b, int base, int g, float2* s_cz, Hook&& hook) {
+__device__ __forceinline__ int judge_rows_exact(const Args& a, int b, int base, int g, float2* s_cz, int* s_xn,
+                                                Hook&& hook) {
   __shared__ float2 s_part[kSeqWaves];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1183,7 +1223,7 @@ __device__ __forceinline__ int judge_rows_exact(const Args& a, int b, int base, 
           lxb = reinterpret_cast<const uint32_t*>(Lseq + static_cast<size_t>(ir) * V)[xc >> 1];
         else
           lxb = elem_bits(Lseq + static_cast<size_t>(ir) * V, xc);
-        qx = a.q[static_cast<size_t>(base + ir) * V + xc];
+        qx = a.onehot ? 1.f : a.q[static_cast<size_t>(base + ir) * V + xc];
         hook();
       },
       [&](const Raw<T>& lr, int k) {
@@ -1263,6 +1303,7 @@ __device__ __forceinline__ int judge_rows_exact(const Args& a, int b, int base, 
   if (wave == 0) {
     if (lane < n) a.emitted[base + b + lane] = x;
     if (lane == 0) a.acc[b] = n;
+    if (lane == n) *s_xn = x;  // the rejected draft (n < g)
   }
   return n;
 }
@@ -1274,6 +1315,7 @@ template <typename T, bool RAGGED, bool NT1>
 __global__ __launch_bounds__(kSeqThreads) void k_verify_seq(Args a) {
   __shared__ double s_tab[kExpN];
   __shared__ float2 s_cz[kFuseMaxGamma];
+  __shared__ int s_xn;
   const int b = blockIdx.x;
   int base, g;
   if (!seq_geom<RAGGED>(a, b, base, g)) {
@@ -1292,8 +1334,8 @@ __global__ __launch_bounds__(kSeqThreads) void k_verify_seq(Args a) {
       if (tab) tab_build(sT, a);
     };
     const int n = g == 0 ? 0
-                  : a.V >= kSeqWaves * kIter ? judge_rows_exact<T, true, NT1>(a, b, base, g, s_cz, hook)
-                                             : judge_rows_exact<T, false, NT1>(a, b, base, g, s_cz, hook);
+                  : a.V >= kSeqWaves * kIter ? judge_rows_exact<T, true, NT1>(a, b, base, g, s_cz, &s_xn, hook)
+                                             : judge_rows_exact<T, false, NT1>(a, b, base, g, s_cz, &s_xn, hook);
     if (g == 0) {
       if (tab) tab_build(sT, a);
       if (threadIdx.x == 0) a.acc[b] = 0;
@@ -1302,16 +1344,17 @@ __global__ __launch_bounds__(kSeqThreads) void k_verify_seq(Args a) {
     const double cr = n < g ? static_cast<double>(s_cz[n].x) : 0.0;
     const double zr = n < g ? static_cast<double>(s_cz[n].y) : 0.0;
     // table scale: sum 2^(l k2) = z 2^c
-    if (tab && final_draw_tab(a, b, base, g, n, zr * exp2(cr), sT)) return;
-    final_draw<T, true>(a, b, base, g, n, cr, zr, s_tab);
+    const int xn = n < g ? s_xn : -1;
+    if (tab && final_draw_tab(a, b, base, g, n, zr * exp2(cr), sT, xn)) return;
+    final_draw<T, true>(a, b, base, g, n, cr, zr, s_tab, xn);
   } else {
     const int n = g == 0 ? 0
-                  : a.V >= kSeqWaves * kIter ? judge_rows_exact<T, true, NT1>(a, b, base, g, s_cz, [] {})
-                                             : judge_rows_exact<T, false, NT1>(a, b, base, g, s_cz, [] {});
+                  : a.V >= kSeqWaves * kIter ? judge_rows_exact<T, true, NT1>(a, b, base, g, s_cz, &s_xn, [] {})
+                                             : judge_rows_exact<T, false, NT1>(a, b, base, g, s_cz, &s_xn, [] {});
     if (g == 0 && threadIdx.x == 0) a.acc[b] = 0;
     __syncthreads();  // s_cz of row n, s_tab
     final_draw<T, true>(a, b, base, g, n, n < g ? static_cast<double>(s_cz[n].x) : 0.0,
-                        n < g ? static_cast<double>(s_cz[n].y) : 0.0, s_tab);
+                        n < g ? static_cast<double>(s_cz[n].y) : 0.0, s_tab, n < g ? s_xn : -1);
   }
 }
 
@@ -1695,6 +1738,96 @@ void choose_split(int R, int V, int& split, int& span) {
 
 }  // namespace
 
+namespace {
+int run_impl(spec_verify_ctx* ctx, void* hip_stream, int batch, int gamma, const int32_t* cu_gamma,
+             int total_draft_rows, float temperature, const void* logits, const float* q, bool onehot,
+             const int32_t* draft_ids, const float* uniforms, int32_t* accepted_count, int32_t* emitted_tokens,
+             float* residual_sum, float* p_draft) {
+  if (!ctx) return SV_EINVAL;
+  const int rc = spec_verify_check_args(
+      ctx->V, ctx->dtype, ctx->max_batch, ctx->max_rows, ctx->max_gamma, batch, gamma, cu_gamma != nullptr,
+      total_draft_rows, temperature, logits != nullptr, onehot || q != nullptr, draft_ids != nullptr,
+      uniforms != nullptr, accepted_count != nullptr, emitted_tokens != nullptr, residual_sum != nullptr, ctx->msg,
+      sizeof(ctx->msg));
+  if (rc != SV_OK) return rc;
+  if (batch == 0) return SV_OK;
+  const size_t esz = ctx->dtype == SV_BF16 ? 2 : 4;
+  if (reinterpret_cast<uintptr_t>(logits) % esz != 0 || (q && reinterpret_cast<uintptr_t>(q) % 4 != 0)) {
+    set_msg(ctx->msg, sizeof(ctx->msg), "logits / q not aligned to their element size");
+    return SV_EINVAL;
+  }
+  if (cu_gamma && batch > kMaxRaggedBatch) {
+    set_msg(ctx->msg, sizeof(ctx->msg), "ragged batches (cu_gamma) are limited to 65536 sequences");
+    return SV_EINVAL;
+  }
+  const bool greedy = temperature == 0.f;
+  const bool aligned = ctx->V % kGroup == 0 && reinterpret_cast<uintptr_t>(logits) % 16 == 0 &&
+                       (greedy || reinterpret_cast<uintptr_t>(q) % 16 == 0);
+  Args a{};
+  a.logits = logits;
+  a.q = greedy || onehot ? nullptr : q;
+  a.onehot = onehot && !greedy ? 1 : 0;
+  a.ids = draft_ids;
+  a.u = greedy ? nullptr : uniforms;
+  a.cu = cu_gamma;
+  a.acc = accepted_count;
+  a.emitted = emitted_tokens;
+  a.rsum = residual_sum;
+  a.pdraft = greedy ? nullptr : p_draft;
+  a.p1 = ctx->p1;
+  a.accept = ctx->accept;
+  a.err = ctx->err;
+  a.B = batch;
+  a.gamma = cu_gamma ? -1 : gamma;
+  a.V = ctx->V;
+  a.R = total_draft_rows;
+  a.max_gamma = ctx->max_gamma;
+  choose_split(a.R, a.V, a.split, a.span);
+  const unsigned long long max_threads = 1ull << 32;
+  if (static_cast<unsigned long long>(a.R) * a.split * kThreads >= max_threads ||
+      static_cast<unsigned long long>(a.B) * kSeqThreads >= max_threads) {
+    set_msg(ctx->msg, sizeof(ctx->msg), "launch grid too large: reduce the batch");
+    return SV_EINVAL;
+  }
+  a.tlo = 1;
+  a.thi = 0;  // no value table
+  if (greedy) {
+    a.k2 = 0.f;
+    a.k2d = 0.0;
+  } else {
+    a.k2d = 1.4426950408889634 / static_cast<double>(temperature);
+    a.k2 = static_cast<float>(a.k2d);
+    // bf16 value table window: magnitudes below 2^etop, |x k2| < 990, kTabBinades octaves
+    const int etop = static_cast<int>(floor(log2(990.0 / a.k2d)));
+    const int be_hi = etop + 127 > 255 ? 255 : etop + 127;  // biased exponent, exclusive
+    const int be_lo = be_hi - kTabBinades < 0 ? 0 : be_hi - kTabBinades;
+    if (ctx->dtype == SV_BF16 && be_hi > be_lo) {
+      a.tlo = be_lo * 128;
+      a.thi = be_hi * 128 - 1;
+    }
+  }
+  DeviceGuard guard(ctx->device);
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  // one launch per call when there are enough sequences to give every compute unit one
+  const int gmax = cu_gamma ? ctx->max_gamma : gamma;
+  const bool fused = ctx->path_mode != SV_PATH_TWO_LAUNCH && !greedy && aligned && gmax <= kFuseMaxGamma &&
+                     (ctx->path_mode == SV_PATH_ONE_LAUNCH || batch >= ctx->cus);
+  const bool rg = cu_gamma != nullptr;
+  hipError_t e;
+  if (fused)
+    e = ctx->dtype == SV_BF16 ? (rg ? launch_fused<uint16_t, true>(ctx, a, st) : launch_fused<uint16_t, false>(ctx, a, st))
+                              : (rg ? launch_fused<float, true>(ctx, a, st) : launch_fused<float, false>(ctx, a, st));
+  else
+    e = ctx->dtype == SV_BF16 ? launch_dt<uint16_t>(ctx, a, st, greedy, aligned, rg)
+                              : launch_dt<float>(ctx, a, st, greedy, aligned, rg);
+  if (e != hipSuccess) return hip_fail(ctx, "kernel launch", e);
+  ctx->last_stream = st;
+  ctx->ran = true;
+  ctx->last_path = fused ? SV_PATH_ONE_LAUNCH : SV_PATH_TWO_LAUNCH;
+  return SV_OK;
+}
+}  // namespace
+
 extern "C" {
 
 int spec_verify_check_args(int vocab, int logits_dtype, int max_batch, int max_draft_rows, int max_gamma,
@@ -1787,87 +1920,18 @@ int spec_verify_run(spec_verify_ctx* ctx, void* hip_stream, int batch, int gamma
                     int total_draft_rows, float temperature, const void* logits, const float* q,
                     const int32_t* draft_ids, const float* uniforms, int32_t* accepted_count,
                     int32_t* emitted_tokens, float* residual_sum, float* p_draft) {
-  if (!ctx) return SV_EINVAL;
-  const int rc = spec_verify_check_args(
-      ctx->V, ctx->dtype, ctx->max_batch, ctx->max_rows, ctx->max_gamma, batch, gamma, cu_gamma != nullptr,
-      total_draft_rows, temperature, logits != nullptr, q != nullptr, draft_ids != nullptr, uniforms != nullptr,
-      accepted_count != nullptr, emitted_tokens != nullptr, residual_sum != nullptr, ctx->msg, sizeof(ctx->msg));
-  if (rc != SV_OK) return rc;
-  if (batch == 0) return SV_OK;
-  const size_t esz = ctx->dtype == SV_BF16 ? 2 : 4;
-  if (reinterpret_cast<uintptr_t>(logits) % esz != 0 || (q && reinterpret_cast<uintptr_t>(q) % 4 != 0)) {
-    set_msg(ctx->msg, sizeof(ctx->msg), "logits / q not aligned to their element size");
-    return SV_EINVAL;
-  }
-  if (cu_gamma && batch > kMaxRaggedBatch) {
-    set_msg(ctx->msg, sizeof(ctx->msg), "ragged batches (cu_gamma) are limited to 65536 sequences");
-    return SV_EINVAL;
-  }
-  const bool greedy = temperature == 0.f;
-  const bool aligned = ctx->V % kGroup == 0 && reinterpret_cast<uintptr_t>(logits) % 16 == 0 &&
-                       (greedy || reinterpret_cast<uintptr_t>(q) % 16 == 0);
-  Args a{};
-  a.logits = logits;
-  a.q = greedy ? nullptr : q;
-  a.ids = draft_ids;
-  a.u = greedy ? nullptr : uniforms;
-  a.cu = cu_gamma;
-  a.acc = accepted_count;
-  a.emitted = emitted_tokens;
-  a.rsum = residual_sum;
-  a.pdraft = greedy ? nullptr : p_draft;
-  a.p1 = ctx->p1;
-  a.accept = ctx->accept;
-  a.err = ctx->err;
-  a.B = batch;
-  a.gamma = cu_gamma ? -1 : gamma;
-  a.V = ctx->V;
-  a.R = total_draft_rows;
-  a.max_gamma = ctx->max_gamma;
-  choose_split(a.R, a.V, a.split, a.span);
-  const unsigned long long max_threads = 1ull << 32;
-  if (static_cast<unsigned long long>(a.R) * a.split * kThreads >= max_threads ||
-      static_cast<unsigned long long>(a.B) * kSeqThreads >= max_threads) {
-    set_msg(ctx->msg, sizeof(ctx->msg), "launch grid too large: reduce the batch");
-    return SV_EINVAL;
-  }
-  a.tlo = 1;
-  a.thi = 0;  // no value table
-  if (greedy) {
-    a.k2 = 0.f;
-    a.k2d = 0.0;
-  } else {
-    a.k2d = 1.4426950408889634 / static_cast<double>(temperature);
-    a.k2 = static_cast<float>(a.k2d);
-    // bf16 value table window: magnitudes below 2^etop, |x k2| < 990, kTabBinades octaves
-    const int etop = static_cast<int>(floor(log2(990.0 / a.k2d)));
-    const int be_hi = etop + 127 > 255 ? 255 : etop + 127;  // biased exponent, exclusive
-    const int be_lo = be_hi - kTabBinades < 0 ? 0 : be_hi - kTabBinades;
-    if (ctx->dtype == SV_BF16 && be_hi > be_lo) {
-      a.tlo = be_lo * 128;
-      a.thi = be_hi * 128 - 1;
-    }
-  }
-  DeviceGuard guard(ctx->device);
-  hipStream_t st = static_cast<hipStream_t>(hip_stream);
-  // one launch per call when there are enough sequences to give every compute unit one
-  const int gmax = cu_gamma ? ctx->max_gamma : gamma;
-  const bool fused = ctx->path_mode != SV_PATH_TWO_LAUNCH && !greedy && aligned && gmax <= kFuseMaxGamma &&
-                     (ctx->path_mode == SV_PATH_ONE_LAUNCH || batch >= ctx->cus);
-  const bool rg = cu_gamma != nullptr;
-  hipError_t e;
-  if (fused)
-    e = ctx->dtype == SV_BF16 ? (rg ? launch_fused<uint16_t, true>(ctx, a, st) : launch_fused<uint16_t, false>(ctx, a, st))
-                              : (rg ? launch_fused<float, true>(ctx, a, st) : launch_fused<float, false>(ctx, a, st));
-  else
-    e = ctx->dtype == SV_BF16 ? launch_dt<uint16_t>(ctx, a, st, greedy, aligned, rg)
-                              : launch_dt<float>(ctx, a, st, greedy, aligned, rg);
-  if (e != hipSuccess) return hip_fail(ctx, "kernel launch", e);
-  ctx->last_stream = st;
-  ctx->ran = true;
-  ctx->last_path = fused ? SV_PATH_ONE_LAUNCH : SV_PATH_TWO_LAUNCH;
-  return SV_OK;
+  return run_impl(ctx, hip_stream, batch, gamma, cu_gamma, total_draft_rows, temperature, logits, q, false,
+                  draft_ids, uniforms, accepted_count, emitted_tokens, residual_sum, p_draft);
 }
+
+int spec_verify_run_onehot(spec_verify_ctx* ctx, void* hip_stream, int batch, int gamma, const int32_t* cu_gamma,
+                           int total_draft_rows, float temperature, const void* logits, const int32_t* draft_ids,
+                           const float* uniforms, int32_t* accepted_count, int32_t* emitted_tokens,
+                           float* residual_sum, float* p_draft) {
+  return run_impl(ctx, hip_stream, batch, gamma, cu_gamma, total_draft_rows, temperature, logits, nullptr, true,
+                  draft_ids, uniforms, accepted_count, emitted_tokens, residual_sum, p_draft);
+}
+
 
 int spec_sample_run(spec_verify_ctx* ctx, void* hip_stream, int rows, int mode, float temperature, const void* x,
                     const float* uniforms, int32_t* tokens) {

@@ -11,6 +11,7 @@ from .binding import (SV_BF16, SV_EDATA, SV_F32, spec_verify_create, spec_verify
                       spec_verify_kernel_times, spec_verify_last_error, spec_verify_last_path,
                       spec_verify_run, spec_verify_set_path, spec_verify_set_timing,
                       spec_verify_set_timing_stride, spec_verify_status, spec_sample_run,
+                      spec_verify_run_onehot,
                       SV_SAMPLE_LOGITS, SV_SAMPLE_WEIGHTS)
 
 
@@ -62,11 +63,12 @@ class Verifier:
     def run(self, logits, draft_ids, *, temperature: float, q=None, uniforms=None,
             gamma: Optional[int] = None, cu_gamma=None, total_draft_rows: Optional[int] = None,
             out: Optional[VerifyOutputs] = None, want_p_draft: bool = True,
-            stream=None) -> VerifyOutputs:
+            stream=None, onehot: bool = False) -> VerifyOutputs:
         """Enqueue one verification step on `stream` (default: torch's current stream).
 
         Uniform gamma: pass `gamma`. Ragged: pass `cu_gamma` (int32 [B+1] on the device)
         and the host value `total_draft_rows` (defaults to draft_ids.numel()).
+        onehot=True: deterministic drafts, q = one-hot(draft); `q` is not passed.
         """
         import torch
         if _dtype_code(logits) != self.dtype_code:
@@ -86,8 +88,9 @@ class Verifier:
         self._check("logits", logits, None, (R + B) * V)
         self._check("draft_ids", draft_ids, torch.int32, R)
         greedy = float(temperature) == 0.0
-        if not greedy:
+        if not greedy and not onehot:
             self._check("q", q, torch.float32, R * V)
+        if not greedy:
             self._check("uniforms", uniforms, torch.float32, R + B)
         if out is None:
             dev = self.device
@@ -101,9 +104,14 @@ class Verifier:
         self._check("residual_sum", out.residual_sum, torch.float32, B)
         self._check("p_draft", out.p_draft, torch.float32, R)
         st = stream if stream is not None else torch.cuda.current_stream(self.device)
-        spec_verify_run(self.ctx, st, B, g_arg, cu_gamma, R, float(temperature), logits,
-                        None if greedy else q, draft_ids, None if greedy else uniforms,
-                        out.accepted_count, out.emitted_tokens, out.residual_sum, out.p_draft)
+        if onehot:
+            spec_verify_run_onehot(self.ctx, st, B, g_arg, cu_gamma, R, float(temperature), logits, draft_ids,
+                                   None if greedy else uniforms, out.accepted_count, out.emitted_tokens,
+                                   out.residual_sum, out.p_draft)
+        else:
+            spec_verify_run(self.ctx, st, B, g_arg, cu_gamma, R, float(temperature), logits,
+                            None if greedy else q, draft_ids, None if greedy else uniforms,
+                            out.accepted_count, out.emitted_tokens, out.residual_sum, out.p_draft)
         return out
 
     def sample(self, x, *, uniforms=None, temperature: float = 1.0, tokens=None, stream=None):

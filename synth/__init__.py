@@ -246,6 +246,27 @@ def make_greedy(name, gammas, V, dtype, sigma_logit, agree, seed) -> Workload:
     return Workload(name, B, V, dtype, 0.0, gammas, cu, ug, logits, None, draft_ids, None)
 
 
+def make_onehot(name, gammas, V, dtype, T, sigma_logit, agree, seed) -> Workload:
+    """Workload with deterministic drafts (an n-gram style proposer): draft = target argmax
+    (lowest index) with prob `agree`, else a uniform random id; q is left None (the
+    draft distribution is one-hot at the draft). Uniforms drawn as fp32 in [0, 1)."""
+    w = make_greedy(name, gammas, V, dtype, sigma_logit, agree, seed)
+    st = _streams(seed)
+    ru = np.random.Generator(np.random.PCG64(st["uniforms"]))
+    u = ru.random(w.target_rows, dtype=np.float32)
+    return Workload(name, w.B, V, dtype, float(T), w.gammas, w.cu_gamma, w.uniform_gamma, w.logits, None,
+                    w.draft_ids, u)
+
+
+def onehot_q(w) -> np.ndarray:
+    """The one-hot draft distributions of a deterministic-draft workload (fp32 [R, V]);
+    an id outside [0, V) gives an all-zero row."""
+    q = np.zeros((w.draft_rows, w.V), dtype=np.float32)
+    ok = (w.draft_ids >= 0) & (w.draft_ids < w.V)
+    q[np.nonzero(ok)[0], w.draft_ids[ok]] = 1.0
+    return q
+
+
 # The five workloads the verification step is measured and checked on.
 CONFIGS = {
     "C1": dict(B=1, gamma=4, V=32, dtype="f32", T=1.0, sigma_logit=2.0, sigma_noise=0.5,

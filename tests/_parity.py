@@ -30,7 +30,7 @@ def tolerance(dtype: str) -> float:
     return 1e-5 if dtype == "f32" else 2e-3
 
 
-def to_device(w, device="cuda"):
+def to_device(w, device="cuda", with_q=True):
     """Host workload -> dict of device tensors (the layout of the C ABI)."""
     import torch
     d = {}
@@ -38,20 +38,22 @@ def to_device(w, device="cuda"):
         d["logits"] = torch.from_numpy(w.logits.view(np.int16)).view(torch.bfloat16).to(device)
     else:
         d["logits"] = torch.from_numpy(w.logits).to(device)
-    d["q"] = torch.from_numpy(w.q).to(device) if w.q is not None else None
+    d["q"] = torch.from_numpy(w.q).to(device) if (w.q is not None and with_q) else None
     d["draft_ids"] = torch.from_numpy(w.draft_ids).to(device)
     d["uniforms"] = torch.from_numpy(w.uniforms).to(device) if w.uniforms is not None else None
     d["cu_gamma"] = torch.from_numpy(w.cu_gamma).to(device)
     return d
 
 
-def run_gpu(verifier, w, dev=None, ragged=None, want_p_draft=True):
-    """Run the library on workload w; returns host numpy outputs and the status code."""
+def run_gpu(verifier, w, dev=None, ragged=None, want_p_draft=True, onehot=False):
+    """Run the library on workload w; returns host numpy outputs and the status code.
+    onehot: the drafts are deterministic (q = one-hot(draft)) and q is not passed."""
     import torch
-    dev = dev or to_device(w)
+    dev = dev or to_device(w, with_q=not onehot)
     if ragged is None:
         ragged = w.uniform_gamma is None
-    kw = dict(temperature=w.T, q=dev["q"], uniforms=dev["uniforms"], want_p_draft=want_p_draft)
+    kw = dict(temperature=w.T, q=None if onehot else dev["q"], uniforms=dev["uniforms"],
+              want_p_draft=want_p_draft, onehot=onehot)
     if ragged:
         out = verifier.run(dev["logits"], dev["draft_ids"], cu_gamma=dev["cu_gamma"],
                            total_draft_rows=w.draft_rows, **kw)
