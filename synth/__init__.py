@@ -37,7 +37,8 @@ import numpy as np
 
 __all__ = [
     "Workload", "CONFIGS", "make_config", "make_sampling", "make_greedy",
-    "pack", "bf16_round", "bf16_widen", "config_number",
+    "pack", "bf16_round", "bf16_widen", "config_number", "make_onehot",
+    "Contexts", "make_ngram_contexts",
 ]
 
 _BLOCK = 64  # rows per independently seeded block
@@ -258,13 +259,50 @@ def make_onehot(name, gammas, V, dtype, T, sigma_logit, agree, seed) -> Workload
                     w.draft_ids, u)
 
 
-def onehot_q(w) -> np.ndarray:
-    """The one-hot draft distributions of a deterministic-draft workload (fp32 [R, V]);
-    an id outside [0, V) gives an all-zero row."""
-    q = np.zeros((w.draft_rows, w.V), dtype=np.float32)
-    ok = (w.draft_ids >= 0) & (w.draft_ids < w.V)
-    q[np.nonzero(ok)[0], w.draft_ids[ok]] = 1.0
-    return q
+@dataclasses.dataclass
+class Contexts:
+    """A packed batch of token contexts (host arrays)."""
+    B: int
+    tokens: np.ndarray   # int32 [sum L_b]
+    cu_ctx: np.ndarray   # int32 [B+1] exclusive prefix of L_b
+
+    def context(self, b: int) -> np.ndarray:
+        return self.tokens[self.cu_ctx[b]:self.cu_ctx[b + 1]]
+
+
+def make_ngram_contexts(B, lengths, V, seed, copy_prob=0.7, prompt_frac=0.6) -> Contexts:
+    """Copy-heavy contexts (summaries, edits, retrieval answers that repeat their input).
+
+    lengths: (L_min, L_max), each L_b uniform in it (inclusive). The first prompt_frac of
+    a context are ids uniform in [0, V); the rest is built piece by piece: with
+    probability copy_prob a span of 4..32 tokens copied from a uniform earlier place,
+    else 1..4 fresh uniform ids; the last piece is cut at L_b."""
+    st = _streams(seed)
+    rg = np.random.Generator(np.random.PCG64(st["drafts"]))
+    lo, hi = lengths
+    L = rg.integers(lo, hi + 1, B)
+    cu = pack(L)
+    out = np.empty(int(cu[-1]), dtype=np.int32)
+    for b in range(B):
+        n = int(L[b])
+        c = np.empty(n, dtype=np.int32)
+        k = min(n, max(1, int(prompt_frac * n))) if n else 0
+        c[:k] = rg.integers(0, V, k)
+        while k < n:
+            if rg.random() < copy_prob and k >= 4:
+                m = min(int(rg.integers(4, 33)), n - k)
+                j = int(rg.integers(0, k))
+                if j + m <= k:
+                    c[k:k + m] = c[j:j + m]
+                else:
+                    for t in range(m):  # element by element: the copy overlaps itself
+                        c[k + t] = c[j + t]
+            else:
+                m = min(int(rg.integers(1, 5)), n - k)
+                c[k:k + m] = rg.integers(0, V, m)
+            k += m
+        out[cu[b]:cu[b + 1]] = c
+    return Contexts(B, out, cu)
 
 
 # The five workloads the verification step is measured and checked on.

@@ -35,12 +35,21 @@ def lib():
     return sv
 
 
+def onehot_q(w) -> np.ndarray:
+    """The one-hot draft distributions written out densely for the oracle (fp32 [R, V]);
+    an id outside [0, V) gives an all-zero row."""
+    q = np.zeros((w.draft_rows, w.V), dtype=np.float32)
+    ok = (w.draft_ids >= 0) & (w.draft_ids < w.V)
+    q[np.nonzero(ok)[0], w.draft_ids[ok]] = 1.0
+    return q
+
+
 def check_onehot(sv, w, label, ragged=None, expect=None):
     """Runs w (q None) under each plan through the one-hot entry point; the oracle sees
     the same workload with q = one-hot(draft)."""
     expect = sv.SV_OK if expect is None else expect
     _say(label, f"B={w.B} V={w.V} dtype={w.dtype} T={w.T} rows={w.draft_rows}")
-    wq = dataclasses.replace(w, q=synth.onehot_q(w))
+    wq = dataclasses.replace(w, q=onehot_q(w))
     ora = oracle_batch(wq)
     dev = to_device(w, with_q=False)
     code = sv.SV_BF16 if w.dtype == "bf16" else sv.SV_F32
