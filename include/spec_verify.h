@@ -86,7 +86,8 @@ enum {
   SV_DATA_DRAFT_ID = 1,   /* a draft id outside [0, V) */
   SV_DATA_NONFINITE = 2,  /* a row normaliser not finite / not positive */
   SV_DATA_UNIFORM = 4,    /* a uniform outside [0, 1) */
-  SV_DATA_CU_GAMMA = 8    /* malformed cu_gamma */
+  SV_DATA_CU_GAMMA = 8,   /* malformed cu_gamma */
+  SV_DATA_CONTEXT = 16    /* malformed cu_ctx (spec_ngram_propose) */
 };
 
 /*
@@ -137,11 +138,16 @@ int spec_verify_run(spec_verify_ctx *ctx, void *hip_stream, int batch, int gamma
                     float *residual_sum, float *p_draft);
 
 /*
- * The same step for deterministic drafts (n-gram or prompt-lookup proposals): the draft
- * distribution is one-hot at the proposed id, q = onehot(x), so no q is passed or read.
- * Then the accept test is u < p(x), and after a rejection at n the draw is from
- * max(0, p_n - onehot(x_n)) = p_n with x_n removed, S = 1 - p_n(x_n) (p_n(x_n) = 1 draws
- * from p_n and reports S = 0). An id outside [0, V) is rejected and removes nothing.
+ * The same step for deterministic drafts, such as prompt-lookup (n-gram) proposals
+ * ("Speculative Decoding", atonlee.tistory.com/330, ch.5; the pages do not say how such
+ * drafts are verified, and this entry point takes the plain reading that the draft
+ * distribution is one-hot at the proposed id, q = onehot(x)). No q is passed or read.
+ * With the accept rule of ch.3 the test becomes u < p(x), and after a rejection at n
+ * the draw is from max(0, p_n - onehot(x_n)) = p_n with x_n removed, S = 1 - p_n(x_n)
+ * (p_n(x_n) = 1 draws from p_n and reports S = 0).
+ * An id of -1 means "no draft at this slot" (spec_ngram_propose pads with it): the slot
+ * is rejected, nothing is removed from p_n and no data flag is raised. Any other id
+ * outside [0, V) is handled the same way but raises SV_DATA_DRAFT_ID.
  * Arguments, outputs and errors as spec_verify_run without q; with T == 0 it is the
  * greedy rule.
  */
@@ -192,6 +198,39 @@ int spec_verify_last_path(const spec_verify_ctx *ctx);
 enum { SV_SAMPLE_LOGITS = 0, SV_SAMPLE_WEIGHTS = 1 };
 int spec_sample_run(spec_verify_ctx *ctx, void *hip_stream, int rows, int mode, float temperature,
                     const void *x, const float *uniforms, int32_t *tokens);
+
+/*
+ * Prompt-lookup (n-gram) draft proposer ("Speculative Decoding", atonlee.tistory.com/330,
+ * ch.5 prompt lookup; "투기적 디코딩 — 초안 모델을 무엇으로 세울 것인가",
+ * ailab.paldyn.com, "네 가지 방식"): for every context, the current suffix is looked up
+ * earlier in the same context and the tokens that followed it there are proposed.
+ * Readings of what the pages leave open: suffix lengths n = n_max .. n_min are tried and
+ * the longest that occurs earlier wins; the occurrence must end before the last token
+ * (it may overlap the suffix); of that length the most recent occurrence is used; at most
+ * gamma following tokens are proposed, fewer where the context ends.
+ *
+ *   batch        B >= 0 contexts (B == 0: nothing is enqueued; returns SV_OK).
+ *   tokens       device int32 [total_tokens], the contexts packed back to back; ids are
+ *                only compared for equality (any int32 value).
+ *   cu_ctx       device int32 [B+1], exclusive prefix of the context lengths.
+ *   total_tokens host copy of cu_ctx[B] (>= 0).
+ *   n_min, n_max 1 <= n_min <= n_max <= SV_NGRAM_MAX_N.
+ *   gamma        0 <= gamma <= 1024 drafts per context.
+ * Outputs (device, caller-owned, written completely):
+ *   draft_ids    int32 [B, gamma]: row b holds its proposal, then -1 (the no-draft mark
+ *                of spec_verify_run_onehot), so the rows feed that call with a uniform
+ *                gamma.
+ *   draft_len    int32 [B]: the proposal lengths (0 when nothing matched).
+ * Errors: SV_EINVAL (ctx NULL, a required pointer NULL, sizes out of range; nothing is
+ * launched), SV_EHIP. Offsets outside [0, total_tokens] or decreasing give that context
+ * no proposal and set SV_DATA_CONTEXT (reported by spec_verify_status).
+ * Runs on the context's device and stream like spec_verify_run; the vocabulary and
+ * workspace of the context are not used.
+ */
+enum { SV_NGRAM_MAX_N = 64 };
+int spec_ngram_propose(spec_verify_ctx *ctx, void *hip_stream, int batch, const int32_t *tokens,
+                       const int32_t *cu_ctx, int total_tokens, int n_min, int n_max, int gamma,
+                       int32_t *draft_ids, int32_t *draft_len);
 
 /*
  * Synchronize the stream of the last run, read and clear the device's sticky

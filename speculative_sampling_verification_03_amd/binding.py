@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(PKG, "libspecverify.so")
 
 SV_OK, SV_EINVAL, SV_ENOMEM, SV_EHIP, SV_EDATA = 0, 1, 2, 3, 4
 SV_F32, SV_BF16 = 0, 1
-SV_DATA_DRAFT_ID, SV_DATA_NONFINITE, SV_DATA_UNIFORM, SV_DATA_CU_GAMMA = 1, 2, 4, 8
+SV_DATA_DRAFT_ID, SV_DATA_NONFINITE, SV_DATA_UNIFORM, SV_DATA_CU_GAMMA, SV_DATA_CONTEXT = 1, 2, 4, 8, 16
+SV_NGRAM_MAX_N = 64
 SV_PATH_AUTO, SV_PATH_TWO_LAUNCH, SV_PATH_ONE_LAUNCH = 0, 1, 2
 SV_SAMPLE_LOGITS, SV_SAMPLE_WEIGHTS = 0, 1
 _CODE_NAMES = {SV_OK: "SV_OK", SV_EINVAL: "SV_EINVAL", SV_ENOMEM: "SV_ENOMEM",
@@ -27,7 +28,7 @@ EXPORTED = (
     "spec_verify_create", "spec_verify_run", "spec_verify_status",
     "spec_verify_last_error", "spec_verify_destroy", "spec_verify_set_timing",
     "spec_verify_kernel_times", "spec_verify_check_args", "spec_verify_set_path", "spec_verify_set_timing_stride",
-    "spec_verify_last_path", "spec_sample_run", "spec_verify_run_onehot",
+    "spec_verify_last_path", "spec_sample_run", "spec_verify_run_onehot", "spec_ngram_propose",
 )
 
 
@@ -70,6 +71,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.spec_verify_check_args.restype = i32
     lib.spec_verify_run_onehot.argtypes = [vp, vp, i32, i32, vp, i32, f32, vp, vp, vp, vp, vp, vp, vp]
     lib.spec_verify_run_onehot.restype = i32
+    lib.spec_ngram_propose.argtypes = [vp, vp, i32, vp, vp, i32, i32, i32, i32, vp, vp]
+    lib.spec_ngram_propose.restype = i32
     lib.spec_sample_run.argtypes = [vp, vp, i32, i32, f32, vp, vp, vp]
     lib.spec_sample_run.restype = i32
     lib.spec_verify_set_timing_stride.argtypes = [vp, i32]
@@ -145,6 +148,16 @@ def spec_sample_run(ctx: int, stream, rows: int, mode: int, temperature: float, 
     (SV_SAMPLE_WEIGHTS); raises SpecVerifyError on a non-OK code."""
     rc = load_library().spec_sample_run(ctx, _stream(stream), rows, mode, float(temperature), _ptr(x),
                                         _ptr(uniforms), _ptr(tokens))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, _msg(ctx))
+
+
+def spec_ngram_propose(ctx: int, stream, batch: int, tokens, cu_ctx, total_tokens: int, n_min: int,
+                       n_max: int, gamma: int, draft_ids, draft_len) -> None:
+    """Enqueue the prompt-lookup proposer; raises SpecVerifyError on a non-OK code."""
+    rc = load_library().spec_ngram_propose(ctx, _stream(stream), batch, _ptr(tokens), _ptr(cu_ctx),
+                                           total_tokens, n_min, n_max, gamma, _ptr(draft_ids),
+                                           _ptr(draft_len))
     if rc != SV_OK:
         raise SpecVerifyError(rc, _msg(ctx))
 

@@ -47,6 +47,7 @@
 
 #include "spec_verify.h"
 #include "sv_device.h"
+#include "sv_ngram.h"
 
 using namespace sv;
 
@@ -93,10 +94,15 @@ struct Args {
   // tlo..thi, thi < 0x7F80; tlo > thi when the table is not used
   int tlo, thi;
   int onehot;      // drafts are deterministic: q = one-hot(draft), q is not read
+  int nodraft;     // an id of -1 marks "no draft here": rejected without the data flag
 };
 
 __device__ __forceinline__ bool finite_pos(float z) { return z > 0.f && z <= FLT_MAX; }
 __device__ __forceinline__ bool finite_f(float v) { return v >= -FLT_MAX && v <= FLT_MAX; }
+// A draft id that raises the data flag: outside [0, V), unless it is the no-draft mark.
+__device__ __forceinline__ bool bad_id(const Args& a, int x) {
+  return !(x >= 0 && x < a.V) && !(a.nodraft && x == -1);
+}
 
 // Geometry of sequence b; false when cu_gamma is malformed.
 template <bool RAGGED>
@@ -137,7 +143,7 @@ __device__ __forceinline__ bool accept_decision(int x, float lx, float qx, float
     const double thr = px >= qd ? 1.0 : px / qd;  // no division when p >= q
     acc = static_cast<double>(uu) < thr;         // strict
     if (flag_errors && !(uu >= 0.f && uu < 1.f)) atomicOr(a.err, SV_DATA_UNIFORM);
-  } else if (flag_errors) {
+  } else if (flag_errors && bad_id(a, x)) {
     atomicOr(a.err, SV_DATA_DRAFT_ID);
   }
   if (flag_errors && !(finite_pos(z) && finite_f(c))) atomicOr(a.err, SV_DATA_NONFINITE);
@@ -313,7 +319,7 @@ __global__ __launch_bounds__(kThreads) void k_rowargmax(Args a) {
     if (ACCEPT) {
       // accept iff the draft equals the target argmax ([P1] ch.3 greedy; [P4])
       a.accept[d] = x == I ? 1 : 0;
-      if (!(x >= 0 && x < a.V)) atomicOr(a.err, SV_DATA_DRAFT_ID);
+      if (bad_id(a, x)) atomicOr(a.err, SV_DATA_DRAFT_ID);
     }
   }
 }
@@ -429,7 +435,7 @@ __device__ __forceinline__ int first_rejection(const Args& a, int b, int base, i
       s_tok[i] = I;
       const int x = a.ids[d];
       acc = x == I;
-      if (!(x >= 0 && x < a.V)) atomicOr(a.err, SV_DATA_DRAFT_ID);
+      if (bad_id(a, x)) atomicOr(a.err, SV_DATA_DRAFT_ID);
     } else {
       float C = -FLT_MAX, Z = 0.f;
       for (int k = 0; k < a.split; ++k) {
@@ -1767,6 +1773,7 @@ int run_impl(spec_verify_ctx* ctx, void* hip_stream, int batch, int gamma, const
   a.logits = logits;
   a.q = greedy || onehot ? nullptr : q;
   a.onehot = onehot && !greedy ? 1 : 0;
+  a.nodraft = onehot ? 1 : 0;
   a.ids = draft_ids;
   a.u = greedy ? nullptr : uniforms;
   a.cu = cu_gamma;
@@ -1971,6 +1978,43 @@ int spec_sample_run(spec_verify_ctx* ctx, void* hip_stream, int rows, int mode, 
   return SV_OK;
 }
 
+int spec_ngram_propose(spec_verify_ctx* ctx, void* hip_stream, int batch, const int32_t* tokens,
+                       const int32_t* cu_ctx, int total_tokens, int n_min, int n_max, int gamma,
+                       int32_t* draft_ids, int32_t* draft_len) {
+  if (!ctx) return SV_EINVAL;
+  auto bad = [&](const char* m) {
+    set_msg(ctx->msg, sizeof(ctx->msg), m);
+    return SV_EINVAL;
+  };
+  if (batch < 0) return bad("batch must be >= 0");
+  if (total_tokens < 0) return bad("total_tokens must be >= 0");
+  if (!(n_min >= 1 && n_min <= n_max && n_max <= SV_NGRAM_MAX_N))
+    return bad("need 1 <= n_min <= n_max <= SV_NGRAM_MAX_N");
+  if (gamma < 0 || gamma > 1024) return bad("gamma must be in [0, 1024]");
+  if (batch == 0) return SV_OK;
+  if (!cu_ctx || !draft_len) return bad("cu_ctx or draft_len is NULL");
+  if (total_tokens > 0 && !tokens) return bad("tokens is NULL");
+  if (gamma > 0 && !draft_ids) return bad("draft_ids is NULL");
+  DeviceGuard guard(ctx->device);
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  NgramArgs a{};
+  a.tok = tokens;
+  a.cu = cu_ctx;
+  a.ids = draft_ids;
+  a.len = draft_len;
+  a.err = ctx->err;
+  a.B = batch;
+  a.total = total_tokens;
+  a.n_min = n_min;
+  a.n_max = n_max;
+  a.gamma = gamma;
+  const hipError_t e = sv_launch_ngram(a, st);
+  if (e != hipSuccess) return hip_fail(ctx, "kernel launch", e);
+  ctx->last_stream = st;
+  ctx->ran = true;
+  return SV_OK;
+}
+
 int spec_verify_set_path(spec_verify_ctx* ctx, int mode) {
   if (!ctx || (mode != SV_PATH_AUTO && mode != SV_PATH_TWO_LAUNCH && mode != SV_PATH_ONE_LAUNCH)) return SV_EINVAL;
   ctx->path_mode = mode;
@@ -1991,11 +2035,12 @@ int spec_verify_status(spec_verify_ctx* ctx) {
   const int zero = 0;
   e = hipMemcpy(ctx->err, &zero, sizeof(int), hipMemcpyHostToDevice);
   if (e != hipSuccess) return hip_fail(ctx, "hipMemcpy", e);
-  snprintf(ctx->msg, sizeof(ctx->msg), "device data error flags 0x%x:%s%s%s%s", flag,
+  snprintf(ctx->msg, sizeof(ctx->msg), "device data error flags 0x%x:%s%s%s%s%s", flag,
            (flag & SV_DATA_DRAFT_ID) ? " draft-id-out-of-range" : "",
            (flag & SV_DATA_NONFINITE) ? " non-finite-normaliser" : "",
            (flag & SV_DATA_UNIFORM) ? " uniform-out-of-[0,1)" : "",
-           (flag & SV_DATA_CU_GAMMA) ? " malformed-cu_gamma" : "");
+           (flag & SV_DATA_CU_GAMMA) ? " malformed-cu_gamma" : "",
+           (flag & SV_DATA_CONTEXT) ? " malformed-cu_ctx" : "");
   return SV_EDATA;
 }
 

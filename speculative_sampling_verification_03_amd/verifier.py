@@ -11,7 +11,7 @@ from .binding import (SV_BF16, SV_EDATA, SV_F32, spec_verify_create, spec_verify
                       spec_verify_kernel_times, spec_verify_last_error, spec_verify_last_path,
                       spec_verify_run, spec_verify_set_path, spec_verify_set_timing,
                       spec_verify_set_timing_stride, spec_verify_status, spec_sample_run,
-                      spec_verify_run_onehot,
+                      spec_verify_run_onehot, spec_ngram_propose,
                       SV_SAMPLE_LOGITS, SV_SAMPLE_WEIGHTS)
 
 
@@ -142,6 +142,26 @@ class Verifier:
         spec_sample_run(self.ctx, st, rows, mode, float(temperature), x,
                         None if (mode == SV_SAMPLE_LOGITS and float(temperature) == 0.0) else uniforms, tokens)
         return tokens
+
+    def propose_ngram(self, tokens, cu_ctx, *, gamma: int, n_min: int = 1, n_max: int = 4,
+                      total_tokens: Optional[int] = None, draft_ids=None, draft_len=None, stream=None):
+        """Prompt-lookup drafts for B packed contexts (tokens int32, cu_ctx int32 [B+1] on the
+        device; total_tokens defaults to tokens.numel()). Returns (draft_ids int32 [B, gamma]
+        with -1 after each proposal, draft_len int32 [B]); the ids feed run(..., onehot=True)."""
+        import torch
+        self._check("tokens", tokens, torch.int32)
+        self._check("cu_ctx", cu_ctx, torch.int32)
+        B = cu_ctx.numel() - 1
+        total = int(tokens.numel() if total_tokens is None else total_tokens)
+        if draft_ids is None:
+            draft_ids = torch.empty((B, gamma), dtype=torch.int32, device=self.device)
+        if draft_len is None:
+            draft_len = torch.empty(B, dtype=torch.int32, device=self.device)
+        self._check("draft_ids", draft_ids, torch.int32, B * gamma)
+        self._check("draft_len", draft_len, torch.int32, B)
+        st = stream if stream is not None else torch.cuda.current_stream(self.device)
+        spec_ngram_propose(self.ctx, st, B, tokens, cu_ctx, total, n_min, n_max, gamma, draft_ids, draft_len)
+        return draft_ids, draft_len
 
     def status(self) -> int:
         """SV_OK, or SV_EDATA when the device flagged a data error (see last_error)."""

@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "spec_verify.h")
 def declared_functions():
     text = open(HEADER, encoding="utf-8").read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(spec_(?:verify|sample)_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(spec_(?:verify|sample|ngram)_\w+)\s*\(", text)))
 
 
 def test_library_built():
@@ -37,8 +37,10 @@ def test_exports_every_declared_symbol():
 
 def test_library_links_no_torch():
     out = subprocess.run(["ldd", sv.LIB_PATH], capture_output=True, text=True).stdout
-    assert "torch" not in out and "c10" not in out
-    assert "amdhip64" in out
+    # library names and paths only: the load addresses are hex and can contain "c10"
+    deps = " ".join(re.sub(r"\(0x[0-9a-f]+\)", "", line) for line in out.splitlines())
+    assert "torch" not in deps and "c10" not in deps
+    assert "amdhip64" in deps
 
 
 BASE = dict(vocab=1000, logits_dtype=sv.SV_BF16, max_batch=64, max_draft_rows=512, max_gamma=8,
@@ -96,6 +98,9 @@ def test_null_context_calls():
     assert lib.spec_verify_set_timing_stride(None, 2) == sv.SV_EINVAL
     assert lib.spec_sample_run(None, None, 1, sv.SV_SAMPLE_WEIGHTS, 1.0, None, None, None) == sv.SV_EINVAL
     assert lib.spec_verify_last_path(None) == -sv.SV_EINVAL
+    assert lib.spec_ngram_propose(None, None, 1, None, None, 0, 1, 2, 4, None, None) == sv.SV_EINVAL
+    assert lib.spec_verify_run_onehot(None, None, 1, 1, None, 1, 1.0, None, None, None, None, None, None,
+                                      None) == sv.SV_EINVAL
     lib.spec_verify_destroy(None)  # NULL-safe
     rc = lib.spec_verify_run(None, None, 1, 1, None, 1, 1.0, None, None, None, None, None, None, None, None)
     assert rc == sv.SV_EINVAL

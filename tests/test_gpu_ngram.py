@@ -1,0 +1,181 @@
+"""GPU parity of the prompt-lookup (n-gram) proposer (spec_ngram_propose) against the
+oracle, bit for bit, and of a whole deterministic-draft round: proposals from the GPU
+fed to spec_verify_run_onehot, against the oracle's proposals and verification.
+
+Contexts and logits come from the seeded generators in `synth`; expected values from
+`oracle` only.
+"""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+from _parity import compare, oracle_batch, run_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+def _say(*a):
+    print("[gpu-case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import speculative_sampling_verification_03_amd as sv
+    sv.load_library()
+    return sv
+
+
+@pytest.fixture(scope="module")
+def ver(lib):
+    v = lib.Verifier(1000, lib.SV_F32, 1, 1, 1)
+    yield v
+    v.close()
+
+
+def _propose(v, ctx, n_min, n_max, gamma):
+    t = torch.from_numpy(ctx.tokens).cuda() if ctx.tokens.size else torch.zeros(1, dtype=torch.int32, device="cuda")
+    cu = torch.from_numpy(ctx.cu_ctx).cuda()
+    ids, lens = v.propose_ngram(t, cu, gamma=gamma, n_min=n_min, n_max=n_max, total_tokens=int(ctx.tokens.size))
+    return ids.cpu().numpy(), lens.cpu().numpy()
+
+
+def _check(v, lib, ctx, n_min, n_max, gamma, label):
+    _say(label, f"B={ctx.B} tokens={ctx.tokens.size} n={n_min}..{n_max} gamma={gamma}")
+    ids, lens = _propose(v, ctx, n_min, n_max, gamma)
+    assert v.status() == lib.SV_OK, v.last_error()
+    ids_o, lens_o = O.ngram_propose_batch(ctx.tokens, ctx.cu_ctx, n_min, n_max, gamma)
+    bad = np.flatnonzero((lens != lens_o) | np.any(ids.reshape(ctx.B, gamma) != ids_o, axis=1))
+    _say(label, f"proposing={int((lens_o > 0).sum())} mean_len={lens_o.mean():.2f} mismatches={bad.size}")
+    assert bad.size == 0, [(int(b), lens[b], lens_o[b]) for b in bad[:5]]
+    return ids, lens
+
+
+@pytest.mark.parametrize("n_min,n_max,gamma", [(1, 4, 4), (2, 8, 8), (3, 3, 5), (1, 1, 1)])
+def test_ngram_parity_copy_heavy(lib, ver, n_min, n_max, gamma):
+    ctx = synth.make_ngram_contexts(96, (0, 3000), 128256, seed=100 + n_max)
+    _check(ver, lib, ctx, n_min, n_max, gamma, "copy-heavy")
+
+
+def test_ngram_parity_long_contexts(lib, ver):
+    """256 contexts of 8192 tokens: several chunks per context, both the early stop and
+    the full scan."""
+    ctx = synth.make_ngram_contexts(256, (8192, 8192), 128256, seed=7)
+    _check(ver, lib, ctx, 2, 8, 4, "long contexts")
+    ctx = synth.make_ngram_contexts(64, (20000, 40000), 128256, seed=8, copy_prob=0.05)
+    _check(ver, lib, ctx, 3, 6, 4, "long, rarely repeating")
+
+
+def test_ngram_small_alphabets(lib, ver):
+    """Many partial matches (ids from 2..4 symbols) exercise the suffix comparison."""
+    rng = np.random.default_rng(9)
+    B = 128
+    L = rng.integers(0, 5000, B)
+    L[:6] = (0, 1, 2, 3, 4097, 2048)
+    cu = synth.pack(L)
+    tokens = np.concatenate([rng.integers(0, int(rng.integers(2, 5)), int(n)) for n in L]).astype(np.int32)
+    ctx = synth.Contexts(B, tokens, cu)
+    for n_min, n_max, gamma in ((1, 16, 6), (4, 64, 3), (64, 64, 2)):
+        _check(ver, lib, ctx, n_min, n_max, gamma, f"small alphabets n={n_min}..{n_max}")
+
+
+def test_ngram_constant_and_periodic(lib, ver):
+    L = [1, 2, 5, 300, 2049, 7000]
+    parts = [np.full(n, 42, np.int32) for n in L] + [np.tile(np.arange(7, dtype=np.int32), 700)]
+    ctx = synth.Contexts(len(parts), np.concatenate(parts), synth.pack([p.size for p in parts]))
+    _check(ver, lib, ctx, 1, 8, 5, "constant and periodic")
+
+
+def test_ngram_empty_batch_and_gamma_zero(lib, ver):
+    t = torch.zeros(4, dtype=torch.int32, device="cuda")
+    cu = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ids, lens = ver.propose_ngram(t, cu, gamma=4)
+    assert ids.numel() == 0 and lens.numel() == 0
+    ctx = synth.make_ngram_contexts(8, (10, 50), 100, seed=10)
+    ids, lens = _propose(ver, ctx, 1, 4, 0)
+    assert np.all(lens == 0) and ids.size == 0
+    assert ver.status() == lib.SV_OK
+
+
+def test_ngram_host_errors(lib, ver):
+    t = torch.zeros(8, dtype=torch.int32, device="cuda")
+    cu = torch.tensor([0, 4, 8], dtype=torch.int32, device="cuda")
+    for kw in (dict(n_min=0, n_max=2, gamma=2), dict(n_min=3, n_max=2, gamma=2),
+               dict(n_min=1, n_max=lib.SV_NGRAM_MAX_N + 1, gamma=2), dict(n_min=1, n_max=2, gamma=1025)):
+        with pytest.raises(lib.SpecVerifyError):
+            ver.propose_ngram(t, cu, **kw)
+
+
+def test_ngram_malformed_offsets_flagged(lib, ver):
+    ctx = synth.make_ngram_contexts(6, (100, 400), 1000, seed=11)
+    cu = ctx.cu_ctx.copy()
+    cu[3] = cu[2] - 1  # context 2 ends before it starts; context 3 starts there
+    bad = synth.Contexts(6, ctx.tokens, cu)
+    ids, lens = _propose(ver, bad, 1, 4, 4)
+    assert ver.status() == lib.SV_EDATA and "cu_ctx" in ver.last_error()
+    assert lens[2] == 0 and np.all(ids[2] == -1)
+    ids_o, lens_o = O.ngram_propose_batch(ctx.tokens, ctx.cu_ctx, 1, 4, 4)
+    for b in (0, 1, 4, 5):
+        assert lens[b] == lens_o[b] and np.array_equal(ids[b], ids_o[b])
+
+
+def _boost_drafts(w, ids_rows, rng, frac):
+    """Raise the target logit of a draft id above the row maximum in a fraction of the
+    rows, so that rounds accept several drafts (the copy-heavy case)."""
+    L = w.logits_f32().copy()
+    for b in range(w.B):
+        for i in range(w.uniform_gamma):
+            x = int(ids_rows[b, i])
+            if x >= 0 and rng.random() < frac:
+                r = w.logit_row(b, i)
+                L[r, x] = L[r].max() + 2.0
+    w.logits = synth.bf16_round(L) if w.dtype == "bf16" else L
+
+
+def onehot_q(w):
+    q = np.zeros((w.draft_rows, w.V), dtype=np.float32)
+    ok = (w.draft_ids >= 0) & (w.draft_ids < w.V)
+    q[np.nonzero(ok)[0], w.draft_ids[ok]] = 1.0
+    return q
+
+
+@pytest.mark.parametrize("dtype,V,T", [("f32", 32000, 0.8), ("bf16", 128256, 1.0), ("bf16", 128256, 0.0)])
+def test_ngram_round_end_to_end(lib, dtype, V, T):
+    """Proposals on the GPU feed the one-hot verification (uniform gamma, -1 pads); both
+    must equal the oracle's proposer followed by the oracle's verification."""
+    B, gamma = 64, 4
+    ctx = synth.make_ngram_contexts(B, (200, 3000), V, seed=12)
+    code = lib.SV_BF16 if dtype == "bf16" else lib.SV_F32
+    v = lib.Verifier(V, code, B, B * gamma, gamma)
+    _say("n-gram round", f"B={B} V={V} {dtype} T={T}")
+    ids, lens = _propose(v, ctx, 2, 6, gamma)
+    ids_o, lens_o = O.ngram_propose_batch(ctx.tokens, ctx.cu_ctx, 2, 6, gamma)
+    assert np.array_equal(ids, ids_o) and np.array_equal(lens, lens_o)
+    w = synth.make_onehot("ngram-round", np.full(B, gamma), V, dtype, T if T > 0 else 1.0, 3.0, 0.0, seed=13)
+    w.draft_ids = ids_o.reshape(-1).astype(np.int32)
+    _boost_drafts(w, ids_o, np.random.default_rng(14), 0.75)
+    if T == 0.0:
+        w = dataclasses.replace(w, T=0.0, uniforms=None)
+    wq = dataclasses.replace(w, q=onehot_q(w)) if T > 0 else w
+    ora = oracle_batch(wq)
+    dev = to_device(w, with_q=False)
+    dev["draft_ids"] = torch.from_numpy(ids.reshape(-1).copy()).cuda()  # the GPU's own proposals
+    plans = ((lib.SV_PATH_TWO_LAUNCH, True), (lib.SV_PATH_ONE_LAUNCH, True), (lib.SV_PATH_ONE_LAUNCH, False))
+    for plan, want_p in (plans if T > 0 else plans[:1]):
+        v.set_path(plan)
+        gpu = run_gpu(v, w, dev=dev, want_p_draft=want_p, onehot=True)
+        assert gpu["status"] == lib.SV_OK, v.last_error()  # -1 pads raise no flag
+        rep = compare(wq, gpu, ora)
+        _say("n-gram round", f"plan={v.last_path()}", rep.summary(),
+             f"mean accepted={gpu['accepted_count'].mean():.2f}")
+        assert rep.ok(), rep.summary()
+        # a round never accepts past the end of its proposal
+        assert np.all(gpu["accepted_count"] <= lens)
+    v.close()
