@@ -130,6 +130,71 @@ def bench_sampling(sv, torch, sets, dev, code, args, iters=100):
     return res
 
 
+def _timed(torch, go, iters, warm=10):
+    """Seconds per call of go(k) on torch's current stream (events around the loop)."""
+    for k in range(warm):
+        go(k)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for k in range(iters):
+        go(k)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / iters
+
+
+def bench_ngram(sv, torch, dev, iters=200):
+    """Deterministic drafts: the prompt-lookup proposer over copy-heavy contexts, and the
+    one-hot verification of drafts the target is often confident about, at B=256 gamma=4
+    V=128256 bf16, T=1."""
+    import numpy as np
+    import synth
+    res = {}
+    B, L, gamma, n_min, n_max = 256, 8192, 4, 2, 6
+    ctx = synth.make_ngram_contexts(B, (L, L), 128256, seed=31)
+    tok = torch.from_numpy(ctx.tokens).to(dev)
+    cu = torch.from_numpy(ctx.cu_ctx).to(dev)
+    ver = sv.Verifier(128256, sv.SV_BF16, B, B * gamma, gamma)
+    ids = torch.empty((B, gamma), dtype=torch.int32, device=dev)
+    lens = torch.empty(B, dtype=torch.int32, device=dev)
+    dt = _timed(torch, lambda k: ver.propose_ngram(tok, cu, gamma=gamma, n_min=n_min, n_max=n_max,
+                                                 draft_ids=ids, draft_len=lens), iters)
+    assert ver.status() == sv.SV_OK, ver.last_error()
+    ctx_bytes = ctx.tokens.nbytes + ctx.cu_ctx.nbytes + ids.numel() * 4 + B * 4
+    ln = lens.cpu().numpy()
+    res["ngram_propose"] = {
+        "workload": f"B={B} contexts of {L} tokens (copy-heavy), n={n_min}..{n_max}, gamma={gamma}",
+        "us_per_call": dt * 1e6, "contexts_per_s": B / dt,
+        "context_GBps": ctx_bytes / dt / 1e9,
+        "context_bytes_basis": "every context read once (an upper bound: the scan stops early)",
+        "proposing_fraction": float((ln > 0).mean()), "mean_draft_len": float(ln.mean())}
+    log(f"[bench] F3 n-gram proposer: {B} x {L} tokens in {dt * 1e6:.1f} us "
+        f"({ctx_bytes / dt / 1e9:.0f} GB/s over whole contexts), mean proposal {ln.mean():.2f}")
+
+    w = synth.make_onehot("C3-onehot", np.full(B, gamma), 128256, "bf16", 1.0, 3.0, 1.0, seed=32)
+    synth.boost_drafts(w, 0.8, 4.0, seed=33)
+    d = {"logits": torch.from_numpy(w.logits.view(np.int16)).view(torch.bfloat16).to(dev),
+         "ids": torch.from_numpy(w.draft_ids).to(dev), "u": torch.from_numpy(w.uniforms).to(dev)}
+    out = sv.VerifyOutputs(torch.empty(B, dtype=torch.int32, device=dev),
+                           torch.empty(w.target_rows, dtype=torch.int32, device=dev),
+                           torch.empty(B, dtype=torch.float32, device=dev), None)
+    dt = _timed(torch, lambda k: ver.run(d["logits"], d["ids"], temperature=1.0, uniforms=d["u"], gamma=gamma,
+                                         out=out, onehot=True), iters)
+    assert ver.status() == sv.SV_OK, ver.last_error()
+    n = out.accepted_count.cpu().numpy()
+    res["onehot_verify"] = {
+        "workload": f"B={B} gamma={gamma} V=128256 bf16 logits, T=1, one-hot drafts (no q), "
+                    "target confident about 80% of the drafts",
+        "plan": {sv.SV_PATH_ONE_LAUNCH: "one launch", sv.SV_PATH_TWO_LAUNCH: "two launches"}.get(ver.last_path()),
+        "us_per_step": dt * 1e6, "positions_per_s": B * gamma / dt,
+        "tokens_per_round": float(np.mean(n + 1))}
+    log(f"[bench] F3 one-hot verification: {dt * 1e6:.1f} us/step, {B * gamma / dt / 1e6:.2f} M positions/s, "
+        f"{np.mean(n + 1):.2f} tokens/round")
+    ver.close()
+    return res
+
+
 def cpu_baseline(w, seconds):
     """The oracle as it stands, single process, cycling over the sequences of one input
     set until about `seconds` of CPU work have been done."""
@@ -164,7 +229,7 @@ def main():
     ap.add_argument("--sets", type=int, default=2, help="input sets rotated across steps")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-next", action="store_true", help="skip the follow-on measurements (F1 sampling)")
+    ap.add_argument("--no-next", action="store_true", help="skip the follow-on measurements (sampling, deterministic drafts)")
     ap.add_argument("--no-every-row", action="store_true",
                     help="skip the second timing with p(x) requested (every draft row read)")
     ap.add_argument("--plan", choices=("auto", "two", "one"), default="auto",
@@ -320,6 +385,7 @@ def main():
     next_rows = {}
     if not args.no_next and w0.T > 0:
         next_rows["F1_sample"] = bench_sampling(sv, torch, sets, dev, code, args)
+        next_rows["F3_deterministic_drafts"] = bench_ngram(sv, torch, dev)
 
     # acceptance metrics of the measured inputs
     acc = np.concatenate(nb)

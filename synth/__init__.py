@@ -37,7 +37,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "CONFIGS", "make_config", "make_sampling", "make_greedy",
-    "pack", "bf16_round", "bf16_widen", "config_number", "make_onehot",
+    "pack", "bf16_round", "bf16_widen", "config_number", "make_onehot", "boost_drafts",
     "Contexts", "make_ngram_contexts",
 ]
 
@@ -257,6 +257,20 @@ def make_onehot(name, gammas, V, dtype, T, sigma_logit, agree, seed) -> Workload
     u = ru.random(w.target_rows, dtype=np.float32)
     return Workload(name, w.B, V, dtype, float(T), w.gammas, w.cu_gamma, w.uniform_gamma, w.logits, None,
                     w.draft_ids, u)
+
+
+def boost_drafts(w: Workload, frac: float, margin: float, seed: int) -> Workload:
+    """Make the target confident about some drafts, as in copy-heavy text: in a fraction
+    `frac` of the draft rows with a valid id, that id's target logit is set to the row's
+    maximum plus `margin` (then stored in the workload's dtype). Changes w.logits in place."""
+    rg = np.random.Generator(np.random.PCG64(_streams(seed)["noise"]))
+    coin = rg.random(w.draft_rows)
+    lrow = _row_maps(w.cu_gamma)
+    for r in np.flatnonzero((coin < frac) & (w.draft_ids >= 0) & (w.draft_ids < w.V)):
+        row = w.logits_f32(slice(int(lrow[r]), int(lrow[r]) + 1))[0].copy()
+        row[w.draft_ids[r]] = row.max() + np.float32(margin)
+        w.logits[lrow[r]] = bf16_round(row) if w.dtype == "bf16" else row
+    return w
 
 
 @dataclasses.dataclass

@@ -126,19 +126,6 @@ def test_ngram_malformed_offsets_flagged(lib, ver):
         assert lens[b] == lens_o[b] and np.array_equal(ids[b], ids_o[b])
 
 
-def _boost_drafts(w, ids_rows, rng, frac):
-    """Raise the target logit of a draft id above the row maximum in a fraction of the
-    rows, so that rounds accept several drafts (the copy-heavy case)."""
-    L = w.logits_f32().copy()
-    for b in range(w.B):
-        for i in range(w.uniform_gamma):
-            x = int(ids_rows[b, i])
-            if x >= 0 and rng.random() < frac:
-                r = w.logit_row(b, i)
-                L[r, x] = L[r].max() + 2.0
-    w.logits = synth.bf16_round(L) if w.dtype == "bf16" else L
-
-
 def onehot_q(w):
     q = np.zeros((w.draft_rows, w.V), dtype=np.float32)
     ok = (w.draft_ids >= 0) & (w.draft_ids < w.V)
@@ -160,7 +147,7 @@ def test_ngram_round_end_to_end(lib, dtype, V, T):
     assert np.array_equal(ids, ids_o) and np.array_equal(lens, lens_o)
     w = synth.make_onehot("ngram-round", np.full(B, gamma), V, dtype, T if T > 0 else 1.0, 3.0, 0.0, seed=13)
     w.draft_ids = ids_o.reshape(-1).astype(np.int32)
-    _boost_drafts(w, ids_o, np.random.default_rng(14), 0.75)
+    synth.boost_drafts(w, 0.75, 2.0, seed=14)
     if T == 0.0:
         w = dataclasses.replace(w, T=0.0, uniforms=None)
     wq = dataclasses.replace(w, q=onehot_q(w)) if T > 0 else w
