@@ -37,7 +37,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "CONFIGS", "make_config", "make_sampling", "make_greedy",
-    "pack", "bf16_round", "bf16_widen", "config_number", "make_onehot", "boost_drafts",
+    "pack", "bf16_round", "bf16_widen", "config_number", "make_onehot", "boost_drafts", "controlled_alpha_rows",
     "Contexts", "make_ngram_contexts",
 ]
 
@@ -271,6 +271,21 @@ def boost_drafts(w: Workload, frac: float, margin: float, seed: int) -> Workload
         row[w.draft_ids[r]] = row.max() + np.float32(margin)
         w.logits[lrow[r]] = bf16_round(row) if w.dtype == "bf16" else row
     return w
+
+
+def controlled_alpha_rows(alphas, V: int):
+    """Per-sequence target logits and draft distributions with a known overlap alpha_b:
+    p = a*s + (1-a)*u, q = a*s + (1-a)*w, s uniform on all V ids, u uniform on the first
+    half, w on the second half (V even), so sum_v min(p, q) = a. Returns (logits = log p
+    as fp32 [B, V], q fp32 [B, V]). Needs every alpha_b > 0 (p > 0 everywhere)."""
+    a = np.asarray(alphas, dtype=np.float64)[:, None]
+    assert V % 2 == 0 and np.all(a > 0)
+    s = np.full(V, 1.0 / V)
+    u = np.r_[np.full(V // 2, 2.0 / V), np.zeros(V // 2)]
+    w = u[::-1]
+    p = a * s + (1 - a) * u
+    q = a * s + (1 - a) * w
+    return np.log(p).astype(np.float32), q.astype(np.float32)
 
 
 @dataclasses.dataclass
