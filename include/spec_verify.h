@@ -87,7 +87,8 @@ enum {
   SV_DATA_NONFINITE = 2,  /* a row normaliser not finite / not positive */
   SV_DATA_UNIFORM = 4,    /* a uniform outside [0, 1) */
   SV_DATA_CU_GAMMA = 8,   /* malformed cu_gamma */
-  SV_DATA_CONTEXT = 16    /* malformed cu_ctx (spec_ngram_propose) */
+  SV_DATA_CONTEXT = 16,   /* malformed cu_ctx (spec_ngram_propose) */
+  SV_DATA_STATE = 32      /* adaptive draft-length state out of range (spec_adapt_gamma) */
 };
 
 /*
@@ -231,6 +232,37 @@ enum { SV_NGRAM_MAX_N = 64 };
 int spec_ngram_propose(spec_verify_ctx *ctx, void *hip_stream, int batch, const int32_t *tokens,
                        const int32_t *cu_ctx, int total_tokens, int n_min, int n_max, int gamma,
                        int32_t *draft_ids, int32_t *draft_len);
+
+/*
+ * Adaptive draft length per sequence ("투기적 디코딩 — 초안 모델을 무엇으로 세울 것인가",
+ * ailab.paldyn.com, "도입할 때 순서대로 확인할 것": after rejections in a row go down
+ * to 1, raise again while acceptances continue; "Speculative Decoding",
+ * atonlee.tistory.com/330, ch.4: the best length follows the acceptance rate). Run it
+ * after a verification step to get the next round's draft lengths and packed layout.
+ * Readings of what the pages leave open: a round "accepts" when every draft was accepted
+ * (accepted_count[b] >= gamma[b]) and "rejects" otherwise; after up_after accepting
+ * rounds in a row gamma[b] goes up by one (at most gamma_max), after down_after
+ * rejecting rounds in a row it is cut to 1; a sequence with accepted_count -1 (its
+ * round was not run) keeps its state.
+ *
+ *   batch          0 <= B <= 65536 (B == 0: nothing is enqueued; returns SV_OK).
+ *   accepted_count device int32 [B], the round's output of spec_verify_run.
+ *   gamma          device int32 [B], in/out: the draft lengths of the round just
+ *                  verified, replaced by the next round's, in [1, gamma_max] (0 stays 0
+ *                  only when the round was not run).
+ *   streak         device int32 [B], in/out: accepting (> 0) or rejecting (< 0) rounds
+ *                  in a row; start at 0.
+ *   gamma_max      1 <= gamma_max <= 1024; up_after, down_after >= 1.
+ *   cu_gamma_next  device int32 [B+1], out: exclusive prefix of the new gamma, the
+ *                  cu_gamma of the next spec_verify_run (its total_draft_rows is
+ *                  cu_gamma_next[B]).
+ * Errors: SV_EINVAL (ctx NULL, a NULL pointer, values out of range; nothing launched),
+ * SV_EHIP. A gamma outside [0, gamma_max] or a streak outside [-down_after, up_after]
+ * on entry is clamped into range and sets SV_DATA_STATE. One workgroup does the batch.
+ */
+int spec_adapt_gamma(spec_verify_ctx *ctx, void *hip_stream, int batch, const int32_t *accepted_count,
+                     int32_t *gamma, int32_t *streak, int gamma_max, int up_after, int down_after,
+                     int32_t *cu_gamma_next);
 
 /*
  * Synchronize the stream of the last run, read and clear the device's sticky

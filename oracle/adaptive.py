@@ -24,7 +24,8 @@ Readings where the pages leave the rule open (also listed in the design notes):
   * After a rejecting round: s = min(s, 0) - 1; once -s reaches down_after, gamma is
     cut to 1 and s restarts at 0.
   * A sequence whose round was not run (accepted count -1, a flagged input) keeps its
-    state. A gamma outside [0, gamma_max] in the state is first clamped into it.
+    state. A gamma outside [0, gamma_max] or a streak outside [-down_after, up_after]
+    in the state is first clamped into that range.
   * The next round's packed layout is the exclusive prefix of the new gamma_b.
 """
 from __future__ import annotations
@@ -38,7 +39,7 @@ def adapt_gamma(gamma: int, streak: int, accepted: int, gamma_max: int, up_after
                 down_after: int):
     """One sequence, one round: returns the new (gamma, streak)."""
     g = min(max(int(gamma), 0), gamma_max)
-    s = int(streak)
+    s = min(max(int(streak), -down_after), up_after)
     n = int(accepted)
     if n < 0:
         return g, s

@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(PKG, "libspecverify.so")
 
 SV_OK, SV_EINVAL, SV_ENOMEM, SV_EHIP, SV_EDATA = 0, 1, 2, 3, 4
 SV_F32, SV_BF16 = 0, 1
-SV_DATA_DRAFT_ID, SV_DATA_NONFINITE, SV_DATA_UNIFORM, SV_DATA_CU_GAMMA, SV_DATA_CONTEXT = 1, 2, 4, 8, 16
+SV_DATA_DRAFT_ID, SV_DATA_NONFINITE, SV_DATA_UNIFORM, SV_DATA_CU_GAMMA, SV_DATA_CONTEXT, SV_DATA_STATE = \
+    1, 2, 4, 8, 16, 32
 SV_NGRAM_MAX_N = 64
 SV_PATH_AUTO, SV_PATH_TWO_LAUNCH, SV_PATH_ONE_LAUNCH = 0, 1, 2
 SV_SAMPLE_LOGITS, SV_SAMPLE_WEIGHTS = 0, 1
@@ -29,6 +30,7 @@ EXPORTED = (
     "spec_verify_last_error", "spec_verify_destroy", "spec_verify_set_timing",
     "spec_verify_kernel_times", "spec_verify_check_args", "spec_verify_set_path", "spec_verify_set_timing_stride",
     "spec_verify_last_path", "spec_sample_run", "spec_verify_run_onehot", "spec_ngram_propose",
+    "spec_adapt_gamma",
 )
 
 
@@ -73,6 +75,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.spec_verify_run_onehot.restype = i32
     lib.spec_ngram_propose.argtypes = [vp, vp, i32, vp, vp, i32, i32, i32, i32, vp, vp]
     lib.spec_ngram_propose.restype = i32
+    lib.spec_adapt_gamma.argtypes = [vp, vp, i32, vp, vp, vp, i32, i32, i32, vp]
+    lib.spec_adapt_gamma.restype = i32
     lib.spec_sample_run.argtypes = [vp, vp, i32, i32, f32, vp, vp, vp]
     lib.spec_sample_run.restype = i32
     lib.spec_verify_set_timing_stride.argtypes = [vp, i32]
@@ -158,6 +162,15 @@ def spec_ngram_propose(ctx: int, stream, batch: int, tokens, cu_ctx, total_token
     rc = load_library().spec_ngram_propose(ctx, _stream(stream), batch, _ptr(tokens), _ptr(cu_ctx),
                                            total_tokens, n_min, n_max, gamma, _ptr(draft_ids),
                                            _ptr(draft_len))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, _msg(ctx))
+
+
+def spec_adapt_gamma(ctx: int, stream, batch: int, accepted_count, gamma, streak, gamma_max: int,
+                     up_after: int, down_after: int, cu_gamma_next) -> None:
+    """Enqueue the adaptive draft-length update; raises SpecVerifyError on a non-OK code."""
+    rc = load_library().spec_adapt_gamma(ctx, _stream(stream), batch, _ptr(accepted_count), _ptr(gamma),
+                                         _ptr(streak), gamma_max, up_after, down_after, _ptr(cu_gamma_next))
     if rc != SV_OK:
         raise SpecVerifyError(rc, _msg(ctx))
 

@@ -12,8 +12,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libspecverify.so")
-SOURCES = [os.path.join(CSRC, "spec_verify.hip"), os.path.join(CSRC, "ngram.hip")]
+SOURCES = [os.path.join(CSRC, "spec_verify.hip"), os.path.join(CSRC, "ngram.hip"),
+           os.path.join(CSRC, "adapt.hip")]
 DEPS = SOURCES + [os.path.join(CSRC, "sv_device.h"), os.path.join(CSRC, "sv_ngram.h"),
+                  os.path.join(CSRC, "sv_adapt.h"),
                   os.path.join(INCLUDE, "spec_verify.h")]
 
 ARCH = os.environ.get("SPEC_VERIFY_ARCH", "gfx950")

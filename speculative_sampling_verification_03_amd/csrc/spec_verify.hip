@@ -47,6 +47,7 @@
 
 #include "spec_verify.h"
 #include "sv_device.h"
+#include "sv_adapt.h"
 #include "sv_ngram.h"
 
 using namespace sv;
@@ -2015,6 +2016,38 @@ int spec_ngram_propose(spec_verify_ctx* ctx, void* hip_stream, int batch, const 
   return SV_OK;
 }
 
+int spec_adapt_gamma(spec_verify_ctx* ctx, void* hip_stream, int batch, const int32_t* accepted_count,
+                     int32_t* gamma, int32_t* streak, int gamma_max, int up_after, int down_after,
+                     int32_t* cu_gamma_next) {
+  if (!ctx) return SV_EINVAL;
+  auto bad = [&](const char* m) {
+    set_msg(ctx->msg, sizeof(ctx->msg), m);
+    return SV_EINVAL;
+  };
+  if (batch < 0 || batch > kAdaptMaxBatch) return bad("batch must be in [0, 65536]");
+  if (gamma_max < 1 || gamma_max > 1024) return bad("gamma_max must be in [1, 1024]");
+  if (up_after < 1 || down_after < 1) return bad("up_after and down_after must be >= 1");
+  if (batch == 0) return SV_OK;
+  if (!accepted_count || !gamma || !streak || !cu_gamma_next) return bad("a state or output pointer is NULL");
+  DeviceGuard guard(ctx->device);
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  AdaptArgs a{};
+  a.acc = accepted_count;
+  a.gamma = gamma;
+  a.streak = streak;
+  a.cu = cu_gamma_next;
+  a.err = ctx->err;
+  a.B = batch;
+  a.gmax = gamma_max;
+  a.up = up_after;
+  a.down = down_after;
+  const hipError_t e = sv_launch_adapt(a, st);
+  if (e != hipSuccess) return hip_fail(ctx, "kernel launch", e);
+  ctx->last_stream = st;
+  ctx->ran = true;
+  return SV_OK;
+}
+
 int spec_verify_set_path(spec_verify_ctx* ctx, int mode) {
   if (!ctx || (mode != SV_PATH_AUTO && mode != SV_PATH_TWO_LAUNCH && mode != SV_PATH_ONE_LAUNCH)) return SV_EINVAL;
   ctx->path_mode = mode;
@@ -2035,12 +2068,13 @@ int spec_verify_status(spec_verify_ctx* ctx) {
   const int zero = 0;
   e = hipMemcpy(ctx->err, &zero, sizeof(int), hipMemcpyHostToDevice);
   if (e != hipSuccess) return hip_fail(ctx, "hipMemcpy", e);
-  snprintf(ctx->msg, sizeof(ctx->msg), "device data error flags 0x%x:%s%s%s%s%s", flag,
+  snprintf(ctx->msg, sizeof(ctx->msg), "device data error flags 0x%x:%s%s%s%s%s%s", flag,
            (flag & SV_DATA_DRAFT_ID) ? " draft-id-out-of-range" : "",
            (flag & SV_DATA_NONFINITE) ? " non-finite-normaliser" : "",
            (flag & SV_DATA_UNIFORM) ? " uniform-out-of-[0,1)" : "",
            (flag & SV_DATA_CU_GAMMA) ? " malformed-cu_gamma" : "",
-           (flag & SV_DATA_CONTEXT) ? " malformed-cu_ctx" : "");
+           (flag & SV_DATA_CONTEXT) ? " malformed-cu_ctx" : "",
+           (flag & SV_DATA_STATE) ? " adaptive-state-out-of-range" : "");
   return SV_EDATA;
 }
 

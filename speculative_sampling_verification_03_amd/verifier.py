@@ -11,7 +11,7 @@ from .binding import (SV_BF16, SV_EDATA, SV_F32, spec_verify_create, spec_verify
                       spec_verify_kernel_times, spec_verify_last_error, spec_verify_last_path,
                       spec_verify_run, spec_verify_set_path, spec_verify_set_timing,
                       spec_verify_set_timing_stride, spec_verify_status, spec_sample_run,
-                      spec_verify_run_onehot, spec_ngram_propose,
+                      spec_verify_run_onehot, spec_ngram_propose, spec_adapt_gamma,
                       SV_SAMPLE_LOGITS, SV_SAMPLE_WEIGHTS)
 
 
@@ -162,6 +162,23 @@ class Verifier:
         st = stream if stream is not None else torch.cuda.current_stream(self.device)
         spec_ngram_propose(self.ctx, st, B, tokens, cu_ctx, total, n_min, n_max, gamma, draft_ids, draft_len)
         return draft_ids, draft_len
+
+    def adapt_gamma(self, accepted_count, gamma, streak, *, gamma_max: int, up_after: int = 2,
+                    down_after: int = 2, cu_gamma_next=None, stream=None):
+        """Next round's draft lengths from this round's accepted counts: `gamma` and `streak`
+        (int32 [B] on the device) are updated in place; returns cu_gamma_next (int32 [B+1])."""
+        import torch
+        B = gamma.numel()
+        self._check("accepted_count", accepted_count, torch.int32, B)
+        self._check("gamma", gamma, torch.int32, B)
+        self._check("streak", streak, torch.int32, B)
+        if cu_gamma_next is None:
+            cu_gamma_next = torch.empty(B + 1, dtype=torch.int32, device=self.device)
+        self._check("cu_gamma_next", cu_gamma_next, torch.int32, B + 1)
+        st = stream if stream is not None else torch.cuda.current_stream(self.device)
+        spec_adapt_gamma(self.ctx, st, B, accepted_count, gamma, streak, gamma_max, up_after, down_after,
+                         cu_gamma_next)
+        return cu_gamma_next
 
     def status(self) -> int:
         """SV_OK, or SV_EDATA when the device flagged a data error (see last_error)."""

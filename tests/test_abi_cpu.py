@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "spec_verify.h")
 def declared_functions():
     text = open(HEADER, encoding="utf-8").read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(spec_(?:verify|sample|ngram)_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(spec_(?:verify|sample|ngram|adapt)_\w+)\s*\(", text)))
 
 
 def test_library_built():
@@ -99,6 +99,7 @@ def test_null_context_calls():
     assert lib.spec_sample_run(None, None, 1, sv.SV_SAMPLE_WEIGHTS, 1.0, None, None, None) == sv.SV_EINVAL
     assert lib.spec_verify_last_path(None) == -sv.SV_EINVAL
     assert lib.spec_ngram_propose(None, None, 1, None, None, 0, 1, 2, 4, None, None) == sv.SV_EINVAL
+    assert lib.spec_adapt_gamma(None, None, 1, None, None, None, 8, 2, 2, None) == sv.SV_EINVAL
     assert lib.spec_verify_run_onehot(None, None, 1, 1, None, 1, 1.0, None, None, None, None, None, None,
                                       None) == sv.SV_EINVAL
     lib.spec_verify_destroy(None)  # NULL-safe

@@ -66,6 +66,9 @@ def test_edges():
     assert O.adapt_gamma(12, 0, 0, 8, 2, 1) == (1, 0)         # clamped, then cut
     assert O.adapt_gamma(-3, 1, 0, 8, 2, 1) == (1, 0)         # clamped to 0, accepted, raised
     assert O.adapt_gamma(1, 0, 1, 1, 1, 1) == (1, 0)          # cap of 1
+    assert O.adapt_gamma(3, 2**31 - 1, -1, 8, 2, 3) == (3, 2)  # streak clamped to [-3, 2]
+    assert O.adapt_gamma(3, -2**31, 3, 8, 2, 3) == (3, 1)
+    assert O.adapt_gamma(3, -2**31, 0, 8, 2, 3) == (1, 0)
     g, s, cu = O.adapt_gamma_batch([1, 4, 0], [0, 1, 0], [1, 4, -1], 8, 2, 2)
     assert list(g) == [1, 5, 0] and list(s) == [1, 0, 0] and list(cu) == [0, 1, 6, 6]
 
