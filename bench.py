@@ -195,6 +195,72 @@ def bench_ngram(sv, torch, dev, iters=200):
     return res
 
 
+def bench_adaptive(sv, torch, dev, warm_rounds=10, rounds=30, c=0.05):
+    """Adaptive draft length against fixed ones on C5's sequences: B=1024, V=128256 bf16,
+    T=1, a fixed target row p_b and draft row q_b per sequence with sigma_b ~ U[0.2, 2]
+    (per-position acceptance from ~0.3 to ~0.9). Every round packs the rows for the
+    current gamma_b (index_select), draws the drafts from q_b on the GPU (spec_sample_run)
+    with seeded uniforms, verifies, and (adaptive) updates gamma_b on the GPU. Reports
+    tokens per round and per cost unit 1 + c*gamma_b (c = draft/target cost, 0.05 as in
+    the speedup table of the pages), and the GPU time of verification + controller."""
+    import numpy as np
+    import synth
+    cfg = synth.CONFIGS["C5"]
+    B, V, gmax = 1024, cfg["V"], 8
+    st = np.random.Generator(np.random.PCG64(0xADA))
+    sig = st.uniform(cfg["sigma_noise"][0], cfg["sigma_noise"][1], size=B)
+    w = synth.make_sampling("C5-rows", np.ones(B, np.int32), V, "bf16", 1.0, cfg["sigma_logit"], sig, 0xADA1)
+    base_l = torch.from_numpy(w.logits[np.arange(B) * 2].view(np.int16)).view(torch.bfloat16).to(dev)
+    base_q = torch.from_numpy(w.q).to(dev)
+    ver = sv.Verifier(V, sv.SV_BF16, B, B * gmax, gmax)
+    drafter = sv.Verifier(V, sv.SV_BF16, B * gmax, 1, 1)  # one draw per draft row
+    gen = torch.Generator(device=dev)
+    res = {}
+    for mode in ("fixed 4", "fixed 8", "adaptive"):
+        gen.manual_seed(0xADA2)
+        g0 = 4 if mode != "fixed 8" else 8
+        g_dev = torch.full((B,), g0, dtype=torch.int32, device=dev)
+        s_dev = torch.zeros(B, dtype=torch.int32, device=dev)
+        cu_dev = torch.arange(0, (B + 1) * g0, g0, dtype=torch.int32, device=dev)
+        toks, cost, pos, gpu_ms, gam = 0.0, 0.0, 0, 0.0, []
+        for k in range(warm_rounds + rounds):
+            g = g_dev.cpu().numpy()
+            R = int(g.sum())
+            seq_t = torch.from_numpy(np.repeat(np.arange(B), g + 1)).to(dev)
+            seq_d = torch.from_numpy(np.repeat(np.arange(B), g)).to(dev)
+            L = base_l.index_select(0, seq_t)
+            Q = base_q.index_select(0, seq_d)
+            ids = drafter.sample_weights(Q, uniforms=torch.rand(R, generator=gen, device=dev))
+            u = torch.rand(R + B, generator=gen, device=dev)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            out = ver.run(L, ids, temperature=1.0, q=Q, uniforms=u, cu_gamma=cu_dev, total_draft_rows=R,
+                          want_p_draft=False)
+            if mode == "adaptive":
+                cu_dev = ver.adapt_gamma(out.accepted_count, g_dev, s_dev, gamma_max=gmax)
+            e1.record()
+            torch.cuda.synchronize()
+            n = out.accepted_count.cpu().numpy()
+            if k >= warm_rounds:
+                toks += float((n + 1).sum())
+                cost += float((1 + c * g).sum())
+                pos += R
+                gpu_ms += e0.elapsed_time(e1)
+                gam.append(g.mean())
+        assert ver.status() == sv.SV_OK, ver.last_error()
+        assert drafter.status() == sv.SV_OK, drafter.last_error()
+        res[mode] = {"tokens_per_round": toks / (rounds * B), "tokens_per_cost_unit": toks / cost,
+                     "mean_gamma": float(np.mean(gam)), "us_per_round": gpu_ms * 1e3 / rounds,
+                     "verified_positions_per_s": pos / (gpu_ms * 1e-3)}
+        log(f"[bench] F2 {mode}: {toks / (rounds * B):.3f} tokens/round, {toks / cost:.3f} per cost unit "
+            f"(c={c}), mean gamma {np.mean(gam):.2f}, {gpu_ms * 1e3 / rounds:.1f} us/round")
+    ver.close()
+    drafter.close()
+    res["workload"] = (f"C5 sequences: B={B}, V={V} bf16, T=1, fixed p_b and q_b, sigma_b ~ U[0.2, 2]; "
+                       f"{rounds} rounds after {warm_rounds}; gamma_max={gmax}, up_after=1, down_after=2")
+    return res
+
+
 def cpu_baseline(w, seconds):
     """The oracle as it stands, single process, cycling over the sequences of one input
     set until about `seconds` of CPU work have been done."""
@@ -229,7 +295,7 @@ def main():
     ap.add_argument("--sets", type=int, default=2, help="input sets rotated across steps")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-next", action="store_true", help="skip the follow-on measurements (sampling, deterministic drafts)")
+    ap.add_argument("--no-next", action="store_true", help="skip the follow-on measurements (sampling, adaptive gamma, deterministic drafts)")
     ap.add_argument("--no-every-row", action="store_true",
                     help="skip the second timing with p(x) requested (every draft row read)")
     ap.add_argument("--plan", choices=("auto", "two", "one"), default="auto",
@@ -385,6 +451,7 @@ def main():
     next_rows = {}
     if not args.no_next and w0.T > 0:
         next_rows["F1_sample"] = bench_sampling(sv, torch, sets, dev, code, args)
+        next_rows["F2_adaptive_gamma"] = bench_adaptive(sv, torch, dev)
         next_rows["F3_deterministic_drafts"] = bench_ngram(sv, torch, dev)
 
     # acceptance metrics of the measured inputs

@@ -240,10 +240,11 @@ int spec_ngram_propose(spec_verify_ctx *ctx, void *hip_stream, int batch, const 
  * atonlee.tistory.com/330, ch.4: the best length follows the acceptance rate). Run it
  * after a verification step to get the next round's draft lengths and packed layout.
  * Readings of what the pages leave open: a round "accepts" when every draft was accepted
- * (accepted_count[b] >= gamma[b]) and "rejects" otherwise; after up_after accepting
- * rounds in a row gamma[b] goes up by one (at most gamma_max), after down_after
- * rejecting rounds in a row it is cut to 1; a sequence with accepted_count -1 (its
- * round was not run) keeps its state.
+ * (accepted_count[b] >= gamma[b]) and "rejects" when its first draft was rejected
+ * (accepted_count[b] == 0); a partly accepted round breaks both runs. After up_after
+ * accepting rounds in a row gamma[b] goes up by one (at most gamma_max), after
+ * down_after rejecting rounds in a row it is cut to 1; a sequence with accepted_count -1
+ * (its round was not run) keeps its state.
  *
  *   batch          0 <= B <= 65536 (B == 0: nothing is enqueued; returns SV_OK).
  *   accepted_count device int32 [B], the round's output of spec_verify_run.

@@ -15,14 +15,20 @@ What it computes, from the pages:
        adjust it as they go.
 
 Readings where the pages leave the rule open (also listed in the design notes):
-  * The unit is a round of one sequence. A round "accepts" when every draft was
-    accepted (n_b == gamma_b, the bonus round) and "rejects" otherwise.
+  * The unit is a round (a step) of one sequence. A round "accepts" when every draft
+    was accepted (n_b == gamma_b, the bonus round: a run of gamma_b acceptances) and
+    "rejects" when its first draft was rejected (n_b == 0). A round that accepted some
+    drafts and then rejected one is neither: it breaks both runs.
   * State per sequence: gamma_b in [0, gamma_max] and a streak s_b: s_b > 0 counts the
     fully accepted rounds in a row, s_b < 0 minus the rejecting rounds in a row.
   * After a fully accepted round: s = max(s, 0) + 1; once s reaches up_after, gamma
     goes up by one (at most gamma_max) and s restarts at 0.
   * After a rejecting round: s = min(s, 0) - 1; once -s reaches down_after, gamma is
     cut to 1 and s restarts at 0.
+  * After a partly accepted round: s = 0.
+  * A round that "rejects" whenever it ends at a rejection would count most rounds of
+    long drafts as rejections and cut gamma to 1 even where acceptance is high; that
+    loses to a fixed gamma, whereas the page says the simple rule beats a fixed value.
   * A sequence whose round was not run (accepted count -1, a flagged input) keeps its
     state. A gamma outside [0, gamma_max] or a streak outside [-down_after, up_after]
     in the state is first clamped into that range.
@@ -43,16 +49,18 @@ def adapt_gamma(gamma: int, streak: int, accepted: int, gamma_max: int, up_after
     n = int(accepted)
     if n < 0:
         return g, s
-    if n >= g:  # every draft accepted
+    if n >= g:     # every draft accepted
         s = max(s, 0) + 1
         if s >= up_after:
             g = min(g + 1, gamma_max)
             s = 0
-    else:       # the round ended at a rejection
+    elif n == 0:   # the first draft was rejected
         s = min(s, 0) - 1
         if -s >= down_after:
             g = 1
             s = 0
+    else:          # some accepted, then a rejection
+        s = 0
     return g, s
 
 

@@ -3,10 +3,11 @@
 // length goes down to 1, while acceptances continue it goes up again; "Speculative
 // Decoding", atonlee.tistory.com/330, ch.4: the best length follows the acceptance rate).
 //
-// Readings of the rule: a round accepts when every draft was accepted, else it rejects;
-// up_after accepting rounds in a row raise gamma by one (at most gamma_max), down_after
-// rejecting rounds in a row cut it to 1; a sequence whose round was not run (accepted
-// count -1) keeps its state; a state outside its range is clamped and flagged.
+// Readings of the rule: a round accepts when every draft was accepted and rejects when
+// its first draft was rejected; a partly accepted round breaks both runs. up_after
+// accepting rounds in a row raise gamma by one (at most gamma_max), down_after rejecting
+// rounds in a row cut it to 1; a sequence whose round was not run (accepted count -1)
+// keeps its state; a state outside its range is clamped and flagged.
 //
 // One workgroup updates the whole batch (B <= 65536: a few hundred KB of state) and
 // writes the exclusive prefix of the new lengths, the cu_gamma of the next round, so the
@@ -54,12 +55,14 @@ __global__ __launch_bounds__(kAdThreads) void k_adapt_gamma(AdaptArgs a) {
           g = min(g + 1, a.gmax);
           s = 0;
         }
-      } else {       // the round ended at a rejection
+      } else if (n == 0) {  // the first draft was rejected
         s = min(s, 0) - 1;
         if (-s >= a.down) {
           g = 1;
           s = 0;
         }
+      } else {              // some accepted, then a rejection: both runs break
+        s = 0;
       }
     }
     a.gamma[b] = g;

@@ -163,7 +163,7 @@ class Verifier:
         spec_ngram_propose(self.ctx, st, B, tokens, cu_ctx, total, n_min, n_max, gamma, draft_ids, draft_len)
         return draft_ids, draft_len
 
-    def adapt_gamma(self, accepted_count, gamma, streak, *, gamma_max: int, up_after: int = 2,
+    def adapt_gamma(self, accepted_count, gamma, streak, *, gamma_max: int, up_after: int = 1,
                     down_after: int = 2, cu_gamma_next=None, stream=None):
         """Next round's draft lengths from this round's accepted counts: `gamma` and `streak`
         (int32 [B] on the device) are updated in place; returns cu_gamma_next (int32 [B+1])."""
