@@ -895,13 +895,20 @@ __device__ __forceinline__ float last_span_weight(int V) {
 // ---- bf16 value table: 2^(x k2) in fp64 for every bf16 x whose magnitude bits lie in
 // [tlo, thi] (|x k2| < 990), both signs: entry 2 (mag - tlo) + sign. Magnitudes below tlo
 // use the tlo entry (|x| below 2^-40 of the window top: relative error under 3e-12);
-// above thi (and inf / NaN) a lookup is flagged and the exp2_tab path takes over.
+// above thi (and inf / NaN) they land on a sentinel pair of +inf after the window, so a
+// sum over such a row is not finite and the exp2_tab path takes over.
 constexpr int kTabBinades = 48;
-constexpr int kTabEntries = 2 * kTabBinades * 128;
+constexpr int kTabEntries = 2 * kTabBinades * 128 + 2;
 
-__device__ __forceinline__ double tab_lookup(uint32_t mag, uint32_t sgn, const double* sT, uint32_t tlo,
-                                             uint32_t thi) {
-  return sT[2 * (min(max(mag, tlo), thi) - tlo) + sgn];
+// clamp(x, 0, hi) in one instruction (hi >= 0)
+__device__ __forceinline__ int med3_0(int x, int hi) {
+  int r;
+  asm("v_med3_i32 %0, %1, 0, %2" : "=v"(r) : "v"(x), "s"(hi));
+  return r;
+}
+// tsent = thi + 1 - tlo, the sentinel's index
+__device__ __forceinline__ double tab_lookup(uint32_t mag, uint32_t sgn, const double* sT, int tlo, int tsent) {
+  return sT[2 * med3_0(static_cast<int>(mag) - tlo, tsent) + sgn];
 }
 // Fills sT. Within a binade the 128 values of x form an arithmetic sequence, so their
 // 2^(x k2) form a geometric one: each of 768 threads takes 16 consecutive entries of one
@@ -927,6 +934,8 @@ __device__ __forceinline__ void tab_build(double* sT, const Args& a) {
       dst[2 * m] = v;
       v *= R;
     }
+  } else if (h == 2 * kTabBinades && t % (128 / kTabPiece) < 2) {  // two idle threads: the sentinel pair
+    sT[2 * (a.thi + 1 - a.tlo) + t % (128 / kTabPiece)] = __builtin_inf();
   }
 }
 
@@ -937,7 +946,6 @@ __device__ __forceinline__ void tab_build(double* sT, const Args& a) {
 __device__ __forceinline__ bool final_draw_tab(const Args& a, int b, int base, int g, int n, double Zq,
                                                const double* sT, int xn = -1) {
   __shared__ double s_reg[kSeqWaves][3];  // residual: (D, Q, Zr); bonus: (s, -, -)
-  __shared__ uint32_t s_mx[kSeqWaves];
   __shared__ double s_wt[2][kSeqWaves];   // re-sweep: per-wave totals, by pass parity
   __shared__ int s_cand, s_last;          // re-sweep: first crossing, last positive entry
   const int lane = threadIdx.x & 63;
@@ -947,7 +955,7 @@ __device__ __forceinline__ bool final_draw_tab(const Args& a, int b, int base, i
   }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int V = a.V;
-  const uint32_t tlo = a.tlo, thi = a.thi;
+  const int tlo = a.tlo, tsent = a.thi + 1 - a.tlo;
   const bool residual = n < g;
   // one-hot drafts: max(0, p - onehot(x_n)) is p with x_n removed, drawn like a bonus row
   const bool oh = residual && a.onehot;
@@ -962,16 +970,14 @@ __device__ __forceinline__ bool final_draw_tab(const Args& a, int b, int base, i
   const int r0 = min(V, wave * rw), r1 = min(V, r0 + rw);
   const int nfull = (r1 - r0) / kIter;
   const int mstart = r0 + nfull * kIter;
-  uint32_t mx = 0;
   // the 8 table values of one group of raw bf16 words
   auto lookup8 = [&](const Raw<uint16_t>& lr, double (&e)[kGroup]) {
     const uint32_t w[4] = {lr.v[0].x, lr.v[0].y, lr.v[0].z, lr.v[0].w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const uint32_t ml = w[k] & 0x7FFFu, mh = (w[k] >> 16) & 0x7FFFu;
-      mx = max(mx, max(ml, mh));
-      e[2 * k] = tab_lookup(ml, (w[k] >> 15) & 1u, sT, tlo, thi);
-      e[2 * k + 1] = tab_lookup(mh, w[k] >> 31, sT, tlo, thi);
+      e[2 * k] = tab_lookup(ml, (w[k] >> 15) & 1u, sT, tlo, tsent);
+      e[2 * k + 1] = tab_lookup(mh, w[k] >> 31, sT, tlo, tsent);
     }
   };
   if (qres) {
@@ -1066,8 +1072,6 @@ __device__ __forceinline__ bool final_draw_tab(const Args& a, int b, int base, i
       s_reg[wave][2] = 0.0;
     }
   }
-  mx = static_cast<uint32_t>(wave_max_int_dpp(static_cast<int>(mx)));
-  if (lane == 0) s_mx[wave] = mx;
   __syncthreads();
 
   // ---- totals and the region where the inclusive prefix first exceeds t: every wave
@@ -1076,7 +1080,8 @@ __device__ __forceinline__ bool final_draw_tab(const Args& a, int b, int base, i
   const double u = uf;
   const int r = lane < kSeqWaves ? lane : 0;
   const bool live = lane < kSeqWaves;
-  if (__ballot(live && s_mx[r] > thi) != 0) return false;
+  // a value outside the table reached the sentinel: the region's sum is not finite
+  if (__ballot(live && !(s_reg[r][qres ? 2 : 0] <= DBL_MAX)) != 0) return false;
   int kind;  // 0: residual; 1: degenerate residual (S <= 0), draw from p; 2: from p; 3: p without x_n
   int excl = -1;
   double Z64, S = 0.0, delta = 0.0, t, wgt;
@@ -1095,7 +1100,7 @@ __device__ __forceinline__ bool final_draw_tab(const Args& a, int b, int base, i
     t = u * Z64;
     if (oh) {
       // S = 1 - p(x_n); the region holding x_n loses e(x_n)
-      const double ex_n = excl_ok ? tab_lookup(lxn & 0x7FFFu, lxn >> 15, sT, tlo, thi) : 0.0;
+      const double ex_n = excl_ok ? tab_lookup(lxn & 0x7FFFu, lxn >> 15, sT, tlo, tsent) : 0.0;
       S = (Z64 - ex_n) / Z64;
       if (S > 0.0) {
         kind = 3;
