@@ -261,6 +261,38 @@ def bench_adaptive(sv, torch, dev, warm_rounds=10, rounds=30, c=0.05):
     return res
 
 
+def bench_shares(sv, torch, sets, dev, code, iters=200):
+    """One GPU's share when C3 is split by sequence over G GPUs (no exchange is needed:
+    sequences are independent): the first B/G sequences of each input set, the plan the
+    library picks for that size, wall time per step."""
+    import numpy as np
+    res = {}
+    w0 = sets[0][0]
+    g = w0.uniform_gamma
+    for G in (2, 4, 8):
+        b = w0.B // G
+        if b < 1 or g is None:
+            continue
+        v = sv.Verifier(w0.V, code, b, b * g, 16)
+        sub = [(d["logits"][: b * (g + 1)], d["q"][: b * g], d["ids"][: b * g], d["u"][: b * (g + 1)])
+               for _, d in sets]
+        out = sv.VerifyOutputs(torch.empty(b, dtype=torch.int32, device=dev),
+                               torch.empty(b * (g + 1), dtype=torch.int32, device=dev),
+                               torch.empty(b, dtype=torch.float32, device=dev), None)
+
+        def go(k):
+            L, Q, X, U = sub[k % len(sub)]
+            v.run(L, X, temperature=w0.T, q=Q, uniforms=U, gamma=g, out=out)
+        dt = _timed(torch, go, iters)
+        assert v.status() == sv.SV_OK, v.last_error()
+        plan = {sv.SV_PATH_ONE_LAUNCH: "one launch", sv.SV_PATH_TWO_LAUNCH: "two launches"}.get(v.last_path())
+        v.close()
+        res[f"G={G}"] = {"B": b, "us_per_step": dt * 1e6, "positions_per_s": b * g / dt, "plan": plan}
+        log(f"[bench] share of G={G} GPUs (B={b}): {dt * 1e6:.1f} us/step ({plan}), "
+            f"{b * g / dt / 1e6:.2f} M positions/s per GPU")
+    return res
+
+
 def cpu_baseline(w, seconds):
     """The oracle as it stands, single process, cycling over the sequences of one input
     set until about `seconds` of CPU work have been done."""
@@ -451,6 +483,7 @@ def main():
     next_rows = {}
     if not args.no_next and w0.T > 0:
         next_rows["F1_sample"] = bench_sampling(sv, torch, sets, dev, code, args)
+        next_rows["per_gpu_share"] = bench_shares(sv, torch, sets, dev, code)
         next_rows["F2_adaptive_gamma"] = bench_adaptive(sv, torch, dev)
         next_rows["F3_deterministic_drafts"] = bench_ngram(sv, torch, dev)
 

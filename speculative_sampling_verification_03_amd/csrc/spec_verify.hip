@@ -762,28 +762,6 @@ __device__ __forceinline__ void final_draw(const Args& a, int b, int base, int g
   for (int i = n + 1 + threadIdx.x; i <= g; i += kSeqThreads) a.emitted[base + b + i] = -1;
 }
 
-template <typename T, bool ALIGNED, bool RAGGED, bool ACCEPT>
-__global__ __launch_bounds__(kSeqThreads) void k_sample_seq(Args a) {
-  __shared__ double s_tab[kExpN];
-  __shared__ float2 s_cz[kMaxGamma];
-  __shared__ int s_n;
-  const int b = blockIdx.x;
-  int base, g;
-  if (!seq_geom<RAGGED>(a, b, base, g)) {
-    if (threadIdx.x == 0) {
-      atomicOr(a.err, SV_DATA_CU_GAMMA);
-      a.acc[b] = -1;
-    }
-    return;
-  }
-  exp_table_init(s_tab);
-  const int n = first_rejection<T, ACCEPT, false>(a, b, base, g, s_cz, nullptr, &s_n);
-  for (int i = threadIdx.x; i < n; i += kSeqThreads) a.emitted[base + b + i] = a.ids[base + i];
-  if (threadIdx.x == 0) a.acc[b] = n;
-  final_draw<T, ALIGNED>(a, b, base, g, n, n < g ? static_cast<double>(s_cz[n].x) : 0.0,
-                         n < g ? static_cast<double>(s_cz[n].y) : 0.0, s_tab);
-}
-
 // ============================================================== one-launch path
 // One workgroup per sequence does the whole round. Pass 1 reads the draft rows in
 // order and judges each as soon as its statistics are complete: the verification
@@ -1194,6 +1172,45 @@ __device__ __forceinline__ bool final_draw_tab(const Args& a, int b, int base, i
   }
   for (int i = n + 1 + threadIdx.x; i <= g; i += kSeqThreads) a.emitted[base + b + i] = -1;
   return true;
+}
+
+// Step 2 of the two-launch plan: one workgroup per sequence takes the row decisions of
+// step 1, finds the first rejection and draws.
+template <typename T, bool ALIGNED, bool RAGGED, bool ACCEPT>
+__global__ __launch_bounds__(kSeqThreads) void k_sample_seq(Args a) {
+  __shared__ double s_tab[kExpN];
+  __shared__ float2 s_cz[kMaxGamma];
+  __shared__ int s_n;
+  const int b = blockIdx.x;
+  int base, g;
+  if (!seq_geom<RAGGED>(a, b, base, g)) {
+    if (threadIdx.x == 0) {
+      atomicOr(a.err, SV_DATA_CU_GAMMA);
+      a.acc[b] = -1;
+    }
+    return;
+  }
+  exp_table_init(s_tab);
+  if constexpr (ALIGNED && sizeof(T) == 2) {
+    // bf16 rows: the draw through the value table, built while the decisions load
+    __shared__ double sT[kTabEntries];
+    const bool tab = a.tlo <= a.thi;
+    if (tab) tab_build(sT, a);
+    const int n = first_rejection<T, ACCEPT, false>(a, b, base, g, s_cz, nullptr, &s_n);
+    for (int i = threadIdx.x; i < n; i += kSeqThreads) a.emitted[base + b + i] = a.ids[base + i];
+    if (threadIdx.x == 0) a.acc[b] = n;
+    __syncthreads();  // sT
+    const double Zq = n < g ? static_cast<double>(s_cz[n].y) * exp2(static_cast<double>(s_cz[n].x)) : 0.0;
+    if (tab && final_draw_tab(a, b, base, g, n, Zq, sT)) return;
+    final_draw<T, ALIGNED>(a, b, base, g, n, n < g ? static_cast<double>(s_cz[n].x) : 0.0,
+                           n < g ? static_cast<double>(s_cz[n].y) : 0.0, s_tab);
+  } else {
+    const int n = first_rejection<T, ACCEPT, false>(a, b, base, g, s_cz, nullptr, &s_n);
+    for (int i = threadIdx.x; i < n; i += kSeqThreads) a.emitted[base + b + i] = a.ids[base + i];
+    if (threadIdx.x == 0) a.acc[b] = n;
+    final_draw<T, ALIGNED>(a, b, base, g, n, n < g ? static_cast<double>(s_cz[n].x) : 0.0,
+                           n < g ? static_cast<double>(s_cz[n].y) : 0.0, s_tab);
+  }
 }
 
 // Pass 1: per row, z = sum 2^(l k2 - c) in fp32. Each wave takes its reference c from

@@ -387,6 +387,41 @@ def test_repeatable_bit_for_bit(lib, plan):
                 assert np.array_equal(a[k], b[k], equal_nan=True), k
 
 
+@pytest.mark.skip(reason="cooperative draw taken out: its first GPU runs stalled in the first one-launch C3 "
+                         "call (the owner's waves read the shared sub-region sums independently and could "
+                         "take different barrier counts); kept as a record of the case")
+@pytest.mark.parametrize("cfg,batch", [("C3", None), ("C3", 96), ("C5", 200)])
+def test_cooperative_draw_slices(lib, cfg, batch):
+    """The one-launch plan's cooperative draw (workgroups that are done sweep slices of
+    rows still being drawn) under 1, 2 and 4 slices: each setting matches the oracle and
+    repeats bit for bit; the settings agree with each other."""
+    w = synth.make_config(cfg, seed=17, batch=batch)
+    ragged = w.uniform_gamma is None
+    v = verifier(lib, w.V, w.dtype, w.B, w.draft_rows)
+    v.set_path(lib.SV_PATH_ONE_LAUNCH)
+    dev = to_device(w)
+    ora = oracle_batch(w)
+    runs = {}
+    for slices in (1, 2, 4):
+        v.set_draw_slices(slices)
+        for want_p in (True, False):
+            _say("cooperative draw", cfg, f"B={w.B} slices={slices} p_draft={want_p}")
+            a = run_gpu(v, w, dev=dev, ragged=ragged, want_p_draft=want_p)
+            b = run_gpu(v, w, dev=dev, ragged=ragged, want_p_draft=want_p)
+            assert a["status"] == lib.SV_OK and b["status"] == lib.SV_OK, v.last_error()
+            assert v.last_path() == lib.SV_PATH_ONE_LAUNCH
+            for k in ("accepted_count", "emitted_tokens", "residual_sum"):
+                assert np.array_equal(a[k], b[k]), (slices, k)
+            rep = compare(w, a, ora)
+            _say("cooperative draw", rep.summary())
+            assert rep.ok(), (slices, rep.summary())
+            runs[(slices, want_p)] = a
+    v.set_draw_slices(4)
+    for key, r in runs.items():
+        assert np.array_equal(r["emitted_tokens"], runs[(4, True)]["emitted_tokens"]), key
+        np.testing.assert_allclose(r["residual_sum"], runs[(4, True)]["residual_sum"], rtol=1e-6, atol=1e-12)
+
+
 def test_side_stream_and_timing(lib):
     w = synth.make_config("C3", seed=16, batch=32)
     v = verifier(lib, w.V, w.dtype, w.B, w.draft_rows)
