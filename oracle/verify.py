@@ -103,8 +103,13 @@ def inverse_cdf(weights: np.ndarray, u: float):
 
 
 def first_argmax(row) -> int:
-    """Greedy target token: argmax with the lowest index on ties."""
-    return int(np.argmax(np.asarray(row, dtype=np.float64)))
+    """Greedy target token: argmax with the lowest index on ties.
+
+    A NaN logit is not a value of the target and never wins (reading: the pages define
+    greedy as taking the target's most likely token and say nothing of NaN); a row with
+    nothing above -inf gives index 0."""
+    x = np.asarray(row, dtype=np.float64)
+    return int(np.argmax(np.where(np.isnan(x), -np.inf, x)))
 
 
 @dataclasses.dataclass

@@ -443,3 +443,12 @@ def test_greedy_controlled_agreement_follows_E():
     toks = res.accepted_count.astype(np.float64) + 1
     E = O.expected_tokens_per_round(alpha, gamma)
     assert abs(toks.mean() - E) < 5 * toks.std() / math.sqrt(len(toks))
+
+
+def test_first_argmax_ties_and_nan():
+    """Lowest index on ties (the library's argmax); NaN entries never win."""
+    assert O.first_argmax([1.0, 3.0, 2.0, 3.0]) == np.argmax([1.0, 3.0, 2.0, 3.0]) == 1
+    assert O.first_argmax([np.nan, 1.0, 3.0, np.nan, 3.0]) == 2
+    assert O.first_argmax([np.nan, np.nan]) == 0
+    assert O.first_argmax([-np.inf, np.nan, -np.inf]) == 0
+    assert O.first_argmax([-np.inf, -5.0, np.nan]) == 1
