@@ -159,14 +159,17 @@ int spec_verify_run_onehot(spec_verify_ctx *ctx, void *hip_stream, int batch, in
                            float *p_draft);
 
 /*
- * Launch plan. A run either takes two launches (row statistics of every draft row,
- * then one workgroup per sequence for the first-rejection scan and the draw) or
- * one launch (one workgroup per sequence that judges its rows left to right,
- * stops reading at the first rejection and then draws). The one-launch plan needs
- * T > 0, V a multiple of 8, 16-byte aligned logits and q, gamma_b <= 64 (for
- * ragged runs: the context's max_gamma <= 64) and, under SV_PATH_AUTO, at least as
- * many sequences as the device has compute units. With p_draft requested it still
- * reads every row. Both plans return the same outputs.
+ * Launch plan. A run either takes two launches (row statistics or argmaxes of every
+ * draft row, then one workgroup per sequence for the first-rejection scan and the
+ * draw) or one launch (one workgroup per sequence that judges its rows left to right,
+ * stops reading at the first rejection and then draws; in greedy mode the argmax of
+ * the first mismatching row, or of the bonus row, is the token). The one-launch plan
+ * needs V a multiple of 8, 16-byte aligned logits (and q when T > 0), gamma_b <= 64
+ * (for ragged runs: the context's max_gamma <= 64) and, under SV_PATH_AUTO, at least
+ * as many sequences as the device has compute units. With p_draft requested (T > 0)
+ * it still reads every row. Both plans return the same outputs, except that a draft
+ * id after the first rejection is not examined by the one-launch plan (so it cannot
+ * raise SV_DATA_DRAFT_ID there).
  *   spec_verify_set_path(ctx, mode): SV_PATH_AUTO (default), SV_PATH_TWO_LAUNCH, or
  *     SV_PATH_ONE_LAUNCH (taken whenever the run allows it, whatever B). Returns
  *     SV_OK or SV_EINVAL (NULL ctx, unknown mode).

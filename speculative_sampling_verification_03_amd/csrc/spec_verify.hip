@@ -1387,6 +1387,98 @@ __global__ __launch_bounds__(kSeqThreads) void k_verify_seq(Args a) {
   }
 }
 
+// Greedy in one launch ([P1] ch.3 greedy; [P4] "출력이 변하지 않는다는 것이 핵심이다"): one
+// workgroup per sequence walks rows 0..g through the same register ring as the sampling
+// path and takes each row's argmax (largest value, lowest index); draft i is accepted iff
+// it equals the argmax of row i. The walk stops at the first mismatch, whose argmax is the
+// emitted token, or after the bonus row g. Rows after the mismatch are not read.
+template <typename T, bool RAGGED, bool NT1>
+__global__ __launch_bounds__(kSeqThreads) void k_greedy_seq1(Args a) {
+  __shared__ float s_v[kSeqWaves];
+  __shared__ int s_i[kSeqWaves];
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int base, g;
+  if (!seq_geom<RAGGED>(a, b, base, g)) {
+    if (threadIdx.x == 0) {
+      atomicOr(a.err, SV_DATA_CU_GAMMA);
+      a.acc[b] = -1;
+    }
+    return;
+  }
+  const int V = a.V;
+  const T* Lseq = static_cast<const T*>(a.logits) + static_cast<size_t>(base + b) * V;
+  const int x = g > 0 ? a.ids[base + min(lane, g - 1)] : -1;  // lane i: draft i
+  constexpr int kSpan = kSeqWaves * kIter;
+  const int lane_off = wave * kIter + lane * kGroup;
+  const int nsp = (V + kSpan - 1) / kSpan;
+  const bool wide = V >= kSpan;
+  // index of this lane's first entry in span k, matching walk_rows' loads
+  auto entry0 = [&](int k) {
+    return wide ? (k < nsp - 1 ? k * kSpan : V - kSpan) + lane_off : min(lane_off, V - kGroup);
+  };
+  float bv = -INFINITY;
+  int bi = entry0(0);  // a row of -inf (or NaN) still yields its lowest index
+  int n = g, tok = -1;
+  auto step = [&](const Raw<T>& lr, int k) {
+    float xv[kGroup];
+    unpack(lr, xv);
+    const int e = entry0(k);
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j)
+      if (xv[j] > bv) {  // strict: a lane visits its entries in increasing index order
+        bv = xv[j];
+        bi = e + j;
+      }
+  };
+  auto row_end = [&](int i) -> bool {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float v2 = __shfl_xor(bv, o);
+      const int i2 = __shfl_xor(bi, o);
+      argmax_merge(bv, bi, v2, i2);
+    }
+    if (lane == 0) {
+      s_v[wave] = bv;
+      s_i[wave] = bi;
+    }
+    __syncthreads();
+    // every wave merges the 16 partials in the same order and takes the same decision
+    float Vm = s_v[0];
+    int I = s_i[0];
+    for (int w = 1; w < kSeqWaves; ++w) argmax_merge(Vm, I, s_v[w], s_i[w]);
+    bv = -INFINITY;
+    bi = entry0(0);
+    __syncthreads();  // s_v / s_i are rewritten by the next row
+    if (i == g) {  // the bonus row
+      tok = I;
+      return true;
+    }
+    const int xi = __shfl(x, i);
+    if (wave == 0 && lane == 0 && bad_id(a, xi)) atomicOr(a.err, SV_DATA_DRAFT_ID);
+    if (xi != I) {
+      n = i;
+      tok = I;
+      return true;
+    }
+    return false;
+  };
+  if (wide)
+    walk_rows<T, true, NT1>(Lseq, V, g + 1, [] {}, step, row_end);
+  else
+    walk_rows<T, false, NT1>(Lseq, V, g + 1, [] {}, step, row_end);
+  if (wave == 0) {
+    if (lane < n) a.emitted[base + b + lane] = x;
+    if (lane == 0) {
+      a.acc[b] = n;
+      a.emitted[base + b + n] = tok;
+      a.rsum[b] = 0.f;
+    }
+  }
+  for (int i = n + 1 + threadIdx.x; i <= g; i += kSeqThreads) a.emitted[base + b + i] = -1;
+}
+
 // ============================================================== sampling from given weights
 // One token per row from weights w >= 0 (fp32, normalised or not): the inverse CDF of
 // the draw ([P1] ch.2; [P3] 단계 1 draws the drafts from q), t = u sum(w), the first v
@@ -1614,7 +1706,7 @@ constexpr int kKernels = 2;  // most kernels one call launches
 constexpr int kEventsPerRun = 2 * kKernels;
 
 // The launch sequences a call can take.
-enum Path { kPathSample2 = 0, kPathGreedy2 = 1, kPathSample1 = 2, kPaths = 3 };
+enum Path { kPathSample2 = 0, kPathGreedy2 = 1, kPathSample1 = 2, kPathGreedy1 = 3, kPaths = 4 };
 struct PathInfo {
   int nk;
   const char* names[kKernels];
@@ -1623,6 +1715,7 @@ const PathInfo kPathInfo[kPaths] = {
     {2, {"k_rowstats", "k_sample_seq"}},
     {2, {"k_rowargmax", "k_greedy_seq"}},
     {1, {"k_verify_seq", nullptr}},
+    {1, {"k_greedy_seq1", nullptr}},
 };
 
 }  // namespace
@@ -1696,6 +1789,17 @@ hipError_t launch_fused(spec_verify_ctx* ctx, const Args& a, hipStream_t st) {
   hipEvent_t* ev = timing_slot(ctx, kPathSample1);
   const void* fn = a.B <= ctx->cus ? reinterpret_cast<const void*>(&k_verify_seq<T, RG, true>)
                                    : reinterpret_cast<const void*>(&k_verify_seq<T, RG, false>);
+  const hipError_t e = launch_one(fn, dim3(a.B), dim3(kSeqThreads), a, st, ev, 0);
+  if (e != hipSuccess) return e;
+  if (ev) ++ctx->timing_runs;
+  return hipGetLastError();
+}
+
+template <typename T, bool RG>
+hipError_t launch_fused_greedy(spec_verify_ctx* ctx, const Args& a, hipStream_t st) {
+  hipEvent_t* ev = timing_slot(ctx, kPathGreedy1);
+  const void* fn = a.B <= ctx->cus ? reinterpret_cast<const void*>(&k_greedy_seq1<T, RG, true>)
+                                   : reinterpret_cast<const void*>(&k_greedy_seq1<T, RG, false>);
   const hipError_t e = launch_one(fn, dim3(a.B), dim3(kSeqThreads), a, st, ev, 0);
   if (e != hipSuccess) return e;
   if (ev) ++ctx->timing_runs;
@@ -1840,11 +1944,15 @@ int run_impl(spec_verify_ctx* ctx, void* hip_stream, int batch, int gamma, const
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   // one launch per call when there are enough sequences to give every compute unit one
   const int gmax = cu_gamma ? ctx->max_gamma : gamma;
-  const bool fused = ctx->path_mode != SV_PATH_TWO_LAUNCH && !greedy && aligned && gmax <= kFuseMaxGamma &&
+  const bool fused = ctx->path_mode != SV_PATH_TWO_LAUNCH && aligned && gmax <= kFuseMaxGamma &&
                      (ctx->path_mode == SV_PATH_ONE_LAUNCH || batch >= ctx->cus);
   const bool rg = cu_gamma != nullptr;
   hipError_t e;
-  if (fused)
+  if (fused && greedy)
+    e = ctx->dtype == SV_BF16
+            ? (rg ? launch_fused_greedy<uint16_t, true>(ctx, a, st) : launch_fused_greedy<uint16_t, false>(ctx, a, st))
+            : (rg ? launch_fused_greedy<float, true>(ctx, a, st) : launch_fused_greedy<float, false>(ctx, a, st));
+  else if (fused)
     e = ctx->dtype == SV_BF16 ? (rg ? launch_fused<uint16_t, true>(ctx, a, st) : launch_fused<uint16_t, false>(ctx, a, st))
                               : (rg ? launch_fused<float, true>(ctx, a, st) : launch_fused<float, false>(ctx, a, st));
   else

@@ -270,6 +270,36 @@ def test_greedy_bf16_ties(lib):
     check_parity(lib, w, "greedy ties")
 
 
+@pytest.mark.parametrize("dtype,V", [("bf16", 12000), ("f32", 8192), ("bf16", 1000)])
+def test_greedy_one_launch(lib, dtype, V):
+    """Greedy through the one-launch plan (rows read up to the first mismatch): ragged
+    gamma_b in 0..8, a wide row with a partial last span, a short row, rows of -inf and
+    NaN entries, an out-of-range id."""
+    rng = np.random.default_rng([56, V])
+    gammas = rng.integers(0, 9, 160)
+    gammas[:4] = (0, 8, 1, 3)
+    w = synth.make_greedy("greedy one launch", gammas, V, dtype, 3.0, 0.8, seed=57 + V)
+    L = w.logits_f32().copy()
+    L[w.logit_row(2, 0), :] = -np.inf  # every entry -inf: the argmax is index 0
+    L[w.logit_row(1, 0), rng.integers(0, V, 50)] = np.nan
+    w.logits = synth.bf16_round(L) if dtype == "bf16" else L
+    w.draft_ids = w.draft_ids.copy()
+    w.draft_ids[w.draft_row(2, 0)] = 0  # accepted: equals that argmax
+    w.draft_ids[w.draft_row(3, 0)] = V + 3  # judged by both plans: rejected and flagged
+    v = verifier(lib, w.V, w.dtype, w.B, max(w.draft_rows, 1))
+    _say("greedy one launch", f"{dtype} V={V} B={w.B}")
+    ora = oracle_batch(w)
+    for plan in (lib.SV_PATH_ONE_LAUNCH, lib.SV_PATH_TWO_LAUNCH):
+        v.set_path(plan)
+        gpu = run_gpu(v, w, ragged=True)
+        assert v.last_path() == plan
+        assert gpu["status"] == lib.SV_EDATA and "draft-id" in v.last_error()
+        rep = compare(w, gpu, ora)
+        _say("greedy one launch", f"plan={plan}", rep.summary())
+        assert rep.ok(), rep.summary()
+    v.set_path(lib.SV_PATH_AUTO)
+
+
 def test_large_gamma(lib):
     w = synth.make_sampling("gamma40", np.full(16, 40), 2000, "f32", 1.0, 1.0, 0.2, seed=55)
     check_parity(lib, w, "gamma=40", max_gamma=64)
