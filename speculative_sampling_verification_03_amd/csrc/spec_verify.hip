@@ -1798,6 +1798,7 @@ hipError_t launch_fused(spec_verify_ctx* ctx, const Args& a, hipStream_t st) {
 template <typename T, bool RG>
 hipError_t launch_fused_greedy(spec_verify_ctx* ctx, const Args& a, hipStream_t st) {
   hipEvent_t* ev = timing_slot(ctx, kPathGreedy1);
+  // nontemporal row loads when every sequence has its own compute unit, as for sampling
   const void* fn = a.B <= ctx->cus ? reinterpret_cast<const void*>(&k_greedy_seq1<T, RG, true>)
                                    : reinterpret_cast<const void*>(&k_greedy_seq1<T, RG, false>);
   const hipError_t e = launch_one(fn, dim3(a.B), dim3(kSeqThreads), a, st, ev, 0);
