@@ -96,6 +96,11 @@ struct Args {
   int tlo, thi;
   int onehot;      // drafts are deterministic: q = one-hot(draft), q is not read
   int nodraft;     // an id of -1 marks "no draft here": rejected without the data flag
+  // split draw of the two-launch plan (bf16): nslice workgroups sweep one drawn row
+  int nslice;
+  double* dsum;    // [B][kMaxSub][3] sub-region sums
+  float2* dcz;     // [B] (c, z) of the rejected row
+  int* dn;         // [B] first rejection n (-1: the sequence was not run)
 };
 
 __device__ __forceinline__ bool finite_pos(float z) { return z > 0.f && z <= FLT_MAX; }
@@ -917,48 +922,53 @@ __device__ __forceinline__ void tab_build(double* sT, const Args& a) {
   }
 }
 
-// The draw through the value table (bf16 rows): the same arithmetic as final_draw with
-// e = 2^(l k2) looked up instead of computed (reference 0); the residual's Zq comes in
-// on that scale. Returns false, having written nothing, when the drawn row holds a value
-// outside the table; the caller then runs final_draw.
-__device__ __forceinline__ bool final_draw_tab(const Args& a, int b, int base, int g, int n, double Zq,
-                                               const double* sT, int xn = -1) {
-  __shared__ double s_reg[kSeqWaves][3];  // residual: (D, Q, Zr); bonus: (s, -, -)
-  __shared__ double s_wt[2][kSeqWaves];   // re-sweep: per-wave totals, by pass parity
-  __shared__ int s_cand, s_last;          // re-sweep: first crossing, last positive entry
-  const int lane = threadIdx.x & 63;
-  if (threadIdx.x == 0) {
-    s_cand = INT_MAX;
-    s_last = -1;
+// ---- the draw through the value table, in two parts: sweeps that form fp64 sums over
+// sub-regions of the drawn row, and a finish that searches the sums and re-sweeps one
+// sub-region. final_draw_tab runs both in one workgroup (16 sub-regions, one per wave);
+// the split draw of the two-launch plan runs the sweeps of one row in several
+// workgroups (k_draw_part) and the finish in another launch (k_draw_fin).
+constexpr int kMaxSlices = 4;                     // workgroups sweeping one row in the split draw
+constexpr int kMaxSub = kMaxSlices * kSeqWaves;   // 64 sub-regions: lane k of a wave holds sub-region k
+constexpr int kSplitMaxB = 1024;                  // sequences the split draw's workspace holds
+
+// Width of one of ns sub-regions of a row: a multiple of kRing iterations, so a wave's
+// sweep has no partial ring round except at the end of the row.
+__device__ __forceinline__ int sub_width(int V, int ns) {
+  const int per = (V + ns - 1) / ns;
+  return (per + kRing * kIter - 1) / (kRing * kIter) * (kRing * kIter);
+}
+
+// The 8 table values of one group of raw bf16 words.
+__device__ __forceinline__ void lookup8(const Raw<uint16_t>& lr, double (&e)[kGroup], const double* sT, int tlo,
+                                        int tsent) {
+  const uint32_t w[4] = {lr.v[0].x, lr.v[0].y, lr.v[0].z, lr.v[0].w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t ml = w[k] & 0x7FFFu, mh = (w[k] >> 16) & 0x7FFFu;
+    e[2 * k] = tab_lookup(ml, (w[k] >> 15) & 1u, sT, tlo, tsent);
+    e[2 * k + 1] = tab_lookup(mh, w[k] >> 31, sT, tlo, tsent);
   }
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int V = a.V;
-  const int tlo = a.tlo, tsent = a.thi + 1 - a.tlo;
-  const bool residual = n < g;
-  // one-hot drafts: max(0, p - onehot(x_n)) is p with x_n removed, drawn like a bonus row
-  const bool oh = residual && a.onehot;
-  const bool qres = residual && !oh;
-  const uint16_t* lrow =
-      static_cast<const uint16_t*>(a.logits) + static_cast<size_t>(base + b + (residual ? n : g)) * V;
-  const float* qrow = qres ? a.q + static_cast<size_t>(base + n) * V : nullptr;
-  if (oh && xn < 0) xn = a.ids[base + n];
-  const bool excl_ok = oh && xn >= 0 && xn < V;  // an invalid id removes nothing
-  const uint32_t lxn = excl_ok ? static_cast<uint32_t>(lrow[xn]) : 0u;
-  const int rw = region_width(V);
-  const int r0 = min(V, wave * rw), r1 = min(V, r0 + rw);
+}
+
+// The drawn row of sequence b (row n after a rejection, the bonus row g otherwise) and,
+// for a q residual, its q row.
+__device__ __forceinline__ const uint16_t* drawn_row(const Args& a, int b, int base, int g, int n) {
+  return static_cast<const uint16_t*>(a.logits) + static_cast<size_t>(base + b + (n < g ? n : g)) * a.V;
+}
+__device__ __forceinline__ const float* drawn_q(const Args& a, int base, int g, int n) {
+  return n < g && !a.onehot ? a.q + static_cast<size_t>(base + n) * a.V : nullptr;
+}
+
+// One wave's sweep of entries [r0, r1) of a drawn row through the value table, through a
+// ring of kRing register buffers. Residual (qrow != null): D = sum max(w, 0), Q = sum of
+// q where w > 0, Zr = sum e, with w = e - q Zq; bonus: D = sum e. Totals in every lane.
+__device__ __forceinline__ void tab_sweep(const uint16_t* lrow, const float* qrow, int r0, int r1, double Zq,
+                                          const double* sT, int tlo, int tsent, double& Dout, double& Qout,
+                                          double& Zout) {
+  const int lane = threadIdx.x & 63;
   const int nfull = (r1 - r0) / kIter;
   const int mstart = r0 + nfull * kIter;
-  // the 8 table values of one group of raw bf16 words
-  auto lookup8 = [&](const Raw<uint16_t>& lr, double (&e)[kGroup]) {
-    const uint32_t w[4] = {lr.v[0].x, lr.v[0].y, lr.v[0].z, lr.v[0].w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t ml = w[k] & 0x7FFFu, mh = (w[k] >> 16) & 0x7FFFu;
-      e[2 * k] = tab_lookup(ml, (w[k] >> 15) & 1u, sT, tlo, tsent);
-      e[2 * k + 1] = tab_lookup(mh, w[k] >> 31, sT, tlo, tsent);
-    }
-  };
-  if (qres) {
+  if (qrow) {
     // residual max(0, p - q) ([P1] ch.3; [P3] 단계 3), normalisation deferred as in final_draw
     double D = 0.0, Zr = 0.0;
     float Q = 0.f;
@@ -966,7 +976,7 @@ __device__ __forceinline__ bool final_draw_tab(const Args& a, int b, int base, i
       float qv[kGroup];
       unpack(qr, qv);
       double e[kGroup];
-      lookup8(lr, e);
+      lookup8(lr, e, sT, tlo, tsent);
 #pragma unroll
       for (int j = 0; j < kGroup; ++j) {
         const double w = fma(-static_cast<double>(qv[j]), Zq, e[j]);
@@ -996,7 +1006,7 @@ __device__ __forceinline__ bool final_draw_tab(const Args& a, int b, int base, i
         }
       }
     }
-    for (int e0 = mstart; e0 < r1; e0 += kIter) {  // the rest of the region; lanes past r1 idle
+    for (int e0 = mstart; e0 < r1; e0 += kIter) {  // the rest of the range; lanes past r1 idle
       Raw<uint16_t> lr;
       Raw<float> qr;
       const int e = e0 + lane * kGroup;
@@ -1004,20 +1014,15 @@ __device__ __forceinline__ bool final_draw_tab(const Args& a, int b, int base, i
       load_raw_in<float, kNtDraw>(qrow, min(e, r1 - kGroup), qr);
       if (e < r1) step(lr, qr);
     }
-    D = wave_sum_dpp(D);
-    Zr = wave_sum_dpp(Zr);
-    const double Qd = wave_sum_dpp(static_cast<double>(Q));
-    if (lane == 0) {
-      s_reg[wave][0] = D;
-      s_reg[wave][1] = Qd;
-      s_reg[wave][2] = Zr;
-    }
+    Dout = wave_sum_dpp(D);
+    Zout = wave_sum_dpp(Zr);
+    Qout = wave_sum_dpp(static_cast<double>(Q));
   } else {
     // bonus row ([P1] ch.2; [P3] 단계 3): sum of 2^(l k2), no running max needed
     double sacc = 0.0;
     auto step = [&](const Raw<uint16_t>& lr) {
       double e[kGroup];
-      lookup8(lr, e);
+      lookup8(lr, e, sT, tlo, tsent);
       sacc += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
     };
     if (nfull > 0) {
@@ -1043,47 +1048,69 @@ __device__ __forceinline__ bool final_draw_tab(const Args& a, int b, int base, i
       load_raw_in<uint16_t, kNtDraw>(lrow, min(e, r1 - kGroup), lr);
       if (e < r1) step(lr);
     }
-    sacc = wave_sum_dpp(sacc);
-    if (lane == 0) {
-      s_reg[wave][0] = sacc;
-      s_reg[wave][1] = 0.0;
-      s_reg[wave][2] = 0.0;
-    }
+    Dout = wave_sum_dpp(sacc);
+    Qout = 0.0;
+    Zout = 0.0;
   }
-  __syncthreads();
+}
 
-  // ---- totals and the region where the inclusive prefix first exceeds t: every wave
-  // reads the 16 region sums and takes the same decision (lane r holds region r)
+// The finish of the table draw: lane k < ns of every wave holds sub-region k's sums
+// (rD, rQ, rZ) (the same values in every wave, so all waves take the same decisions).
+// Writes emitted[n], the -1 padding and residual_sum[b]. Returns false, having written
+// nothing, when the drawn row holds a value outside the table (a sum is not finite).
+__device__ __forceinline__ bool tab_finish(const Args& a, int b, int base, int g, int n, double Zq,
+                                           const double* sT, int xn, int ns, double rD, double rQ, double rZ) {
+  __shared__ double s_wt[2][kSeqWaves];  // re-sweep: per-wave totals, by pass parity
+  __shared__ int s_cand, s_last;         // re-sweep: first crossing, last positive entry
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int V = a.V;
+  const int tlo = a.tlo, tsent = a.thi + 1 - a.tlo;
+  const int sw = sub_width(V, ns);
+  const bool residual = n < g;
+  // one-hot drafts: max(0, p - onehot(x_n)) is p with x_n removed, drawn like a bonus row
+  const bool oh = residual && a.onehot;
+  const bool qres = residual && !oh;
+  const uint16_t* lrow = drawn_row(a, b, base, g, n);
+  const float* qrow = drawn_q(a, base, g, n);
+  if (oh && xn < 0) xn = a.ids[base + n];
+  const bool excl_ok = oh && xn >= 0 && xn < V;  // an invalid id removes nothing
+  const uint32_t lxn = excl_ok ? static_cast<uint32_t>(lrow[xn]) : 0u;
+  if (threadIdx.x == 0) {
+    s_cand = INT_MAX;
+    s_last = -1;
+  }
+
+  // ---- totals and the sub-region where the inclusive prefix first exceeds t
   const float uf = a.u[base + b + g];
   const double u = uf;
-  const int r = lane < kSeqWaves ? lane : 0;
-  const bool live = lane < kSeqWaves;
-  // a value outside the table reached the sentinel: the region's sum is not finite
-  if (__ballot(live && !(s_reg[r][qres ? 2 : 0] <= DBL_MAX)) != 0) return false;
+  const bool live = lane < ns;
+  // a value outside the table reached the sentinel: the sub-region's sum is not finite
+  if (__ballot(live && !((qres ? rZ : rD) <= DBL_MAX)) != 0) return false;
   int kind;  // 0: residual; 1: degenerate residual (S <= 0), draw from p; 2: from p; 3: p without x_n
   int excl = -1;
   double Z64, S = 0.0, delta = 0.0, t, wgt;
   if (qres) {
-    Z64 = wave_sum_dpp(live ? s_reg[r][2] : 0.0);
+    Z64 = wave_sum_dpp(live ? rZ : 0.0);
     delta = (Z64 - Zq) / Z64;
-    wgt = live ? s_reg[r][0] / Z64 - s_reg[r][1] * delta : 0.0;
+    wgt = live ? rD / Z64 - rQ * delta : 0.0;
     S = wave_sum_dpp(wgt);
     kind = S > 0.0 ? 0 : 1;
-    if (kind == 1) wgt = live ? s_reg[r][2] : 0.0;
+    if (kind == 1) wgt = live ? rZ : 0.0;
     t = kind == 0 ? u * S : u * Z64;
   } else {
-    wgt = live ? s_reg[r][0] : 0.0;
+    wgt = live ? rD : 0.0;
     Z64 = wave_sum_dpp(wgt);
     kind = 2;
     t = u * Z64;
     if (oh) {
-      // S = 1 - p(x_n); the region holding x_n loses e(x_n)
+      // S = 1 - p(x_n); the sub-region holding x_n loses e(x_n)
       const double ex_n = excl_ok ? tab_lookup(lxn & 0x7FFFu, lxn >> 15, sT, tlo, tsent) : 0.0;
       S = (Z64 - ex_n) / Z64;
       if (S > 0.0) {
         kind = 3;
         excl = excl_ok ? xn : -1;
-        if (excl_ok && live && r == xn / rw) wgt = fmax(wgt - ex_n, 0.0);
+        if (excl_ok && live && lane == xn / sw) wgt = fmax(wgt - ex_n, 0.0);
         t = u * wave_sum_dpp(live ? wgt : 0.0);
       }
     }
@@ -1104,11 +1131,11 @@ __device__ __forceinline__ bool final_draw_tab(const Args& a, int b, int base, i
     if (!(uf >= 0.f && uf < 1.f)) atomicOr(a.err, SV_DATA_UNIFORM);
   }
 
-  // ---- re-sweep of region r* in passes of kPass entries: wave w scans the w-th kIter
+  // ---- re-sweep of sub-region r* in passes of kPass entries: wave w scans the w-th kIter
   // entries of a pass, lane l owns 8 consecutive entries; two barriers per pass
   int tok = V - 1;
   if (rs >= 0) {
-    const int R0 = min(V, rs * rw), R1 = min(V, R0 + rw);
+    const int R0 = min(V, rs * sw), R1 = min(V, R0 + sw);
     const double invZ = 1.0 / Z64;
     int parity = 0;
     for (int p0 = R0; p0 < R1; p0 += kPass, parity ^= 1) {
@@ -1123,7 +1150,7 @@ __device__ __forceinline__ bool final_draw_tab(const Args& a, int b, int base, i
         unpack(qr, qv);
       }
       double ev[kGroup];
-      lookup8(lr, ev);
+      lookup8(lr, ev, sT, tlo, tsent);
       double rv[kGroup];
       double tot = 0.0;
 #pragma unroll
@@ -1174,6 +1201,31 @@ __device__ __forceinline__ bool final_draw_tab(const Args& a, int b, int base, i
   return true;
 }
 
+
+// The draw through the value table (bf16 rows) in one workgroup: the same arithmetic as
+// final_draw with e = 2^(l k2) looked up instead of computed (reference 0); the residual's
+// Zq comes in on that scale. Returns false, having written nothing, when the drawn row
+// holds a value outside the table; the caller then runs final_draw.
+__device__ __forceinline__ bool final_draw_tab(const Args& a, int b, int base, int g, int n, double Zq,
+                                               const double* sT, int xn = -1) {
+  __shared__ double s_reg[kSeqWaves][3];  // residual: (D, Q, Zr); bonus: (s, -, -)
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int sw = sub_width(a.V, kSeqWaves);
+  const int r0 = min(a.V, wave * sw), r1 = min(a.V, r0 + sw);
+  double D, Q, Z;
+  tab_sweep(drawn_row(a, b, base, g, n), drawn_q(a, base, g, n), r0, r1, Zq, sT, a.tlo, a.thi + 1 - a.tlo, D,
+            Q, Z);
+  if (lane == 0) {
+    s_reg[wave][0] = D;
+    s_reg[wave][1] = Q;
+    s_reg[wave][2] = Z;
+  }
+  __syncthreads();
+  const int k = lane < kSeqWaves ? lane : 0;
+  return tab_finish(a, b, base, g, n, Zq, sT, xn, kSeqWaves, lane < kSeqWaves ? s_reg[k][0] : 0.0,
+                    lane < kSeqWaves ? s_reg[k][1] : 0.0, lane < kSeqWaves ? s_reg[k][2] : 0.0);
+}
 // Step 2 of the two-launch plan: one workgroup per sequence takes the row decisions of
 // step 1, finds the first rejection and draws.
 template <typename T, bool ALIGNED, bool RAGGED, bool ACCEPT>
@@ -1211,6 +1263,81 @@ __global__ __launch_bounds__(kSeqThreads) void k_sample_seq(Args a) {
     final_draw<T, ALIGNED>(a, b, base, g, n, n < g ? static_cast<double>(s_cz[n].x) : 0.0,
                            n < g ? static_cast<double>(s_cz[n].y) : 0.0, s_tab);
   }
+}
+
+// The split draw of the two-launch plan (bf16 rows, few sequences): workgroup (b, s) of
+// k_draw_part finds sequence b's first rejection from step 1's decisions (every slice
+// does it; only slice 0 writes the outputs of the scan), then sweeps slice s of the drawn
+// row (16 sub-regions, one per wave) and stores the fp64 sums; k_draw_fin reads the
+// 16 nslice sums of the sequence (written by the previous launch) and finishes the draw.
+template <bool RAGGED, bool ACCEPT>
+__global__ __launch_bounds__(kSeqThreads) void k_draw_part(Args a) {
+  __shared__ double sT[kTabEntries];
+  __shared__ float2 s_cz[kMaxGamma];
+  __shared__ int s_n;
+  const int b = blockIdx.x / a.nslice, s = blockIdx.x - b * a.nslice;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int base, g;
+  if (!seq_geom<RAGGED>(a, b, base, g)) {
+    if (s == 0 && threadIdx.x == 0) {
+      atomicOr(a.err, SV_DATA_CU_GAMMA);
+      a.acc[b] = -1;
+      a.dn[b] = -1;
+    }
+    return;
+  }
+  tab_build(sT, a);
+  const int n = first_rejection<uint16_t, ACCEPT, false>(a, b, base, g, s_cz, nullptr, &s_n);
+  if (s == 0) {
+    for (int i = threadIdx.x; i < n; i += kSeqThreads) a.emitted[base + b + i] = a.ids[base + i];
+    if (threadIdx.x == 0) {
+      a.acc[b] = n;
+      a.dn[b] = n;
+      a.dcz[b] = n < g ? s_cz[n] : make_float2(0.f, 0.f);
+    }
+  }
+  __syncthreads();  // sT
+  const double Zq = n < g ? static_cast<double>(s_cz[n].y) * exp2(static_cast<double>(s_cz[n].x)) : 0.0;
+  const int ns = kSeqWaves * a.nslice, sw = sub_width(a.V, ns);
+  const int k = kSeqWaves * s + wave;
+  const int r0 = min(a.V, k * sw), r1 = min(a.V, r0 + sw);
+  double D, Q, Z;
+  tab_sweep(drawn_row(a, b, base, g, n), drawn_q(a, base, g, n), r0, r1, Zq, sT, a.tlo, a.thi + 1 - a.tlo, D, Q,
+            Z);
+  if (lane == 0) {
+    double* dst = a.dsum + (static_cast<size_t>(b) * kMaxSub + k) * 3;
+    dst[0] = D;
+    dst[1] = Q;
+    dst[2] = Z;
+  }
+}
+
+template <bool RAGGED>
+__global__ __launch_bounds__(kSeqThreads) void k_draw_fin(Args a) {
+  __shared__ double sT[kTabEntries];
+  __shared__ double s_tab[kExpN];
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  int base, g;
+  if (!seq_geom<RAGGED>(a, b, base, g)) return;  // flagged by k_draw_part
+  tab_build(sT, a);
+  exp_table_init(s_tab);
+  const int n = a.dn[b];
+  const float2 cz = a.dcz[b];
+  const int ns = kSeqWaves * a.nslice;
+  double rD = 0.0, rQ = 0.0, rZ = 0.0;
+  if (lane < ns) {  // every wave reads the same sums
+    const double* src = a.dsum + (static_cast<size_t>(b) * kMaxSub + lane) * 3;
+    rD = src[0];
+    rQ = src[1];
+    rZ = src[2];
+  }
+  __syncthreads();  // sT, s_tab
+  const double cr = n < g ? static_cast<double>(cz.x) : 0.0;
+  const double zr = n < g ? static_cast<double>(cz.y) : 0.0;
+  if (tab_finish(a, b, base, g, n, zr * exp2(cr), sT, -1, ns, rD, rQ, rZ)) return;
+  final_draw<uint16_t, true>(a, b, base, g, n, cr, zr, s_tab);
 }
 
 // Pass 1: per row, z = sum 2^(l k2 - c) in fp32. Each wave takes its reference c from
@@ -1702,11 +1829,11 @@ __global__ __launch_bounds__(kSeqThreads) void k_greedy_seq(Args a) {
 }
 
 // ============================================================== host side
-constexpr int kKernels = 2;  // most kernels one call launches
+constexpr int kKernels = 3;  // most kernels one call launches
 constexpr int kEventsPerRun = 2 * kKernels;
 
 // The launch sequences a call can take.
-enum Path { kPathSample2 = 0, kPathGreedy2 = 1, kPathSample1 = 2, kPathGreedy1 = 3, kPaths = 4 };
+enum Path { kPathSample2 = 0, kPathGreedy2 = 1, kPathSample1 = 2, kPathGreedy1 = 3, kPathSample3 = 4, kPaths = 5 };
 struct PathInfo {
   int nk;
   const char* names[kKernels];
@@ -1716,6 +1843,7 @@ const PathInfo kPathInfo[kPaths] = {
     {2, {"k_rowargmax", "k_greedy_seq"}},
     {1, {"k_verify_seq", nullptr}},
     {1, {"k_greedy_seq1", nullptr}},
+    {3, {"k_rowstats", "k_draw_part", "k_draw_fin"}},
 };
 
 }  // namespace
@@ -1737,6 +1865,11 @@ struct spec_verify_ctx {
   hipEvent_t* ev = nullptr;
   int timing_path = -1;  // the path of the recorded runs (runs on another path are not recorded)
   int path_mode = SV_PATH_AUTO, last_path = SV_PATH_AUTO;
+  // split draw of the two-launch plan (bf16 contexts, up to split_cap sequences)
+  double* dsum = nullptr;
+  float2* dcz = nullptr;
+  int* dn = nullptr;
+  int split_cap = 0;
   char msg[512] = {0};
 };
 
@@ -1831,8 +1964,48 @@ hipError_t launch_path(spec_verify_ctx* ctx, const Args& a, hipStream_t st, bool
   return hipGetLastError();
 }
 
+// The split draw: with at most a quarter as many sequences as compute units, four
+// workgroups share the sweep of each drawn row (bf16 rows through the value table).
+// Measured on MI355X at C3's rows: B = 32, 64 save 3-4 us per step; with two slices
+// (B = 128) the third launch costs what the split saves.
+int split_slices(const spec_verify_ctx* ctx, const Args& a) {
+  if (ctx->dtype != SV_BF16 || a.tlo > a.thi || a.B < 1 || a.B > ctx->split_cap) return 1;
+  return ctx->cus / a.B >= kMaxSlices ? kMaxSlices : 1;
+}
+
+template <bool RG, bool AC>
+hipError_t launch_split(spec_verify_ctx* ctx, const Args& a0, hipStream_t st, int nslice) {
+  hipEvent_t* ev = timing_slot(ctx, kPathSample3);
+  Args a = a0;
+  a.nslice = nslice;
+  a.dsum = ctx->dsum;
+  a.dcz = ctx->dcz;
+  a.dn = ctx->dn;
+  hipError_t e = hipSuccess;
+  if (a.R > 0) {
+    e = launch_one(reinterpret_cast<const void*>(&k_rowstats<uint16_t, true, RG, AC>),
+                   dim3(static_cast<unsigned>(a.R) * a.split), dim3(kThreads), a, st, ev, 0);
+  } else if (ev) {
+    (void)hipEventRecord(ev[0], st);
+    (void)hipEventRecord(ev[1], st);
+  }
+  if (e != hipSuccess) return e;
+  e = launch_one(reinterpret_cast<const void*>(&k_draw_part<RG, AC>), dim3(static_cast<unsigned>(a.B) * nslice),
+                 dim3(kSeqThreads), a, st, ev, 1);
+  if (e != hipSuccess) return e;
+  e = launch_one(reinterpret_cast<const void*>(&k_draw_fin<RG>), dim3(a.B), dim3(kSeqThreads), a, st, ev, 2);
+  if (e != hipSuccess) return e;
+  if (ev) ++ctx->timing_runs;
+  return hipGetLastError();
+}
+
 template <typename T, bool AL, bool RG>
 hipError_t launch_ac(spec_verify_ctx* ctx, const Args& a, hipStream_t st, bool greedy) {
+  if constexpr (AL && sizeof(T) == 2) {
+    const int ns = greedy ? 1 : split_slices(ctx, a);
+    if (ns > 1)
+      return a.split == 1 ? launch_split<RG, true>(ctx, a, st, ns) : launch_split<RG, false>(ctx, a, st, ns);
+  }
   // rows that are not split run their accept test inside the row-statistics kernel
   return a.split == 1 ? launch_path<T, AL, RG, true>(ctx, a, st, greedy)
                       : launch_path<T, AL, RG, false>(ctx, a, st, greedy);
@@ -2036,7 +2209,12 @@ int spec_verify_create(spec_verify_ctx** out, int device, int vocab, int logits_
   const size_t n_ac = up(sizeof(int32_t) * static_cast<size_t>(max_draft_rows > 0 ? max_draft_rows : 1));
   const size_t n_sb = up(sizeof(int32_t) * static_cast<size_t>(max_batch > 0 ? max_batch : 1));
   const size_t n_er = 256;
-  if (hipMalloc(&ctx->ws, n_p1 + n_ac + 2 * n_sb + n_er) != hipSuccess) {
+  // split draw (bf16): sub-region sums, (c, z) and n per sequence
+  ctx->split_cap = logits_dtype == SV_BF16 ? (max_batch < kSplitMaxB ? max_batch : kSplitMaxB) : 0;
+  const size_t cap = static_cast<size_t>(ctx->split_cap);
+  const size_t n_ds = up(sizeof(double) * 3 * kMaxSub * cap), n_dc = up(sizeof(float2) * cap),
+               n_dn = up(sizeof(int) * cap);
+  if (hipMalloc(&ctx->ws, n_p1 + n_ac + 2 * n_sb + n_er + n_ds + n_dc + n_dn) != hipSuccess) {
     delete ctx;
     return SV_ENOMEM;
   }
@@ -2046,6 +2224,12 @@ int spec_verify_create(spec_verify_ctx** out, int device, int vocab, int logits_
   ctx->s_acc = reinterpret_cast<int32_t*>(p + n_p1 + n_ac);
   ctx->s_rsum = reinterpret_cast<float*>(p + n_p1 + n_ac + n_sb);
   ctx->err = reinterpret_cast<int*>(p + n_p1 + n_ac + 2 * n_sb);
+  if (cap > 0) {
+    char* c = p + n_p1 + n_ac + 2 * n_sb + n_er;
+    ctx->dsum = reinterpret_cast<double*>(c);
+    ctx->dcz = reinterpret_cast<float2*>(c + n_ds);
+    ctx->dn = reinterpret_cast<int*>(c + n_ds + n_dc);
+  }
   if (hipMemset(ctx->err, 0, n_er) != hipSuccess) {
     (void)hipFree(ctx->ws);
     delete ctx;

@@ -452,6 +452,38 @@ def test_cooperative_draw_slices(lib, cfg, batch):
         np.testing.assert_allclose(r["residual_sum"], runs[(4, True)]["residual_sum"], rtol=1e-6, atol=1e-12)
 
 
+@pytest.mark.parametrize("cfg,batch,kernels", [
+    ("C3", 32, ("k_rowstats", "k_draw_part", "k_draw_fin")),     # 4 workgroups per drawn row
+    ("C5", 64, ("k_rowstats", "k_draw_part", "k_draw_fin")),     # ragged
+    ("C3", 100, ("k_rowstats", "k_sample_seq")),                 # one workgroup per drawn row
+    ("C3", 160, ("k_rowstats", "k_sample_seq")),
+])
+def test_two_launch_draw_kernels(lib, cfg, batch, kernels):
+    """Below the one-launch threshold the draw runs in one workgroup per sequence, or, with
+    at most a quarter as many sequences as compute units, split over four: both match the
+    oracle, and the timing hook names the kernels that ran."""
+    w = synth.make_config(cfg, seed=18, batch=batch)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if (w.B * 4 <= cus) != (kernels[1] == "k_draw_part"):
+        pytest.skip("the draw split depends on the number of compute units")
+    ragged = w.uniform_gamma is None
+    v = verifier(lib, w.V, w.dtype, w.B, w.draft_rows)
+    v.set_path(lib.SV_PATH_TWO_LAUNCH)
+    ora = oracle_batch(w)
+    for want_p in (True, False):
+        _say("two-launch draw", cfg, f"B={w.B} p_draft={want_p}")
+        v.set_timing(1)
+        gpu = run_gpu(v, w, ragged=ragged, want_p_draft=want_p)
+        kt, runs = v.kernel_times()
+        v.set_timing(0)
+        assert gpu["status"] == lib.SV_OK, v.last_error()
+        assert tuple(nm for nm, _ in kt) == kernels and runs == 1, kt
+        rep = compare(w, gpu, ora)
+        _say("two-launch draw", rep.summary())
+        assert rep.ok(), rep.summary()
+    v.set_path(lib.SV_PATH_AUTO)
+
+
 def test_side_stream_and_timing(lib):
     w = synth.make_config("C3", seed=16, batch=32)
     v = verifier(lib, w.V, w.dtype, w.B, w.draft_rows)
@@ -468,7 +500,10 @@ def test_side_stream_and_timing(lib):
         v.set_timing(0)
     s.synchronize()
     assert runs == 3
-    assert [n for n, _ in times] == ["k_rowstats", "k_sample_seq"]
+    # 32 sequences: at most a quarter as many as compute units, so the draw is split
+    split = w.B * 4 <= torch.cuda.get_device_properties(0).multi_processor_count
+    assert [n for n, _ in times] == (["k_rowstats", "k_draw_part", "k_draw_fin"] if split
+                                     else ["k_rowstats", "k_sample_seq"])
     assert all(t > 0 for _, t in times)
     gpu = dict(accepted_count=out.accepted_count.cpu().numpy(), emitted_tokens=out.emitted_tokens.cpu().numpy(),
                residual_sum=out.residual_sum.cpu().numpy(), p_draft=out.p_draft.cpu().numpy())
