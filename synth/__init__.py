@@ -37,7 +37,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "CONFIGS", "make_config", "make_sampling", "make_greedy",
-    "pack", "bf16_round", "bf16_widen", "config_number", "make_onehot", "boost_drafts", "controlled_alpha_rows",
+    "pack", "fp32_temperature", "bf16_round", "bf16_widen", "config_number", "make_onehot", "boost_drafts", "controlled_alpha_rows",
     "Contexts", "make_ngram_contexts",
 ]
 
@@ -101,6 +101,12 @@ class Workload:
         if self.uniforms is not None:
             n += self.uniforms.nbytes
         return n
+
+
+def fp32_temperature(T) -> float:
+    """The temperature as the verification step receives it: a 32-bit float (0.8 becomes
+    0.800000011920929). Workloads carry that value, so every side computes with it."""
+    return float(np.float32(T))
 
 
 def pack(gammas) -> np.ndarray:
@@ -221,7 +227,7 @@ def make_sampling(name, gammas, V, dtype, T, sigma_logit, sigma_noise, seed,
     ru = np.random.Generator(np.random.PCG64(st["uniforms"]))
     uniforms = ru.random(R + B, dtype=np.float32)
     ug = int(gammas[0]) if B and np.all(gammas == gammas[0]) else None
-    return Workload(name, B, V, dtype, float(T), gammas, cu, ug, logits, q, draft_ids, uniforms)
+    return Workload(name, B, V, dtype, fp32_temperature(T), gammas, cu, ug, logits, q, draft_ids, uniforms)
 
 
 def make_greedy(name, gammas, V, dtype, sigma_logit, agree, seed) -> Workload:
@@ -255,7 +261,7 @@ def make_onehot(name, gammas, V, dtype, T, sigma_logit, agree, seed) -> Workload
     st = _streams(seed)
     ru = np.random.Generator(np.random.PCG64(st["uniforms"]))
     u = ru.random(w.target_rows, dtype=np.float32)
-    return Workload(name, w.B, V, dtype, float(T), w.gammas, w.cu_gamma, w.uniform_gamma, w.logits, None,
+    return Workload(name, w.B, V, dtype, fp32_temperature(T), w.gammas, w.cu_gamma, w.uniform_gamma, w.logits, None,
                     w.draft_ids, u)
 
 

@@ -2,7 +2,7 @@
 import multiprocessing as mp
 import os
 
-_NPROC = max(1, min(8, len(os.sched_getaffinity(0))))
+_NPROC = max(1, min(16, len(os.sched_getaffinity(0))))
 
 
 def pmap(fn, args):

@@ -143,7 +143,7 @@ def _custom(name, logits, q, ids, u, gammas, T, dtype="f32"):
     else:
         lg = np.ascontiguousarray(logits, dtype=np.float32)
     ug = int(gammas[0]) if len(gammas) and np.all(gammas == gammas[0]) else None
-    return synth.Workload(name, len(gammas), lg.shape[1], dtype, float(T), gammas, cu, ug, lg,
+    return synth.Workload(name, len(gammas), lg.shape[1], dtype, synth.fp32_temperature(T), gammas, cu, ug, lg,
                           None if q is None else np.ascontiguousarray(q, np.float32),
                           np.asarray(ids, np.int32),
                           None if u is None else np.asarray(u, np.float32))

@@ -58,6 +58,7 @@ def _logits_tensor(w, rows):
 
 @pytest.mark.parametrize("cfg,T", [("C3", 1.0), ("C2", 0.8), ("C3", 0.6)])
 def test_sample_logits_parity(lib, cfg, T):
+    T = synth.fp32_temperature(T)  # the value the library receives
     w = synth.make_config(cfg, seed=21, batch=40)
     rows = slice(0, w.target_rows)
     L = _logits_tensor(w, rows)
