@@ -47,6 +47,53 @@ def _one_sequence(w, b, ids, u):
                           w.logits[lr], w.q[dr], np.asarray(ids, np.int32), np.asarray(u, np.float32))
 
 
+def test_greedy_at_1e5_sequences(lib):
+    """C4 (greedy, B = 512 base sequences, gamma = 8, V = 152064 bf16): 102400 sequences,
+    each draft the target argmax with probability 0.8, else a uniform id; greedy has no
+    threshold, so every sequence must match the oracle exactly."""
+    w = synth.make_config("C4", seed=33)
+    reps = CHUNK // w.B
+    chunks = TOTAL // (reps * w.B)
+    R0, T0 = w.draft_rows, w.target_rows
+    _say("1e5", "C4", f"base B={w.B} x {reps} replicas x {chunks} chunks = {chunks * reps * w.B} sequences")
+    v = lib.Verifier(w.V, lib.SV_BF16, reps * w.B, reps * R0, 16)
+    L = torch.from_numpy(w.logits.view(np.int16)).view(torch.bfloat16).cuda().repeat(reps, 1)
+    cu = torch.from_numpy(synth.pack(np.tile(w.gammas, reps))).cuda()
+    lrow = np.concatenate([np.arange(w.logit_row(b, 0), w.logit_row(b, 0) + int(w.gammas[b])) for b in range(w.B)])
+    top = np.array([O.first_argmax(w.logits_f64(slice(r, r + 1))[0]) for r in lrow], np.int32)
+    rng = np.random.default_rng(34)
+    total = exact = 0
+    bad = []
+    for c in range(chunks):
+        agree = rng.random((reps, R0)) < 0.8
+        ids = np.where(agree, top[None, :], rng.integers(0, w.V, (reps, R0))).astype(np.int32)
+        out = v.run(L, torch.from_numpy(ids.reshape(-1)).cuda(), temperature=0.0, cu_gamma=cu,
+                    total_draft_rows=reps * R0)
+        n_g = out.accepted_count.cpu().numpy().reshape(reps, w.B)
+        em_g = out.emitted_tokens.cpu().numpy().reshape(reps, T0)
+        assert v.status() == lib.SV_OK, v.last_error()
+
+        def job(r):
+            res = []
+            for b in range(w.B):
+                g = int(w.gammas[b])
+                l0, d0 = w.logit_row(b, 0), w.draft_row(b, 0)
+                o = O.verify_sequence(w.logits_f64(slice(l0, l0 + g + 1)), None, ids[r, d0:d0 + g], None, 0.0)
+                want = list(o.tokens) + [-1] * (g - o.n)
+                res.append(o.n == n_g[r, b] and list(em_g[r, l0:l0 + g + 1]) == want)
+            return res
+
+        for r, res in enumerate(pmap(job, range(reps))):
+            for b, same in enumerate(res):
+                total += 1
+                exact += same
+                if not same:
+                    bad.append((c, r, b))
+        _say("1e5", "C4", f"chunk {c + 1}/{chunks}: sequences={total} exact={exact}")
+    v.close()
+    assert total >= 10 ** 5 and not bad, bad[:5]
+
+
 @pytest.mark.parametrize("cfg,base_batch", [("C2", 64), ("C3", 256), ("C5", 256)])
 def test_parity_at_1e5_sequences(lib, cfg, base_batch):
     w = synth.make_config(cfg, seed=31, batch=base_batch)
