@@ -1514,6 +1514,34 @@ __global__ __launch_bounds__(kSeqThreads) void k_verify_seq(Args a) {
   }
 }
 
+// Rounds with no drafts (gamma = 0: one token per row drawn from p, [P1] ch.2 bonus draw)
+// with more rows than compute units: one workgroup per compute unit builds the value
+// table once and draws row after row (rows b, b + gridDim.x, ...), instead of one
+// workgroup, and one table, per row.
+template <typename T>
+__global__ __launch_bounds__(kSeqThreads) void k_sample_rows(Args a) {
+  __shared__ double s_tab[kExpN];
+  exp_table_init(s_tab);
+  if constexpr (sizeof(T) == 2) {
+    __shared__ double sT[kTabEntries];
+    const bool tab = a.tlo <= a.thi;
+    if (tab) tab_build(sT, a);
+    __syncthreads();  // sT, s_tab
+    for (int b = blockIdx.x; b < a.B; b += gridDim.x) {
+      if (threadIdx.x == 0) a.acc[b] = 0;
+      if (!(tab && final_draw_tab(a, b, 0, 0, 0, 0.0, sT))) final_draw<T, true>(a, b, 0, 0, 0, 0.0, 0.0, s_tab);
+      __syncthreads();  // the draw's LDS is reused by the next row
+    }
+  } else {
+    __syncthreads();  // s_tab
+    for (int b = blockIdx.x; b < a.B; b += gridDim.x) {
+      if (threadIdx.x == 0) a.acc[b] = 0;
+      final_draw<T, true>(a, b, 0, 0, 0, 0.0, 0.0, s_tab);
+      __syncthreads();
+    }
+  }
+}
+
 // Greedy in one launch ([P1] ch.3 greedy; [P4] "출력이 변하지 않는다는 것이 핵심이다"): one
 // workgroup per sequence walks rows 0..g through the same register ring as the sampling
 // path and takes each row's argmax (largest value, lowest index); draft i is accepted iff
@@ -1833,7 +1861,9 @@ constexpr int kKernels = 3;  // most kernels one call launches
 constexpr int kEventsPerRun = 2 * kKernels;
 
 // The launch sequences a call can take.
-enum Path { kPathSample2 = 0, kPathGreedy2 = 1, kPathSample1 = 2, kPathGreedy1 = 3, kPathSample3 = 4, kPaths = 5 };
+enum Path {
+  kPathSample2 = 0, kPathGreedy2 = 1, kPathSample1 = 2, kPathGreedy1 = 3, kPathSample3 = 4, kPathRows = 5, kPaths = 6
+};
 struct PathInfo {
   int nk;
   const char* names[kKernels];
@@ -1844,6 +1874,7 @@ const PathInfo kPathInfo[kPaths] = {
     {1, {"k_verify_seq", nullptr}},
     {1, {"k_greedy_seq1", nullptr}},
     {3, {"k_rowstats", "k_draw_part", "k_draw_fin"}},
+    {1, {"k_sample_rows", nullptr}},
 };
 
 }  // namespace
@@ -1919,6 +1950,14 @@ hipError_t launch_one(const void* fn, dim3 grid, dim3 block, const Args& a, hipS
 
 template <typename T, bool RG>
 hipError_t launch_fused(spec_verify_ctx* ctx, const Args& a, hipStream_t st) {
+  if (!RG && a.gamma == 0 && a.B > ctx->cus) {  // draws only: one workgroup per compute unit
+    hipEvent_t* ev = timing_slot(ctx, kPathRows);
+    const hipError_t e = launch_one(reinterpret_cast<const void*>(&k_sample_rows<T>), dim3(ctx->cus),
+                                    dim3(kSeqThreads), a, st, ev, 0);
+    if (e != hipSuccess) return e;
+    if (ev) ++ctx->timing_runs;
+    return hipGetLastError();
+  }
   hipEvent_t* ev = timing_slot(ctx, kPathSample1);
   const void* fn = a.B <= ctx->cus ? reinterpret_cast<const void*>(&k_verify_seq<T, RG, true>)
                                    : reinterpret_cast<const void*>(&k_verify_seq<T, RG, false>);

@@ -56,10 +56,13 @@ def _logits_tensor(w, rows):
     return torch.from_numpy(w.logits[rows]).cuda()
 
 
-@pytest.mark.parametrize("cfg,T", [("C3", 1.0), ("C2", 0.8), ("C3", 0.6)])
-def test_sample_logits_parity(lib, cfg, T):
+@pytest.mark.parametrize("cfg,T,batch", [("C3", 1.0, 40), ("C2", 0.8, 40), ("C3", 0.6, 40),
+                                         ("C3", 1.0, 150), ("C2", 0.8, 80)])
+def test_sample_logits_parity(lib, cfg, T, batch):
+    """Rows from the configurations' target rows (batch 150 / 80: more rows than compute
+    units, which the one-launch plan draws with one workgroup per compute unit)."""
     T = synth.fp32_temperature(T)  # the value the library receives
-    w = synth.make_config(cfg, seed=21, batch=40)
+    w = synth.make_config(cfg, seed=21, batch=batch)
     rows = slice(0, w.target_rows)
     L = _logits_tensor(w, rows)
     nrows = w.target_rows
