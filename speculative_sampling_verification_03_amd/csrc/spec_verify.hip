@@ -894,14 +894,17 @@ __device__ __forceinline__ double tab_lookup(uint32_t mag, uint32_t sgn, const d
   return sT[2 * med3_0(static_cast<int>(mag) - tlo, tsent) + sgn];
 }
 // Fills sT. Within a binade the 128 values of x form an arithmetic sequence, so their
-// 2^(x k2) form a geometric one: each of 768 threads takes 16 consecutive entries of one
-// (binade, sign), computes the first with exp2 and steps by R = 2^(dx k2) (relative error
-// under 16 * 2^-52 + the exp2 error). The caller syncs before the first lookup.
+// 2^(x k2) form a geometric one: each of 768 threads takes the 16 entries m = j, j + 8,
+// ..., j + 120 of one (binade, sign), computes the first with exp2 and steps by
+// R = 2^(8 dx k2) (relative error under 16 * 2^-52 + the exp2 error). Threads j = 0..7
+// of the two signs of a binade write 16 adjacent entries per step, so the stores meet
+// no LDS bank conflict. The caller syncs before the first lookup.
 constexpr int kTabPiece = 16;
-static_assert(2 * kTabBinades * (128 / kTabPiece) <= kSeqThreads, "one table piece per thread");
+constexpr int kTabThreadsPerSign = 128 / kTabPiece;
+static_assert(2 * kTabBinades * kTabThreadsPerSign <= kSeqThreads, "one table piece per thread");
 __device__ __forceinline__ void tab_build(double* sT, const Args& a) {
   const int t = threadIdx.x;
-  const int h = t / (128 / kTabPiece), m0 = (t % (128 / kTabPiece)) * kTabPiece;
+  const int h = t / kTabThreadsPerSign, j = t % kTabThreadsPerSign;
   const int be_lo = a.tlo >> 7, nb = ((a.thi + 1) >> 7) - be_lo;
   if (h < 2 * nb) {
     const int be = be_lo + (h >> 1);
@@ -909,16 +912,16 @@ __device__ __forceinline__ void tab_build(double* sT, const Args& a) {
     // x = 2^(be - 127) (1 + m / 128) for be >= 1; subnormal binade: x = m 2^-133
     const double x0 = be >= 1 ? ldexp(1.0, be - 127) : 0.0;
     const double dx = ldexp(1.0, (be >= 1 ? be : 1) - 127 - 7);
-    double v = exp2(sgn * (x0 + m0 * dx) * a.k2d);
-    const double R = exp2(sgn * dx * a.k2d);
-    double* dst = sT + 2 * (be * 128 + m0 - a.tlo) + (h & 1);
+    double v = exp2(sgn * (x0 + j * dx) * a.k2d);
+    const double R = exp2(sgn * (kTabThreadsPerSign * dx) * a.k2d);
+    double* dst = sT + 2 * (be * 128 + j - a.tlo) + (h & 1);
 #pragma unroll
-    for (int m = 0; m < kTabPiece; ++m) {
-      dst[2 * m] = v;
+    for (int k = 0; k < kTabPiece; ++k) {
+      dst[2 * kTabThreadsPerSign * k] = v;
       v *= R;
     }
-  } else if (h == 2 * kTabBinades && t % (128 / kTabPiece) < 2) {  // two idle threads: the sentinel pair
-    sT[2 * (a.thi + 1 - a.tlo) + t % (128 / kTabPiece)] = __builtin_inf();
+  } else if (h == 2 * kTabBinades && j < 2) {  // two idle threads: the sentinel pair
+    sT[2 * (a.thi + 1 - a.tlo) + j] = __builtin_inf();
   }
 }
 
@@ -938,15 +941,41 @@ __device__ __forceinline__ int sub_width(int V, int ns) {
   return (per + kRing * kIter - 1) / (kRing * kIter) * (kRing * kIter);
 }
 
+// Byte offsets into the value table of the two bf16 values of one 32-bit word (low half
+// first), both halves at once with packed 16-bit integer operations: the entry is
+// 2 min(max(mag - tlo, 0), tsent) + sign, as in tab_lookup. tlo2 and tsent2 hold tlo and
+// tsent in both halves; `three` is a register holding 3. (A packed operation takes an
+// inline constant in its low half only, so op_sel_hi makes the high lane read the low
+// half of the constants 15 and 2.)
+__device__ __forceinline__ void tab_pair_offsets(uint32_t w, uint32_t tlo2, uint32_t tsent2, uint32_t three,
+                                                 uint32_t& olo, uint32_t& ohi) {
+  uint32_t m, i, s, e;
+  asm("v_and_b32 %0, 0x7fff7fff, %1" : "=v"(m) : "v"(w));
+  asm("v_pk_sub_u16 %0, %1, %2 clamp" : "=v"(i) : "v"(m), "s"(tlo2));  // saturates at 0
+  asm("v_pk_min_u16 %0, %1, %2" : "=v"(i) : "v"(i), "s"(tsent2));
+  asm("v_pk_lshrrev_b16 %0, 15, %1 op_sel_hi:[0,1]" : "=v"(s) : "v"(w));
+  asm("v_pk_mad_u16 %0, %1, 2, %2 op_sel_hi:[1,0,1]" : "=v"(e) : "v"(i), "v"(s));
+  asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:WORD_0"
+      : "=v"(olo)
+      : "v"(three), "v"(e));
+  asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:WORD_1"
+      : "=v"(ohi)
+      : "v"(three), "v"(e));
+}
+
 // The 8 table values of one group of raw bf16 words.
 __device__ __forceinline__ void lookup8(const Raw<uint16_t>& lr, double (&e)[kGroup], const double* sT, int tlo,
                                         int tsent) {
   const uint32_t w[4] = {lr.v[0].x, lr.v[0].y, lr.v[0].z, lr.v[0].w};
+  const uint32_t tlo2 = static_cast<uint32_t>(tlo) * 0x10001u, tsent2 = static_cast<uint32_t>(tsent) * 0x10001u;
+  const uint32_t three = 3;
+  const char* base = reinterpret_cast<const char*>(sT);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const uint32_t ml = w[k] & 0x7FFFu, mh = (w[k] >> 16) & 0x7FFFu;
-    e[2 * k] = tab_lookup(ml, (w[k] >> 15) & 1u, sT, tlo, tsent);
-    e[2 * k + 1] = tab_lookup(mh, w[k] >> 31, sT, tlo, tsent);
+    uint32_t olo, ohi;
+    tab_pair_offsets(w[k], tlo2, tsent2, three, olo, ohi);
+    e[2 * k] = *reinterpret_cast<const double*>(base + olo);
+    e[2 * k + 1] = *reinterpret_cast<const double*>(base + ohi);
   }
 }
 
@@ -1481,10 +1510,10 @@ __global__ __launch_bounds__(kSeqThreads) void k_verify_seq(Args a) {
     }
     return;
   }
-  exp_table_init(s_tab);
   if constexpr (sizeof(T) == 2) {
     __shared__ double sT[kTabEntries];
     const bool tab = a.tlo <= a.thi;
+    if (!tab) exp_table_init(s_tab);  // with the table, only the fallback draw needs it
     // the value table is built while the first loads of pass 1 are in flight
     auto hook = [&] {
       if (tab) tab_build(sT, a);
@@ -1496,14 +1525,19 @@ __global__ __launch_bounds__(kSeqThreads) void k_verify_seq(Args a) {
       if (tab) tab_build(sT, a);
       if (threadIdx.x == 0) a.acc[b] = 0;
     }
-    __syncthreads();  // s_cz of row n, s_tab, sT
+    __syncthreads();  // s_cz of row n, sT (s_tab without the table)
     const double cr = n < g ? static_cast<double>(s_cz[n].x) : 0.0;
     const double zr = n < g ? static_cast<double>(s_cz[n].y) : 0.0;
     // table scale: sum 2^(l k2) = z 2^c
     const int xn = n < g ? s_xn : -1;
     if (tab && final_draw_tab(a, b, base, g, n, zr * exp2(cr), sT, xn)) return;
+    if (tab) {
+      exp_table_init(s_tab);
+      __syncthreads();  // s_tab
+    }
     final_draw<T, true>(a, b, base, g, n, cr, zr, s_tab, xn);
   } else {
+    exp_table_init(s_tab);
     const int n = g == 0 ? 0
                   : a.V >= kSeqWaves * kIter ? judge_rows_exact<T, true, NT1>(a, b, base, g, s_cz, &s_xn, [] {})
                                              : judge_rows_exact<T, false, NT1>(a, b, base, g, s_cz, &s_xn, [] {});
