@@ -439,9 +439,11 @@ def main():
     needed = float(np.mean([needed_per_set[k % len(sets)] for k in range(args.steps)]))
 
     # the roofline is taken on the kernel that moves the most bytes: the whole step when
-    # it is one launch, else the row-statistics pass (every draft row once)
+    # it is one launch (a ragged batch with more sequences than compute units first runs
+    # the small ordering kernel, which moves no row data), else the row-statistics pass
+    # (every draft row once)
     kt = dict(ktimes)
-    k1 = ktimes[0][0]
+    k1 = ktimes[-1][0] if one_launch else ktimes[0][0]
     sl = 2 if w0.dtype == "bf16" else 4
     if one_launch:
         k1_bytes, k1_needed = path_bytes, needed

@@ -167,9 +167,12 @@ int spec_verify_run_onehot(spec_verify_ctx *ctx, void *hip_stream, int batch, in
  * needs V a multiple of 8, 16-byte aligned logits (and q when T > 0), gamma_b <= 64
  * (for ragged runs: the context's max_gamma <= 64) and, under SV_PATH_AUTO, at least
  * as many sequences as the device has compute units. With p_draft requested (T > 0)
- * it still reads every row. Both plans return the same outputs, except that a draft
- * id after the first rejection is not examined by the one-launch plan (so it cannot
- * raise SV_DATA_DRAFT_ID there).
+ * it still reads every row. A ragged run with more sequences than compute units
+ * first launches a one-workgroup kernel that orders the sequences by gamma_b,
+ * longest first (the workspace holds the order); workgroups then take the sequences
+ * in that order, so the short ones are dispatched last. Both plans return the same
+ * outputs, except that a draft id after the first rejection is not examined by the
+ * one-launch plan (so it cannot raise SV_DATA_DRAFT_ID there).
  *   spec_verify_set_path(ctx, mode): SV_PATH_AUTO (default), SV_PATH_TWO_LAUNCH, or
  *     SV_PATH_ONE_LAUNCH (taken whenever the run allows it, whatever B). Returns
  *     SV_OK or SV_EINVAL (NULL ctx, unknown mode).

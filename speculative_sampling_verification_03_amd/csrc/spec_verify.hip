@@ -101,6 +101,8 @@ struct Args {
   double* dsum;    // [B][kMaxSub][3] sub-region sums
   float2* dcz;     // [B] (c, z) of the rejected row
   int* dn;         // [B] first rejection n (-1: the sequence was not run)
+  // one-launch plan of a ragged batch: the sequence each workgroup takes (null: its index)
+  int* order;      // [B]
 };
 
 __device__ __forceinline__ bool finite_pos(float z) { return z > 0.f && z <= FLT_MAX; }
@@ -1493,6 +1495,51 @@ __device__ __forceinline__ int judge_rows_exact(const Args& a, int b, int base, 
   return n;
 }
 
+// The order in which the one-launch plan takes the sequences of a ragged batch with
+// more sequences than compute units: longest draft first, a counting sort by gamma_b,
+// descending (the order of equal gamma_b is arbitrary). Workgroups are dispatched in
+// index order as compute units free up, so the short sequences go last and the step
+// ends with less imbalance. A malformed gamma_b lands in some bin, so every sequence
+// appears once; the verification kernel flags it. One workgroup.
+constexpr int kOrderThreads = 1024;
+constexpr int kOrderKeep = 8;  // bins a thread keeps in registers between the two passes
+__global__ __launch_bounds__(kOrderThreads) void k_order_by_gamma(Args a) {
+  __shared__ int s_bin[kFuseMaxGamma + 1];
+  auto bin = [&](int b) {
+    const int g = static_cast<int>(static_cast<uint32_t>(a.cu[b + 1]) - static_cast<uint32_t>(a.cu[b]));
+    return kFuseMaxGamma - min(max(g, 0), kFuseMaxGamma);
+  };
+  for (int i = threadIdx.x; i <= kFuseMaxGamma; i += kOrderThreads) s_bin[i] = 0;
+  __syncthreads();
+  int keep[kOrderKeep];
+#pragma unroll
+  for (int k = 0; k < kOrderKeep; ++k) {
+    const int b = threadIdx.x + k * kOrderThreads;
+    keep[k] = b < a.B ? bin(b) : 0;
+  }
+#pragma unroll
+  for (int k = 0; k < kOrderKeep; ++k)
+    if (threadIdx.x + k * kOrderThreads < a.B) atomicAdd(&s_bin[keep[k]], 1);
+  for (int b = threadIdx.x + kOrderKeep * kOrderThreads; b < a.B; b += kOrderThreads) atomicAdd(&s_bin[bin(b)], 1);
+  __syncthreads();
+  if (threadIdx.x == 0) {  // exclusive prefix over the bins
+    int run = 0;
+    for (int i = 0; i <= kFuseMaxGamma; ++i) {
+      const int c = s_bin[i];
+      s_bin[i] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kOrderKeep; ++k) {
+    const int b = threadIdx.x + k * kOrderThreads;
+    if (b < a.B) a.order[atomicAdd(&s_bin[keep[k]], 1)] = b;
+  }
+  for (int b = threadIdx.x + kOrderKeep * kOrderThreads; b < a.B; b += kOrderThreads)
+    a.order[atomicAdd(&s_bin[bin(b)], 1)] = b;
+}
+
 // NT1: the judged rows are read with nontemporal loads. Measured on MI355X this helps
 // when every sequence has its own compute unit (B <= CUs: C3, 4.6% faster) and costs
 // when workgroups run in several rounds (C5, 1.6% slower), so the host picks it by B.
@@ -1501,7 +1548,7 @@ __global__ __launch_bounds__(kSeqThreads) void k_verify_seq(Args a) {
   __shared__ double s_tab[kExpN];
   __shared__ float2 s_cz[kFuseMaxGamma];
   __shared__ int s_xn;
-  const int b = blockIdx.x;
+  const int b = RAGGED && a.order ? a.order[blockIdx.x] : blockIdx.x;
   int base, g;
   if (!seq_geom<RAGGED>(a, b, base, g)) {
     if (threadIdx.x == 0) {
@@ -1585,7 +1632,7 @@ template <typename T, bool RAGGED, bool NT1>
 __global__ __launch_bounds__(kSeqThreads) void k_greedy_seq1(Args a) {
   __shared__ float s_v[kSeqWaves];
   __shared__ int s_i[kSeqWaves];
-  const int b = blockIdx.x;
+  const int b = RAGGED && a.order ? a.order[blockIdx.x] : blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int base, g;
@@ -1896,7 +1943,8 @@ constexpr int kEventsPerRun = 2 * kKernels;
 
 // The launch sequences a call can take.
 enum Path {
-  kPathSample2 = 0, kPathGreedy2 = 1, kPathSample1 = 2, kPathGreedy1 = 3, kPathSample3 = 4, kPathRows = 5, kPaths = 6
+  kPathSample2 = 0, kPathGreedy2 = 1, kPathSample1 = 2, kPathGreedy1 = 3, kPathSample3 = 4, kPathRows = 5,
+  kPathSample1R = 6, kPathGreedy1R = 7, kPaths = 8
 };
 struct PathInfo {
   int nk;
@@ -1909,6 +1957,8 @@ const PathInfo kPathInfo[kPaths] = {
     {1, {"k_greedy_seq1", nullptr}},
     {3, {"k_rowstats", "k_draw_part", "k_draw_fin"}},
     {1, {"k_sample_rows", nullptr}},
+    {2, {"k_order_by_gamma", "k_verify_seq"}},
+    {2, {"k_order_by_gamma", "k_greedy_seq1"}},
 };
 
 }  // namespace
@@ -1935,6 +1985,7 @@ struct spec_verify_ctx {
   float2* dcz = nullptr;
   int* dn = nullptr;
   int split_cap = 0;
+  int* order = nullptr;  // [max_batch] sequence order of the one-launch plan (ragged batches)
   char msg[512] = {0};
 };
 
@@ -1992,10 +2043,20 @@ hipError_t launch_fused(spec_verify_ctx* ctx, const Args& a, hipStream_t st) {
     if (ev) ++ctx->timing_runs;
     return hipGetLastError();
   }
-  hipEvent_t* ev = timing_slot(ctx, kPathSample1);
+  // a ragged batch with more sequences than compute units: longest draft first
+  const bool ordered = RG && a.B > ctx->cus;
+  Args ao = a;
+  ao.order = ordered ? ctx->order : nullptr;
+  hipEvent_t* ev = timing_slot(ctx, ordered ? kPathSample1R : kPathSample1);
+  int k = 0;
+  if (ordered) {
+    const hipError_t e = launch_one(reinterpret_cast<const void*>(&k_order_by_gamma), dim3(1),
+                                    dim3(kOrderThreads), ao, st, ev, k++);
+    if (e != hipSuccess) return e;
+  }
   const void* fn = a.B <= ctx->cus ? reinterpret_cast<const void*>(&k_verify_seq<T, RG, true>)
                                    : reinterpret_cast<const void*>(&k_verify_seq<T, RG, false>);
-  const hipError_t e = launch_one(fn, dim3(a.B), dim3(kSeqThreads), a, st, ev, 0);
+  const hipError_t e = launch_one(fn, dim3(a.B), dim3(kSeqThreads), ao, st, ev, k);
   if (e != hipSuccess) return e;
   if (ev) ++ctx->timing_runs;
   return hipGetLastError();
@@ -2003,11 +2064,20 @@ hipError_t launch_fused(spec_verify_ctx* ctx, const Args& a, hipStream_t st) {
 
 template <typename T, bool RG>
 hipError_t launch_fused_greedy(spec_verify_ctx* ctx, const Args& a, hipStream_t st) {
-  hipEvent_t* ev = timing_slot(ctx, kPathGreedy1);
+  const bool ordered = RG && a.B > ctx->cus;  // longest draft first, as for sampling
+  Args ao = a;
+  ao.order = ordered ? ctx->order : nullptr;
+  hipEvent_t* ev = timing_slot(ctx, ordered ? kPathGreedy1R : kPathGreedy1);
+  int k = 0;
+  if (ordered) {
+    const hipError_t e = launch_one(reinterpret_cast<const void*>(&k_order_by_gamma), dim3(1),
+                                    dim3(kOrderThreads), ao, st, ev, k++);
+    if (e != hipSuccess) return e;
+  }
   // nontemporal row loads when every sequence has its own compute unit, as for sampling
   const void* fn = a.B <= ctx->cus ? reinterpret_cast<const void*>(&k_greedy_seq1<T, RG, true>)
                                    : reinterpret_cast<const void*>(&k_greedy_seq1<T, RG, false>);
-  const hipError_t e = launch_one(fn, dim3(a.B), dim3(kSeqThreads), a, st, ev, 0);
+  const hipError_t e = launch_one(fn, dim3(a.B), dim3(kSeqThreads), ao, st, ev, k);
   if (e != hipSuccess) return e;
   if (ev) ++ctx->timing_runs;
   return hipGetLastError();
@@ -2287,7 +2357,7 @@ int spec_verify_create(spec_verify_ctx** out, int device, int vocab, int logits_
   const size_t cap = static_cast<size_t>(ctx->split_cap);
   const size_t n_ds = up(sizeof(double) * 3 * kMaxSub * cap), n_dc = up(sizeof(float2) * cap),
                n_dn = up(sizeof(int) * cap);
-  if (hipMalloc(&ctx->ws, n_p1 + n_ac + 2 * n_sb + n_er + n_ds + n_dc + n_dn) != hipSuccess) {
+  if (hipMalloc(&ctx->ws, n_p1 + n_ac + 3 * n_sb + n_er + n_ds + n_dc + n_dn) != hipSuccess) {
     delete ctx;
     return SV_ENOMEM;
   }
@@ -2303,6 +2373,7 @@ int spec_verify_create(spec_verify_ctx** out, int device, int vocab, int logits_
     ctx->dcz = reinterpret_cast<float2*>(c + n_ds);
     ctx->dn = reinterpret_cast<int*>(c + n_ds + n_dc);
   }
+  ctx->order = reinterpret_cast<int*>(p + n_p1 + n_ac + 2 * n_sb + n_er + n_ds + n_dc + n_dn);
   if (hipMemset(ctx->err, 0, n_er) != hipSuccess) {
     (void)hipFree(ctx->ws);
     delete ctx;

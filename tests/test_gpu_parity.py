@@ -401,6 +401,81 @@ def test_malformed_cu_gamma_flagged(lib, plan):
     assert gpu["accepted_count"][3] == -1
 
 
+@pytest.mark.parametrize("dtype,T", [("bf16", 1.0), ("f32", 0.7), ("bf16", 0.0)])
+def test_ordered_one_launch_ragged(lib, dtype, T):
+    """A ragged batch with more sequences than compute units: the one-launch plan first
+    orders the sequences, longest draft first (k_order_by_gamma), then verifies them in
+    that order; every sequence's result is the oracle's."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    B = 2 * cus + 37
+    rng = np.random.default_rng([61, int(T * 10)])
+    gammas = rng.integers(0, 9, B)
+    gammas[:3] = (0, 8, 0)
+    V = 3000
+    if T > 0:
+        w = synth.make_sampling("ordered ragged", gammas, V, dtype, T, 2.0, 1.0, seed=62)
+    else:
+        w = synth.make_greedy("ordered ragged greedy", gammas, V, dtype, 3.0, 0.8, seed=63)
+    v = verifier(lib, w.V, w.dtype, w.B, max(w.draft_rows, 1))
+    v.set_path(lib.SV_PATH_ONE_LAUNCH)
+    _say("ordered one launch", f"{dtype} T={T} B={w.B}")
+    v.set_timing(1)
+    gpu = run_gpu(v, w, ragged=True, want_p_draft=T > 0)
+    times, runs = v.kernel_times()
+    v.set_timing(0)
+    v.set_path(lib.SV_PATH_AUTO)
+    assert gpu["status"] == lib.SV_OK, v.last_error()
+    assert [n for n, _ in times] == ["k_order_by_gamma", "k_verify_seq" if T > 0 else "k_greedy_seq1"]
+    rep = compare(w, gpu, oracle_batch(w))
+    _say("ordered one launch", rep.summary())
+    assert rep.ok(), rep.summary()
+
+
+def test_ordered_one_launch_many_sequences(lib):
+    """More sequences than the ordering kernel keeps in registers (8 per thread of 1024):
+    its loop over the rest; V = 96 keeps the oracle quick."""
+    B = 9000
+    gammas = np.random.default_rng(66).integers(0, 9, B)
+    w = synth.make_sampling("ordered many", gammas, 96, "f32", 1.0, 1.5, 0.8, seed=67)
+    v = verifier(lib, w.V, w.dtype, w.B, max(w.draft_rows, 1))
+    v.set_path(lib.SV_PATH_ONE_LAUNCH)
+    _say("ordered one launch", f"B={B} V=96")
+    gpu = run_gpu(v, w, ragged=True)
+    v.set_path(lib.SV_PATH_AUTO)
+    assert gpu["status"] == lib.SV_OK, v.last_error()
+    rep = compare(w, gpu, oracle_batch(w))
+    _say("ordered one launch", rep.summary())
+    assert rep.ok(), rep.summary()
+
+
+def test_ordered_one_launch_malformed_cu_gamma(lib):
+    """The ordering places a sequence with a malformed gamma_b somewhere; the verification
+    still flags it, and the sequences whose offsets are intact match the oracle."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    B = cus + 50
+    gammas = np.random.default_rng(64).integers(1, 9, B)
+    w = synth.make_sampling("ordered malformed", gammas, 2048, "bf16", 1.0, 2.0, 1.0, seed=65)
+    dev = to_device(w)
+    bad = w.cu_gamma.copy()
+    bad[3], bad[4] = bad[4], bad[3]  # sequence 3 decreasing; 2 and 4 change length
+    bad[B - 1] = np.int32(-5)  # sequences B-2 and B-1 malformed
+    dev["cu_gamma"] = torch.from_numpy(bad).cuda()
+    v = verifier(lib, w.V, w.dtype, w.B, w.draft_rows)
+    v.set_path(lib.SV_PATH_ONE_LAUNCH)
+    gpu = run_gpu(v, w, dev=dev, ragged=True, want_p_draft=False)
+    v.set_path(lib.SV_PATH_AUTO)
+    assert gpu["status"] == lib.SV_EDATA and "cu_gamma" in v.last_error()
+    assert gpu["accepted_count"][3] == -1
+    ora = oracle_batch(w)
+    for b in range(B):
+        if b in (2, 3, 4) or b >= B - 2:
+            continue
+        n = int(ora.accepted_count[b])
+        assert gpu["accepted_count"][b] == n, b
+        r0 = w.logit_row(b, 0)
+        assert list(gpu["emitted_tokens"][r0:r0 + n + 1]) == list(ora.emitted_tokens[r0:r0 + n + 1]), b
+
+
 # ---------------------------------------------------------------- determinism, streams, timing
 
 @pytest.mark.parametrize("plan", PLAN_IDS)
