@@ -81,6 +81,38 @@ def test_sample_logits_parity(lib, cfg, T, batch):
         v.close()
 
 
+def test_sample_logits_rows_outside_table(lib):
+    """More rows than compute units (one workgroup per compute unit draws row after row),
+    with rows holding a logit beyond the value table's window (|l k2| > 990 at T = 1):
+    those rows are drawn on the exp2 path, the others through the table; all must match
+    the oracle."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    nrows = 3 * cus + 11
+    w = synth.make_config("C3", seed=23, batch=(nrows + 4) // 5, vocab=32000)
+    L = w.logits_f32()[:nrows].copy()
+    rng = np.random.default_rng(71)
+    hot = rng.choice(nrows, 40, replace=False)
+    for r in hot[:20]:
+        L[r, rng.integers(0, w.V)] = 2000.0  # far outside: the row is one-hot
+    for r in hot[20:]:
+        L[r, rng.integers(0, w.V, 3)] = 700.0  # just outside (700 k2 > 990): three equal peaks
+    bits = synth.bf16_round(L)
+    L = synth.bf16_widen(bits)  # the values the GPU reads (2000 and 700 are exact in bf16)
+    Lt = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+    u = np.random.default_rng(72).random(nrows, dtype=np.float32)
+    v = lib.Verifier(w.V, lib.SV_BF16, nrows, 1, 1)
+    v.set_path(lib.SV_PATH_ONE_LAUNCH)
+    _say("sample logits outside table", f"rows={nrows} V={w.V}")
+    tok = v.sample(Lt, uniforms=torch.from_numpy(u).cuda(), temperature=1.0).cpu().numpy()
+    assert v.status() == lib.SV_OK, v.last_error()
+    P = [O.target_distribution(L[r].astype(np.float64), 1.0) for r in range(nrows)]
+    bad, flagged = compare_tokens(P, u, tok)
+    assert not bad and flagged == 0, bad[:5]
+    for r in hot[:20]:
+        assert L[r, tok[r]] == 2000.0
+    v.close()
+
+
 def test_sample_logits_greedy(lib):
     w = synth.make_config("C4", seed=22, batch=24, vocab=8192)
     L = _logits_tensor(w, slice(0, w.target_rows))
