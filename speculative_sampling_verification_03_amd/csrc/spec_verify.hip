@@ -99,8 +99,7 @@ struct Args {
   // split draw of the two-launch plan (bf16): nslice workgroups sweep one drawn row
   int nslice;
   double* dsum;    // [B][kMaxSub][3] sub-region sums
-  float2* dcz;     // [B] (c, z) of the rejected row
-  int* dn;         // [B] first rejection n (-1: the sequence was not run)
+  int* dcnt;       // [B] slices of the sequence's sweep done (zero between calls)
   // one-launch plan of a ragged batch: the sequence each workgroup takes (null: its index)
   int* order;      // [B]
 };
@@ -931,7 +930,7 @@ __device__ __forceinline__ void tab_build(double* sT, const Args& a) {
 // sub-regions of the drawn row, and a finish that searches the sums and re-sweeps one
 // sub-region. final_draw_tab runs both in one workgroup (16 sub-regions, one per wave);
 // the split draw of the two-launch plan runs the sweeps of one row in several
-// workgroups (k_draw_part) and the finish in another launch (k_draw_fin).
+// workgroups (k_draw_part), the last of which to finish also runs the finish.
 constexpr int kMaxSlices = 4;                     // workgroups sweeping one row in the split draw
 constexpr int kMaxSub = kMaxSlices * kSeqWaves;   // 64 sub-regions: lane k of a wave holds sub-region k
 constexpr int kSplitMaxB = 1024;                  // sequences the split draw's workspace holds
@@ -1299,13 +1298,18 @@ __global__ __launch_bounds__(kSeqThreads) void k_sample_seq(Args a) {
 // The split draw of the two-launch plan (bf16 rows, few sequences): workgroup (b, s) of
 // k_draw_part finds sequence b's first rejection from step 1's decisions (every slice
 // does it; only slice 0 writes the outputs of the scan), then sweeps slice s of the drawn
-// row (16 sub-regions, one per wave) and stores the fp64 sums; k_draw_fin reads the
-// 16 nslice sums of the sequence (written by the previous launch) and finishes the draw.
+// row (16 sub-regions, one per wave) and stores the fp64 sums. Each slice then counts
+// itself done; the slice that completes the count (whichever finishes last) reads all
+// 16 nslice sums and finishes the draw. No workgroup waits for another. The XCDs' L2
+// caches are not coherent with each other, so the sums and the count are written and
+// read at system scope (past the L2s), and each wave waits for its sums' stores to
+// complete before the count is taken; no cache-wide write-back or invalidate is needed.
 template <bool RAGGED, bool ACCEPT>
 __global__ __launch_bounds__(kSeqThreads) void k_draw_part(Args a) {
   __shared__ double sT[kTabEntries];
+  __shared__ double s_tab[kExpN];
   __shared__ float2 s_cz[kMaxGamma];
-  __shared__ int s_n;
+  __shared__ int s_n, s_last;
   const int b = blockIdx.x / a.nslice, s = blockIdx.x - b * a.nslice;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1314,7 +1318,6 @@ __global__ __launch_bounds__(kSeqThreads) void k_draw_part(Args a) {
     if (s == 0 && threadIdx.x == 0) {
       atomicOr(a.err, SV_DATA_CU_GAMMA);
       a.acc[b] = -1;
-      a.dn[b] = -1;
     }
     return;
   }
@@ -1322,14 +1325,12 @@ __global__ __launch_bounds__(kSeqThreads) void k_draw_part(Args a) {
   const int n = first_rejection<uint16_t, ACCEPT, false>(a, b, base, g, s_cz, nullptr, &s_n);
   if (s == 0) {
     for (int i = threadIdx.x; i < n; i += kSeqThreads) a.emitted[base + b + i] = a.ids[base + i];
-    if (threadIdx.x == 0) {
-      a.acc[b] = n;
-      a.dn[b] = n;
-      a.dcz[b] = n < g ? s_cz[n] : make_float2(0.f, 0.f);
-    }
+    if (threadIdx.x == 0) a.acc[b] = n;
   }
   __syncthreads();  // sT
-  const double Zq = n < g ? static_cast<double>(s_cz[n].y) * exp2(static_cast<double>(s_cz[n].x)) : 0.0;
+  const double cr = n < g ? static_cast<double>(s_cz[n].x) : 0.0;
+  const double zr = n < g ? static_cast<double>(s_cz[n].y) : 0.0;
+  const double Zq = zr * exp2(cr);
   const int ns = kSeqWaves * a.nslice, sw = sub_width(a.V, ns);
   const int k = kSeqWaves * s + wave;
   const int r0 = min(a.V, k * sw), r1 = min(a.V, r0 + sw);
@@ -1338,36 +1339,29 @@ __global__ __launch_bounds__(kSeqThreads) void k_draw_part(Args a) {
             Z);
   if (lane == 0) {
     double* dst = a.dsum + (static_cast<size_t>(b) * kMaxSub + k) * 3;
-    dst[0] = D;
-    dst[1] = Q;
-    dst[2] = Z;
+    __hip_atomic_store(dst, D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __hip_atomic_store(dst + 1, Q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __hip_atomic_store(dst + 2, Z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the stores are complete before the count
   }
-}
-
-template <bool RAGGED>
-__global__ __launch_bounds__(kSeqThreads) void k_draw_fin(Args a) {
-  __shared__ double sT[kTabEntries];
-  __shared__ double s_tab[kExpN];
-  const int b = blockIdx.x;
-  const int lane = threadIdx.x & 63;
-  int base, g;
-  if (!seq_geom<RAGGED>(a, b, base, g)) return;  // flagged by k_draw_part
-  tab_build(sT, a);
-  exp_table_init(s_tab);
-  const int n = a.dn[b];
-  const float2 cz = a.dcz[b];
-  const int ns = kSeqWaves * a.nslice;
+  __syncthreads();
+  // the count is kept past the per-XCD L2 caches (system scope), where every slice sees it
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(&a.dcnt[b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == a.nslice - 1;
+  __syncthreads();
+  if (!s_last) return;
+  // the last slice: every slice's sums are complete in memory
+  if (threadIdx.x == 0) __hip_atomic_store(&a.dcnt[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   double rD = 0.0, rQ = 0.0, rZ = 0.0;
   if (lane < ns) {  // every wave reads the same sums
-    const double* src = a.dsum + (static_cast<size_t>(b) * kMaxSub + lane) * 3;
-    rD = src[0];
-    rQ = src[1];
-    rZ = src[2];
+    double* src = a.dsum + (static_cast<size_t>(b) * kMaxSub + lane) * 3;
+    rD = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    rQ = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    rZ = __hip_atomic_load(src + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   }
-  __syncthreads();  // sT, s_tab
-  const double cr = n < g ? static_cast<double>(cz.x) : 0.0;
-  const double zr = n < g ? static_cast<double>(cz.y) : 0.0;
-  if (tab_finish(a, b, base, g, n, zr * exp2(cr), sT, -1, ns, rD, rQ, rZ)) return;
+  if (tab_finish(a, b, base, g, n, Zq, sT, -1, ns, rD, rQ, rZ)) return;
+  exp_table_init(s_tab);
+  __syncthreads();  // s_tab
   final_draw<uint16_t, true>(a, b, base, g, n, cr, zr, s_tab);
 }
 
@@ -1955,7 +1949,7 @@ const PathInfo kPathInfo[kPaths] = {
     {2, {"k_rowargmax", "k_greedy_seq"}},
     {1, {"k_verify_seq", nullptr}},
     {1, {"k_greedy_seq1", nullptr}},
-    {3, {"k_rowstats", "k_draw_part", "k_draw_fin"}},
+    {2, {"k_rowstats", "k_draw_part"}},
     {1, {"k_sample_rows", nullptr}},
     {2, {"k_order_by_gamma", "k_verify_seq"}},
     {2, {"k_order_by_gamma", "k_greedy_seq1"}},
@@ -1982,8 +1976,7 @@ struct spec_verify_ctx {
   int path_mode = SV_PATH_AUTO, last_path = SV_PATH_AUTO;
   // split draw of the two-launch plan (bf16 contexts, up to split_cap sequences)
   double* dsum = nullptr;
-  float2* dcz = nullptr;
-  int* dn = nullptr;
+  int* dcnt = nullptr;
   int split_cap = 0;
   int* order = nullptr;  // [max_batch] sequence order of the one-launch plan (ragged batches)
   char msg[512] = {0};
@@ -2107,13 +2100,13 @@ hipError_t launch_path(spec_verify_ctx* ctx, const Args& a, hipStream_t st, bool
   return hipGetLastError();
 }
 
-// The split draw: with at most a quarter as many sequences as compute units, four
-// workgroups share the sweep of each drawn row (bf16 rows through the value table).
-// Measured on MI355X at C3's rows: B = 32, 64 save 3-4 us per step; with two slices
-// (B = 128) the third launch costs what the split saves.
+// The split draw: with at most half as many sequences as compute units, two or four
+// workgroups share the sweep of each drawn row (bf16 rows through the value table):
+// four when there are at least four compute units per sequence, else two.
 int split_slices(const spec_verify_ctx* ctx, const Args& a) {
   if (ctx->dtype != SV_BF16 || a.tlo > a.thi || a.B < 1 || a.B > ctx->split_cap) return 1;
-  return ctx->cus / a.B >= kMaxSlices ? kMaxSlices : 1;
+  const int per = ctx->cus / a.B;
+  return per >= kMaxSlices ? kMaxSlices : per >= 2 ? 2 : 1;
 }
 
 template <bool RG, bool AC>
@@ -2122,8 +2115,7 @@ hipError_t launch_split(spec_verify_ctx* ctx, const Args& a0, hipStream_t st, in
   Args a = a0;
   a.nslice = nslice;
   a.dsum = ctx->dsum;
-  a.dcz = ctx->dcz;
-  a.dn = ctx->dn;
+  a.dcnt = ctx->dcnt;
   hipError_t e = hipSuccess;
   if (a.R > 0) {
     e = launch_one(reinterpret_cast<const void*>(&k_rowstats<uint16_t, true, RG, AC>),
@@ -2135,8 +2127,6 @@ hipError_t launch_split(spec_verify_ctx* ctx, const Args& a0, hipStream_t st, in
   if (e != hipSuccess) return e;
   e = launch_one(reinterpret_cast<const void*>(&k_draw_part<RG, AC>), dim3(static_cast<unsigned>(a.B) * nslice),
                  dim3(kSeqThreads), a, st, ev, 1);
-  if (e != hipSuccess) return e;
-  e = launch_one(reinterpret_cast<const void*>(&k_draw_fin<RG>), dim3(a.B), dim3(kSeqThreads), a, st, ev, 2);
   if (e != hipSuccess) return e;
   if (ev) ++ctx->timing_runs;
   return hipGetLastError();
@@ -2352,12 +2342,11 @@ int spec_verify_create(spec_verify_ctx** out, int device, int vocab, int logits_
   const size_t n_ac = up(sizeof(int32_t) * static_cast<size_t>(max_draft_rows > 0 ? max_draft_rows : 1));
   const size_t n_sb = up(sizeof(int32_t) * static_cast<size_t>(max_batch > 0 ? max_batch : 1));
   const size_t n_er = 256;
-  // split draw (bf16): sub-region sums, (c, z) and n per sequence
+  // split draw (bf16): sub-region sums and a count of finished slices per sequence
   ctx->split_cap = logits_dtype == SV_BF16 ? (max_batch < kSplitMaxB ? max_batch : kSplitMaxB) : 0;
   const size_t cap = static_cast<size_t>(ctx->split_cap);
-  const size_t n_ds = up(sizeof(double) * 3 * kMaxSub * cap), n_dc = up(sizeof(float2) * cap),
-               n_dn = up(sizeof(int) * cap);
-  if (hipMalloc(&ctx->ws, n_p1 + n_ac + 3 * n_sb + n_er + n_ds + n_dc + n_dn) != hipSuccess) {
+  const size_t n_ds = up(sizeof(double) * 3 * kMaxSub * cap), n_dc = up(sizeof(int) * cap);
+  if (hipMalloc(&ctx->ws, n_p1 + n_ac + 3 * n_sb + n_er + n_ds + n_dc) != hipSuccess) {
     delete ctx;
     return SV_ENOMEM;
   }
@@ -2370,11 +2359,11 @@ int spec_verify_create(spec_verify_ctx** out, int device, int vocab, int logits_
   if (cap > 0) {
     char* c = p + n_p1 + n_ac + 2 * n_sb + n_er;
     ctx->dsum = reinterpret_cast<double*>(c);
-    ctx->dcz = reinterpret_cast<float2*>(c + n_ds);
-    ctx->dn = reinterpret_cast<int*>(c + n_ds + n_dc);
+    ctx->dcnt = reinterpret_cast<int*>(c + n_ds);
   }
-  ctx->order = reinterpret_cast<int*>(p + n_p1 + n_ac + 2 * n_sb + n_er + n_ds + n_dc + n_dn);
-  if (hipMemset(ctx->err, 0, n_er) != hipSuccess) {
+  ctx->order = reinterpret_cast<int*>(p + n_p1 + n_ac + 2 * n_sb + n_er + n_ds + n_dc);
+  if (hipMemset(ctx->err, 0, n_er) != hipSuccess ||
+      (ctx->dcnt && hipMemset(ctx->dcnt, 0, n_dc) != hipSuccess) || hipDeviceSynchronize() != hipSuccess) {
     (void)hipFree(ctx->ws);
     delete ctx;
     return SV_EHIP;

@@ -528,18 +528,20 @@ def test_cooperative_draw_slices(lib, cfg, batch):
 
 
 @pytest.mark.parametrize("cfg,batch,kernels", [
-    ("C3", 32, ("k_rowstats", "k_draw_part", "k_draw_fin")),     # 4 workgroups per drawn row
-    ("C5", 64, ("k_rowstats", "k_draw_part", "k_draw_fin")),     # ragged
-    ("C3", 100, ("k_rowstats", "k_sample_seq")),                 # one workgroup per drawn row
-    ("C3", 160, ("k_rowstats", "k_sample_seq")),
+    ("C3", 32, ("k_rowstats", "k_draw_part")),      # 4 workgroups per drawn row
+    ("C5", 64, ("k_rowstats", "k_draw_part")),      # ragged
+    ("C3", 100, ("k_rowstats", "k_draw_part")),     # 2 workgroups per drawn row
+    ("C3", 128, ("k_rowstats", "k_draw_part")),
+    ("C3", 160, ("k_rowstats", "k_sample_seq")),    # one workgroup per drawn row
 ])
 def test_two_launch_draw_kernels(lib, cfg, batch, kernels):
     """Below the one-launch threshold the draw runs in one workgroup per sequence, or, with
-    at most a quarter as many sequences as compute units, split over four: both match the
-    oracle, and the timing hook names the kernels that ran."""
+    at most half as many sequences as compute units, split over two or four (the slice
+    that finishes last completes the draw): all match the oracle, and the timing hook
+    names the kernels that ran."""
     w = synth.make_config(cfg, seed=18, batch=batch)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    if (w.B * 4 <= cus) != (kernels[1] == "k_draw_part"):
+    if (w.B * 2 <= cus) != (kernels[1] == "k_draw_part"):
         pytest.skip("the draw split depends on the number of compute units")
     ragged = w.uniform_gamma is None
     v = verifier(lib, w.V, w.dtype, w.B, w.draft_rows)
@@ -559,6 +561,35 @@ def test_two_launch_draw_kernels(lib, cfg, batch, kernels):
     v.set_path(lib.SV_PATH_AUTO)
 
 
+@pytest.mark.parametrize("batch", [64, 128])
+def test_split_draw_repeated_calls(lib, batch):
+    """The split draw's last slice finishes each sequence through a count kept across the
+    XCDs' caches and zeroed again by the finishing slice: 100 calls in a row on two input
+    sets must each give the first call's (oracle-checked) outputs for that set."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if batch * 2 > cus:
+        pytest.skip("the draw split depends on the number of compute units")
+    ws = [synth.make_config("C3", seed=s, batch=batch) for s in (19, 20)]
+    devs = [to_device(w) for w in ws]
+    v = verifier(lib, ws[0].V, ws[0].dtype, batch, ws[0].draft_rows)
+    v.set_path(lib.SV_PATH_TWO_LAUNCH)
+    first = []
+    for w, d in zip(ws, devs):
+        gpu = run_gpu(v, w, dev=d, want_p_draft=False)
+        assert gpu["status"] == lib.SV_OK, v.last_error()
+        rep = compare(w, gpu, oracle_batch(w))
+        assert rep.ok(), rep.summary()
+        first.append(gpu)
+    _say("split draw repeated", f"B={batch}")
+    for k in range(100):
+        i = k % 2
+        gpu = run_gpu(v, ws[i], dev=devs[i], want_p_draft=False)
+        for key in ("accepted_count", "emitted_tokens", "residual_sum"):
+            assert np.array_equal(gpu[key], first[i][key]), (k, key)
+    assert v.status() == lib.SV_OK, v.last_error()
+    v.set_path(lib.SV_PATH_AUTO)
+
+
 def test_side_stream_and_timing(lib):
     w = synth.make_config("C3", seed=16, batch=32)
     v = verifier(lib, w.V, w.dtype, w.B, w.draft_rows)
@@ -575,10 +606,9 @@ def test_side_stream_and_timing(lib):
         v.set_timing(0)
     s.synchronize()
     assert runs == 3
-    # 32 sequences: at most a quarter as many as compute units, so the draw is split
-    split = w.B * 4 <= torch.cuda.get_device_properties(0).multi_processor_count
-    assert [n for n, _ in times] == (["k_rowstats", "k_draw_part", "k_draw_fin"] if split
-                                     else ["k_rowstats", "k_sample_seq"])
+    # 32 sequences: at most half as many as compute units, so the draw is split
+    split = w.B * 2 <= torch.cuda.get_device_properties(0).multi_processor_count
+    assert [n for n, _ in times] == (["k_rowstats", "k_draw_part"] if split else ["k_rowstats", "k_sample_seq"])
     assert all(t > 0 for _, t in times)
     gpu = dict(accepted_count=out.accepted_count.cpu().numpy(), emitted_tokens=out.emitted_tokens.cpu().numpy(),
                residual_sum=out.residual_sum.cpu().numpy(), p_draft=out.p_draft.cpu().numpy())
