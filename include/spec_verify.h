@@ -88,7 +88,9 @@ enum {
   SV_DATA_UNIFORM = 4,    /* a uniform outside [0, 1) */
   SV_DATA_CU_GAMMA = 8,   /* malformed cu_gamma */
   SV_DATA_CONTEXT = 16,   /* malformed cu_ctx (spec_ngram_propose) */
-  SV_DATA_STATE = 32      /* adaptive draft-length state out of range (spec_adapt_gamma) */
+  SV_DATA_STATE = 32,     /* adaptive draft-length state out of range (spec_adapt_gamma) */
+  SV_DATA_STALL = 64      /* a wait between the waves of one workgroup reached its bound: the
+                             outputs of that call are not valid (not expected in use) */
 };
 
 /*

@@ -9,6 +9,7 @@ HIP stream. Torch is used only for device memory and streams.
 from .binding import (  # noqa: F401
     EXPORTED, LIB_PATH, SV_BF16, SV_EDATA, SV_EHIP, SV_EINVAL, SV_ENOMEM, SV_F32, SV_OK,
     SV_DATA_CONTEXT, SV_DATA_CU_GAMMA, SV_DATA_STATE, SV_DATA_DRAFT_ID, SV_DATA_NONFINITE, SV_DATA_UNIFORM,
+    SV_DATA_STALL,
     SV_NGRAM_MAX_N,
     SV_PATH_AUTO, SV_PATH_ONE_LAUNCH, SV_PATH_TWO_LAUNCH, SV_SAMPLE_LOGITS, SV_SAMPLE_WEIGHTS,
     SpecVerifyError, load_library, spec_verify_check_args, spec_verify_create,

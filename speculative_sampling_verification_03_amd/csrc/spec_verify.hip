@@ -1589,25 +1589,203 @@ __global__ __launch_bounds__(kSeqThreads) void k_verify_seq(Args a) {
   }
 }
 
+// ---- the row kernel's two teams: the 16 waves form two teams of eight, each drawing its
+// own rows, so that one team's finish (search and re-sweep, bound by latency) overlaps
+// the other team's sweep (bound by HBM). A team meets at team barriers: each wave adds
+// one to its team's LDS counter, then polls it until the whole team has arrived. Every
+// poll loop is bounded: past kSpinCap polls the wave raises SV_DATA_STALL and goes on,
+// so no wave waits without end.
+constexpr int kTeams = 2;
+constexpr int kTeamWaves = kSeqWaves / kTeams;
+constexpr int kTeamPass = kTeamWaves * kIter;  // entries a team re-sweeps per pass
+constexpr int kSpinCap = 1 << 22;
+static_assert(kSeqWaves % kTeams == 0, "teams of equal size");
+
+// `target` counts the arrivals this wave has waited for so far (the same in every wave
+// of the team).
+__device__ __forceinline__ void team_barrier(int* cnt, int& target, int* err) {
+  target += kTeamWaves;
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");  // this wave's writes are done
+  if ((threadIdx.x & 63) == 0) atomicAdd(cnt, 1);
+  int polls = 0;
+  while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target) {
+    if (++polls > kSpinCap) {
+      if ((threadIdx.x & 63) == 0) atomicOr(err, SV_DATA_STALL);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  asm volatile("" ::: "memory");
+}
+
+// A team's finish of row b drawn from p (gamma = 0): lane k < kSeqWaves of every wave of
+// the team holds the table sum of sub-region k (width sw); the same search as tab_finish
+// (t = u Z, the sub-region where the inclusive prefix first exceeds t, else the last
+// positive one), then the team re-sweeps that sub-region in passes of kTeamPass entries
+// for the first entry whose prefix exceeds t. Writes emitted[b] and residual_sum[b] = 0.
+// Ends with a team barrier, after which the team's LDS may be reused.
+__device__ __forceinline__ void team_finish(const Args& a, int b, const double* sT, double rD, int sw, int tw,
+                                            double (*s_wt)[kTeamWaves], int* s_cand, int* s_last, int* cnt,
+                                            int& target) {
+  const int lane = threadIdx.x & 63;
+  const int V = a.V;
+  const int tlo = a.tlo, tsent = a.thi + 1 - a.tlo;
+  const uint16_t* lrow = drawn_row(a, b, 0, 0, 0);
+  const bool live = lane < kSeqWaves;
+  const double wgt = live ? rD : 0.0;
+  const double Z64 = wave_sum_dpp(wgt);
+  const float uf = a.u[b];
+  const double t = static_cast<double>(uf) * Z64;
+  const double inc = wave_incl_scan_dpp(wgt);
+  const unsigned long long cross = __ballot(live && inc > t);
+  int rs = cross ? __ffsll(cross) - 1 : -1;
+  double run = readlane_d(inc - wgt, rs < 0 ? 0 : rs);
+  bool take_last = false;
+  if (rs < 0) {  // no crossing (rounding, or u >= 1): last positive-weight entry
+    take_last = true;
+    const unsigned long long pos = __ballot(live && wgt > 0.0);
+    rs = pos ? 63 - __clzll(pos) : -1;
+    run = 0.0;
+  }
+  if (tw == 0 && lane == 0) {
+    if (!(Z64 > 0.0 && Z64 <= DBL_MAX)) atomicOr(a.err, SV_DATA_NONFINITE);
+    if (!(uf >= 0.f && uf < 1.f)) atomicOr(a.err, SV_DATA_UNIFORM);
+    *s_cand = INT_MAX;
+    *s_last = -1;
+  }
+  int tok = V - 1;
+  if (rs >= 0) {
+    const int R0 = min(V, rs * sw), R1 = min(V, R0 + sw);
+    int parity = 0;
+    for (int p0 = R0; p0 < R1; p0 += kTeamPass, parity ^= 1) {
+      const int e = p0 + tw * kIter + lane * kGroup;
+      const bool in = e < R1;
+      Raw<uint16_t> lr;
+      load_raw_in(lrow, min(e, R1 - kGroup), lr);
+      double rv[kGroup];
+      lookup8(lr, rv, sT, tlo, tsent);
+      double tot = 0.0;
+#pragma unroll
+      for (int j = 0; j < kGroup; ++j) {
+        rv[j] = in ? rv[j] : 0.0;
+        tot += rv[j];
+      }
+      const double linc = wave_incl_scan_dpp(tot);
+      if (lane == 63) s_wt[parity][tw] = linc;
+      team_barrier(cnt, target, a.err);
+      double acc = run, tsum = run;
+      for (int w2 = 0; w2 < kTeamWaves; ++w2) {
+        const double v2 = s_wt[parity][w2];
+        if (w2 < tw) acc += v2;
+        tsum += v2;
+      }
+      acc += linc - tot;
+      int c2 = INT_MAX, lp = -1;
+#pragma unroll
+      for (int j = 0; j < kGroup; ++j) {
+        acc += rv[j];
+        if (!take_last && c2 == INT_MAX && acc > t) c2 = e + j;
+        if (rv[j] > 0.0) lp = e + j;
+      }
+      c2 = wave_min_int_dpp(c2);
+      lp = wave_max_int_dpp(lp);
+      if (lane == 0) {
+        if (c2 != INT_MAX) atomicMin(s_cand, c2);
+        if (lp >= 0) atomicMax(s_last, lp);
+      }
+      run = tsum;
+      team_barrier(cnt, target, a.err);
+      if (*s_cand != INT_MAX) break;
+    }
+    tok = *s_cand != INT_MAX ? *s_cand : (*s_last >= 0 ? *s_last : V - 1);
+  }
+  if (tw == 0 && lane == 0) {
+    a.emitted[b] = tok;
+    a.rsum[b] = 0.f;
+  }
+  team_barrier(cnt, target, a.err);  // s_cand, s_last and the sums are read
+}
+
 // Rounds with no drafts (gamma = 0: one token per row drawn from p, [P1] ch.2 bonus draw)
 // with more rows than compute units: one workgroup per compute unit builds the value
 // table once and draws row after row (rows b, b + gridDim.x, ...), instead of one
-// workgroup, and one table, per row.
+// workgroup, and one table, per row. bf16 rows: two teams of eight waves take
+// alternate rows (team_finish); a row holding a value outside the table is marked and
+// drawn afterwards by the whole workgroup on the exp2 path.
+constexpr int kFallbackMark = -2;  // emitted[b] of a row left for the exp2 path
 template <typename T>
 __global__ __launch_bounds__(kSeqThreads) void k_sample_rows(Args a) {
   __shared__ double s_tab[kExpN];
-  exp_table_init(s_tab);
   if constexpr (sizeof(T) == 2) {
     __shared__ double sT[kTabEntries];
+    __shared__ double s_rs[kTeams][kSeqWaves];          // a team's sub-region sums of its row
+    __shared__ double s_wt[kTeams][2][kTeamWaves];      // re-sweep: per-wave totals, by pass parity
+    __shared__ int s_cand[kTeams], s_last[kTeams], s_cnt[kTeams];
+    __shared__ int s_fb, s_nfb;
     const bool tab = a.tlo <= a.thi;
-    if (tab) tab_build(sT, a);
-    __syncthreads();  // sT, s_tab
+    if (!tab) {
+      exp_table_init(s_tab);
+      __syncthreads();  // s_tab
+      for (int b = blockIdx.x; b < a.B; b += gridDim.x) {
+        if (threadIdx.x == 0) a.acc[b] = 0;
+        final_draw<T, true>(a, b, 0, 0, 0, 0.0, 0.0, s_tab);
+        __syncthreads();  // the draw's LDS is reused by the next row
+      }
+      return;
+    }
+    tab_build(sT, a);
+    if (threadIdx.x < kTeams) s_cnt[threadIdx.x] = 0;
+    if (threadIdx.x == 0) s_nfb = 0;
+    __syncthreads();  // sT, s_cnt, s_nfb
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int team = wave / kTeamWaves, tw = wave % kTeamWaves;
+    const int V = a.V;
+    const int sw = sub_width(V, kSeqWaves);
+    int target = 0;
+    for (int b = blockIdx.x + team * gridDim.x; b < a.B; b += kTeams * gridDim.x) {
+      if (tw == 0 && lane == 0) a.acc[b] = 0;
+      // this wave's two sub-regions of the row: tw and tw + kTeamWaves
+#pragma unroll
+      for (int h = 0; h < kTeams; ++h) {
+        const int k = tw + h * kTeamWaves;
+        const int r0 = min(V, k * sw), r1 = min(V, r0 + sw);
+        double D, Q, Z;
+        tab_sweep(drawn_row(a, b, 0, 0, 0), nullptr, r0, r1, 0.0, sT, a.tlo, a.thi + 1 - a.tlo, D, Q, Z);
+        if (lane == 0) s_rs[team][k] = D;
+      }
+      team_barrier(&s_cnt[team], target, a.err);  // s_rs[team]
+      const double rD = s_rs[team][lane < kSeqWaves ? lane : 0];
+      // a value outside the table reached the sentinel: a sub-region sum is not finite
+      if (__ballot(lane < kSeqWaves && !(rD <= DBL_MAX)) != 0) {
+        if (tw == 0 && lane == 0) {
+          a.emitted[b] = kFallbackMark;
+          atomicAdd(&s_nfb, 1);
+        }
+        team_barrier(&s_cnt[team], target, a.err);  // s_rs[team] is read
+        continue;
+      }
+      team_finish(a, b, sT, rD, sw, tw, s_wt[team], &s_cand[team], &s_last[team], &s_cnt[team], target);
+    }
+    __syncthreads();  // both teams are done; marked rows are visible to the workgroup
+    if (s_nfb == 0) return;
+    bool exp_ready = false;
     for (int b = blockIdx.x; b < a.B; b += gridDim.x) {
-      if (threadIdx.x == 0) a.acc[b] = 0;
-      if (!(tab && final_draw_tab(a, b, 0, 0, 0, 0.0, sT))) final_draw<T, true>(a, b, 0, 0, 0, 0.0, 0.0, s_tab);
+      if (threadIdx.x == 0) s_fb = a.emitted[b] == kFallbackMark;
+      __syncthreads();  // s_fb
+      const bool fb = s_fb;
+      __syncthreads();  // s_fb is read before the next row rewrites it
+      if (!fb) continue;
+      if (!exp_ready) {
+        exp_table_init(s_tab);
+        __syncthreads();  // s_tab
+        exp_ready = true;
+      }
+      final_draw<T, true>(a, b, 0, 0, 0, 0.0, 0.0, s_tab);
       __syncthreads();  // the draw's LDS is reused by the next row
     }
   } else {
+    exp_table_init(s_tab);
     __syncthreads();  // s_tab
     for (int b = blockIdx.x; b < a.B; b += gridDim.x) {
       if (threadIdx.x == 0) a.acc[b] = 0;
@@ -2516,13 +2694,14 @@ int spec_verify_status(spec_verify_ctx* ctx) {
   const int zero = 0;
   e = hipMemcpy(ctx->err, &zero, sizeof(int), hipMemcpyHostToDevice);
   if (e != hipSuccess) return hip_fail(ctx, "hipMemcpy", e);
-  snprintf(ctx->msg, sizeof(ctx->msg), "device data error flags 0x%x:%s%s%s%s%s%s", flag,
+  snprintf(ctx->msg, sizeof(ctx->msg), "device data error flags 0x%x:%s%s%s%s%s%s%s", flag,
            (flag & SV_DATA_DRAFT_ID) ? " draft-id-out-of-range" : "",
            (flag & SV_DATA_NONFINITE) ? " non-finite-normaliser" : "",
            (flag & SV_DATA_UNIFORM) ? " uniform-out-of-[0,1)" : "",
            (flag & SV_DATA_CU_GAMMA) ? " malformed-cu_gamma" : "",
            (flag & SV_DATA_CONTEXT) ? " malformed-cu_ctx" : "",
-           (flag & SV_DATA_STATE) ? " adaptive-state-out-of-range" : "");
+           (flag & SV_DATA_STATE) ? " adaptive-state-out-of-range" : "",
+           (flag & SV_DATA_STALL) ? " internal-wait-bound-reached" : "");
   return SV_EDATA;
 }
 
