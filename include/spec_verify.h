@@ -163,8 +163,10 @@ int spec_verify_run_onehot(spec_verify_ctx *ctx, void *hip_stream, int batch, in
 /*
  * Launch plan. A run either takes two launches (row statistics or argmaxes of every
  * draft row, then one workgroup per sequence for the first-rejection scan and the
- * draw; bf16 sampling runs with at most half as many sequences as compute units give
- * each sequence two or four workgroups that share the draw) or one launch (one workgroup per sequence that judges its rows left to right,
+ * draw; sampling runs with 16-byte aligned rows, V a multiple of 8 and at most half as
+ * many sequences as compute units give each sequence two or four workgroups that
+ * share the draw, fewer when the rows are too short to divide) or one launch (one
+ * workgroup per sequence that judges its rows left to right,
  * stops reading at the first rejection and then draws; in greedy mode the argmax of
  * the first mismatching row, or of the bonus row, is the token). The one-launch plan
  * needs V a multiple of 8, 16-byte aligned logits (and q when T > 0), gamma_b <= 64

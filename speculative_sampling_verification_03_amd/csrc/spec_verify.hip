@@ -96,7 +96,7 @@ struct Args {
   int tlo, thi;
   int onehot;      // drafts are deterministic: q = one-hot(draft), q is not read
   int nodraft;     // an id of -1 marks "no draft here": rejected without the data flag
-  // split draw of the two-launch plan (bf16): nslice workgroups sweep one drawn row
+  // split draw of the two-launch plan: nslice workgroups sweep one drawn row
   int nslice;
   double* dsum;    // [B][kMaxSub][3] sub-region sums
   int* dcnt;       // [B] slices of the sequence's sweep done (zero between calls)
@@ -474,47 +474,28 @@ __device__ __forceinline__ int region_width(int V) {
   return (per + kRing * kIter - 1) / (kRing * kIter) * (kRing * kIter);
 }
 
-// The draw that ends a sequence's round ([P1] ch.2-3; [P2] "미리 그려놓고 한 번에 검증한다";
-// [P3] 단계 3): after a rejection at n < g, one token from norm(max(0, p_n - q_n)); when
-// all g drafts were accepted, the bonus token from p_g. Writes emitted[n], the -1
-// padding after it and residual_sum[b]. For a residual, row n's statistics come in as
-// a reference cref (in octaves) and Zq = sum 2^(l k2 - cref) over the row, exact or
-// fp32-rounded (unused for the bonus). Every thread of the block calls it; s_tab holds
-// the exp2_tab table.
+// Width of each of ns regions of a row for the split fp32 draw: ceil(V / ns) rounded up
+// to whole sweep iterations, so short rows (V = 32000) still spread over every slice.
+__host__ __device__ inline int iter_width(int V, int ns) {
+  const int per = (V + ns - 1) / ns;
+  return (per + kIter - 1) / kIter * kIter;
+}
+
+// One wave's fp64 sweep of entries [r0, r1) of a drawn row through a ring of kRing
+// register buffers, e = 2^(l k2 - cr) by exp2_tab (KN = N k2, CN = N cr).
+// Residual (qrow != null), with w = e - q Zq: s0 = sum max(w, 0), s1 = sum of q where
+// w > 0, s2 = sum e. Bonus (qrow == null): s0 = the range's max logit (-inf when the
+// range is empty), s1 = sum 2^((l - s0) k2), s2 = 0. The sums are wave-uniform.
 template <typename T, bool ALIGNED>
-__device__ __forceinline__ void final_draw(const Args& a, int b, int base, int g, int n, double cref,
-                                           double Zq_in, const double* s_tab, int xn = -1) {
-  __shared__ double s_reg[kSeqWaves][3];  // residual: (D, Q, Zr); bonus: (m, s, -)
-  __shared__ double s_wt[kSeqWaves];      // re-sweep: per-wave totals of a pass
-  __shared__ int s_wc[kSeqWaves], s_wl[kSeqWaves];
-  __shared__ double s_bc[6];  // search result: t, P (prefix before the region), Z64, delta, S, ref
-  __shared__ int s_bi[4];     // search result: region r*, kind, take_last, excluded id
+__device__ __forceinline__ void draw_sweep(const T* lrow, const float* qrow, int r0, int r1, double KN, double CN,
+                                           double Zq, const double* s_tab, double& s0, double& s1, double& s2) {
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar
-  const int V = a.V;
-  const bool residual = n < g;
-  // one-hot drafts: max(0, p - onehot(x_n)) is p with x_n removed, drawn like a bonus row
-  const bool oh = residual && a.onehot;
-  const bool qres = residual && !oh;
-  const T* lrow = static_cast<const T*>(a.logits) + static_cast<size_t>(base + b + (residual ? n : g)) * V;
-  const float* qrow = qres ? a.q + static_cast<size_t>(base + n) * V : nullptr;
-  if (oh && xn < 0) xn = a.ids[base + n];
-  const bool excl_ok = oh && xn >= 0 && xn < V;  // an invalid id removes nothing
-  const float lxn = excl_ok ? load_one(lrow, xn) : 0.f;
-  const double KN = kExpScale * a.k2d;  // exp2_tab(l KN - N c) = 2^(l k2 - c)
-  const double cr = residual ? cref : 0.0;
-  const double Zq = residual ? Zq_in : 0.0;
-  const int rw = region_width(V);
-  const int r0 = min(V, wave * rw), r1 = min(V, r0 + rw);
   // whole iterations are read without checks (only possible when aligned); the rest, masked
   const int nfull = ALIGNED ? (r1 - r0) / kIter : 0;
   const int mstart = r0 + nfull * kIter;
   const uint32_t linf = neg_inf_word<T>();
-
-  // ---- one fp64 sweep of this wave's region through a ring of kRing register buffers
-  if (qres) {
+  if (qrow) {
     // residual max(0, p - q) ([P1] ch.3; [P3] 단계 3), normalisation deferred
-    const double CN = kExpScale * cr;
     double D = 0.0, Zr = 0.0;
     float Q = 0.f;
     auto step = [&](const Raw<T>& lr, const Raw<float>& qr) {
@@ -552,7 +533,7 @@ __device__ __forceinline__ void final_draw(const Args& a, int b, int base, int g
         }
       }
     }
-    // the rest of the region, masked per lane (fills contribute nothing); the trip count
+    // the rest of the range, masked per lane (fills contribute nothing); the trip count
     // is the same for every lane of the wave
     for (int e0 = mstart; e0 < r1; e0 += kIter) {
       Raw<T> lr;
@@ -561,16 +542,11 @@ __device__ __forceinline__ void final_draw(const Args& a, int b, int base, int g
       load_raw<float, ALIGNED>(qrow, e0 + lane * kGroup, r1, qr, 0u);
       step(lr, qr);
     }
-    D = wave_sum(D);
-    Zr = wave_sum(Zr);
-    Q = wave_sum(Q);
-    if (lane == 0) {
-      s_reg[wave][0] = D;
-      s_reg[wave][1] = Q;
-      s_reg[wave][2] = Zr;
-    }
+    s0 = wave_sum(D);
+    s1 = wave_sum(Q);
+    s2 = wave_sum(Zr);
   } else {
-    // bonus row ([P1] ch.2; [P3] 단계 3): running region max mw, sum 2^((l - mw) k2)
+    // bonus row ([P1] ch.2; [P3] 단계 3): running range max mw, sum 2^((l - mw) k2)
     float mw = -INFINITY;
     double mK = 0.0, sacc = 0.0;
     auto step = [&](const Raw<T>& lr) {
@@ -613,41 +589,66 @@ __device__ __forceinline__ void final_draw(const Args& a, int b, int base, int g
       load_raw<T, ALIGNED>(lrow, e0 + lane * kGroup, r1, lr, linf);
       step(lr);
     }
-    sacc = wave_sum(sacc);
-    if (lane == 0) {
-      s_reg[wave][0] = mw;
-      s_reg[wave][1] = sacc;
-      s_reg[wave][2] = 0.0;
-    }
+    s0 = mw;
+    s1 = wave_sum(sacc);
+    s2 = 0.0;
   }
-  __syncthreads();
+}
+
+// The finish of the draw over ns <= 64 regions of width rw (region r covers
+// [r rw, min(V, (r + 1) rw))): lane r < ns of wave 0 holds region r's sums (v0, v1, v2)
+// from draw_sweep (the other lanes and waves are ignored). Wave 0 forms the totals and
+// finds the region where the inclusive prefix first exceeds t; the block re-sweeps that
+// region with an fp64 scan and writes emitted[n], the -1 padding after it and
+// residual_sum[b]. Every thread of the block calls it.
+template <typename T, bool ALIGNED>
+__device__ __forceinline__ void draw_finish(const Args& a, int b, int base, int g, int n, double cr, double Zq,
+                                            const double* s_tab, int xn, int ns, int rw, double v0, double v1,
+                                            double v2) {
+  __shared__ double s_wt[kSeqWaves];  // re-sweep: per-wave totals of a pass
+  __shared__ int s_wc[kSeqWaves], s_wl[kSeqWaves];
+  __shared__ double s_bc[6];  // search result: t, P (prefix before the region), Z64, delta, S, ref
+  __shared__ int s_bi[4];     // search result: region r*, kind, take_last, excluded id
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar
+  const int V = a.V;
+  const bool residual = n < g;
+  // one-hot drafts: max(0, p - onehot(x_n)) is p with x_n removed, drawn like a bonus row
+  const bool oh = residual && a.onehot;
+  const bool qres = residual && !oh;
+  const T* lrow = static_cast<const T*>(a.logits) + static_cast<size_t>(base + b + (residual ? n : g)) * V;
+  const float* qrow = qres ? a.q + static_cast<size_t>(base + n) * V : nullptr;
+  const double KN = kExpScale * a.k2d;  // exp2_tab(l KN - N c) = 2^(l k2 - c)
+  const uint32_t linf = neg_inf_word<T>();
+  const float uf = a.u[base + b + g];
 
   // ---- totals and the region where the inclusive prefix first exceeds t (wave 0,
   // lane r holding region r)
-  const float uf = a.u[base + b + g];
   if (wave == 0) {
+    if (oh && xn < 0) xn = a.ids[base + n];
+    const bool excl_ok = oh && xn >= 0 && xn < V;  // an invalid id removes nothing
+    const float lxn = excl_ok ? load_one(lrow, xn) : 0.f;
     const double u = uf;
-    const int r = lane < kSeqWaves ? lane : 0;
-    const bool live = lane < kSeqWaves;
+    const bool live = lane < ns;
     int kind;  // 0: residual; 1: degenerate residual (S <= 0), draw from p; 2: from p; 3: p without x_n
     int excl = -1;
     double Z64, S = 0.0, delta = 0.0, ref, t, wgt;
     if (qres) {
-      Z64 = wave_sum(live ? s_reg[r][2] : 0.0);
+      Z64 = wave_sum(live ? v2 : 0.0);
       delta = (Z64 - Zq) / Z64;
-      wgt = live ? s_reg[r][0] / Z64 - s_reg[r][1] * delta : 0.0;
+      wgt = live ? v0 / Z64 - v1 * delta : 0.0;
       S = wave_sum(wgt);
       kind = S > 0.0 ? 0 : 1;
-      if (kind == 1) wgt = live ? s_reg[r][2] : 0.0;
+      if (kind == 1) wgt = live ? v2 : 0.0;
       t = kind == 0 ? u * S : u * Z64;
       ref = kExpScale * cr;
     } else {
-      double M = live ? s_reg[r][0] : -INFINITY;
+      const double mr = live ? v0 : -INFINITY;
+      double M = mr;
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) M = fmax(M, __shfl_xor(M, o));
       ref = M * KN;
-      const double mr = live ? s_reg[r][0] : -INFINITY;
-      wgt = mr > -INFINITY ? s_reg[r][1] * exp2_tab(mr * KN - ref, s_tab) : 0.0;
+      wgt = mr > -INFINITY ? v1 * exp2_tab(mr * KN - ref, s_tab) : 0.0;
       Z64 = wave_sum(wgt);
       kind = 2;
       t = u * Z64;
@@ -658,7 +659,7 @@ __device__ __forceinline__ void final_draw(const Args& a, int b, int base, int g
         if (S > 0.0) {
           kind = 3;
           excl = excl_ok ? xn : -1;
-          if (excl_ok && r == xn / rw && live) wgt = fmax(wgt - ex_n, 0.0);
+          if (excl_ok && live && lane == xn / rw) wgt = fmax(wgt - ex_n, 0.0);
           t = u * wave_sum(live ? wgt : 0.0);
         }
       }
@@ -766,6 +767,42 @@ __device__ __forceinline__ void final_draw(const Args& a, int b, int base, int g
     a.rsum[b] = residual ? static_cast<float>(S) : 0.f;
   }
   for (int i = n + 1 + threadIdx.x; i <= g; i += kSeqThreads) a.emitted[base + b + i] = -1;
+}
+
+// The draw that ends a sequence's round ([P1] ch.2-3; [P2] "미리 그려놓고 한 번에 검증한다";
+// [P3] 단계 3) in one workgroup: after a rejection at n < g, one token from
+// norm(max(0, p_n - q_n)); when all g drafts were accepted, the bonus token from p_g.
+// Writes emitted[n], the -1 padding after it and residual_sum[b]. For a residual, row
+// n's statistics come in as a reference cref (in octaves) and Zq = sum 2^(l k2 - cref)
+// over the row, exact or fp32-rounded (unused for the bonus). Wave w sweeps region w of
+// the row; draw_finish does the rest. Every thread of the block calls it; s_tab holds
+// the exp2_tab table.
+template <typename T, bool ALIGNED>
+__device__ __forceinline__ void final_draw(const Args& a, int b, int base, int g, int n, double cref,
+                                           double Zq_in, const double* s_tab, int xn = -1) {
+  __shared__ double s_reg[kSeqWaves][3];  // residual: (D, Q, Zr); bonus: (m, s, -)
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int V = a.V;
+  const bool residual = n < g;
+  const bool qres = residual && !a.onehot;
+  const T* lrow = static_cast<const T*>(a.logits) + static_cast<size_t>(base + b + (residual ? n : g)) * V;
+  const float* qrow = qres ? a.q + static_cast<size_t>(base + n) * V : nullptr;
+  const double cr = residual ? cref : 0.0;
+  const double Zq = residual ? Zq_in : 0.0;
+  const int rw = region_width(V);
+  const int r0 = min(V, wave * rw), r1 = min(V, r0 + rw);
+  double s0, s1, s2;
+  draw_sweep<T, ALIGNED>(lrow, qrow, r0, r1, kExpScale * a.k2d, kExpScale * cr, Zq, s_tab, s0, s1, s2);
+  if (lane == 0) {
+    s_reg[wave][0] = s0;
+    s_reg[wave][1] = s1;
+    s_reg[wave][2] = s2;
+  }
+  __syncthreads();
+  const int r = lane < kSeqWaves ? lane : 0;
+  draw_finish<T, ALIGNED>(a, b, base, g, n, cr, Zq, s_tab, xn, kSeqWaves, rw, s_reg[r][0], s_reg[r][1],
+                          s_reg[r][2]);
 }
 
 // ============================================================== one-launch path
@@ -937,7 +974,7 @@ constexpr int kSplitMaxB = 1024;                  // sequences the split draw's 
 
 // Width of one of ns sub-regions of a row: a multiple of kRing iterations, so a wave's
 // sweep has no partial ring round except at the end of the row.
-__device__ __forceinline__ int sub_width(int V, int ns) {
+__host__ __device__ inline int sub_width(int V, int ns) {
   const int per = (V + ns - 1) / ns;
   return (per + kRing * kIter - 1) / (kRing * kIter) * (kRing * kIter);
 }
@@ -1295,18 +1332,20 @@ __global__ __launch_bounds__(kSeqThreads) void k_sample_seq(Args a) {
   }
 }
 
-// The split draw of the two-launch plan (bf16 rows, few sequences): workgroup (b, s) of
-// k_draw_part finds sequence b's first rejection from step 1's decisions (every slice
-// does it; only slice 0 writes the outputs of the scan), then sweeps slice s of the drawn
-// row (16 sub-regions, one per wave) and stores the fp64 sums. Each slice then counts
-// itself done; the slice that completes the count (whichever finishes last) reads all
-// 16 nslice sums and finishes the draw. No workgroup waits for another. The XCDs' L2
-// caches are not coherent with each other, so the sums and the count are written and
-// read at system scope (past the L2s), and each wave waits for its sums' stores to
-// complete before the count is taken; no cache-wide write-back or invalidate is needed.
-template <bool RAGGED, bool ACCEPT>
+// The split draw of the two-launch plan (few sequences): workgroup (b, s) of k_draw_part
+// finds sequence b's first rejection from step 1's decisions (every slice does it; only
+// slice 0 writes the outputs of the scan), then sweeps slice s of the drawn row (16
+// regions, one per wave) and stores the fp64 sums: bf16 rows through the value table,
+// fp32 rows with exp2_tab as in final_draw. Each slice then counts itself done; the
+// slice that completes the count (whichever finishes last) reads all 16 nslice sums and
+// finishes the draw. No workgroup waits for another. The XCDs' L2 caches are not
+// coherent with each other, so the sums and the count are written and read at system
+// scope (past the L2s), and each wave waits for its sums' stores to complete before the
+// count is taken; no cache-wide write-back or invalidate is needed.
+template <typename T, bool RAGGED, bool ACCEPT>
 __global__ __launch_bounds__(kSeqThreads) void k_draw_part(Args a) {
-  __shared__ double sT[kTabEntries];
+  constexpr bool kTab = sizeof(T) == 2;  // bf16 rows: the value table
+  __shared__ double sT[kTab ? kTabEntries : 1];
   __shared__ double s_tab[kExpN];
   __shared__ float2 s_cz[kMaxGamma];
   __shared__ int s_n, s_last;
@@ -1321,22 +1360,32 @@ __global__ __launch_bounds__(kSeqThreads) void k_draw_part(Args a) {
     }
     return;
   }
-  tab_build(sT, a);
-  const int n = first_rejection<uint16_t, ACCEPT, false>(a, b, base, g, s_cz, nullptr, &s_n);
+  if constexpr (kTab)
+    tab_build(sT, a);
+  else
+    exp_table_init(s_tab);
+  const int n = first_rejection<T, ACCEPT, false>(a, b, base, g, s_cz, nullptr, &s_n);
   if (s == 0) {
     for (int i = threadIdx.x; i < n; i += kSeqThreads) a.emitted[base + b + i] = a.ids[base + i];
     if (threadIdx.x == 0) a.acc[b] = n;
   }
-  __syncthreads();  // sT
+  __syncthreads();  // sT / s_tab
   const double cr = n < g ? static_cast<double>(s_cz[n].x) : 0.0;
   const double zr = n < g ? static_cast<double>(s_cz[n].y) : 0.0;
-  const double Zq = zr * exp2(cr);
-  const int ns = kSeqWaves * a.nslice, sw = sub_width(a.V, ns);
+  const int ns = kSeqWaves * a.nslice;
+  const int sw = kTab ? sub_width(a.V, ns) : iter_width(a.V, ns);
   const int k = kSeqWaves * s + wave;
   const int r0 = min(a.V, k * sw), r1 = min(a.V, r0 + sw);
   double D, Q, Z;
-  tab_sweep(drawn_row(a, b, base, g, n), drawn_q(a, base, g, n), r0, r1, Zq, sT, a.tlo, a.thi + 1 - a.tlo, D, Q,
-            Z);
+  if constexpr (kTab) {
+    tab_sweep(drawn_row(a, b, base, g, n), drawn_q(a, base, g, n), r0, r1, zr * exp2(cr), sT, a.tlo,
+              a.thi + 1 - a.tlo, D, Q, Z);
+  } else {
+    const bool residual = n < g;
+    const float* lrow = static_cast<const float*>(a.logits) + static_cast<size_t>(base + b + (residual ? n : g)) * a.V;
+    draw_sweep<float, true>(lrow, drawn_q(a, base, g, n), r0, r1, kExpScale * a.k2d, kExpScale * cr, zr, s_tab, D,
+                            Q, Z);
+  }
   if (lane == 0) {
     double* dst = a.dsum + (static_cast<size_t>(b) * kMaxSub + k) * 3;
     __hip_atomic_store(dst, D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
@@ -1359,10 +1408,14 @@ __global__ __launch_bounds__(kSeqThreads) void k_draw_part(Args a) {
     rQ = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     rZ = __hip_atomic_load(src + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   }
-  if (tab_finish(a, b, base, g, n, Zq, sT, -1, ns, rD, rQ, rZ)) return;
-  exp_table_init(s_tab);
-  __syncthreads();  // s_tab
-  final_draw<uint16_t, true>(a, b, base, g, n, cr, zr, s_tab);
+  if constexpr (kTab) {
+    if (tab_finish(a, b, base, g, n, zr * exp2(cr), sT, -1, ns, rD, rQ, rZ)) return;
+    exp_table_init(s_tab);
+    __syncthreads();  // s_tab
+    final_draw<uint16_t, true>(a, b, base, g, n, cr, zr, s_tab);
+  } else {
+    draw_finish<float, true>(a, b, base, g, n, n < g ? cr : 0.0, n < g ? zr : 0.0, s_tab, -1, ns, sw, rD, rQ, rZ);
+  }
 }
 
 // Pass 1: per row, z = sum 2^(l k2 - c) in fp32. Each wave takes its reference c from
@@ -2152,7 +2205,7 @@ struct spec_verify_ctx {
   hipEvent_t* ev = nullptr;
   int timing_path = -1;  // the path of the recorded runs (runs on another path are not recorded)
   int path_mode = SV_PATH_AUTO, last_path = SV_PATH_AUTO;
-  // split draw of the two-launch plan (bf16 contexts, up to split_cap sequences)
+  // split draw of the two-launch plan (up to split_cap sequences)
   double* dsum = nullptr;
   int* dcnt = nullptr;
   int split_cap = 0;
@@ -2279,15 +2332,25 @@ hipError_t launch_path(spec_verify_ctx* ctx, const Args& a, hipStream_t st, bool
 }
 
 // The split draw: with at most half as many sequences as compute units, two or four
-// workgroups share the sweep of each drawn row (bf16 rows through the value table):
-// four when there are at least four compute units per sequence, else two.
+// workgroups share the sweep of each drawn row (bf16 rows through the value table, fp32
+// rows with exp2_tab): four when there are at least four compute units per sequence,
+// else two. bf16 rows split only when the temperature admits the value table.
+// Fewer slices when the row is too short for the last one to get any of it.
 int split_slices(const spec_verify_ctx* ctx, const Args& a) {
-  if (ctx->dtype != SV_BF16 || a.tlo > a.thi || a.B < 1 || a.B > ctx->split_cap) return 1;
+  const bool bf16 = ctx->dtype == SV_BF16;
+  if ((bf16 && a.tlo > a.thi) || a.B < 1 || a.B > ctx->split_cap) return 1;
   const int per = ctx->cus / a.B;
-  return per >= kMaxSlices ? kMaxSlices : per >= 2 ? 2 : 1;
+  int s = per >= kMaxSlices ? kMaxSlices : per >= 2 ? 2 : 1;
+  while (s > 1) {
+    const int ns = kSeqWaves * s;
+    const long long w = bf16 ? sub_width(a.V, ns) : iter_width(a.V, ns);
+    if (static_cast<long long>(ns - kSeqWaves) * w < a.V) break;
+    s /= 2;
+  }
+  return s;
 }
 
-template <bool RG, bool AC>
+template <typename T, bool RG, bool AC>
 hipError_t launch_split(spec_verify_ctx* ctx, const Args& a0, hipStream_t st, int nslice) {
   hipEvent_t* ev = timing_slot(ctx, kPathSample3);
   Args a = a0;
@@ -2296,14 +2359,14 @@ hipError_t launch_split(spec_verify_ctx* ctx, const Args& a0, hipStream_t st, in
   a.dcnt = ctx->dcnt;
   hipError_t e = hipSuccess;
   if (a.R > 0) {
-    e = launch_one(reinterpret_cast<const void*>(&k_rowstats<uint16_t, true, RG, AC>),
+    e = launch_one(reinterpret_cast<const void*>(&k_rowstats<T, true, RG, AC>),
                    dim3(static_cast<unsigned>(a.R) * a.split), dim3(kThreads), a, st, ev, 0);
   } else if (ev) {
     (void)hipEventRecord(ev[0], st);
     (void)hipEventRecord(ev[1], st);
   }
   if (e != hipSuccess) return e;
-  e = launch_one(reinterpret_cast<const void*>(&k_draw_part<RG, AC>), dim3(static_cast<unsigned>(a.B) * nslice),
+  e = launch_one(reinterpret_cast<const void*>(&k_draw_part<T, RG, AC>), dim3(static_cast<unsigned>(a.B) * nslice),
                  dim3(kSeqThreads), a, st, ev, 1);
   if (e != hipSuccess) return e;
   if (ev) ++ctx->timing_runs;
@@ -2312,10 +2375,10 @@ hipError_t launch_split(spec_verify_ctx* ctx, const Args& a0, hipStream_t st, in
 
 template <typename T, bool AL, bool RG>
 hipError_t launch_ac(spec_verify_ctx* ctx, const Args& a, hipStream_t st, bool greedy) {
-  if constexpr (AL && sizeof(T) == 2) {
+  if constexpr (AL) {
     const int ns = greedy ? 1 : split_slices(ctx, a);
     if (ns > 1)
-      return a.split == 1 ? launch_split<RG, true>(ctx, a, st, ns) : launch_split<RG, false>(ctx, a, st, ns);
+      return a.split == 1 ? launch_split<T, RG, true>(ctx, a, st, ns) : launch_split<T, RG, false>(ctx, a, st, ns);
   }
   // rows that are not split run their accept test inside the row-statistics kernel
   return a.split == 1 ? launch_path<T, AL, RG, true>(ctx, a, st, greedy)
@@ -2520,8 +2583,8 @@ int spec_verify_create(spec_verify_ctx** out, int device, int vocab, int logits_
   const size_t n_ac = up(sizeof(int32_t) * static_cast<size_t>(max_draft_rows > 0 ? max_draft_rows : 1));
   const size_t n_sb = up(sizeof(int32_t) * static_cast<size_t>(max_batch > 0 ? max_batch : 1));
   const size_t n_er = 256;
-  // split draw (bf16): sub-region sums and a count of finished slices per sequence
-  ctx->split_cap = logits_dtype == SV_BF16 ? (max_batch < kSplitMaxB ? max_batch : kSplitMaxB) : 0;
+  // split draw: sub-region sums and a count of finished slices per sequence
+  ctx->split_cap = max_batch < kSplitMaxB ? max_batch : kSplitMaxB;
   const size_t cap = static_cast<size_t>(ctx->split_cap);
   const size_t n_ds = up(sizeof(double) * 3 * kMaxSub * cap), n_dc = up(sizeof(int) * cap);
   if (hipMalloc(&ctx->ws, n_p1 + n_ac + 3 * n_sb + n_er + n_ds + n_dc) != hipSuccess) {

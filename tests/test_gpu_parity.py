@@ -223,9 +223,11 @@ def test_low_temperature_outside_table(lib, batch):
     """T = 0.01 with bf16 logits ~N(0, 3^2): the value table's window ends at
     |l| < 990 T / log2(e) ~ 6.9, so nearly every drawn row holds a value outside it and
     the draw falls back to the exp2_tab path in every plan (one launch; two launches,
-    split over slices for B = 32). All must match the oracle."""
+    split over slices for B = 32, whose rows are long enough to split). All must match
+    the oracle."""
     T = synth.fp32_temperature(0.01)
-    w = synth.make_sampling("low T", np.full(batch, 4), 32000, "bf16", T, 3.0, 0.7, seed=58 + batch)
+    V = 32000 if batch > 128 else 128256
+    w = synth.make_sampling("low T", np.full(batch, 4), V, "bf16", T, 3.0, 0.7, seed=58 + batch)
     check_parity(lib, w, f"low T B={batch}")
 
 
@@ -544,6 +546,9 @@ def test_cooperative_draw_slices(lib, cfg, batch):
     ("C3", 100, ("k_rowstats", "k_draw_part")),     # 2 workgroups per drawn row
     ("C3", 128, ("k_rowstats", "k_draw_part")),
     ("C3", 160, ("k_rowstats", "k_sample_seq")),    # one workgroup per drawn row
+    ("C2", 64, ("k_rowstats", "k_draw_part")),      # fp32 rows, 4 workgroups per drawn row
+    ("C2", 100, ("k_rowstats", "k_draw_part")),     # fp32 rows, 2 workgroups per drawn row
+    ("C2", 160, ("k_rowstats", "k_sample_seq")),
 ])
 def test_two_launch_draw_kernels(lib, cfg, batch, kernels):
     """Below the one-launch threshold the draw runs in one workgroup per sequence, or, with
@@ -572,15 +577,15 @@ def test_two_launch_draw_kernels(lib, cfg, batch, kernels):
     v.set_path(lib.SV_PATH_AUTO)
 
 
-@pytest.mark.parametrize("batch", [64, 128])
-def test_split_draw_repeated_calls(lib, batch):
+@pytest.mark.parametrize("cfg,batch", [("C3", 64), ("C3", 128), ("C2", 64)])
+def test_split_draw_repeated_calls(lib, cfg, batch):
     """The split draw's last slice finishes each sequence through a count kept across the
     XCDs' caches and zeroed again by the finishing slice: 100 calls in a row on two input
     sets must each give the first call's (oracle-checked) outputs for that set."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     if batch * 2 > cus:
         pytest.skip("the draw split depends on the number of compute units")
-    ws = [synth.make_config("C3", seed=s, batch=batch) for s in (19, 20)]
+    ws = [synth.make_config(cfg, seed=s, batch=batch) for s in (19, 20)]
     devs = [to_device(w) for w in ws]
     v = verifier(lib, ws[0].V, ws[0].dtype, batch, ws[0].draft_rows)
     v.set_path(lib.SV_PATH_TWO_LAUNCH)
@@ -591,7 +596,7 @@ def test_split_draw_repeated_calls(lib, batch):
         rep = compare(w, gpu, oracle_batch(w))
         assert rep.ok(), rep.summary()
         first.append(gpu)
-    _say("split draw repeated", f"B={batch}")
+    _say("split draw repeated", cfg, f"B={batch}")
     for k in range(100):
         i = k % 2
         gpu = run_gpu(v, ws[i], dev=devs[i], want_p_draft=False)
