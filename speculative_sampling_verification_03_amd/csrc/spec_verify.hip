@@ -600,11 +600,13 @@ __device__ __forceinline__ void draw_sweep(const T* lrow, const float* qrow, int
 // from draw_sweep (the other lanes and waves are ignored). Wave 0 forms the totals and
 // finds the region where the inclusive prefix first exceeds t; the block re-sweeps that
 // region with an fp64 scan and writes emitted[n], the -1 padding after it and
-// residual_sum[b]. Every thread of the block calls it.
+// residual_sum[b]. uf is the sequence's uniform at position g (loaded by the caller
+// before its sweep, off the draw's chain of dependent loads). Every thread of the block
+// calls it.
 template <typename T, bool ALIGNED>
 __device__ __forceinline__ void draw_finish(const Args& a, int b, int base, int g, int n, double cr, double Zq,
                                             const double* s_tab, int xn, int ns, int rw, double v0, double v1,
-                                            double v2) {
+                                            double v2, float uf) {
   __shared__ double s_wt[kSeqWaves];  // re-sweep: per-wave totals of a pass
   __shared__ int s_wc[kSeqWaves], s_wl[kSeqWaves];
   __shared__ double s_bc[6];  // search result: t, P (prefix before the region), Z64, delta, S, ref
@@ -620,7 +622,6 @@ __device__ __forceinline__ void draw_finish(const Args& a, int b, int base, int 
   const float* qrow = qres ? a.q + static_cast<size_t>(base + n) * V : nullptr;
   const double KN = kExpScale * a.k2d;  // exp2_tab(l KN - N c) = 2^(l k2 - c)
   const uint32_t linf = neg_inf_word<T>();
-  const float uf = a.u[base + b + g];
 
   // ---- totals and the region where the inclusive prefix first exceeds t (wave 0,
   // lane r holding region r)
@@ -792,6 +793,7 @@ __device__ __forceinline__ void final_draw(const Args& a, int b, int base, int g
   const double Zq = residual ? Zq_in : 0.0;
   const int rw = region_width(V);
   const int r0 = min(V, wave * rw), r1 = min(V, r0 + rw);
+  const float uf = a.u[base + b + g];
   double s0, s1, s2;
   draw_sweep<T, ALIGNED>(lrow, qrow, r0, r1, kExpScale * a.k2d, kExpScale * cr, Zq, s_tab, s0, s1, s2);
   if (lane == 0) {
@@ -802,7 +804,7 @@ __device__ __forceinline__ void final_draw(const Args& a, int b, int base, int g
   __syncthreads();
   const int r = lane < kSeqWaves ? lane : 0;
   draw_finish<T, ALIGNED>(a, b, base, g, n, cr, Zq, s_tab, xn, kSeqWaves, rw, s_reg[r][0], s_reg[r][1],
-                          s_reg[r][2]);
+                          s_reg[r][2], uf);
 }
 
 // ============================================================== one-launch path
@@ -1125,8 +1127,10 @@ __device__ __forceinline__ void tab_sweep(const uint16_t* lrow, const float* qro
 // (rD, rQ, rZ) (the same values in every wave, so all waves take the same decisions).
 // Writes emitted[n], the -1 padding and residual_sum[b]. Returns false, having written
 // nothing, when the drawn row holds a value outside the table (a sum is not finite).
+// uf is the sequence's uniform at position g, loaded by the caller before its sweep.
 __device__ __forceinline__ bool tab_finish(const Args& a, int b, int base, int g, int n, double Zq,
-                                           const double* sT, int xn, int ns, double rD, double rQ, double rZ) {
+                                           const double* sT, int xn, int ns, double rD, double rQ, double rZ,
+                                           float uf) {
   __shared__ double s_wt[2][kSeqWaves];  // re-sweep: per-wave totals, by pass parity
   __shared__ int s_cand, s_last;         // re-sweep: first crossing, last positive entry
   const int lane = threadIdx.x & 63;
@@ -1149,7 +1153,6 @@ __device__ __forceinline__ bool tab_finish(const Args& a, int b, int base, int g
   }
 
   // ---- totals and the sub-region where the inclusive prefix first exceeds t
-  const float uf = a.u[base + b + g];
   const double u = uf;
   const bool live = lane < ns;
   // a value outside the table reached the sentinel: the sub-region's sum is not finite
@@ -1280,6 +1283,7 @@ __device__ __forceinline__ bool final_draw_tab(const Args& a, int b, int base, i
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int sw = sub_width(a.V, kSeqWaves);
   const int r0 = min(a.V, wave * sw), r1 = min(a.V, r0 + sw);
+  const float uf = a.u[base + b + g];
   double D, Q, Z;
   tab_sweep(drawn_row(a, b, base, g, n), drawn_q(a, base, g, n), r0, r1, Zq, sT, a.tlo, a.thi + 1 - a.tlo, D,
             Q, Z);
@@ -1291,7 +1295,7 @@ __device__ __forceinline__ bool final_draw_tab(const Args& a, int b, int base, i
   __syncthreads();
   const int k = lane < kSeqWaves ? lane : 0;
   return tab_finish(a, b, base, g, n, Zq, sT, xn, kSeqWaves, lane < kSeqWaves ? s_reg[k][0] : 0.0,
-                    lane < kSeqWaves ? s_reg[k][1] : 0.0, lane < kSeqWaves ? s_reg[k][2] : 0.0);
+                    lane < kSeqWaves ? s_reg[k][1] : 0.0, lane < kSeqWaves ? s_reg[k][2] : 0.0, uf);
 }
 // Step 2 of the two-launch plan: one workgroup per sequence takes the row decisions of
 // step 1, finds the first rejection and draws.
@@ -1364,6 +1368,7 @@ __global__ __launch_bounds__(kSeqThreads) void k_draw_part(Args a) {
     tab_build(sT, a);
   else
     exp_table_init(s_tab);
+  const float uf = a.u[base + b + g];  // the draw's uniform, used by the finishing slice
   const int n = first_rejection<T, ACCEPT, false>(a, b, base, g, s_cz, nullptr, &s_n);
   if (s == 0) {
     for (int i = threadIdx.x; i < n; i += kSeqThreads) a.emitted[base + b + i] = a.ids[base + i];
@@ -1409,12 +1414,13 @@ __global__ __launch_bounds__(kSeqThreads) void k_draw_part(Args a) {
     rZ = __hip_atomic_load(src + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   }
   if constexpr (kTab) {
-    if (tab_finish(a, b, base, g, n, zr * exp2(cr), sT, -1, ns, rD, rQ, rZ)) return;
+    if (tab_finish(a, b, base, g, n, zr * exp2(cr), sT, -1, ns, rD, rQ, rZ, uf)) return;
     exp_table_init(s_tab);
     __syncthreads();  // s_tab
     final_draw<uint16_t, true>(a, b, base, g, n, cr, zr, s_tab);
   } else {
-    draw_finish<float, true>(a, b, base, g, n, n < g ? cr : 0.0, n < g ? zr : 0.0, s_tab, -1, ns, sw, rD, rQ, rZ);
+    draw_finish<float, true>(a, b, base, g, n, n < g ? cr : 0.0, n < g ? zr : 0.0, s_tab, -1, ns, sw, rD, rQ, rZ,
+                             uf);
   }
 }
 
@@ -1679,7 +1685,7 @@ __device__ __forceinline__ void team_barrier(int* cnt, int& target, int* err) {
 // Ends with a team barrier, after which the team's LDS may be reused.
 __device__ __forceinline__ void team_finish(const Args& a, int b, const double* sT, double rD, int sw, int tw,
                                             double (*s_wt)[kTeamWaves], int* s_cand, int* s_last, int* cnt,
-                                            int& target) {
+                                            int& target, float uf) {
   const int lane = threadIdx.x & 63;
   const int V = a.V;
   const int tlo = a.tlo, tsent = a.thi + 1 - a.tlo;
@@ -1687,7 +1693,6 @@ __device__ __forceinline__ void team_finish(const Args& a, int b, const double* 
   const bool live = lane < kSeqWaves;
   const double wgt = live ? rD : 0.0;
   const double Z64 = wave_sum_dpp(wgt);
-  const float uf = a.u[b];
   const double t = static_cast<double>(uf) * Z64;
   const double inc = wave_incl_scan_dpp(wgt);
   const unsigned long long cross = __ballot(live && inc > t);
@@ -1798,6 +1803,7 @@ __global__ __launch_bounds__(kSeqThreads) void k_sample_rows(Args a) {
     int target = 0;
     for (int b = blockIdx.x + team * gridDim.x; b < a.B; b += kTeams * gridDim.x) {
       if (tw == 0 && lane == 0) a.acc[b] = 0;
+      const float uf = a.u[b];  // loaded before the sweep, used after it
       // this wave's two sub-regions of the row: tw and tw + kTeamWaves
 #pragma unroll
       for (int h = 0; h < kTeams; ++h) {
@@ -1818,7 +1824,7 @@ __global__ __launch_bounds__(kSeqThreads) void k_sample_rows(Args a) {
         team_barrier(&s_cnt[team], target, a.err);  // s_rs[team] is read
         continue;
       }
-      team_finish(a, b, sT, rD, sw, tw, s_wt[team], &s_cand[team], &s_last[team], &s_cnt[team], target);
+      team_finish(a, b, sT, rD, sw, tw, s_wt[team], &s_cand[team], &s_last[team], &s_cnt[team], target, uf);
     }
     __syncthreads();  // both teams are done; marked rows are visible to the workgroup
     if (s_nfb == 0) return;
