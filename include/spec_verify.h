@@ -190,6 +190,67 @@ int spec_verify_set_path(spec_verify_ctx *ctx, int mode);
 int spec_verify_last_path(const spec_verify_ctx *ctx);
 
 /*
+ * Vocabulary-parallel verification, one shard's part. The accept rule, the first
+ * rejection and the draws are those of spec_verify_run ("Speculative Decoding",
+ * atonlee.tistory.com/330, ch.3; "Fast Inference from Transformers via Speculative
+ * Decoding" notes, 방법론 상세, 단계 3); only where the sums over the vocabulary are
+ * taken moves. The vocabulary [0, vocab_total) is cut into `shards` contiguous column
+ * ranges, shard k holding ids [bounds[k], bounds[k + 1]). A device that holds shard k
+ * passes only its columns: logits [sum(gamma_b + 1), W_k] and q [sum gamma_b, W_k],
+ * row-major with row pitch W_k = bounds[k + 1] - bounds[k], which must equal the
+ * context's vocab. Batch, gamma, cu_gamma, temperature, draft ids and uniforms are those
+ * of spec_verify_run and the same on every shard. A round is three calls per shard, with
+ * two all-gathers between them (done by the caller, e.g. over RCCL; each record array
+ * is gathered in shard order into one contiguous array):
+ *   1. spec_vshard_rows writes `rec`: one 16-byte record per judged row (T > 0: the
+ *      sum(gamma_b) draft rows; T == 0: those, then the B bonus rows), holding this
+ *      shard's softmax state of the row and, on the shard owning the draft id, the id's
+ *      logit and q entry (T == 0: the row's max and its lowest global index).
+ *      All-gather -> rec_all [shards][records].
+ *   2. spec_vshard_decide merges the records in shard order, so every shard takes the
+ *      same decisions. It writes accepted_count, the accepted tokens and p_draft (T == 0:
+ *      every output, and step 3 does nothing). T > 0: it then sweeps this shard's columns
+ *      of the drawn row and writes `part` (fp64 [B][3], this shard's totals) and `local`
+ *      (fp64 [B][52], kept on this device for step 3). All-gather part ->
+ *      part_all [shards][B][3].
+ *   3. spec_vshard_finish finds the shard whose columns hold each sequence's drawn
+ *      token (the last shard when no column has weight). Only that shard writes
+ *      emitted_tokens[n_b], the -1 padding after it and residual_sum[b]; the others
+ *      leave those entries untouched, so a final exchange (or one shared buffer) gives
+ *      every device the outputs.
+ * The results are those of spec_verify_run on the whole vocabulary, up to the rounding
+ * of the merged sums.
+ *   sh         host struct: vocab_total, shards (1..64), shard (this device's index),
+ *              bounds (host int32 [shards + 1], bounds[0] = 0, increasing,
+ *              bounds[shards] = vocab_total).
+ *   rec, rec_all, part, part_all, local: caller-owned device buffers of the sizes above.
+ * Ownership, streams and the sticky data flag are as for spec_verify_run (ids are
+ * checked against vocab_total); nothing is allocated and nothing synchronizes.
+ * Errors: SV_EINVAL (NULL ctx, description or required pointer; bad bounds; a shard
+ * width that differs from the context's vocab; the checks of spec_verify_run), SV_EHIP.
+ */
+typedef struct spec_vshard {
+  int vocab_total;
+  int shards;
+  int shard;
+  const int32_t *bounds;
+} spec_vshard;
+int spec_vshard_rows(spec_verify_ctx *ctx, void *hip_stream, const spec_vshard *sh, int batch,
+                     int gamma, const int32_t *cu_gamma, int total_draft_rows, float temperature,
+                     const void *logits, const float *q, const int32_t *draft_ids, void *rec);
+int spec_vshard_decide(spec_verify_ctx *ctx, void *hip_stream, const spec_vshard *sh, int batch,
+                       int gamma, const int32_t *cu_gamma, int total_draft_rows, float temperature,
+                       const void *logits, const float *q, const int32_t *draft_ids,
+                       const float *uniforms, const void *rec_all, int32_t *accepted_count,
+                       int32_t *emitted_tokens, float *residual_sum, float *p_draft, double *part,
+                       double *local);
+int spec_vshard_finish(spec_verify_ctx *ctx, void *hip_stream, const spec_vshard *sh, int batch,
+                       int gamma, const int32_t *cu_gamma, int total_draft_rows, float temperature,
+                       const void *logits, const float *q, const float *uniforms,
+                       const double *part_all, const double *local, int32_t *emitted_tokens,
+                       float *residual_sum);
+
+/*
  * Sampling one token per row from a given distribution: the draw of verification on
  * its own (decoding with the target alone, x ~ p, or drawing drafts, x ~ q), following
  * the draw's rule: t = u * sum(w) over the row's weights w, the token is the first id

@@ -16,5 +16,7 @@ from .binding import (  # noqa: F401
     spec_verify_destroy, spec_verify_kernel_times, spec_verify_last_error, spec_verify_last_path,
     spec_verify_run, spec_verify_set_path, spec_verify_set_timing, spec_verify_set_timing_stride,
     spec_verify_status, spec_sample_run, spec_verify_run_onehot, spec_ngram_propose, spec_adapt_gamma,
+    spec_vshard_rows, spec_vshard_decide, spec_vshard_finish, vshard_desc, VShardDesc,
+    VSHARD_REC_BYTES, VSHARD_PART_DOUBLES, VSHARD_LOCAL_DOUBLES,
 )
-from .verifier import Verifier, VerifyOutputs  # noqa: F401
+from .verifier import VocabShard, Verifier, VerifyOutputs  # noqa: F401

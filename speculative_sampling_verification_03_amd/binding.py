@@ -31,7 +31,7 @@ EXPORTED = (
     "spec_verify_last_error", "spec_verify_destroy", "spec_verify_set_timing",
     "spec_verify_kernel_times", "spec_verify_check_args", "spec_verify_set_path", "spec_verify_set_timing_stride",
     "spec_verify_last_path", "spec_sample_run", "spec_verify_run_onehot", "spec_ngram_propose",
-    "spec_adapt_gamma",
+    "spec_adapt_gamma", "spec_vshard_rows", "spec_vshard_decide", "spec_vshard_finish",
 )
 
 
@@ -42,6 +42,24 @@ class SpecVerifyError(RuntimeError):
 
 
 _lib = None
+
+# Sizes of the vocabulary-shard exchange records (include/spec_verify.h).
+VSHARD_REC_BYTES = 16      # per judged row
+VSHARD_PART_DOUBLES = 3    # per sequence, exchanged
+VSHARD_LOCAL_DOUBLES = 52  # per sequence, kept on the shard's device
+
+
+class VShardDesc(ctypes.Structure):
+    """struct spec_vshard: vocab_total, shards, shard, bounds (host int32 [shards + 1])."""
+    _fields_ = [("vocab_total", ctypes.c_int), ("shards", ctypes.c_int), ("shard", ctypes.c_int),
+                ("bounds", ctypes.POINTER(ctypes.c_int32))]
+
+
+def vshard_desc(bounds, shard: int):
+    """A spec_vshard for shard `shard` of the column bounds `bounds` (a sequence of ints);
+    returns the struct and the array it points to (keep both alive)."""
+    arr = (ctypes.c_int32 * len(bounds))(*[int(x) for x in bounds])
+    return VShardDesc(int(bounds[-1]), len(bounds) - 1, int(shard), arr), arr
 
 
 def load_library(path: Optional[str] = None) -> ctypes.CDLL:
@@ -78,6 +96,14 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.spec_ngram_propose.restype = i32
     lib.spec_adapt_gamma.argtypes = [vp, vp, i32, vp, vp, vp, i32, i32, i32, vp]
     lib.spec_adapt_gamma.restype = i32
+    lib.spec_vshard_rows.argtypes = [vp, vp, ctypes.POINTER(VShardDesc), i32, i32, vp, i32, f32, vp, vp, vp, vp]
+    lib.spec_vshard_rows.restype = i32
+    lib.spec_vshard_decide.argtypes = [vp, vp, ctypes.POINTER(VShardDesc), i32, i32, vp, i32, f32, vp, vp, vp,
+                                       vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.spec_vshard_decide.restype = i32
+    lib.spec_vshard_finish.argtypes = [vp, vp, ctypes.POINTER(VShardDesc), i32, i32, vp, i32, f32, vp, vp, vp,
+                                       vp, vp, vp, vp]
+    lib.spec_vshard_finish.restype = i32
     lib.spec_sample_run.argtypes = [vp, vp, i32, i32, f32, vp, vp, vp]
     lib.spec_sample_run.restype = i32
     lib.spec_verify_set_timing_stride.argtypes = [vp, i32]
@@ -144,6 +170,40 @@ def spec_verify_run_onehot(ctx: int, stream, batch: int, gamma: int, cu_gamma, t
         ctx, _stream(stream), batch, gamma, _ptr(cu_gamma), total_draft_rows, float(temperature),
         _ptr(logits), _ptr(draft_ids), _ptr(uniforms), _ptr(accepted_count), _ptr(emitted_tokens),
         _ptr(residual_sum), _ptr(p_draft))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, _msg(ctx))
+
+
+def spec_vshard_rows(ctx: int, stream, desc, batch: int, gamma: int, cu_gamma, total_draft_rows: int,
+                     temperature: float, logits, q, draft_ids, rec) -> None:
+    """Step 1 of vocabulary-parallel verification on one shard (records of its columns)."""
+    rc = load_library().spec_vshard_rows(ctx, _stream(stream), ctypes.byref(desc), batch, gamma, _ptr(cu_gamma),
+                                         total_draft_rows, float(temperature), _ptr(logits), _ptr(q),
+                                         _ptr(draft_ids), _ptr(rec))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, _msg(ctx))
+
+
+def spec_vshard_decide(ctx: int, stream, desc, batch: int, gamma: int, cu_gamma, total_draft_rows: int,
+                       temperature: float, logits, q, draft_ids, uniforms, rec_all, accepted_count,
+                       emitted_tokens, residual_sum, p_draft, part, local) -> None:
+    """Step 2: the decisions from every shard's records, and this shard's draw sums."""
+    rc = load_library().spec_vshard_decide(
+        ctx, _stream(stream), ctypes.byref(desc), batch, gamma, _ptr(cu_gamma), total_draft_rows,
+        float(temperature), _ptr(logits), _ptr(q), _ptr(draft_ids), _ptr(uniforms), _ptr(rec_all),
+        _ptr(accepted_count), _ptr(emitted_tokens), _ptr(residual_sum), _ptr(p_draft), _ptr(part), _ptr(local))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, _msg(ctx))
+
+
+def spec_vshard_finish(ctx: int, stream, desc, batch: int, gamma: int, cu_gamma, total_draft_rows: int,
+                       temperature: float, logits, q, uniforms, part_all, local, emitted_tokens,
+                       residual_sum) -> None:
+    """Step 3: the drawn token, written by the shard that owns it."""
+    rc = load_library().spec_vshard_finish(
+        ctx, _stream(stream), ctypes.byref(desc), batch, gamma, _ptr(cu_gamma), total_draft_rows,
+        float(temperature), _ptr(logits), _ptr(q), _ptr(uniforms), _ptr(part_all), _ptr(local),
+        _ptr(emitted_tokens), _ptr(residual_sum))
     if rc != SV_OK:
         raise SpecVerifyError(rc, _msg(ctx))
 

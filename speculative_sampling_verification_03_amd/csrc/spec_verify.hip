@@ -162,25 +162,13 @@ __device__ __forceinline__ bool accept_test(int x, float lx, float qx, float uu,
 }
 
 // ============================================================== step 1
-template <typename T, bool ALIGNED, bool RAGGED, bool ACCEPT>
-__global__ __launch_bounds__(kThreads) void k_rowstats(Args a) {
-  __shared__ float s_c[kWaves], s_z[kWaves];
-  const int d = blockIdx.x / a.split, k = blockIdx.x - d * a.split;
-  const int b = RAGGED ? seq_of_row(a.cu, a.B, d) : d / a.gamma;
-  const T* row = static_cast<const T*>(a.logits) + static_cast<size_t>(d + b) * a.V;
-  // operands of the accept test, issued first so their latency hides under the stream
-  int x = -1;
-  float lx = 0.f, qx = 0.f, uu = 0.f;
-  if (ACCEPT && threadIdx.x == 0) {
-    x = a.ids[d];
-    uu = a.u[d + b];
-    if (x >= 0 && x < a.V) {
-      lx = load_one(row, x);
-      qx = a.onehot ? 1.f : a.q[static_cast<size_t>(d) * a.V + x];
-    }
-  }
-  const int lo = k * a.span, hi = min(a.V, lo + a.span);
-  const float k2 = a.k2;
+// Base-2 softmax state of entries [lo, hi) of one row over a kThreads block: c = the
+// scaled max (max(l) * k2, clamped to the fp32 range) and z = sum 2^(l k2 - c), kept per
+// thread with a running max, merged over the wave and then the block. Thread 0 returns
+// the block's (C, Z); s_c, s_z are kWaves-entry LDS scratch.
+template <typename T, bool ALIGNED>
+__device__ __forceinline__ void block_row_lse(const T* row, int lo, int hi, float k2, float* s_c, float* s_z,
+                                              float& C, float& Z) {
   float m = -FLT_MAX, c = -FLT_MAX;  // running max of l and its scaled value
   float s[kGroup];
 #pragma unroll
@@ -243,29 +231,17 @@ __global__ __launch_bounds__(kThreads) void k_rowstats(Args a) {
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    float C = s_c[0], Z = s_z[0];
+    C = s_c[0];
+    Z = s_z[0];
     for (int i = 1; i < kWaves; ++i) lse2_merge(C, Z, s_c[i], s_z[i]);
-    a.p1[blockIdx.x] = RowStat{C, Z};
-    if (ACCEPT) {
-      double px;
-      a.accept[d] = accept_test(x, lx, qx, uu, C, Z, a, px) ? 1 : 0;
-      if (a.pdraft) a.pdraft[d] = static_cast<float>(px);
-    }
   }
 }
 
-// Greedy twin: max raw logit of one split of one draft row and its lowest index; an
-// unsplit row also records whether its draft equals that argmax.
-template <typename T, bool ALIGNED, bool RAGGED, bool ACCEPT>
-__global__ __launch_bounds__(kThreads) void k_rowargmax(Args a) {
-  __shared__ float s_v[kWaves];
-  __shared__ int s_i[kWaves];
-  const int d = blockIdx.x / a.split, k = blockIdx.x - d * a.split;
-  const int b = RAGGED ? seq_of_row(a.cu, a.B, d) : d / a.gamma;
-  const T* row = static_cast<const T*>(a.logits) + static_cast<size_t>(d + b) * a.V;
-  int x = -1;
-  if (ACCEPT && threadIdx.x == 0) x = a.ids[d];
-  const int lo = k * a.span, hi = min(a.V, lo + a.span);
+// Max raw logit of entries [lo, hi) of one row and its lowest index, over a kThreads
+// block; thread 0 returns them. A range of -inf (or NaN) entries yields its first index.
+template <typename T, bool ALIGNED>
+__device__ __forceinline__ void block_row_argmax(const T* row, int lo, int hi, float* s_v, int* s_i, float& Vout,
+                                                 int& Iout) {
   float bv = -INFINITY;
   int bi = INT_MAX;
   if (ALIGNED) {
@@ -319,9 +295,58 @@ __global__ __launch_bounds__(kThreads) void k_rowargmax(Args a) {
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    float V = s_v[0];
-    int I = s_i[0];
-    for (int i = 1; i < kWaves; ++i) argmax_merge(V, I, s_v[i], s_i[i]);
+    Vout = s_v[0];
+    Iout = s_i[0];
+    for (int i = 1; i < kWaves; ++i) argmax_merge(Vout, Iout, s_v[i], s_i[i]);
+  }
+}
+
+template <typename T, bool ALIGNED, bool RAGGED, bool ACCEPT>
+__global__ __launch_bounds__(kThreads) void k_rowstats(Args a) {
+  __shared__ float s_c[kWaves], s_z[kWaves];
+  const int d = blockIdx.x / a.split, k = blockIdx.x - d * a.split;
+  const int b = RAGGED ? seq_of_row(a.cu, a.B, d) : d / a.gamma;
+  const T* row = static_cast<const T*>(a.logits) + static_cast<size_t>(d + b) * a.V;
+  // operands of the accept test, issued first so their latency hides under the stream
+  int x = -1;
+  float lx = 0.f, qx = 0.f, uu = 0.f;
+  if (ACCEPT && threadIdx.x == 0) {
+    x = a.ids[d];
+    uu = a.u[d + b];
+    if (x >= 0 && x < a.V) {
+      lx = load_one(row, x);
+      qx = a.onehot ? 1.f : a.q[static_cast<size_t>(d) * a.V + x];
+    }
+  }
+  const int lo = k * a.span, hi = min(a.V, lo + a.span);
+  float C, Z;
+  block_row_lse<T, ALIGNED>(row, lo, hi, a.k2, s_c, s_z, C, Z);
+  if (threadIdx.x == 0) {
+    a.p1[blockIdx.x] = RowStat{C, Z};
+    if (ACCEPT) {
+      double px;
+      a.accept[d] = accept_test(x, lx, qx, uu, C, Z, a, px) ? 1 : 0;
+      if (a.pdraft) a.pdraft[d] = static_cast<float>(px);
+    }
+  }
+}
+
+// Greedy twin: max raw logit of one split of one draft row and its lowest index; an
+// unsplit row also records whether its draft equals that argmax.
+template <typename T, bool ALIGNED, bool RAGGED, bool ACCEPT>
+__global__ __launch_bounds__(kThreads) void k_rowargmax(Args a) {
+  __shared__ float s_v[kWaves];
+  __shared__ int s_i[kWaves];
+  const int d = blockIdx.x / a.split, k = blockIdx.x - d * a.split;
+  const int b = RAGGED ? seq_of_row(a.cu, a.B, d) : d / a.gamma;
+  const T* row = static_cast<const T*>(a.logits) + static_cast<size_t>(d + b) * a.V;
+  int x = -1;
+  if (ACCEPT && threadIdx.x == 0) x = a.ids[d];
+  const int lo = k * a.span, hi = min(a.V, lo + a.span);
+  float V;
+  int I;
+  block_row_argmax<T, ALIGNED>(row, lo, hi, s_v, s_i, V, I);
+  if (threadIdx.x == 0) {
     a.p1[blockIdx.x] = RowStat{V, __int_as_float(I)};
     if (ACCEPT) {
       // accept iff the draft equals the target argmax ([P1] ch.3 greedy; [P4])
@@ -595,6 +620,178 @@ __device__ __forceinline__ void draw_sweep(const T* lrow, const float* qrow, int
   }
 }
 
+// What the search of a draw decided (wave-uniform; published through LDS).
+struct DrawSel {
+  double t;      // the target: u S (residual), u Z64 (from p) or u (Z64 - e(x_n))
+  double P;      // the prefix before the selected region
+  double Z64;    // sum of e over the row
+  double delta;  // (Z64 - Zq) / Z64, residual only
+  double S;      // residual mass (1 - p(x_n) for one-hot drafts; 0 for a bonus row)
+  double ref;    // reference of e = 2^(l k2 - ref / N) in exp2_tab units
+  int rs;        // selected region, -1 if no region has positive weight
+  int kind;      // 0: residual; 1: degenerate residual (S <= 0), draw from p; 2: from p; 3: p without x_n
+  int take_last; // no prefix crossed t (rounding, or u >= 1): the last positive entry
+  int excl;      // the entry removed from p (kind 3), else -1
+};
+
+// Weight of a region (wave 0, one region per lane) from draw_sweep's sums (v0, v1, v2),
+// given the row-wide values of the selection.
+__device__ __forceinline__ double region_weight(int kind, double v0, double v1, double v2, double Z64,
+                                                double delta, double ref, double KN, const double* s_tab) {
+  if (kind == 0) return v0 / Z64 - v1 * delta;
+  if (kind == 1) return v2;
+  return v0 > -INFINITY ? v1 * exp2_tab(v0 * KN - ref, s_tab) : 0.0;
+}
+
+// The region where prefix + the inclusive scan of wgt first exceeds t (lanes < ns),
+// else, or when `last` is set, the last region of positive weight; -1 if none. P
+// returns the prefix before the selected region.
+__device__ __forceinline__ int find_crossing(double wgt, bool live, double t, double prefix, bool last,
+                                             double& P, int& take_last) {
+  const double ex = wave_excl_scan(wgt);
+  const unsigned long long cross = last ? 0ull : __ballot(live && prefix + ex + wgt > t);
+  int rs = cross ? __ffsll(cross) - 1 : -1;
+  P = prefix + __shfl(ex, rs < 0 ? 0 : rs);
+  take_last = last ? 1 : 0;
+  if (rs < 0) {
+    take_last = 1;
+    const unsigned long long pos = __ballot(live && wgt > 0.0);
+    rs = pos ? 63 - __clzll(pos) : -1;
+    P = rs < 0 ? prefix : prefix + __shfl(ex, rs);
+  }
+  return rs;
+}
+
+// The row-wide part of a draw's search (wave 0; lane r < ns holds region r's sums from
+// draw_sweep): totals, residual mass, target and the region where the prefix crosses it.
+// Raises the data flags of a non-finite normaliser or a uniform outside [0, 1).
+__device__ __forceinline__ DrawSel draw_select(const Args& a, bool qres, bool oh, bool excl_ok, int xn, float lxn,
+                                               int ns, int rw, double v0, double v1, double v2, double cr,
+                                               double Zq, float uf, const double* s_tab) {
+  const int lane = threadIdx.x & 63;
+  const double KN = kExpScale * a.k2d;
+  const double u = uf;
+  const bool live = lane < ns;
+  DrawSel d{};
+  d.excl = -1;
+  double wgt;
+  if (qres) {
+    d.Z64 = wave_sum(live ? v2 : 0.0);
+    d.delta = (d.Z64 - Zq) / d.Z64;
+    d.ref = kExpScale * cr;
+    wgt = live ? region_weight(0, v0, v1, v2, d.Z64, d.delta, d.ref, KN, s_tab) : 0.0;
+    d.S = wave_sum(wgt);
+    d.kind = d.S > 0.0 ? 0 : 1;
+    if (d.kind == 1) wgt = live ? v2 : 0.0;
+    d.t = d.kind == 0 ? u * d.S : u * d.Z64;
+  } else {
+    double M = live ? v0 : -INFINITY;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) M = fmax(M, __shfl_xor(M, o));
+    d.ref = M * KN;
+    wgt = live ? region_weight(2, v0, v1, v2, 0.0, 0.0, d.ref, KN, s_tab) : 0.0;
+    d.Z64 = wave_sum(wgt);
+    d.kind = 2;
+    d.t = u * d.Z64;
+    if (oh) {
+      // S = 1 - p(x_n); the region holding x_n loses e(x_n)
+      const double ex_n = excl_ok ? exp2_tab(fma(static_cast<double>(lxn), KN, -d.ref), s_tab) : 0.0;
+      d.S = (d.Z64 - ex_n) / d.Z64;
+      if (d.S > 0.0) {
+        d.kind = 3;
+        d.excl = excl_ok ? xn : -1;
+        if (excl_ok && live && lane == xn / rw) wgt = fmax(wgt - ex_n, 0.0);
+        d.t = u * wave_sum(live ? wgt : 0.0);
+      }
+    }
+  }
+  d.rs = find_crossing(wgt, live, d.t, 0.0, false, d.P, d.take_last);
+  if (lane == 0) {
+    if (!(d.Z64 > 0.0 && d.Z64 <= DBL_MAX)) atomicOr(a.err, SV_DATA_NONFINITE);
+    if (!(uf >= 0.f && uf < 1.f)) atomicOr(a.err, SV_DATA_UNIFORM);
+  }
+  return d;
+}
+
+// The block's re-sweep of entries [R0, R1) of a drawn row in passes of kPass entries
+// (wave w scans the w-th kIter entries of a pass, lane l owns 8 consecutive entries):
+// the first entry whose inclusive prefix (from sel.P) exceeds sel.t, else the last
+// entry of positive weight; -1 if there is none. KN = N k2. Every thread of the block
+// calls it and gets the result.
+template <typename T, bool ALIGNED>
+__device__ __forceinline__ int draw_resweep(const T* lrow, const float* qrow, int R0, int R1, const DrawSel& sel,
+                                            double Zq, double KN, const double* s_tab) {
+  __shared__ double s_wt[kSeqWaves];  // per-wave totals of a pass
+  __shared__ int s_wc[kSeqWaves], s_wl[kSeqWaves];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t linf = neg_inf_word<T>();
+  const int kind = sel.kind, excl = sel.excl;
+  const bool take_last = sel.take_last != 0;
+  const double t = sel.t, delta = sel.delta, ref = sel.ref;
+  const double invZ = 1.0 / sel.Z64;
+  double run = sel.P;
+  int cand = INT_MAX, lastpos = -1;
+  for (int p0 = R0; p0 < R1 && cand == INT_MAX; p0 += kPass) {
+    const int e = p0 + wave * kIter + lane * kGroup;
+    Raw<T> lr;
+    float x[kGroup], qv[kGroup];
+    load_raw<T, ALIGNED>(lrow, e, R1, lr, linf);
+    unpack(lr, x);
+    if (kind == 0) {
+      Raw<float> qr;
+      load_raw<float, ALIGNED>(qrow, e, R1, qr, 0u);
+      unpack(qr, qv);
+    }
+    double rv[kGroup];
+    double tot = 0.0;
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+      const double ev = exp2_tab(fma(static_cast<double>(x[j]), KN, -ref), s_tab);
+      double wv = ev;
+      if (kind == 0) {
+        const double w = fma(-static_cast<double>(qv[j]), Zq, ev);
+        wv = w > 0.0 ? w * invZ - static_cast<double>(qv[j]) * delta : 0.0;
+      }
+      if (e + j == excl) wv = 0.0;
+      rv[j] = wv;
+      tot += wv;
+    }
+    const double lex = wave_excl_scan(tot);
+    if (lane == 63) s_wt[wave] = lex + tot;
+    __syncthreads();
+    double acc = run;
+    for (int w = 0; w < wave; ++w) acc += s_wt[w];
+    acc += lex;
+    int c2 = INT_MAX, lp = -1;
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+      acc += rv[j];
+      if (!take_last && c2 == INT_MAX && acc > t) c2 = e + j;
+      if (rv[j] > 0.0) lp = e + j;
+    }
+    c2 = wave_min_int(c2);
+    lp = wave_max_int(lp);
+    if (lane == 0) {
+      s_wc[wave] = c2;
+      s_wl[wave] = lp;
+    }
+    __syncthreads();
+    int cm = INT_MAX, lm = -1;
+    double tsum = run;
+    for (int w = 0; w < kSeqWaves; ++w) {
+      cm = min(cm, s_wc[w]);
+      lm = max(lm, s_wl[w]);
+      tsum += s_wt[w];
+    }
+    cand = cm;
+    lastpos = max(lastpos, lm);
+    run = tsum;
+    __syncthreads();  // s_wt / s_wc / s_wl are rewritten by the next pass
+  }
+  return cand != INT_MAX ? cand : lastpos;
+}
+
 // The finish of the draw over ns <= 64 regions of width rw (region r covers
 // [r rw, min(V, (r + 1) rw))): lane r < ns of wave 0 holds region r's sums (v0, v1, v2)
 // from draw_sweep (the other lanes and waves are ignored). Wave 0 forms the totals and
@@ -607,12 +804,8 @@ template <typename T, bool ALIGNED>
 __device__ __forceinline__ void draw_finish(const Args& a, int b, int base, int g, int n, double cr, double Zq,
                                             const double* s_tab, int xn, int ns, int rw, double v0, double v1,
                                             double v2, float uf) {
-  __shared__ double s_wt[kSeqWaves];  // re-sweep: per-wave totals of a pass
-  __shared__ int s_wc[kSeqWaves], s_wl[kSeqWaves];
-  __shared__ double s_bc[6];  // search result: t, P (prefix before the region), Z64, delta, S, ref
-  __shared__ int s_bi[4];     // search result: region r*, kind, take_last, excluded id
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar
+  __shared__ DrawSel s_sel;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int V = a.V;
   const bool residual = n < g;
   // one-hot drafts: max(0, p - onehot(x_n)) is p with x_n removed, drawn like a bonus row
@@ -620,152 +813,24 @@ __device__ __forceinline__ void draw_finish(const Args& a, int b, int base, int 
   const bool qres = residual && !oh;
   const T* lrow = static_cast<const T*>(a.logits) + static_cast<size_t>(base + b + (residual ? n : g)) * V;
   const float* qrow = qres ? a.q + static_cast<size_t>(base + n) * V : nullptr;
-  const double KN = kExpScale * a.k2d;  // exp2_tab(l KN - N c) = 2^(l k2 - c)
-  const uint32_t linf = neg_inf_word<T>();
-
-  // ---- totals and the region where the inclusive prefix first exceeds t (wave 0,
-  // lane r holding region r)
   if (wave == 0) {
     if (oh && xn < 0) xn = a.ids[base + n];
     const bool excl_ok = oh && xn >= 0 && xn < V;  // an invalid id removes nothing
     const float lxn = excl_ok ? load_one(lrow, xn) : 0.f;
-    const double u = uf;
-    const bool live = lane < ns;
-    int kind;  // 0: residual; 1: degenerate residual (S <= 0), draw from p; 2: from p; 3: p without x_n
-    int excl = -1;
-    double Z64, S = 0.0, delta = 0.0, ref, t, wgt;
-    if (qres) {
-      Z64 = wave_sum(live ? v2 : 0.0);
-      delta = (Z64 - Zq) / Z64;
-      wgt = live ? v0 / Z64 - v1 * delta : 0.0;
-      S = wave_sum(wgt);
-      kind = S > 0.0 ? 0 : 1;
-      if (kind == 1) wgt = live ? v2 : 0.0;
-      t = kind == 0 ? u * S : u * Z64;
-      ref = kExpScale * cr;
-    } else {
-      const double mr = live ? v0 : -INFINITY;
-      double M = mr;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) M = fmax(M, __shfl_xor(M, o));
-      ref = M * KN;
-      wgt = mr > -INFINITY ? v1 * exp2_tab(mr * KN - ref, s_tab) : 0.0;
-      Z64 = wave_sum(wgt);
-      kind = 2;
-      t = u * Z64;
-      if (oh) {
-        // S = 1 - p(x_n); the region holding x_n loses e(x_n)
-        const double ex_n = excl_ok ? exp2_tab(fma(static_cast<double>(lxn), KN, -ref), s_tab) : 0.0;
-        S = (Z64 - ex_n) / Z64;
-        if (S > 0.0) {
-          kind = 3;
-          excl = excl_ok ? xn : -1;
-          if (excl_ok && live && lane == xn / rw) wgt = fmax(wgt - ex_n, 0.0);
-          t = u * wave_sum(live ? wgt : 0.0);
-        }
-      }
-    }
-    const double ex = wave_excl_scan(wgt);
-    const unsigned long long cross = __ballot(live && ex + wgt > t);
-    int rs = cross ? __ffsll(cross) - 1 : -1;
-    double P = __shfl(ex, rs < 0 ? 0 : rs);
-    int take_last = 0;
-    if (rs < 0) {  // no crossing (rounding, or u >= 1): last positive-weight token
-      take_last = 1;
-      const unsigned long long pos = __ballot(live && wgt > 0.0);
-      rs = pos ? 63 - __clzll(pos) : -1;
-      P = 0.0;
-    }
-    if (lane == 0) {
-      if (!(Z64 > 0.0 && Z64 <= DBL_MAX)) atomicOr(a.err, SV_DATA_NONFINITE);
-      if (!(uf >= 0.f && uf < 1.f)) atomicOr(a.err, SV_DATA_UNIFORM);
-      s_bc[0] = t;
-      s_bc[1] = P;
-      s_bc[2] = Z64;
-      s_bc[3] = delta;
-      s_bc[4] = S;
-      s_bc[5] = ref;
-      s_bi[0] = rs;
-      s_bi[1] = kind;
-      s_bi[2] = take_last;
-      s_bi[3] = excl;
-    }
+    const DrawSel d = draw_select(a, qres, oh, excl_ok, xn, lxn, ns, rw, v0, v1, v2, cr, Zq, uf, s_tab);
+    if ((threadIdx.x & 63) == 0) s_sel = d;
   }
   __syncthreads();
-  const double t = s_bc[0], Z64 = s_bc[2], delta = s_bc[3], S = s_bc[4], ref = s_bc[5];
-  const int rs = s_bi[0], kind = s_bi[1], excl = s_bi[3];
-  const bool take_last = s_bi[2] != 0;
-
-  // ---- re-sweep of region r* in passes of kPass entries: wave w scans the w-th kIter
-  // entries of a pass, lane l owns 8 consecutive entries
+  const DrawSel sel = s_sel;
   int tok = V - 1;
-  if (rs >= 0) {
-    const int R0 = min(V, rs * rw), R1 = min(V, R0 + rw);
-    const double invZ = 1.0 / Z64;
-    double run = s_bc[1];
-    int cand = INT_MAX, lastpos = -1;
-    for (int p0 = R0; p0 < R1 && cand == INT_MAX; p0 += kPass) {
-      const int e = p0 + wave * kIter + lane * kGroup;
-      Raw<T> lr;
-      float x[kGroup], qv[kGroup];
-      load_raw<T, ALIGNED>(lrow, e, R1, lr, linf);
-      unpack(lr, x);
-      if (kind == 0) {
-        Raw<float> qr;
-        load_raw<float, ALIGNED>(qrow, e, R1, qr, 0u);
-        unpack(qr, qv);
-      }
-      double rv[kGroup];
-      double tot = 0.0;
-#pragma unroll
-      for (int j = 0; j < kGroup; ++j) {
-        const double ev = exp2_tab(fma(static_cast<double>(x[j]), KN, -ref), s_tab);
-        double wv = ev;
-        if (kind == 0) {
-          const double w = fma(-static_cast<double>(qv[j]), Zq, ev);
-          wv = w > 0.0 ? w * invZ - static_cast<double>(qv[j]) * delta : 0.0;
-        }
-        if (e + j == excl) wv = 0.0;
-        rv[j] = wv;
-        tot += wv;
-      }
-      const double lex = wave_excl_scan(tot);
-      if (lane == 63) s_wt[wave] = lex + tot;
-      __syncthreads();
-      double acc = run;
-      for (int w = 0; w < wave; ++w) acc += s_wt[w];
-      acc += lex;
-      int c2 = INT_MAX, lp = -1;
-#pragma unroll
-      for (int j = 0; j < kGroup; ++j) {
-        acc += rv[j];
-        if (!take_last && c2 == INT_MAX && acc > t) c2 = e + j;
-        if (rv[j] > 0.0) lp = e + j;
-      }
-      c2 = wave_min_int(c2);
-      lp = wave_max_int(lp);
-      if (lane == 0) {
-        s_wc[wave] = c2;
-        s_wl[wave] = lp;
-      }
-      __syncthreads();
-      int cm = INT_MAX, lm = -1;
-      double tsum = run;
-      for (int w = 0; w < kSeqWaves; ++w) {
-        cm = min(cm, s_wc[w]);
-        lm = max(lm, s_wl[w]);
-        tsum += s_wt[w];
-      }
-      cand = cm;
-      lastpos = max(lastpos, lm);
-      run = tsum;
-      __syncthreads();  // s_wt / s_wc / s_wl are rewritten by the next pass
-    }
-    tok = cand != INT_MAX ? cand : (lastpos >= 0 ? lastpos : V - 1);
+  if (sel.rs >= 0) {
+    const int R0 = min(V, sel.rs * rw), R1 = min(V, R0 + rw);
+    const int r = draw_resweep<T, ALIGNED>(lrow, qrow, R0, R1, sel, Zq, kExpScale * a.k2d, s_tab);
+    if (r >= 0) tok = r;
   }
   if (threadIdx.x == 0) {
     a.emitted[base + b + n] = tok;
-    a.rsum[b] = residual ? static_cast<float>(S) : 0.f;
+    a.rsum[b] = residual ? static_cast<float>(sel.S) : 0.f;
   }
   for (int i = n + 1 + threadIdx.x; i <= g; i += kSeqThreads) a.emitted[base + b + i] = -1;
 }
@@ -1422,6 +1487,278 @@ __global__ __launch_bounds__(kSeqThreads) void k_draw_part(Args a) {
     draw_finish<float, true>(a, b, base, g, n, n < g ? cr : 0.0, n < g ? zr : 0.0, s_tab, -1, ns, sw, rD, rQ, rZ,
                              uf);
   }
+}
+
+// ============================================================== vocabulary-parallel verification
+// One shard's part of a round when the vocabulary is cut into G contiguous column
+// ranges, one per device: the rule ([P1] ch.3; [P3] 단계 3) is unchanged, only where
+// the sums are taken moves. Shard k holds columns [vb[k], vb[k+1]) of every logits and
+// q row. A round takes three steps per shard, with an all-gather of small records
+// between them:
+//   k_vs_rows:   per judged row, this shard's base-2 (c, z) over its columns (greedy: the
+//                max and its lowest global index, bonus rows included) and, on the shard
+//                that owns the draft id, l(x) and q(x): one 16-byte record per row;
+//   k_vs_decide: merges the G records of each row in shard order, so every shard takes
+//                the same decisions; writes the accepted count and tokens (greedy: every
+//                output), then sweeps its columns of the drawn row in 16 regions: their
+//                sums stay local, their total (24 bytes per sequence) is exchanged;
+//   k_vs_finish: from the G totals, the shard whose columns hold the drawn token (the
+//                last shard when no column has weight) searches its own regions,
+//                re-sweeps one of them and writes the token, the -1 padding and S.
+constexpr int kMaxShards = 64;
+constexpr int kLocStride = 4 + 3 * kSeqWaves;  // per sequence: (cr, Zq, n, -), then each region's sums
+struct ShardRec { float c, z, lx, qx; };
+static_assert(sizeof(ShardRec) == 16 && kLocStride == 52, "record sizes stated in spec_verify.h");
+struct VShard {
+  int G, me, nrec;            // shards, this shard, records per shard
+  int vb[kMaxShards + 1];     // column bounds of every shard
+  ShardRec* rec;              // k_vs_rows: this shard's records [nrec]
+  const ShardRec* all;        // k_vs_decide: every shard's records [G][nrec]
+  double* part;               // k_vs_decide: this shard's totals [B][3]
+  const double* part_all;     // k_vs_finish: every shard's totals [G][B][3]
+  double* loc;                // this shard's per-sequence state [B][kLocStride]
+};
+
+// The shard whose columns hold id x, or -1 (x outside the vocabulary).
+__device__ __forceinline__ int shard_of(const VShard& vs, int x) {
+  int own = -1;
+  for (int k = 0; k < vs.G; ++k)
+    if (x >= vs.vb[k] && x < vs.vb[k + 1]) own = k;
+  return own;
+}
+
+// Step 1: one kThreads workgroup per record. Records 0..R-1 are the draft rows; at T = 0
+// records R..R+B-1 are the bonus rows. a.V is this shard's width.
+template <typename T, bool ALIGNED, bool RAGGED, bool GREEDY>
+__global__ __launch_bounds__(kThreads) void k_vs_rows(Args a, VShard vs) {
+  __shared__ float s_c[kWaves], s_z[kWaves];
+  __shared__ int s_i[kWaves];
+  const int r = blockIdx.x;
+  int b, t;
+  if (r < a.R) {
+    b = RAGGED ? seq_of_row(a.cu, a.B, r) : r / a.gamma;
+    t = r + b;
+  } else {  // the bonus row of sequence r - R
+    b = r - a.R;
+    const int c1 = RAGGED ? a.cu[b + 1] : (b + 1) * a.gamma;
+    if (RAGGED && !(c1 >= 0 && c1 <= a.R)) {  // malformed offsets, flagged by k_vs_decide
+      if (threadIdx.x == 0) vs.rec[r] = ShardRec{-INFINITY, __int_as_float(INT_MAX), 0.f, 0.f};
+      return;
+    }
+    t = c1 + b;
+  }
+  const T* row = static_cast<const T*>(a.logits) + static_cast<size_t>(t) * a.V;
+  const int v0 = vs.vb[vs.me];
+  if constexpr (GREEDY) {
+    float V;
+    int I;
+    block_row_argmax<T, ALIGNED>(row, 0, a.V, s_c, s_i, V, I);
+    if (threadIdx.x == 0) vs.rec[r] = ShardRec{V, __int_as_float(I == INT_MAX ? INT_MAX : I + v0), 0.f, 0.f};
+  } else {
+    float lx = 0.f, qx = 0.f;
+    if (threadIdx.x == 0) {  // the accept operands, issued before the stream
+      const int x = a.ids[r];
+      if (x >= v0 && x - v0 < a.V) {
+        lx = load_one(row, x - v0);
+        qx = a.q[static_cast<size_t>(r) * a.V + (x - v0)];
+      }
+    }
+    float C, Z;
+    block_row_lse<T, ALIGNED>(row, 0, a.V, a.k2, s_c, s_z, C, Z);
+    if (threadIdx.x == 0) vs.rec[r] = ShardRec{C, Z, lx, qx};
+  }
+}
+
+// Step 2: one workgroup per sequence. a.V is the whole vocabulary (ids are checked
+// against it); the shard's width comes from vb.
+template <typename T, bool ALIGNED, bool RAGGED, bool GREEDY>
+__global__ __launch_bounds__(kSeqThreads) void k_vs_decide(Args a, VShard vs) {
+  __shared__ double s_tab[kExpN];
+  __shared__ float2 s_cz[kMaxGamma];
+  __shared__ int s_tok[kMaxGamma + 1];
+  __shared__ double s_reg[kSeqWaves][3];
+  __shared__ int s_n;
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  double* loc = GREEDY ? nullptr : vs.loc + static_cast<size_t>(b) * kLocStride;
+  int base, g;
+  if (!seq_geom<RAGGED>(a, b, base, g)) {
+    if (threadIdx.x == 0) {
+      atomicOr(a.err, SV_DATA_CU_GAMMA);
+      a.acc[b] = -1;
+      if (!GREEDY) {
+        loc[2] = -1.0;
+        for (int j = 0; j < 3; ++j) vs.part[static_cast<size_t>(b) * 3 + j] = 0.0;
+      }
+    }
+    return;
+  }
+  if (threadIdx.x == 0) s_n = g;
+  if constexpr (GREEDY) {
+    __syncthreads();
+    for (int i = threadIdx.x; i <= g; i += kSeqThreads) {
+      const int r = i < g ? base + i : a.R + b;
+      float V = -INFINITY;
+      int I = INT_MAX;
+      for (int k = 0; k < vs.G; ++k) {
+        const ShardRec e = vs.all[static_cast<size_t>(k) * vs.nrec + r];
+        argmax_merge(V, I, e.c, __float_as_int(e.z));
+      }
+      s_tok[i] = I;
+      if (i < g) {
+        // accept iff the draft equals the target argmax ([P1] ch.3 greedy; [P4])
+        const int x = a.ids[base + i];
+        if (bad_id(a, x)) atomicOr(a.err, SV_DATA_DRAFT_ID);
+        if (x != I) atomicMin(&s_n, i);
+      }
+    }
+    __syncthreads();
+    const int n = s_n;
+    for (int i = threadIdx.x; i <= g; i += kSeqThreads)
+      a.emitted[base + b + i] = i < n ? a.ids[base + i] : i == n ? s_tok[n] : -1;
+    if (threadIdx.x == 0) {
+      a.acc[b] = n;
+      a.rsum[b] = 0.f;
+    }
+  } else {
+    exp_table_init(s_tab);
+    __syncthreads();
+    for (int i = threadIdx.x; i < g; i += kSeqThreads) {
+      const int d = base + i;
+      const int x = a.ids[d];
+      const int own = shard_of(vs, x);
+      float C = -FLT_MAX, Z = 0.f, lx = 0.f, qx = 0.f;
+      for (int k = 0; k < vs.G; ++k) {
+        const ShardRec e = vs.all[static_cast<size_t>(k) * vs.nrec + d];
+        lse2_merge(C, Z, e.c, e.z);
+        if (k == own) {
+          lx = e.lx;
+          qx = e.qx;
+        }
+      }
+      s_cz[i] = make_float2(C, Z);
+      double px;
+      const bool acc = accept_test(x, lx, qx, a.u[d + b], C, Z, a, px);
+      if (a.pdraft) a.pdraft[d] = static_cast<float>(px);
+      if (!acc) atomicMin(&s_n, i);
+    }
+    __syncthreads();
+    const int n = s_n;
+    for (int i = threadIdx.x; i < n; i += kSeqThreads) a.emitted[base + b + i] = a.ids[base + i];
+    if (threadIdx.x == 0) a.acc[b] = n;
+    // this shard's columns of the drawn row: the residual at row n, else the bonus row g
+    const bool residual = n < g;
+    const int Vs = vs.vb[vs.me + 1] - vs.vb[vs.me];
+    const T* lrow = static_cast<const T*>(a.logits) + static_cast<size_t>(base + b + (residual ? n : g)) * Vs;
+    const float* qrow = residual ? a.q + static_cast<size_t>(base + n) * Vs : nullptr;
+    const double cr = residual ? static_cast<double>(s_cz[n].x) : 0.0;
+    const double Zq = residual ? static_cast<double>(s_cz[n].y) : 0.0;
+    const double KN = kExpScale * a.k2d;
+    const int rw = iter_width(Vs, kSeqWaves);
+    const int r0 = min(Vs, wave * rw), r1 = min(Vs, r0 + rw);
+    double s0, s1, s2;
+    draw_sweep<T, ALIGNED>(lrow, qrow, r0, r1, KN, kExpScale * cr, Zq, s_tab, s0, s1, s2);
+    if (lane == 0) {
+      s_reg[wave][0] = s0;
+      s_reg[wave][1] = s1;
+      s_reg[wave][2] = s2;
+      loc[4 + 3 * wave] = s0;
+      loc[5 + 3 * wave] = s1;
+      loc[6 + 3 * wave] = s2;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      loc[0] = cr;
+      loc[1] = Zq;
+      loc[2] = n;
+      double t0 = 0.0, t1 = 0.0, t2 = 0.0;
+      if (residual) {  // (D, Q, Zr) add up
+        for (int w = 0; w < kSeqWaves; ++w) {
+          t0 += s_reg[w][0];
+          t1 += s_reg[w][1];
+          t2 += s_reg[w][2];
+        }
+      } else {  // (max, sum below it): rescale each region to the shard's max
+        t0 = -INFINITY;
+        for (int w = 0; w < kSeqWaves; ++w) t0 = fmax(t0, s_reg[w][0]);
+        for (int w = 0; w < kSeqWaves; ++w)
+          if (s_reg[w][0] > -INFINITY) t1 += s_reg[w][1] * exp2_tab(s_reg[w][0] * KN - t0 * KN, s_tab);
+      }
+      double* p = vs.part + static_cast<size_t>(b) * 3;
+      p[0] = t0;
+      p[1] = t1;
+      p[2] = t2;
+    }
+  }
+}
+
+// Step 3: one workgroup per sequence; only the shard that owns the drawn token (or, with
+// no weight anywhere, the last shard) writes emitted[n], the -1 padding and S.
+template <typename T, bool ALIGNED, bool RAGGED>
+__global__ __launch_bounds__(kSeqThreads) void k_vs_finish(Args a, VShard vs) {
+  __shared__ double s_tab[kExpN];
+  __shared__ DrawSel s_sel;
+  __shared__ int s_own;
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int base, g;
+  if (!seq_geom<RAGGED>(a, b, base, g)) return;  // flagged by k_vs_decide
+  const double* loc = vs.loc + static_cast<size_t>(b) * kLocStride;
+  exp_table_init(s_tab);
+  const float uf = a.u[base + b + g];
+  const double cr = loc[0], Zq = loc[1];
+  const int n = static_cast<int>(loc[2]);
+  __syncthreads();  // s_tab
+  if (n < 0) return;
+  const bool residual = n < g;
+  const double KN = kExpScale * a.k2d;
+  if (wave == 0) {
+    const bool live = lane < vs.G;
+    double v0 = 0.0, v1 = 0.0, v2 = 0.0;
+    if (live) {
+      const double* p = vs.part_all + (static_cast<size_t>(lane) * a.B + b) * 3;
+      v0 = p[0];
+      v1 = p[1];
+      v2 = p[2];
+    }
+    // shards as regions: the one whose columns the prefix crosses t in
+    DrawSel d = draw_select(a, residual, false, false, -1, 0.f, vs.G, 1, v0, v1, v2, cr, Zq, uf, s_tab);
+    int own = d.rs < 0 ? (vs.me == vs.G - 1 ? 2 : 0) : d.rs == vs.me ? 1 : 0;
+    if (own == 1) {  // this shard's regions, from the prefix before the shard
+      const bool l2 = lane < kSeqWaves;
+      const double* lr = loc + 4 + 3 * (l2 ? lane : 0);
+      const double w = l2 ? region_weight(d.kind, lr[0], lr[1], lr[2], d.Z64, d.delta, d.ref, KN, s_tab) : 0.0;
+      double P;
+      int tl;
+      d.rs = find_crossing(w, l2, d.t, d.P, d.take_last != 0, P, tl);
+      d.P = P;
+      d.take_last = tl;
+    }
+    if (lane == 0) {
+      s_sel = d;
+      s_own = own;
+    }
+  }
+  __syncthreads();
+  if (s_own == 0) return;
+  const DrawSel sel = s_sel;
+  int tok = a.V - 1;
+  if (s_own == 1 && sel.rs >= 0) {
+    const int Vs = vs.vb[vs.me + 1] - vs.vb[vs.me];
+    const int rw = iter_width(Vs, kSeqWaves);
+    const T* lrow = static_cast<const T*>(a.logits) + static_cast<size_t>(base + b + (residual ? n : g)) * Vs;
+    const float* qrow = residual ? a.q + static_cast<size_t>(base + n) * Vs : nullptr;
+    const int R0 = min(Vs, sel.rs * rw), R1 = min(Vs, R0 + rw);
+    const int r = draw_resweep<T, ALIGNED>(lrow, qrow, R0, R1, sel, Zq, KN, s_tab);
+    if (r >= 0) tok = vs.vb[vs.me] + r;
+  }
+  if (threadIdx.x == 0) {
+    a.emitted[base + b + n] = tok;
+    a.rsum[b] = residual ? static_cast<float>(sel.S) : 0.f;
+  }
+  for (int i = n + 1 + threadIdx.x; i <= g; i += kSeqThreads) a.emitted[base + b + i] = -1;
 }
 
 // Pass 1: per row, z = sum 2^(l k2 - c) in fp32. Each wave takes its reference c from
@@ -2518,6 +2855,87 @@ int run_impl(spec_verify_ctx* ctx, void* hip_stream, int batch, int gamma, const
   ctx->last_path = fused ? SV_PATH_ONE_LAUNCH : SV_PATH_TWO_LAUNCH;
   return SV_OK;
 }
+
+// ---------------------------------------------------------------- vocabulary shards
+hipError_t launch_vs(const void* fn, unsigned grid, unsigned block, const Args& a, const VShard& vs,
+                     hipStream_t st) {
+  void* args[] = {const_cast<Args*>(&a), const_cast<VShard*>(&vs)};
+  return hipExtLaunchKernel(fn, dim3(grid), dim3(block), args, 0, st, nullptr, nullptr, 0);
+}
+
+// Checks shared by the three shard steps; fills a (a.V = this shard's width) and vs.
+// has_* name the pointers the step needs (the others count as present).
+int vshard_prepare(spec_verify_ctx* ctx, const spec_vshard* sh, int batch, int gamma, const int32_t* cu_gamma,
+                   int total_draft_rows, float temperature, const void* logits, bool has_q, bool has_ids,
+                   bool has_u, bool has_outputs, Args& a, VShard& vs) {
+  if (!ctx) return SV_EINVAL;
+  auto bad = [&](const char* m) {
+    set_msg(ctx->msg, sizeof(ctx->msg), m);
+    return SV_EINVAL;
+  };
+  if (!sh || !sh->bounds) return bad("the shard description or its bounds is NULL");
+  const int G = sh->shards;
+  if (G < 1 || G > kMaxShards) return bad("shards must be in [1, 64]");
+  if (sh->shard < 0 || sh->shard >= G) return bad("shard must be in [0, shards)");
+  if (sh->bounds[0] != 0 || sh->bounds[G] != sh->vocab_total) return bad("bounds must run from 0 to vocab_total");
+  for (int k = 0; k < G; ++k)
+    if (sh->bounds[k + 1] <= sh->bounds[k]) return bad("bounds must increase");
+  if (sh->bounds[sh->shard + 1] - sh->bounds[sh->shard] != ctx->V)
+    return bad("the context's vocab must equal this shard's width");
+  const int rc = spec_verify_check_args(ctx->V, ctx->dtype, ctx->max_batch, ctx->max_rows, ctx->max_gamma, batch,
+                                        gamma, cu_gamma != nullptr, total_draft_rows, temperature, logits != nullptr,
+                                        has_q, has_ids, has_u, has_outputs, has_outputs, has_outputs, ctx->msg,
+                                        sizeof(ctx->msg));
+  if (rc != SV_OK) return rc;
+  if (cu_gamma && batch > kMaxRaggedBatch) return bad("ragged batches (cu_gamma) are limited to 65536 sequences");
+  const bool greedy = temperature == 0.f;
+  a = Args{};
+  a.logits = logits;
+  a.cu = cu_gamma;
+  a.err = ctx->err;
+  a.B = batch;
+  a.gamma = cu_gamma ? -1 : gamma;
+  a.V = ctx->V;
+  a.R = total_draft_rows;
+  a.max_gamma = ctx->max_gamma;
+  a.tlo = 1;
+  a.thi = 0;
+  a.k2d = greedy ? 0.0 : 1.4426950408889634 / static_cast<double>(temperature);
+  a.k2 = static_cast<float>(a.k2d);
+  vs = VShard{};
+  vs.G = G;
+  vs.me = sh->shard;
+  vs.nrec = total_draft_rows + (greedy ? batch : 0);
+  for (int k = 0; k <= G; ++k) vs.vb[k] = sh->bounds[k];
+  if (static_cast<unsigned long long>(vs.nrec) * kThreads >= (1ull << 32)) return bad("launch grid too large");
+  return SV_OK;
+}
+
+bool vshard_aligned(const spec_verify_ctx* ctx, const void* logits, const float* q, bool greedy) {
+  return ctx->V % kGroup == 0 && reinterpret_cast<uintptr_t>(logits) % 16 == 0 &&
+         (greedy || reinterpret_cast<uintptr_t>(q) % 16 == 0);
+}
+
+// One template instance per (dtype, aligned, ragged, greedy).
+template <template <typename, bool, bool, bool> class K>
+const void* vs_pick(bool bf16, bool al, bool rg, bool gr) {
+#define SV_VS_K(T, A, R, G) reinterpret_cast<const void*>(K<T, A, R, G>::fn)
+  if (bf16) {
+    if (al) return rg ? (gr ? SV_VS_K(uint16_t, true, true, true) : SV_VS_K(uint16_t, true, true, false))
+                      : (gr ? SV_VS_K(uint16_t, true, false, true) : SV_VS_K(uint16_t, true, false, false));
+    return rg ? (gr ? SV_VS_K(uint16_t, false, true, true) : SV_VS_K(uint16_t, false, true, false))
+              : (gr ? SV_VS_K(uint16_t, false, false, true) : SV_VS_K(uint16_t, false, false, false));
+  }
+  if (al) return rg ? (gr ? SV_VS_K(float, true, true, true) : SV_VS_K(float, true, true, false))
+                    : (gr ? SV_VS_K(float, true, false, true) : SV_VS_K(float, true, false, false));
+  return rg ? (gr ? SV_VS_K(float, false, true, true) : SV_VS_K(float, false, true, false))
+            : (gr ? SV_VS_K(float, false, false, true) : SV_VS_K(float, false, false, false));
+#undef SV_VS_K
+}
+template <typename T, bool A, bool R, bool G> struct VsRows { static constexpr auto fn = &k_vs_rows<T, A, R, G>; };
+template <typename T, bool A, bool R, bool G> struct VsDecide { static constexpr auto fn = &k_vs_decide<T, A, R, G>; };
+template <typename T, bool A, bool R, bool G> struct VsFinish { static constexpr auto fn = &k_vs_finish<T, A, R>; };
+
 }  // namespace
 
 extern "C" {
@@ -2635,6 +3053,106 @@ int spec_verify_run_onehot(spec_verify_ctx* ctx, void* hip_stream, int batch, in
                   draft_ids, uniforms, accepted_count, emitted_tokens, residual_sum, p_draft);
 }
 
+
+int spec_vshard_rows(spec_verify_ctx* ctx, void* hip_stream, const spec_vshard* sh, int batch, int gamma,
+                     const int32_t* cu_gamma, int total_draft_rows, float temperature, const void* logits,
+                     const float* q, const int32_t* draft_ids, void* rec) {
+  Args a;
+  VShard vs;
+  const bool greedy = temperature == 0.f;
+  int rc = vshard_prepare(ctx, sh, batch, gamma, cu_gamma, total_draft_rows, temperature, logits, q != nullptr,
+                          draft_ids != nullptr, true, true, a, vs);
+  if (rc != SV_OK) return rc;
+  if (vs.nrec == 0) return SV_OK;
+  if (!rec) {
+    set_msg(ctx->msg, sizeof(ctx->msg), "rec is NULL");
+    return SV_EINVAL;
+  }
+  a.q = greedy ? nullptr : q;
+  a.ids = draft_ids;
+  vs.rec = static_cast<ShardRec*>(rec);
+  DeviceGuard guard(ctx->device);
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const void* fn = vs_pick<VsRows>(ctx->dtype == SV_BF16, vshard_aligned(ctx, logits, q, greedy), cu_gamma != nullptr,
+                                   greedy);
+  const hipError_t e = launch_vs(fn, static_cast<unsigned>(vs.nrec), kThreads, a, vs, st);
+  if (e != hipSuccess) return hip_fail(ctx, "kernel launch", e);
+  ctx->last_stream = st;
+  ctx->ran = true;
+  return SV_OK;
+}
+
+int spec_vshard_decide(spec_verify_ctx* ctx, void* hip_stream, const spec_vshard* sh, int batch, int gamma,
+                       const int32_t* cu_gamma, int total_draft_rows, float temperature, const void* logits,
+                       const float* q, const int32_t* draft_ids, const float* uniforms, const void* rec_all,
+                       int32_t* accepted_count, int32_t* emitted_tokens, float* residual_sum, float* p_draft,
+                       double* part, double* local) {
+  Args a;
+  VShard vs;
+  const bool greedy = temperature == 0.f;
+  int rc = vshard_prepare(ctx, sh, batch, gamma, cu_gamma, total_draft_rows, temperature, logits, q != nullptr,
+                          draft_ids != nullptr, uniforms != nullptr,
+                          accepted_count && emitted_tokens && residual_sum, a, vs);
+  if (rc != SV_OK) return rc;
+  if (batch == 0) return SV_OK;
+  if ((vs.nrec > 0 && !rec_all) || (!greedy && (!part || !local))) {
+    set_msg(ctx->msg, sizeof(ctx->msg), "rec_all, part or local is NULL");
+    return SV_EINVAL;
+  }
+  a.V = sh->vocab_total;  // ids are checked against the whole vocabulary
+  a.q = greedy ? nullptr : q;
+  a.ids = draft_ids;
+  a.u = greedy ? nullptr : uniforms;
+  a.acc = accepted_count;
+  a.emitted = emitted_tokens;
+  a.rsum = residual_sum;
+  a.pdraft = greedy ? nullptr : p_draft;
+  vs.all = static_cast<const ShardRec*>(rec_all);
+  vs.part = part;
+  vs.loc = local;
+  DeviceGuard guard(ctx->device);
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const void* fn = vs_pick<VsDecide>(ctx->dtype == SV_BF16, vshard_aligned(ctx, logits, q, greedy),
+                                     cu_gamma != nullptr, greedy);
+  const hipError_t e = launch_vs(fn, static_cast<unsigned>(batch), kSeqThreads, a, vs, st);
+  if (e != hipSuccess) return hip_fail(ctx, "kernel launch", e);
+  ctx->last_stream = st;
+  ctx->ran = true;
+  return SV_OK;
+}
+
+int spec_vshard_finish(spec_verify_ctx* ctx, void* hip_stream, const spec_vshard* sh, int batch, int gamma,
+                       const int32_t* cu_gamma, int total_draft_rows, float temperature, const void* logits,
+                       const float* q, const float* uniforms, const double* part_all, const double* local,
+                       int32_t* emitted_tokens, float* residual_sum) {
+  Args a;
+  VShard vs;
+  const bool greedy = temperature == 0.f;
+  int rc = vshard_prepare(ctx, sh, batch, gamma, cu_gamma, total_draft_rows, temperature, logits, q != nullptr,
+                          true, uniforms != nullptr, emitted_tokens && residual_sum, a, vs);
+  if (rc != SV_OK) return rc;
+  if (batch == 0 || greedy) return SV_OK;  // at T = 0 the decision step wrote every output
+  if (!part_all || !local) {
+    set_msg(ctx->msg, sizeof(ctx->msg), "part_all or local is NULL");
+    return SV_EINVAL;
+  }
+  a.V = sh->vocab_total;
+  a.q = q;
+  a.u = uniforms;
+  a.emitted = emitted_tokens;
+  a.rsum = residual_sum;
+  vs.part_all = part_all;
+  vs.loc = const_cast<double*>(local);
+  DeviceGuard guard(ctx->device);
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const void* fn = vs_pick<VsFinish>(ctx->dtype == SV_BF16, vshard_aligned(ctx, logits, q, false),
+                                     cu_gamma != nullptr, false);
+  const hipError_t e = launch_vs(fn, static_cast<unsigned>(batch), kSeqThreads, a, vs, st);
+  if (e != hipSuccess) return hip_fail(ctx, "kernel launch", e);
+  ctx->last_stream = st;
+  ctx->ran = true;
+  return SV_OK;
+}
 
 int spec_sample_run(spec_verify_ctx* ctx, void* hip_stream, int rows, int mode, float temperature, const void* x,
                     const float* uniforms, int32_t* tokens) {

@@ -12,7 +12,8 @@ from .binding import (SV_BF16, SV_EDATA, SV_F32, spec_verify_create, spec_verify
                       spec_verify_run, spec_verify_set_path, spec_verify_set_timing,
                       spec_verify_set_timing_stride, spec_verify_status, spec_sample_run,
                       spec_verify_run_onehot, spec_ngram_propose, spec_adapt_gamma,
-                      SV_SAMPLE_LOGITS, SV_SAMPLE_WEIGHTS)
+                      SV_SAMPLE_LOGITS, SV_SAMPLE_WEIGHTS, spec_vshard_rows, spec_vshard_decide,
+                      spec_vshard_finish, vshard_desc, VSHARD_LOCAL_DOUBLES, VSHARD_PART_DOUBLES)
 
 
 class VerifyOutputs(NamedTuple):
@@ -222,3 +223,119 @@ class Verifier:
             self.close()
         except Exception:
             pass
+
+
+class VocabShard:
+    """One shard of vocabulary-parallel verification (spec_vshard_* in spec_verify.h):
+    a context for this shard's columns [bounds[k], bounds[k + 1]) and the three steps of
+    a round. Between the steps the caller gathers every shard's records in shard order
+    (over RCCL across devices, or by concatenation when the shards share one device)."""
+
+    def __init__(self, bounds, shard: int, logits_dtype, max_batch: int, max_draft_rows: int,
+                 max_gamma: int, device: int = 0):
+        self.bounds = [int(x) for x in bounds]
+        self.shard = int(shard)
+        self.width = self.bounds[self.shard + 1] - self.bounds[self.shard]
+        self.ver = Verifier(self.width, logits_dtype, max_batch, max_draft_rows, max_gamma, device)
+        self.desc, self._bounds_arr = vshard_desc(self.bounds, self.shard)
+
+    def _geom(self, logits, draft_ids, gamma, cu_gamma, total_draft_rows):
+        import torch
+        v = self.ver
+        if _dtype_code(logits) != v.dtype_code:
+            raise TypeError("logits dtype differs from the context's")
+        if cu_gamma is not None:
+            v._check("cu_gamma", cu_gamma, torch.int32)
+            B = cu_gamma.numel() - 1
+            R = int(total_draft_rows if total_draft_rows is not None else draft_ids.numel())
+            g_arg = -1
+        else:
+            if gamma is None:
+                raise ValueError("pass gamma or cu_gamma")
+            B = logits.numel() // ((gamma + 1) * self.width)
+            R = B * gamma
+            g_arg = gamma
+        v._check("logits", logits, None, (R + B) * self.width)
+        v._check("draft_ids", draft_ids, torch.int32, R)
+        return B, R, g_arg
+
+    def rows(self, logits, draft_ids, *, temperature: float, q=None, gamma=None, cu_gamma=None,
+             total_draft_rows=None, rec=None, stream=None):
+        """Step 1: this shard's 16-byte record per judged row, as float32 [records, 4]."""
+        import torch
+        B, R, g_arg = self._geom(logits, draft_ids, gamma, cu_gamma, total_draft_rows)
+        greedy = float(temperature) == 0.0
+        if not greedy:
+            self.ver._check("q", q, torch.float32, R * self.width)
+        n = R + (B if greedy else 0)
+        if rec is None:
+            rec = torch.empty((n, 4), dtype=torch.float32, device=self.ver.device)
+        self.ver._check("rec", rec, torch.float32, n * 4)
+        st = stream if stream is not None else torch.cuda.current_stream(self.ver.device)
+        spec_vshard_rows(self.ver.ctx, st, self.desc, B, g_arg, cu_gamma, R, float(temperature), logits,
+                         None if greedy else q, draft_ids, rec)
+        return rec
+
+    def decide(self, logits, draft_ids, rec_all, *, temperature: float, q=None, uniforms=None, gamma=None,
+               cu_gamma=None, total_draft_rows=None, out: Optional[VerifyOutputs] = None,
+               want_p_draft: bool = True, stream=None):
+        """Step 2: the decisions from every shard's records (rec_all: the gathered
+        records, shard by shard) and this shard's sums of each drawn row. Returns
+        (outputs, part, local): part (fp64 [B, 3]) is exchanged, local (fp64 [B, 52])
+        stays for step 3. At T = 0 every output is final here."""
+        import torch
+        B, R, g_arg = self._geom(logits, draft_ids, gamma, cu_gamma, total_draft_rows)
+        greedy = float(temperature) == 0.0
+        G = len(self.bounds) - 1
+        self.ver._check("rec_all", rec_all, torch.float32, G * (R + (B if greedy else 0)) * 4)
+        if not greedy:
+            self.ver._check("q", q, torch.float32, R * self.width)
+            self.ver._check("uniforms", uniforms, torch.float32, R + B)
+        dev = self.ver.device
+        if out is None:
+            out = VerifyOutputs(
+                torch.empty(B, dtype=torch.int32, device=dev),
+                torch.empty(R + B, dtype=torch.int32, device=dev),
+                torch.empty(B, dtype=torch.float32, device=dev),
+                torch.empty(R, dtype=torch.float32, device=dev) if (want_p_draft and not greedy) else None)
+        part = local = None
+        if not greedy:
+            part = torch.empty((B, VSHARD_PART_DOUBLES), dtype=torch.float64, device=dev)
+            local = torch.empty((B, VSHARD_LOCAL_DOUBLES), dtype=torch.float64, device=dev)
+        st = stream if stream is not None else torch.cuda.current_stream(dev)
+        spec_vshard_decide(self.ver.ctx, st, self.desc, B, g_arg, cu_gamma, R, float(temperature), logits,
+                           None if greedy else q, draft_ids, None if greedy else uniforms, rec_all,
+                           out.accepted_count, out.emitted_tokens, out.residual_sum, out.p_draft, part, local)
+        return out, part, local
+
+    def finish(self, logits, part_all, local, out: VerifyOutputs, *, temperature: float, q=None, uniforms=None,
+               gamma=None, cu_gamma=None, total_draft_rows=None, stream=None):
+        """Step 3: the shard that owns a sequence's drawn token writes it, the -1 padding
+        and S into `out`; other shards leave those entries as they are."""
+        import torch
+        if float(temperature) == 0.0:
+            return out
+        if cu_gamma is None:
+            B = logits.numel() // ((gamma + 1) * self.width)
+            R, g_arg = B * gamma, gamma
+        else:
+            B, R, g_arg = cu_gamma.numel() - 1, int(total_draft_rows), -1
+        G = len(self.bounds) - 1
+        self.ver._check("part_all", part_all, torch.float64, G * B * VSHARD_PART_DOUBLES)
+        self.ver._check("local", local, torch.float64, B * VSHARD_LOCAL_DOUBLES)
+        self.ver._check("q", q, torch.float32, R * self.width)
+        self.ver._check("uniforms", uniforms, torch.float32, R + B)
+        st = stream if stream is not None else torch.cuda.current_stream(self.ver.device)
+        spec_vshard_finish(self.ver.ctx, st, self.desc, B, g_arg, cu_gamma, R, float(temperature), logits, q,
+                           uniforms, part_all, local, out.emitted_tokens, out.residual_sum)
+        return out
+
+    def status(self) -> int:
+        return self.ver.status()
+
+    def last_error(self) -> str:
+        return self.ver.last_error()
+
+    def close(self):
+        self.ver.close()
+

@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "spec_verify.h")
 def declared_functions():
     text = open(HEADER, encoding="utf-8").read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(spec_(?:verify|sample|ngram|adapt)_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(spec_(?:verify|sample|ngram|adapt|vshard)_\w+)\s*\(", text)))
 
 
 def test_library_built():
@@ -105,6 +105,10 @@ def test_null_context_calls():
     lib.spec_verify_destroy(None)  # NULL-safe
     rc = lib.spec_verify_run(None, None, 1, 1, None, 1, 1.0, None, None, None, None, None, None, None, None)
     assert rc == sv.SV_EINVAL
+    desc, _arr = sv.vshard_desc([0, 16, 32], 0)
+    assert lib.spec_vshard_rows(None, None, desc, 1, 1, None, 1, 1.0, None, None, None, None) == sv.SV_EINVAL
+    assert lib.spec_vshard_decide(None, None, desc, 1, 1, None, 1, 1.0, *([None] * 11)) == sv.SV_EINVAL
+    assert lib.spec_vshard_finish(None, None, desc, 1, 1, None, 1, 1.0, *([None] * 7)) == sv.SV_EINVAL
 
 
 def test_create_rejects_bad_arguments_before_touching_a_device():
