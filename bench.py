@@ -293,6 +293,83 @@ def bench_shares(sv, torch, sets, dev, code, iters=200):
     return res
 
 
+def bench_vshard(sv, torch, sets, dev, code, G=8, iters=200):
+    """F4: one GPU's share of the workload under vocabulary sharding over G devices. Shard
+    0 holds columns [0, V/G) of every row and runs its three steps per round; the other
+    shards' records are computed once beforehand and stand in for the two all-gathers,
+    which are not timed. Reports the round's time on this device, each step alone, the
+    shard's column bytes per round and the bytes each exchange gathers."""
+    import numpy as np
+    w0, d0 = sets[0]
+    g = w0.uniform_gamma
+    if g is None or w0.T == 0:
+        return {}
+    V, B, R, T = w0.V, w0.B, w0.draft_rows, w0.T
+    bounds = [round(k * V / G) for k in range(G + 1)]
+    L2 = d0["logits"].view(R + B, V)
+    Q2 = d0["q"].view(R, V)
+    ids, u = d0["ids"], d0["u"]
+    shards, cols = [], []
+    rec_all = torch.empty((G * R, 4), dtype=torch.float32, device=dev)
+    part_all = torch.empty((G, B, sv.VSHARD_PART_DOUBLES), dtype=torch.float64, device=dev)
+    for k in range(G):
+        sh = sv.VocabShard(bounds, k, code, B, R, 16)
+        Lk = L2[:, bounds[k]:bounds[k + 1]].contiguous()
+        Qk = Q2[:, bounds[k]:bounds[k + 1]].contiguous()
+        sh.rows(Lk, ids, temperature=T, q=Qk, gamma=g, rec=rec_all[k * R:(k + 1) * R])
+        shards.append(sh)
+        cols.append((Lk, Qk))
+    outs = []
+    for k, sh in enumerate(shards):
+        o, part, loc = sh.decide(cols[k][0], ids, rec_all, temperature=T, q=cols[k][1], uniforms=u, gamma=g,
+                                 want_p_draft=False)
+        part_all[k].copy_(part)
+        outs.append((o, loc))
+    sh0, (L0, Q0), (out, loc0) = shards[0], cols[0], outs[0]
+    for sh in shards[1:]:
+        sh.close()
+    del cols[1:], outs[1:]
+    st = torch.cuda.current_stream(dev)
+    ctx, desc = sh0.ver.ctx, sh0.desc
+
+    def rows(k):
+        sv.spec_vshard_rows(ctx, st, desc, B, g, None, R, T, L0, Q0, ids, rec_all[:R])
+
+    def decide(k):
+        sv.spec_vshard_decide(ctx, st, desc, B, g, None, R, T, L0, Q0, ids, u, rec_all, out.accepted_count,
+                              out.emitted_tokens, out.residual_sum, None, part_all[0], loc0)
+
+    def finish(k):
+        sv.spec_vshard_finish(ctx, st, desc, B, g, None, R, T, L0, Q0, u, part_all, loc0, out.emitted_tokens,
+                              out.residual_sum)
+
+    def round_(k):
+        rows(k)
+        decide(k)
+        finish(k)
+    dt = _timed(torch, round_, iters)
+    steps = {nm: _timed(torch, fn, iters) * 1e6 for nm, fn in
+             (("k_vs_rows", rows), ("k_vs_decide", decide), ("k_vs_finish", finish))}
+    assert sh0.status() == sv.SV_OK, sh0.last_error()
+    acc = out.accepted_count.cpu().numpy()
+    sh0.close()
+    W = bounds[1]
+    s_l = 2 if code == sv.SV_BF16 else 4
+    n_res = int((acc < g).sum())
+    col_bytes = R * W * s_l + B * W * s_l + n_res * W * 4
+    res = {"workload": f"C3 columns [0, {W}) of {G} shards: B={B} gamma={g} V={V}",
+           "us_per_round": dt * 1e6, "step_us": steps,
+           "positions_per_s": R / dt, "column_bytes_per_round": col_bytes,
+           "column_GBps": col_bytes / dt / 1e9,
+           "gathered_bytes": {"records": G * R * sv.VSHARD_REC_BYTES,
+                              "draw_totals": G * B * sv.VSHARD_PART_DOUBLES * 8}}
+    log(f"[bench] F4 vocab shard (1 of {G}, {W} columns): {dt * 1e6:.1f} us/round on this device "
+        f"(rows {steps['k_vs_rows']:.1f}, decide {steps['k_vs_decide']:.1f}, finish {steps['k_vs_finish']:.1f} us "
+        f"alone), {col_bytes / dt / 1e9:.0f} GB/s over its columns; all-gathers of "
+        f"{G * R * sv.VSHARD_REC_BYTES / 1e3:.0f} KB and {G * B * 24 / 1e3:.0f} KB")
+    return res
+
+
 def cpu_baseline(w, seconds):
     """The oracle as it stands, single process, cycling over the sequences of one input
     set until about `seconds` of CPU work have been done."""
@@ -488,6 +565,7 @@ def main():
         next_rows["per_gpu_share"] = bench_shares(sv, torch, sets, dev, code)
         next_rows["F2_adaptive_gamma"] = bench_adaptive(sv, torch, dev)
         next_rows["F3_deterministic_drafts"] = bench_ngram(sv, torch, dev)
+        next_rows["F4_vocab_parallel"] = bench_vshard(sv, torch, sets, dev, code)
 
     # acceptance metrics of the measured inputs
     acc = np.concatenate(nb)
