@@ -87,6 +87,7 @@ struct Args {
   float* pdraft;
   RowStat* p1;     // [rows][split]
   int32_t* accept; // [rows] decisions of step 1 (rows that are not split)
+  float2* lxq;     // [rows] split rows: the draft's logit and q entry, from the split holding it
   int* err;
   int B, gamma, V, R, split, span, max_gamma;
   float k2;        // log2(e) / T, fp32
@@ -307,22 +308,25 @@ __global__ __launch_bounds__(kThreads) void k_rowstats(Args a) {
   const int d = blockIdx.x / a.split, k = blockIdx.x - d * a.split;
   const int b = RAGGED ? seq_of_row(a.cu, a.B, d) : d / a.gamma;
   const T* row = static_cast<const T*>(a.logits) + static_cast<size_t>(d + b) * a.V;
-  // operands of the accept test, issued first so their latency hides under the stream
+  // operands of the accept test, issued first so their latency hides under the stream;
+  // a split row's operands are loaded by the split that holds the draft and kept for
+  // the draw kernel, which then needs no dependent load to judge the row
+  const int lo = k * a.span, hi = min(a.V, lo + a.span);
   int x = -1;
   float lx = 0.f, qx = 0.f, uu = 0.f;
-  if (ACCEPT && threadIdx.x == 0) {
+  if (threadIdx.x == 0) {
     x = a.ids[d];
-    uu = a.u[d + b];
-    if (x >= 0 && x < a.V) {
+    if (ACCEPT) uu = a.u[d + b];
+    if (ACCEPT ? (x >= 0 && x < a.V) : (x >= lo && x < hi)) {
       lx = load_one(row, x);
       qx = a.onehot ? 1.f : a.q[static_cast<size_t>(d) * a.V + x];
     }
   }
-  const int lo = k * a.span, hi = min(a.V, lo + a.span);
   float C, Z;
   block_row_lse<T, ALIGNED>(row, lo, hi, a.k2, s_c, s_z, C, Z);
   if (threadIdx.x == 0) {
     a.p1[blockIdx.x] = RowStat{C, Z};
+    if (!ACCEPT && x >= lo && x < hi) a.lxq[d] = make_float2(lx, qx);
     if (ACCEPT) {
       double px;
       a.accept[d] = accept_test(x, lx, qx, uu, C, Z, a, px) ? 1 : 0;
@@ -448,7 +452,6 @@ __device__ __forceinline__ int first_rejection(const Args& a, int b, int base, i
                                                int* s_n) {
   if (threadIdx.x == 0) *s_n = g;
   __syncthreads();
-  const T* L = static_cast<const T*>(a.logits);
   for (int i = threadIdx.x; i < g; i += kSeqThreads) {
     const int d = base + i;
     bool acc;
@@ -477,8 +480,9 @@ __device__ __forceinline__ int first_rejection(const Args& a, int b, int base, i
       s_cz[i] = make_float2(C, Z);
       const int x = a.ids[d];
       const bool valid = x >= 0 && x < a.V;
-      const float lx = valid ? load_one(L, static_cast<size_t>(d + b) * a.V + x) : 0.f;
-      const float qx = !valid ? 0.f : a.onehot ? 1.f : a.q[static_cast<size_t>(d) * a.V + x];
+      const float2 o = a.lxq[d];  // written by the split of step 1 that holds x (valid x only)
+      const float lx = valid ? o.x : 0.f;
+      const float qx = valid ? o.y : 0.f;
       double px;
       acc = accept_test(x, lx, qx, a.u[d + b], C, Z, a, px);
       if (a.pdraft) a.pdraft[d] = static_cast<float>(px);
@@ -2536,6 +2540,7 @@ struct spec_verify_ctx {
   void* ws = nullptr;
   RowStat* p1 = nullptr;
   int32_t* accept = nullptr;
+  float2* lxq = nullptr;     // split rows: the draft's logit and q entry
   int32_t* s_acc = nullptr;  // sampling: accepted counts (all 0) of the verify launch
   float* s_rsum = nullptr;   // sampling: residual sums (all 0)
   int* err = nullptr;
@@ -2801,6 +2806,7 @@ int run_impl(spec_verify_ctx* ctx, void* hip_stream, int batch, int gamma, const
   a.pdraft = greedy ? nullptr : p_draft;
   a.p1 = ctx->p1;
   a.accept = ctx->accept;
+  a.lxq = ctx->lxq;
   a.err = ctx->err;
   a.B = batch;
   a.gamma = cu_gamma ? -1 : gamma;
@@ -3005,13 +3011,14 @@ int spec_verify_create(spec_verify_ctx** out, int device, int vocab, int logits_
   const size_t n_p1 =
       up(sizeof(RowStat) * static_cast<size_t>(max_draft_rows > 0 ? max_draft_rows : 1) * max_split);
   const size_t n_ac = up(sizeof(int32_t) * static_cast<size_t>(max_draft_rows > 0 ? max_draft_rows : 1));
+  const size_t n_lq = up(sizeof(float2) * static_cast<size_t>(max_draft_rows > 0 ? max_draft_rows : 1));
   const size_t n_sb = up(sizeof(int32_t) * static_cast<size_t>(max_batch > 0 ? max_batch : 1));
   const size_t n_er = 256;
   // split draw: sub-region sums and a count of finished slices per sequence
   ctx->split_cap = max_batch < kSplitMaxB ? max_batch : kSplitMaxB;
   const size_t cap = static_cast<size_t>(ctx->split_cap);
   const size_t n_ds = up(sizeof(double) * 3 * kMaxSub * cap), n_dc = up(sizeof(int) * cap);
-  if (hipMalloc(&ctx->ws, n_p1 + n_ac + 3 * n_sb + n_er + n_ds + n_dc) != hipSuccess) {
+  if (hipMalloc(&ctx->ws, n_p1 + n_ac + 3 * n_sb + n_er + n_ds + n_dc + n_lq) != hipSuccess) {
     delete ctx;
     return SV_ENOMEM;
   }
@@ -3027,6 +3034,7 @@ int spec_verify_create(spec_verify_ctx** out, int device, int vocab, int logits_
     ctx->dcnt = reinterpret_cast<int*>(c + n_ds);
   }
   ctx->order = reinterpret_cast<int*>(p + n_p1 + n_ac + 2 * n_sb + n_er + n_ds + n_dc);
+  ctx->lxq = reinterpret_cast<float2*>(p + n_p1 + n_ac + 3 * n_sb + n_er + n_ds + n_dc);
   if (hipMemset(ctx->err, 0, n_er) != hipSuccess ||
       (ctx->dcnt && hipMemset(ctx->dcnt, 0, n_dc) != hipSuccess) || hipDeviceSynchronize() != hipSuccess) {
     (void)hipFree(ctx->ws);

@@ -4,7 +4,9 @@ cases at most 1e-5 of sequences, no unflagged mismatch) is measured at its own s
 Each workload's sequences are replicas of a base batch from the seeded generator in
 `synth` (the same target rows and draft distributions) with fresh draft ids, drawn
 from q by inverse CDF, and fresh uniforms; the GPU runs them in chunks of 4096
-sequences, and the oracle verifies every sequence on the CPU (forked workers).
+sequences (one call per chunk, or one call per 64 sequences for the small-batch plan,
+whose draw is split over several workgroups per sequence), and the oracle verifies
+every sequence on the CPU (forked workers).
 """
 import math
 import sys
@@ -94,22 +96,28 @@ def test_greedy_at_1e5_sequences(lib):
     assert total >= 10 ** 5 and not bad, bad[:5]
 
 
-@pytest.mark.parametrize("cfg,base_batch", [("C2", 64), ("C3", 256), ("C5", 256)])
-def test_parity_at_1e5_sequences(lib, cfg, base_batch):
+@pytest.mark.parametrize("cfg,base_batch,per_call", [("C2", 64, CHUNK), ("C3", 256, CHUNK), ("C5", 256, CHUNK),
+                                                     ("C2", 64, 64), ("C3", 64, 64)])
+def test_parity_at_1e5_sequences(lib, cfg, base_batch, per_call):
+    """per_call = CHUNK: each chunk in one call (the one-launch plan); per_call = 64: one
+    call per replica of 64 sequences (the two-launch plan with the split draw)."""
     w = synth.make_config(cfg, seed=31, batch=base_batch)
     reps = CHUNK // w.B
     chunks = TOTAL // (reps * w.B)
     R0, T0 = w.draft_rows, w.target_rows
-    _say("1e5", cfg, f"base B={w.B} x {reps} replicas x {chunks} chunks = {chunks * reps * w.B} sequences")
+    _say("1e5", cfg, f"base B={w.B} x {reps} replicas x {chunks} chunks = {chunks * reps * w.B} sequences, "
+         f"{per_call} per call")
     code = lib.SV_BF16 if w.dtype == "bf16" else lib.SV_F32
     v = lib.Verifier(w.V, code, reps * w.B, reps * R0, 16)
     if w.dtype == "bf16":
         base_l = torch.from_numpy(w.logits.view(np.int16)).view(torch.bfloat16).cuda()
     else:
         base_l = torch.from_numpy(w.logits).cuda()
+    base_q = torch.from_numpy(w.q).cuda()
     L = base_l.repeat(reps, 1)
-    Q = torch.from_numpy(w.q).cuda().repeat(reps, 1)
+    Q = base_q.repeat(reps, 1)
     cu = torch.from_numpy(synth.pack(np.tile(w.gammas, reps))).cuda()
+    cu1 = torch.from_numpy(w.cu_gamma).cuda()
     cdf = np.cumsum(w.q.astype(np.float64), axis=1)
     rng = np.random.default_rng([32, synth.config_number(cfg)])
     total = exact = flagged = 0
@@ -121,12 +129,25 @@ def test_parity_at_1e5_sequences(lib, cfg, base_batch):
         for d in range(R0):
             ids[:, d] = np.minimum(np.searchsorted(cdf[d], wd[:, d] * cdf[d, -1], side="right"), w.V - 1)
         u = rng.random((reps, T0), dtype=np.float32)
-        out = v.run(L, torch.from_numpy(ids.reshape(-1)).cuda(), temperature=w.T, q=Q,
-                    uniforms=torch.from_numpy(u.reshape(-1)).cuda(), cu_gamma=cu, total_draft_rows=reps * R0,
-                    want_p_draft=False)
-        n_g = out.accepted_count.cpu().numpy().reshape(reps, w.B)
-        em_g = out.emitted_tokens.cpu().numpy().reshape(reps, T0)
-        s_g = out.residual_sum.cpu().numpy().reshape(reps, w.B)
+        if per_call == CHUNK:
+            out = v.run(L, torch.from_numpy(ids.reshape(-1)).cuda(), temperature=w.T, q=Q,
+                        uniforms=torch.from_numpy(u.reshape(-1)).cuda(), cu_gamma=cu, total_draft_rows=reps * R0,
+                        want_p_draft=False)
+            n_g = out.accepted_count.cpu().numpy().reshape(reps, w.B)
+            em_g = out.emitted_tokens.cpu().numpy().reshape(reps, T0)
+            s_g = out.residual_sum.cpu().numpy().reshape(reps, w.B)
+        else:
+            n_g = np.empty((reps, w.B), np.int32)
+            em_g = np.empty((reps, T0), np.int32)
+            s_g = np.empty((reps, w.B), np.float32)
+            ids_d = torch.from_numpy(ids).cuda()
+            u_d = torch.from_numpy(u).cuda()
+            for r in range(reps):
+                out = v.run(base_l, ids_d[r], temperature=w.T, q=base_q, uniforms=u_d[r], cu_gamma=cu1,
+                            total_draft_rows=R0, want_p_draft=False)
+                n_g[r] = out.accepted_count.cpu().numpy()
+                em_g[r] = out.emitted_tokens.cpu().numpy()
+                s_g[r] = out.residual_sum.cpu().numpy()
         assert v.status() == lib.SV_OK, v.last_error()
 
         def job(r):
