@@ -359,7 +359,7 @@ def bench_vshard(sv, torch, sets, dev, code, G=8, iters=200):
     col_bytes = R * W * s_l + B * W * s_l + n_res * W * 4
     res = {"workload": f"C3 columns [0, {W}) of {G} shards: B={B} gamma={g} V={V}",
            "us_per_round": dt * 1e6, "step_us": steps,
-           "positions_per_s": R / dt, "column_bytes_per_round": col_bytes,
+           "positions_per_s_device_part": R / dt, "column_bytes_per_round": col_bytes,
            "column_GBps": col_bytes / dt / 1e9,
            "gathered_bytes": {"records": G * R * sv.VSHARD_REC_BYTES,
                               "draw_totals": G * B * sv.VSHARD_PART_DOUBLES * 8}}

@@ -11,29 +11,33 @@
 //   [P4] "투기적 디코딩 — 초안 모델을 무엇으로 세울 것인가" (ailab.paldyn.com), "출력이
 //        변하지 않는다는 것이 핵심이다" (greedy reduces to argmax equality).
 //
-// Two launches per call on the caller's stream, no host sync:
-//   1. k_rowstats / k_rowargmax, grid = (draft rows) x split, 256 threads: one read
-//      of every judged target row. Sampling keeps, in base 2 with k2 = log2(e)/T,
-//      the scaled row max c = max(l) * k2 and z = sum 2^(l * k2 - c), i.e. the
-//      softmax normaliser of l / T, in fp32; greedy keeps the max and its lowest
-//      index. When a row is not split, the same workgroup also runs the accept test
-//      of its draft position (p(x) in fp64) and records the decision.
-//   2. k_sample_seq / k_greedy_seq, grid = B, 1024 threads: find the first rejection
-//      n_b, then one fp64 sweep of the single row the sequence draws from: the
-//      rejected row (residual) or row gamma_b (bonus), its exponentials good to
-//      1.5e-13 relative. Each wave owns a contiguous
-//      region of the row. The residual sweep defers normalisation: with
-//      e(v) = 2^(l(v) k2 - c) and Z32 from step 1, w(v) = e(v) - q(v) Z32 and a region
-//      keeps D = sum max(w, 0), Q = sum_{w > 0} q, Zr = sum e. Since
-//      e/Z64 - q = w/Z64 - q (Z64 - Z32)/Z64, the region's residual mass is
-//      D/Z64 - Q (Z64 - Z32)/Z64 with Z64 = sum Zr. The region where the prefix
-//      crosses t = u * S is re-swept with an fp64 block scan and the first token
-//      whose inclusive prefix exceeds t is emitted. The bonus sweep keeps a running
-//      region max instead. Greedy reads row gamma_b only when every draft was accepted.
+// Launch plans (all on the caller's stream, no host sync):
+//   * one launch (k_verify_seq; greedy: k_greedy_seq1), B >= compute units: one
+//     1024-thread workgroup per sequence judges its draft rows left to right in one
+//     read each (base-2 online max and sum in fp32, the accept test in fp64), stops at
+//     the first rejection and draws from the one row it needs. A ragged batch first
+//     orders its sequences longest first (k_order_by_gamma).
+//   * two launches, smaller batches: k_rowstats / k_rowargmax, grid = (draft rows) x
+//     split, 256 threads, one read of every draft row, keep each split's (c, z) or
+//     (max, index); then k_sample_seq / k_greedy_seq, one workgroup per sequence, find
+//     the first rejection and draw; with at most half as many sequences as compute units
+//     k_draw_part shares each draw over two or four workgroups, the last to finish
+//     completing it.
+//   * rows with no drafts (k_sample_rows, k_sample_weights): one token per row.
+//   * vocabulary shards (k_vs_rows, k_vs_decide, k_vs_finish): one device's part when
+//     the columns are split over devices.
+// The draw is one fp64 sweep of the drawn row, e(v) = 2^(l(v) k2 - c), exact to
+// 1.5e-13 relative (bf16 rows through an LDS value table, fp32 rows through exp2_tab),
+// with normalisation deferred: with Z32 from pass 1, w(v) = e(v) - q(v) Z32, and a
+// region keeps D = sum max(w, 0), Q = sum_{w > 0} q, Zr = sum e. Since
+// e/Z64 - q = w/Z64 - q (Z64 - Z32)/Z64, the region's residual mass is
+// D/Z64 - Q (Z64 - Z32)/Z64 with Z64 = sum Zr. The region where the prefix crosses
+// t = u S is re-swept with an fp64 block scan and the first token whose inclusive
+// prefix exceeds t is emitted. The bonus sweep keeps a running region max instead.
 //
-// Cross-workgroup hand-off inside one launch is avoided on purpose: the per-XCD L2
-// caches are not coherent for plain stores, and a device-scope fence (L2 write-back
-// and invalidate) per workgroup costs far more than the kernel boundary.
+// Work is handed between workgroups of one launch only where no workgroup waits for
+// another: the per-XCD L2 caches are not coherent for plain stores, so such hand-offs
+// are stored and loaded at system scope, past the L2s.
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
 

@@ -99,6 +99,19 @@ def test_vshard_parity(lib, cfg, batch, bounds):
     assert rep.ok(), rep.summary()
 
 
+def test_vshard_ragged_with_empty_drafts(lib):
+    """gamma_b in {0, 1, 3, 8}: sequences with no drafts go straight to the bonus draw
+    over every shard's columns."""
+    gammas = np.tile(np.array([0, 1, 3, 8], np.int32), 8)
+    w = synth.make_sampling("ragged 0/1/3/8", gammas, 5000, "bf16", 1.0, 3.0, 0.7, seed=44)
+    bounds = [0, 1700, 3333, 5000]
+    _say("vshard ragged 0/1/3/8", f"B={w.B} bounds={bounds}")
+    gpu = run_sharded(lib, w, bounds)
+    assert all(s == lib.SV_OK for s in gpu["status"]), gpu["status"]
+    rep = compare(w, gpu, oracle_batch(w))
+    assert rep.ok(), rep.summary()
+
+
 def test_vshard_draft_ids_on_shard_edges(lib):
     """Draft ids on both sides of every shard boundary: the owner's l(x) and q(x) decide."""
     w = synth.make_config("C2", seed=41, batch=32)
