@@ -16,7 +16,8 @@
 //     1024-thread workgroup per sequence judges its draft rows left to right in one
 //     read each (base-2 online max and sum in fp32, the accept test in fp64), stops at
 //     the first rejection and draws from the one row it needs. A ragged batch first
-//     orders its sequences longest first (k_order_by_gamma).
+//     orders its sequences longest first (k_order_by_gamma). Greedy batches of up to
+//     four times the compute units add helper workgroups (k_greedy_help).
 //   * two launches, smaller batches: k_rowstats / k_rowargmax, grid = (draft rows) x
 //     split, 256 threads, one read of every draft row, keep each split's (c, z) or
 //     (max, index); then k_sample_seq / k_greedy_seq, one workgroup per sequence, find
@@ -68,6 +69,9 @@ namespace {
 #ifndef SV_SPLIT_MIN_SPAN
 #define SV_SPLIT_MIN_SPAN 2048
 #endif
+#ifndef SV_GREEDY_HELP
+#define SV_GREEDY_HELP 1
+#endif
 constexpr int kMaxSplit = 16;
 constexpr int kMaxGamma = 1024;
 constexpr int kMaxRaggedBatch = 65536;  // row -> sequence search limit
@@ -107,6 +111,13 @@ struct Args {
   int* dcnt;       // [B] slices of the sequence's sweep done (zero between calls)
   // one-launch plan of a ragged batch: the sequence each workgroup takes (null: its index)
   int* order;      // [B]
+  // greedy rows with helpers: per sequence, the next row to claim and the participants,
+  // each tagged with the call's epoch in the high half, and the first mismatch found,
+  // (row << 32) | token
+  unsigned long long* gclaim;  // [B]
+  unsigned long long* gpart;   // [B]
+  unsigned long long* gbest;   // [B]
+  unsigned int gepoch;
 };
 
 __device__ __forceinline__ bool finite_pos(float z) { return z > 0.f && z <= FLT_MAX; }
@@ -927,10 +938,11 @@ __device__ __forceinline__ void stats_step(const Raw<T>& lr, float wgt, float k2
 // span); otherwise the single span's lanes past V read the row's last group instead
 // and must not count it. NT makes the loads nontemporal. Padding spans re-read the last span and are not handed to
 // step. step(buf, k) gets the span index k < nsp; after_prologue() runs once the first
-// loads are in flight; row_end(i) returns true to stop.
-template <typename T, bool WIDE, bool NT, typename Pro, typename Step, typename RowEnd>
-__device__ __forceinline__ void walk_rows(const T* Lseq, int V, int g, Pro&& after_prologue, Step&& step,
-                                          RowEnd&& row_end) {
+// loads are in flight; row_end(i) returns true to stop. row_ptr(i) gives walked row i
+// (at most rows i and i + 1 are in flight: the ring is shorter than a row).
+template <typename T, bool WIDE, bool NT, typename RowPtr, typename Pro, typename Step, typename RowEnd>
+__device__ __forceinline__ void walk_rows_p(RowPtr&& row_ptr, int V, int g, Pro&& after_prologue, Step&& step,
+                                            RowEnd&& row_end) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   constexpr int kSpan = kSeqWaves * kIter;
@@ -942,7 +954,7 @@ __device__ __forceinline__ void walk_rows(const T* Lseq, int V, int g, Pro&& aft
   Raw<T> Lb[kRing1];
   int jl = 0, il = 0, kl = 0;  // next (flattened) iteration to load: row il, span kl
   auto issue = [&](Raw<T>& dst) {
-    const T* rowp = Lseq + static_cast<size_t>(il) * V;
+    const T* rowp = row_ptr(il);
     if (WIDE) {
       const int e0 = kl < nsp - 1 ? kl * kSpan : V - kSpan;
       const char* sb = reinterpret_cast<const char*>(rowp + e0);
@@ -977,6 +989,12 @@ __device__ __forceinline__ void walk_rows(const T* Lseq, int V, int g, Pro&& aft
     }
     if (row_end(i)) break;
   }
+}
+template <typename T, bool WIDE, bool NT, typename Pro, typename Step, typename RowEnd>
+__device__ __forceinline__ void walk_rows(const T* Lseq, int V, int g, Pro&& after_prologue, Step&& step,
+                                          RowEnd&& row_end) {
+  walk_rows_p<T, WIDE, NT>([&](int i) { return Lseq + static_cast<size_t>(i) * V; }, V, g, after_prologue, step,
+                           row_end);
 }
 
 // Weight of this lane's entries in the row's last span (see walk_rows).
@@ -2291,6 +2309,186 @@ __global__ __launch_bounds__(kSeqThreads) void k_greedy_seq1(Args a) {
   for (int i = n + 1 + threadIdx.x; i <= g; i += kSeqThreads) a.emitted[base + b + i] = -1;
 }
 
+// One participant's part of a greedy sequence with helpers (k_greedy_help): walks the
+// rows it claims from the sequence's counter, starting with r0 and r1 (claimed ahead so
+// the next row's first loads overlap the row being read), publishes a mismatch (or the
+// bonus row's argmax) with an atomic min of (row, argmax), stops at a row past g or past
+// the smallest published row, then leaves; the participant that brings the count to zero
+// writes the outputs. Every thread of the block calls it.
+template <typename T>
+__device__ __forceinline__ void greedy_participate(const Args& a, int b, int base, int g, int r0, int r1) {
+  __shared__ float s_v[kSeqWaves];
+  __shared__ int s_i[kSeqWaves];
+  __shared__ int s_ctl[2];
+  __shared__ int s_out[3];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  unsigned long long* claim = a.gclaim + b;
+  unsigned long long* part = a.gpart + b;
+  unsigned long long* best = a.gbest + b;
+  const int V = a.V;
+  const T* L0 = static_cast<const T*>(a.logits) + static_cast<size_t>(base + b) * V;
+  const int x = g > 0 ? a.ids[base + min(lane, g - 1)] : -1;  // lane i: draft i
+  constexpr int kSpan = kSeqWaves * kIter;
+  const int lane_off = wave * kIter + lane * kGroup;
+  const int nsp = (V + kSpan - 1) / kSpan;
+  const bool wide = V >= kSpan;
+  auto entry0 = [&](int k) {
+    return wide ? (k < nsp - 1 ? k * kSpan : V - kSpan) + lane_off : min(lane_off, V - kGroup);
+  };
+  // walked row t is row rc, walked row t + 1 is row rn (both the same in every thread)
+  int tw = 0, rc = r0, rn = r1;
+  auto row_ptr = [&](int il) {
+    const int r = min(il == tw ? rc : rn, g);  // a claim past g reads row g, never judged
+    return L0 + static_cast<size_t>(r) * V;
+  };
+  float bv = -INFINITY;
+  int bi = entry0(0);
+  auto step = [&](const Raw<T>& lr, int k) {
+    float xv[kGroup];
+    unpack(lr, xv);
+    const int e = entry0(k);
+#pragma unroll
+    for (int q = 0; q < kGroup; ++q)
+      if (xv[q] > bv) {
+        bv = xv[q];
+        bi = e + q;
+      }
+  };
+  auto row_end = [&](int t) -> bool {
+    const int i = rc;  // the row just read
+    // the next claim and the published minimum, loaded now so the merge hides them
+    unsigned long long nc = 0, nb = ~0ull;
+    if (threadIdx.x == 0) {
+      nc = __hip_atomic_fetch_add(claim, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      nb = __hip_atomic_load(best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float v2 = __shfl_xor(bv, o);
+      const int i2 = __shfl_xor(bi, o);
+      argmax_merge(bv, bi, v2, i2);
+    }
+    if (lane == 0) {
+      s_v[wave] = bv;
+      s_i[wave] = bi;
+    }
+    __syncthreads();
+    float Vm = s_v[0];
+    int I = s_i[0];
+    for (int w = 1; w < kSeqWaves; ++w) argmax_merge(Vm, I, s_v[w], s_i[w]);
+    bv = -INFINITY;
+    bi = entry0(0);
+    const bool stop = i == g || __shfl(x, i < g ? i : 0) != I;  // the bonus row, or a mismatch
+    if (threadIdx.x == 0) {
+      if (stop) {
+        const unsigned long long mine = (static_cast<unsigned long long>(i) << 32) | static_cast<uint32_t>(I);
+        (void)__hip_atomic_fetch_min(best, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      }
+      s_ctl[0] = static_cast<int>(static_cast<uint32_t>(nc));
+      s_ctl[1] = static_cast<int>(min(nb >> 32, 0x7FFFFFFFull));
+    }
+    __syncthreads();  // s_v / s_i are rewritten by the next row; s_ctl is read
+    const int next = s_ctl[0], known = s_ctl[1];
+    __syncthreads();  // s_ctl is rewritten by the next row
+    if (stop || rn > g || known < rn) return true;
+    tw = t + 1;
+    rc = rn;
+    rn = next;
+    return false;
+  };
+  if (r0 <= g) {
+    if (wide)
+      walk_rows_p<T, true, false>(row_ptr, V, g + 1, [] {}, step, row_end);
+    else
+      walk_rows_p<T, false, false>(row_ptr, V, g + 1, [] {}, step, row_end);
+  }
+  // leave; the participant that brings the count to zero writes the outputs
+  if (threadIdx.x == 0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the published minimum first
+    const unsigned long long p = __hip_atomic_fetch_sub(part, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    s_out[2] = static_cast<uint32_t>(p) == 1u ? 1 : 0;
+    if (s_out[2]) {
+      const unsigned long long m = __hip_atomic_load(best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      const int nr = static_cast<int>(min(m >> 32, static_cast<unsigned long long>(g)));
+      s_out[0] = nr;
+      s_out[1] = static_cast<int>(static_cast<uint32_t>(m));
+      if (nr < g && bad_id(a, a.ids[base + nr])) atomicOr(a.err, SV_DATA_DRAFT_ID);
+    }
+  }
+  __syncthreads();
+  const bool writer = s_out[2] != 0;
+  const int n = s_out[0], tok = s_out[1];
+  __syncthreads();  // s_out is rewritten by a helper's next sequence
+  if (!writer) return;
+  if (wave == 0) {
+    if (lane < n) a.emitted[base + b + lane] = x;
+    if (lane == 0) {
+      a.acc[b] = n;
+      a.emitted[base + b + n] = tok;
+      a.rsum[b] = 0.f;
+    }
+  }
+  for (int i = n + 1 + threadIdx.x; i <= g; i += kSeqThreads) a.emitted[base + b + i] = -1;
+}
+
+// Greedy in one launch with helpers: workgroups 0..B-1 own one sequence each, as in
+// k_greedy_seq1; workgroup B + h is a helper, dispatched only as the owners' slots free
+// up, that joins sequence h (in the same order as the owners) if it still has rows to
+// claim and no mismatch has been published (otherwise every new claim would lie past
+// it), takes part as in greedy_participate and exits. Row n, the first mismatch, is
+// always claimed before any row after it and judged by its claimer, so the minimum holds
+// it when the last participant leaves. Counters carry the call's epoch, so no reset is
+// needed; nothing waits for another workgroup, and all of it is kept past the per-XCD L2
+// caches (system scope).
+template <typename T, bool RAGGED>
+__global__ __launch_bounds__(kSeqThreads) void k_greedy_help(Args a) {
+  __shared__ int s_join[3];
+  const bool helper = blockIdx.x >= static_cast<unsigned>(a.B);
+  const int bi0 = helper ? blockIdx.x - a.B : blockIdx.x;
+  const int b = RAGGED && a.order ? a.order[bi0] : bi0;
+  int base, g;
+  if (!seq_geom<RAGGED>(a, b, base, g)) {
+    if (!helper && threadIdx.x == 0) {
+      atomicOr(a.err, SV_DATA_CU_GAMMA);
+      a.acc[b] = -1;
+    }
+    return;
+  }
+  const unsigned long long E = static_cast<unsigned long long>(a.gepoch) << 32;
+  unsigned long long* claim = a.gclaim + b;
+  unsigned long long* part = a.gpart + b;
+  unsigned long long* best = a.gbest + b;
+  if (threadIdx.x == 0) {
+    int r0 = 0, r1 = 1;
+    if (!helper) {  // fresh state for this call; rows 0 and 1 are the owner's
+      __hip_atomic_store(best, ~0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      __hip_atomic_store(part, E | 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // before the counter shows this epoch
+      __hip_atomic_store(claim, E | 2ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    } else {
+      const unsigned long long c = __hip_atomic_load(claim, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      const bool join = (c >> 32) == a.gepoch && static_cast<uint32_t>(c) <= static_cast<uint32_t>(g) &&
+                        __hip_atomic_load(best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == ~0ull;
+      r0 = r1 = INT_MAX;
+      if (join) {
+        (void)__hip_atomic_fetch_add(part, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // counted before claiming
+        r0 = static_cast<int>(static_cast<uint32_t>(
+            __hip_atomic_fetch_add(claim, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM)));
+        r1 = static_cast<int>(static_cast<uint32_t>(
+            __hip_atomic_fetch_add(claim, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM)));
+      }
+      s_join[0] = join ? 1 : 0;
+    }
+    s_join[1] = r0;
+    s_join[2] = r1;
+  }
+  __syncthreads();
+  if (helper && !s_join[0]) return;  // a helper that did not join leaves nothing behind
+  greedy_participate<T>(a, b, base, g, s_join[1], s_join[2]);
+}
+
 // ============================================================== sampling from given weights
 // One token per row from weights w >= 0 (fp32, normalised or not): the inverse CDF of
 // the draw ([P1] ch.2; [P3] 단계 1 draws the drafts from q), t = u sum(w), the first v
@@ -2520,7 +2718,7 @@ constexpr int kEventsPerRun = 2 * kKernels;
 // The launch sequences a call can take.
 enum Path {
   kPathSample2 = 0, kPathGreedy2 = 1, kPathSample1 = 2, kPathGreedy1 = 3, kPathSample3 = 4, kPathRows = 5,
-  kPathSample1R = 6, kPathGreedy1R = 7, kPaths = 8
+  kPathSample1R = 6, kPathGreedy1R = 7, kPathGreedyH = 8, kPathGreedyHR = 9, kPaths = 10
 };
 struct PathInfo {
   int nk;
@@ -2535,6 +2733,8 @@ const PathInfo kPathInfo[kPaths] = {
     {1, {"k_sample_rows", nullptr}},
     {2, {"k_order_by_gamma", "k_verify_seq"}},
     {2, {"k_order_by_gamma", "k_greedy_seq1"}},
+    {1, {"k_greedy_help", nullptr}},
+    {2, {"k_order_by_gamma", "k_greedy_help"}},
 };
 
 }  // namespace
@@ -2562,6 +2762,11 @@ struct spec_verify_ctx {
   int* dcnt = nullptr;
   int split_cap = 0;
   int* order = nullptr;  // [max_batch] sequence order of the one-launch plan (ragged batches)
+  // greedy rows with helpers: per-sequence claim counter, participants and published minimum
+  unsigned long long* gclaim = nullptr;
+  unsigned long long* gpart = nullptr;
+  unsigned long long* gbest = nullptr;
+  unsigned int gepoch = 0;  // the last call's epoch (0 is never used: the arrays start at 0)
   char msg[512] = {0};
 };
 
@@ -2643,6 +2848,28 @@ hipError_t launch_fused_greedy(spec_verify_ctx* ctx, const Args& a, hipStream_t 
   const bool ordered = RG && a.B > ctx->cus;  // longest draft first, as for sampling
   Args ao = a;
   ao.order = ordered ? ctx->order : nullptr;
+  // helpers while the batch is at most four times the compute units (the longest
+  // sequences then set the time)
+  const bool help = SV_GREEDY_HELP && a.B >= ctx->cus && a.B <= 4 * ctx->cus;
+  if (help) {
+    ao.gclaim = ctx->gclaim;
+    ao.gpart = ctx->gpart;
+    ao.gbest = ctx->gbest;
+    if (++ctx->gepoch == 0) ctx->gepoch = 1;
+    ao.gepoch = ctx->gepoch;
+    hipEvent_t* ev = timing_slot(ctx, ordered ? kPathGreedyHR : kPathGreedyH);
+    int k = 0;
+    if (ordered) {
+      const hipError_t e = launch_one(reinterpret_cast<const void*>(&k_order_by_gamma), dim3(1),
+                                      dim3(kOrderThreads), ao, st, ev, k++);
+      if (e != hipSuccess) return e;
+    }
+    const hipError_t e = launch_one(reinterpret_cast<const void*>(&k_greedy_help<T, RG>),
+                                    dim3(2u * static_cast<unsigned>(a.B)), dim3(kSeqThreads), ao, st, ev, k);
+    if (e != hipSuccess) return e;
+    if (ev) ++ctx->timing_runs;
+    return hipGetLastError();
+  }
   hipEvent_t* ev = timing_slot(ctx, ordered ? kPathGreedy1R : kPathGreedy1);
   int k = 0;
   if (ordered) {
@@ -3016,13 +3243,14 @@ int spec_verify_create(spec_verify_ctx** out, int device, int vocab, int logits_
       up(sizeof(RowStat) * static_cast<size_t>(max_draft_rows > 0 ? max_draft_rows : 1) * max_split);
   const size_t n_ac = up(sizeof(int32_t) * static_cast<size_t>(max_draft_rows > 0 ? max_draft_rows : 1));
   const size_t n_lq = up(sizeof(float2) * static_cast<size_t>(max_draft_rows > 0 ? max_draft_rows : 1));
+  const size_t n_g = up(sizeof(unsigned long long) * static_cast<size_t>(max_batch > 0 ? max_batch : 1));
   const size_t n_sb = up(sizeof(int32_t) * static_cast<size_t>(max_batch > 0 ? max_batch : 1));
   const size_t n_er = 256;
   // split draw: sub-region sums and a count of finished slices per sequence
   ctx->split_cap = max_batch < kSplitMaxB ? max_batch : kSplitMaxB;
   const size_t cap = static_cast<size_t>(ctx->split_cap);
   const size_t n_ds = up(sizeof(double) * 3 * kMaxSub * cap), n_dc = up(sizeof(int) * cap);
-  if (hipMalloc(&ctx->ws, n_p1 + n_ac + 3 * n_sb + n_er + n_ds + n_dc + n_lq) != hipSuccess) {
+  if (hipMalloc(&ctx->ws, n_p1 + n_ac + 3 * n_sb + n_er + n_ds + n_dc + n_lq + 3 * n_g) != hipSuccess) {
     delete ctx;
     return SV_ENOMEM;
   }
@@ -3039,8 +3267,15 @@ int spec_verify_create(spec_verify_ctx** out, int device, int vocab, int logits_
   }
   ctx->order = reinterpret_cast<int*>(p + n_p1 + n_ac + 2 * n_sb + n_er + n_ds + n_dc);
   ctx->lxq = reinterpret_cast<float2*>(p + n_p1 + n_ac + 3 * n_sb + n_er + n_ds + n_dc);
+  {
+    char* gq = p + n_p1 + n_ac + 3 * n_sb + n_er + n_ds + n_dc + n_lq;
+    ctx->gclaim = reinterpret_cast<unsigned long long*>(gq);
+    ctx->gpart = reinterpret_cast<unsigned long long*>(gq + n_g);
+    ctx->gbest = reinterpret_cast<unsigned long long*>(gq + 2 * n_g);
+  }
   if (hipMemset(ctx->err, 0, n_er) != hipSuccess ||
-      (ctx->dcnt && hipMemset(ctx->dcnt, 0, n_dc) != hipSuccess) || hipDeviceSynchronize() != hipSuccess) {
+      (ctx->dcnt && hipMemset(ctx->dcnt, 0, n_dc) != hipSuccess) || hipMemset(ctx->gclaim, 0, 3 * n_g) != hipSuccess ||
+      hipDeviceSynchronize() != hipSuccess) {
     (void)hipFree(ctx->ws);
     delete ctx;
     return SV_EHIP;
