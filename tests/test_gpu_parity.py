@@ -609,6 +609,45 @@ def test_split_draw_repeated_calls(lib, cfg, batch):
     v.set_path(lib.SV_PATH_AUTO)
 
 
+def test_greedy_helpers_repeated_calls(lib):
+    """Greedy one-launch batches of CUs..4 x CUs sequences add helper workgroups that claim
+    rows through per-sequence counters tagged with the call's epoch: 100 calls in a row on
+    two input sets must each give the first (oracle-checked) outputs of that set; one
+    sequence more than 4 x CUs takes the kernel without helpers."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    B = 2 * cus
+    ws = [synth.make_config("C4", seed=s, batch=B, vocab=4096) for s in (21, 22)]
+    devs = [to_device(w) for w in ws]
+    v = verifier(lib, ws[0].V, ws[0].dtype, 4 * cus + 1, (4 * cus + 1) * 8)
+    first = []
+    for w, d in zip(ws, devs):
+        v.set_timing(1)
+        gpu = run_gpu(v, w, dev=d)
+        times, _ = v.kernel_times()
+        v.set_timing(0)
+        assert gpu["status"] == lib.SV_OK, v.last_error()
+        assert [n for n, _ in times] == ["k_greedy_help"], times
+        rep = compare(w, gpu, oracle_batch(w))
+        assert rep.ok(), rep.summary()
+        first.append(gpu)
+    _say("greedy helpers repeated", f"B={B}")
+    for k in range(100):
+        i = k % 2
+        gpu = run_gpu(v, ws[i], dev=devs[i])
+        for key in ("accepted_count", "emitted_tokens"):
+            assert np.array_equal(gpu[key], first[i][key]), (k, key)
+    assert v.status() == lib.SV_OK, v.last_error()
+    big = synth.make_config("C4", seed=23, batch=4 * cus + 1, vocab=4096)
+    v.set_timing(1)
+    gpu = run_gpu(v, big)
+    times, _ = v.kernel_times()
+    v.set_timing(0)
+    assert [n for n, _ in times] == ["k_greedy_seq1"], times
+    rep = compare(big, gpu, oracle_batch(big))
+    assert rep.ok(), rep.summary()
+    v.close()
+
+
 def test_side_stream_and_timing(lib):
     w = synth.make_config("C3", seed=16, batch=32)
     v = verifier(lib, w.V, w.dtype, w.B, w.draft_rows)
