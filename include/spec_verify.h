@@ -176,9 +176,9 @@ int spec_verify_run_onehot(spec_verify_ctx *ctx, void *hip_stream, int batch, in
  * first launches a one-workgroup kernel that orders the sequences by gamma_b,
  * longest first (the workspace holds the order); workgroups then take the sequences
  * in that order, so the short ones are dispatched last. A greedy one-launch run with
- * one to four times as many sequences as compute units adds one helper workgroup per
- * sequence, dispatched as slots free up, which takes rows of a sequence still being
- * judged; the outputs are the same. Both plans return the same
+ * one to four times as many sequences as compute units adds two waves of one helper
+ * workgroup per sequence, dispatched as slots free up, which take rows of a sequence
+ * still being judged; the outputs are the same. Both plans return the same
  * outputs, except that a draft id after the first rejection is not examined by the
  * one-launch plan (so it cannot raise SV_DATA_DRAFT_ID there).
  *   spec_verify_set_path(ctx, mode): SV_PATH_AUTO (default), SV_PATH_TWO_LAUNCH, or

@@ -72,6 +72,9 @@ namespace {
 #ifndef SV_GREEDY_HELP
 #define SV_GREEDY_HELP 1
 #endif
+#ifndef SV_GREEDY_WAVES
+#define SV_GREEDY_WAVES 3  // owners, then this many - 1 waves of helpers
+#endif
 constexpr int kMaxSplit = 16;
 constexpr int kMaxGamma = 1024;
 constexpr int kMaxRaggedBatch = 65536;  // row -> sequence search limit
@@ -2445,7 +2448,7 @@ template <typename T, bool RAGGED>
 __global__ __launch_bounds__(kSeqThreads) void k_greedy_help(Args a) {
   __shared__ int s_join[3];
   const bool helper = blockIdx.x >= static_cast<unsigned>(a.B);
-  const int bi0 = helper ? blockIdx.x - a.B : blockIdx.x;
+  const int bi0 = static_cast<int>(blockIdx.x % static_cast<unsigned>(a.B));
   const int b = RAGGED && a.order ? a.order[bi0] : bi0;
   int base, g;
   if (!seq_geom<RAGGED>(a, b, base, g)) {
@@ -2865,7 +2868,8 @@ hipError_t launch_fused_greedy(spec_verify_ctx* ctx, const Args& a, hipStream_t 
       if (e != hipSuccess) return e;
     }
     const hipError_t e = launch_one(reinterpret_cast<const void*>(&k_greedy_help<T, RG>),
-                                    dim3(2u * static_cast<unsigned>(a.B)), dim3(kSeqThreads), ao, st, ev, k);
+                                    dim3(SV_GREEDY_WAVES * static_cast<unsigned>(a.B)), dim3(kSeqThreads), ao, st,
+                                    ev, k);
     if (e != hipSuccess) return e;
     if (ev) ++ctx->timing_runs;
     return hipGetLastError();
