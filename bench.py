@@ -5,14 +5,19 @@ A step is one call of spec_verify_run over one batch: B = 256 sequences, gamma =
 drafts each, V = 128256, bf16 target logits, fp32 draft distributions, T = 1
 (the full hot path: row statistics + accept test, first-rejection scan,
 residual / bonus draw). Inputs are seeded synthetic data (see synth/), resident
-in HBM before timing starts; several input sets rotate so that no step re-reads
-the previous step's data from the 256 MB last-level cache.
+in HBM before timing starts; input sets rotate, as many as it takes to hold over
+1 GiB, so that no step re-reads the previous steps' data from the 256 MB
+last-level cache.
 
 Prints one JSON line on stdout:
   value       verified positions/s (sum gamma_b per step / seconds per step)
-  roofline    the dominant kernel (the row-statistics pass) against HBM peak:
-              algorithmic bytes per launch / mean launch duration from HIP events
-              recorded on the launch stream during the timed loop
+  roofline    the dominant kernel against HBM peak, from its mean launch duration
+              (HIP events recorded on the launch stream during the timed loop):
+              frac over the method's algorithmic bytes, frac_read over the bytes this
+              launch plan has to read and write, frac_traffic over the HBM bytes the
+              rocprofv3 counters measured for these kernel sources (null without them)
+  next_rows   the other workloads (C1, C2, C4, C5), the follow-on rows and the
+              per-GPU shares, each on its own rotated inputs
   cpu_baseline the CPU oracle timed on a bounded sample of the same inputs
 Diagnostics go to stderr.
 """
@@ -263,8 +268,9 @@ def bench_adaptive(sv, torch, dev, warm_rounds=10, rounds=30, c=0.05):
 
 def bench_shares(sv, torch, sets, dev, code, iters=200):
     """One GPU's share when C3 is split by sequence over G GPUs (no exchange is needed:
-    sequences are independent): the first B/G sequences of each input set, the plan the
-    library picks for that size, wall time per step."""
+    sequences are independent): B/G sequences per step, the plan the library picks for
+    that size, wall time per step. Step k takes slice (k // sets) mod G of input set
+    k mod sets, so every slice of every set is rotated through (G x sets distinct inputs)."""
     import numpy as np
     res = {}
     w0 = sets[0][0]
@@ -274,30 +280,34 @@ def bench_shares(sv, torch, sets, dev, code, iters=200):
         if b < 1 or g is None:
             continue
         v = sv.Verifier(w0.V, code, b, b * g, 16)
-        sub = [(d["logits"][: b * (g + 1)], d["q"][: b * g], d["ids"][: b * g], d["u"][: b * (g + 1)])
-               for _, d in sets]
-        out = sv.VerifyOutputs(torch.empty(b, dtype=torch.int32, device=dev),
-                               torch.empty(b * (g + 1), dtype=torch.int32, device=dev),
-                               torch.empty(b, dtype=torch.float32, device=dev), None)
-
-        def go(k):
-            L, Q, X, U = sub[k % len(sub)]
-            v.run(L, X, temperature=w0.T, q=Q, uniforms=U, gamma=g, out=out)
-        dt = _timed(torch, go, iters)
-        assert v.status() == sv.SV_OK, v.last_error()
-        plan = {sv.SV_PATH_ONE_LAUNCH: "one launch", sv.SV_PATH_TWO_LAUNCH: "two launches"}.get(v.last_path())
+        calls = []
+        for j in range(G):
+            for _, d in sets:
+                L = d["logits"][j * b * (g + 1):(j + 1) * b * (g + 1)]
+                Q = d["q"][j * b * g:(j + 1) * b * g]
+                X = d["ids"][j * b * g:(j + 1) * b * g]
+                U = d["u"][j * b * (g + 1):(j + 1) * b * (g + 1)]
+                out = sv.VerifyOutputs(torch.empty(b, dtype=torch.int32, device=dev),
+                                       torch.empty(b * (g + 1), dtype=torch.int32, device=dev),
+                                       torch.empty(b, dtype=torch.float32, device=dev), None)
+                calls.append(v.bind(L, X, temperature=w0.T, q=Q, uniforms=U, gamma=g, out=out))
+        dt, kt = timed_steps(sv, torch, v, lambda k: calls[k % len(calls)](), iters, 20, 4)
+        plan = plan_name(sv, v)
         v.close()
-        res[f"G={G}"] = {"B": b, "us_per_step": dt * 1e6, "positions_per_s": b * g / dt, "plan": plan}
-        log(f"[bench] share of G={G} GPUs (B={b}): {dt * 1e6:.1f} us/step ({plan}), "
-            f"{b * g / dt / 1e6:.2f} M positions/s per GPU")
+        res[f"G={G}"] = {"B": b, "us_per_step": dt * 1e6, "positions_per_s": b * g / dt, "plan": plan,
+                         "kernel_us": {nm: t * 1e3 for nm, t in kt}, "distinct_inputs": len(calls)}
+        log(f"[bench] share of G={G} GPUs (B={b}): {dt * 1e6:.1f} us/step ({plan}; kernels "
+            + ", ".join(f"{nm} {t * 1e3:.1f}" for nm, t in kt) + f" us), {b * g / dt / 1e6:.2f} M positions/s per GPU")
     return res
 
 
 def bench_vshard(sv, torch, sets, dev, code, G=8, iters=200):
-    """F4: one GPU's share of the workload under vocabulary sharding over G devices. Shard
-    0 holds columns [0, V/G) of every row and runs its three steps per round; the other
-    shards' records are computed once beforehand and stand in for the two all-gathers,
-    which are not timed. Reports the round's time on this device, each step alone, the
+    """F4: one GPU's part of the workload under vocabulary sharding over G devices. Every
+    shard k holds columns [bounds[k], bounds[k + 1]) of every row and has its own context;
+    round j runs the three steps of shard j mod G (so the G shards' columns, 8 x 53 MB at
+    C3, rotate through the last-level cache). The records and draw totals of the other
+    shards are computed once beforehand and stand in for the two all-gathers, which are
+    not timed. Reports the time of one shard's round on this device, each step alone, the
     shard's column bytes per round and the bytes each exchange gathers."""
     import numpy as np
     w0, d0 = sets[0]
@@ -309,63 +319,65 @@ def bench_vshard(sv, torch, sets, dev, code, G=8, iters=200):
     L2 = d0["logits"].view(R + B, V)
     Q2 = d0["q"].view(R, V)
     ids, u = d0["ids"], d0["u"]
-    shards, cols = [], []
     rec_all = torch.empty((G * R, 4), dtype=torch.float32, device=dev)
     part_all = torch.empty((G, B, sv.VSHARD_PART_DOUBLES), dtype=torch.float64, device=dev)
+    sh, cols, outs = [], [], []
     for k in range(G):
-        sh = sv.VocabShard(bounds, k, code, B, R, 16)
+        s_k = sv.VocabShard(bounds, k, code, B, R, 16)
         Lk = L2[:, bounds[k]:bounds[k + 1]].contiguous()
         Qk = Q2[:, bounds[k]:bounds[k + 1]].contiguous()
-        sh.rows(Lk, ids, temperature=T, q=Qk, gamma=g, rec=rec_all[k * R:(k + 1) * R])
-        shards.append(sh)
+        s_k.rows(Lk, ids, temperature=T, q=Qk, gamma=g, rec=rec_all[k * R:(k + 1) * R])
+        sh.append(s_k)
         cols.append((Lk, Qk))
-    outs = []
-    for k, sh in enumerate(shards):
-        o, part, loc = sh.decide(cols[k][0], ids, rec_all, temperature=T, q=cols[k][1], uniforms=u, gamma=g,
-                                 want_p_draft=False)
+    for k in range(G):
+        o, part, loc = sh[k].decide(cols[k][0], ids, rec_all, temperature=T, q=cols[k][1], uniforms=u, gamma=g,
+                                    want_p_draft=False)
         part_all[k].copy_(part)
         outs.append((o, loc))
-    sh0, (L0, Q0), (out, loc0) = shards[0], cols[0], outs[0]
-    for sh in shards[1:]:
-        sh.close()
-    del cols[1:], outs[1:]
     st = torch.cuda.current_stream(dev)
-    ctx, desc = sh0.ver.ctx, sh0.desc
 
-    def rows(k):
-        sv.spec_vshard_rows(ctx, st, desc, B, g, None, R, T, L0, Q0, ids, rec_all[:R])
+    def rows(j):
+        k = j % G
+        sv.spec_vshard_rows(sh[k].ver.ctx, st, sh[k].desc, B, g, None, R, T, cols[k][0], cols[k][1], ids,
+                            rec_all[k * R:(k + 1) * R])
 
-    def decide(k):
-        sv.spec_vshard_decide(ctx, st, desc, B, g, None, R, T, L0, Q0, ids, u, rec_all, out.accepted_count,
-                              out.emitted_tokens, out.residual_sum, None, part_all[0], loc0)
+    def decide(j):
+        k = j % G
+        o, loc = outs[k]
+        sv.spec_vshard_decide(sh[k].ver.ctx, st, sh[k].desc, B, g, None, R, T, cols[k][0], cols[k][1], ids, u,
+                              rec_all, o.accepted_count, o.emitted_tokens, o.residual_sum, None, part_all[k], loc)
 
-    def finish(k):
-        sv.spec_vshard_finish(ctx, st, desc, B, g, None, R, T, L0, Q0, u, part_all, loc0, out.emitted_tokens,
-                              out.residual_sum)
+    def finish(j):
+        k = j % G
+        o, loc = outs[k]
+        sv.spec_vshard_finish(sh[k].ver.ctx, st, sh[k].desc, B, g, None, R, T, cols[k][0], cols[k][1], u,
+                              part_all, loc, o.emitted_tokens, o.residual_sum)
 
-    def round_(k):
-        rows(k)
-        decide(k)
-        finish(k)
+    def round_(j):
+        rows(j)
+        decide(j)
+        finish(j)
     dt = _timed(torch, round_, iters)
     steps = {nm: _timed(torch, fn, iters) * 1e6 for nm, fn in
              (("k_vs_rows", rows), ("k_vs_decide", decide), ("k_vs_finish", finish))}
-    assert sh0.status() == sv.SV_OK, sh0.last_error()
-    acc = out.accepted_count.cpu().numpy()
-    sh0.close()
-    W = bounds[1]
+    for s_k in sh:
+        assert s_k.status() == sv.SV_OK, s_k.last_error()
+    acc = outs[0][0].accepted_count.cpu().numpy()
+    for s_k in sh:
+        s_k.close()
+    W = float(np.mean([bounds[k + 1] - bounds[k] for k in range(G)]))
     s_l = 2 if code == sv.SV_BF16 else 4
     n_res = int((acc < g).sum())
     col_bytes = R * W * s_l + B * W * s_l + n_res * W * 4
-    res = {"workload": f"C3 columns [0, {W}) of {G} shards: B={B} gamma={g} V={V}",
+    res = {"workload": f"C3 columns of one of {G} shards ({W:.0f} columns), the shards rotated: B={B} gamma={g} V={V}",
            "us_per_round": dt * 1e6, "step_us": steps,
            "positions_per_s_device_part": R / dt, "column_bytes_per_round": col_bytes,
            "column_GBps": col_bytes / dt / 1e9,
            "gathered_bytes": {"records": G * R * sv.VSHARD_REC_BYTES,
                               "draw_totals": G * B * sv.VSHARD_PART_DOUBLES * 8}}
-    log(f"[bench] F4 vocab shard (1 of {G}, {W} columns): {dt * 1e6:.1f} us/round on this device "
-        f"(rows {steps['k_vs_rows']:.1f}, decide {steps['k_vs_decide']:.1f}, finish {steps['k_vs_finish']:.1f} us "
-        f"alone), {col_bytes / dt / 1e9:.0f} GB/s over its columns; all-gathers of "
+    log(f"[bench] F4 vocab shard (1 of {G}, {W:.0f} columns, shards rotated): {dt * 1e6:.1f} us/round on this "
+        f"device (rows {steps['k_vs_rows']:.1f}, decide {steps['k_vs_decide']:.1f}, finish "
+        f"{steps['k_vs_finish']:.1f} us alone), {col_bytes / dt / 1e9:.0f} GB/s over its columns; all-gathers of "
         f"{G * R * sv.VSHARD_REC_BYTES / 1e3:.0f} KB and {G * B * 24 / 1e3:.0f} KB")
     return res
 
@@ -395,20 +407,162 @@ def cpu_baseline(w, seconds):
                        f"({w.B} sequences), float64 NumPy oracle in one process, {dt:.1f} s")
 
 
+SET_BYTES_TARGET = 1 << 30  # rotated input bytes per workload (four times the 256 MB last-level cache)
+MAX_SETS = 16
+
+
+def input_bytes(w):
+    """Bytes of one input set of workload w (logits, q, ids, uniforms)."""
+    return (w.logits.nbytes + (w.q.nbytes if w.q is not None else 0) + w.draft_ids.nbytes
+            + (w.uniforms.nbytes if w.uniforms is not None else 0))
+
+
+def auto_sets(config):
+    """Input sets to rotate for `config`: enough to hold SET_BYTES_TARGET, at least two
+    unless one set alone is that large."""
+    import synth
+    w = synth.make_config(config, seed=0)
+    per = input_bytes(w)
+    n = -(-SET_BYTES_TARGET // per)
+    return max(1 if per >= SET_BYTES_TARGET else 2, min(MAX_SETS, n))
+
+
+def load_sets(torch, config, n, dev, batch=None):
+    """n seeded input sets of `config` resident on the device: [(workload, tensors)]."""
+    import numpy as np
+    import synth
+    sets = []
+    for s in range(n):
+        w = synth.make_config(config, seed=s, batch=batch)
+        d = {}
+        if w.dtype == "bf16":
+            d["logits"] = torch.from_numpy(w.logits.view(np.int16)).view(torch.bfloat16).to(dev)
+        else:
+            d["logits"] = torch.from_numpy(w.logits).to(dev)
+        d["q"] = torch.from_numpy(w.q).to(dev) if w.q is not None else None
+        d["ids"] = torch.from_numpy(w.draft_ids).to(dev)
+        d["u"] = torch.from_numpy(w.uniforms).to(dev) if w.uniforms is not None else None
+        d["cu"] = torch.from_numpy(w.cu_gamma).to(dev)
+        sets.append((w, d))
+    return sets
+
+
+class Steps:
+    """Bound steps over rotated input sets on one context: step k runs set k mod n with
+    its own output buffers (p(x) requested when want_p)."""
+
+    def __init__(self, sv, torch, ver, sets, dev, want_p=False):
+        self.sets, self.outs, self.calls = sets, [], []
+        ragged = sets[0][0].uniform_gamma is None
+        for w, d in sets:
+            o = sv.VerifyOutputs(torch.empty(w.B, dtype=torch.int32, device=dev),
+                                 torch.empty(w.target_rows, dtype=torch.int32, device=dev),
+                                 torch.empty(w.B, dtype=torch.float32, device=dev),
+                                 torch.empty(w.draft_rows, dtype=torch.float32, device=dev)
+                                 if want_p and w.T > 0 else None)
+            kw = (dict(cu_gamma=d["cu"], total_draft_rows=w.draft_rows) if ragged
+                  else dict(gamma=w.uniform_gamma))
+            self.calls.append(ver.bind(d["logits"], d["ids"], temperature=w.T, q=d["q"], uniforms=d["u"],
+                                       out=o, **kw))
+            self.outs.append(o)
+
+    def __call__(self, k):
+        self.calls[k % len(self.calls)]()
+
+
+def timed_steps(sv, torch, ver, steps, n, warmup, stride):
+    """Wall seconds per step over n steps (after warmup) and the per-kernel mean
+    durations [(name, ms)] from dispatch events on one step in every `stride`."""
+    for k in range(warmup):
+        steps(k)
+    torch.cuda.synchronize()
+    ver.set_timing((n + stride - 1) // stride, stride)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(n):
+        steps(k)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ktimes, kruns = ver.kernel_times()
+    ver.set_timing(0)
+    assert ver.status() == sv.SV_OK, ver.last_error()
+    assert kruns == (n + stride - 1) // stride, (kruns, n, stride)
+    return (t1 - t0) / n, ktimes
+
+
+def plan_name(sv, ver):
+    return {sv.SV_PATH_ONE_LAUNCH: "one launch", sv.SV_PATH_TWO_LAUNCH: "two launches"}.get(ver.last_path())
+
+
+def traffic_tag(config, one_launch):
+    return f"{config}-{'one' if one_launch else 'two'}"
+
+
+def bench_config(sv, torch, dev, config, n_steps, warmup, stride, plan="auto", batch=None, n_sets=None):
+    """One workload on its own rotated inputs: wall time per step, per-kernel dispatch
+    times, the method's bytes and the bytes the plan reads, against the HBM peak."""
+    import numpy as np
+    import synth
+    n_sets = n_sets or auto_sets(config)
+    sets = load_sets(torch, config, n_sets, dev, batch)
+    w0 = sets[0][0]
+    code = sv.SV_BF16 if w0.dtype == "bf16" else sv.SV_F32
+    ver = sv.Verifier(w0.V, code, w0.B, max(w.draft_rows for w, _ in sets), 16)
+    ver.set_path({"auto": sv.SV_PATH_AUTO, "two": sv.SV_PATH_TWO_LAUNCH, "one": sv.SV_PATH_ONE_LAUNCH}[plan])
+    steps = Steps(sv, torch, ver, sets, dev)
+    acc = []
+    for k in range(len(sets)):
+        steps(k)
+        torch.cuda.synchronize()
+        assert ver.status() == sv.SV_OK, ver.last_error()
+        acc.append(steps.outs[k].accepted_count.cpu().numpy())
+    one = ver.last_path() == sv.SV_PATH_ONE_LAUNCH
+    plan_txt = plan_name(sv, ver)
+    dt, kt = timed_steps(sv, torch, ver, steps, n_steps, warmup, stride)
+    ver.close()
+    method = float(np.mean([method_bytes(w, n) for (w, _), n in zip(sets, acc)]))
+    needed = float(np.mean([needed_bytes(w, n, one) for (w, _), n in zip(sets, acc)]))
+    k_us = sum(t for _, t in kt) * 1e3
+    pos = float(np.mean([w.draft_rows for w, _ in sets]))
+    cfgd = synth.CONFIGS[config]
+    res = {
+        "workload": (f"{config}: B={w0.B} gamma={cfgd['gamma'] if w0.uniform_gamma else 'ragged 1..8'} "
+                     f"V={w0.V} {w0.dtype} logits" + (", fp32 q" if w0.T > 0 else ", greedy") + f", T={w0.T:g}"),
+        "plan": plan_txt, "input_sets": n_sets, "rotated_MB": n_sets * input_bytes(w0) / 1e6,
+        "steps": n_steps, "us_per_step": dt * 1e6, "kernel_us": {nm: t * 1e3 for nm, t in kt},
+        "kernel_us_total": k_us, "positions_per_s": pos / dt,
+        "method_MB": method / 1e6, "read_MB": needed / 1e6,
+        "frac_method": method / (k_us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+        "frac_read": needed / (k_us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+    }
+    # counter bytes of every kernel of the step, where profiles of these sources exist
+    trs = [0.0 if nm == "k_order_by_gamma" else counter_traffic(nm, traffic_tag(config, one)) for nm, _ in kt]
+    tr = sum(trs) if all(t is not None for t in trs) else None
+    res["traffic_MB"] = tr / 1e6 if tr else None
+    res["frac_traffic"] = tr / (k_us * 1e-6) / 1e9 / HBM_PEAK_GBPS if tr else None
+    log(f"[bench] {config}: {dt * 1e6:.2f} us/step ({plan_txt}; kernels "
+        + ", ".join(f"{nm} {t * 1e3:.2f}" for nm, t in kt) + f" us), {pos / dt / 1e6:.2f} M positions/s, "
+        f"reads {needed / 1e6:.1f} MB: {res['frac_read']:.1%} of peak over the kernels' time; "
+        f"{n_sets} sets ({res['rotated_MB']:.0f} MB) rotated")
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default="C3", help="workload (C3 is the measured one; others for development)")
-    ap.add_argument("--sets", type=int, default=2, help="input sets rotated across steps")
+    ap.add_argument("--sets", type=int, default=0, help="input sets rotated across steps (0: enough for 1 GiB)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-next", action="store_true", help="skip the follow-on measurements (sampling, adaptive gamma, deterministic drafts)")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the other workloads and the follow-on measurements")
     ap.add_argument("--no-every-row", action="store_true",
                     help="skip the second timing with p(x) requested (every draft row read)")
     ap.add_argument("--plan", choices=("auto", "two", "one"), default="auto",
-                    help="launch plan (auto: one launch when B >= the number of compute units)")
+                    help="launch plan (auto: the library's choice by batch size)")
+    ap.add_argument("--batch", type=int, default=None, help="sequences per step (default: the workload's)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run plain device copies of MIB MiB (calibrates the HBM byte counters)")
     args = ap.parse_args()
@@ -442,41 +596,15 @@ def main():
         return
     sv.load_library()
 
-    log(f"[bench] generating {args.sets} input set(s) of {args.config}")
-    sets = []
-    for s in range(args.sets):
-        w = synth.make_config(args.config, seed=s)
-        d = {}
-        if w.dtype == "bf16":
-            d["logits"] = torch.from_numpy(w.logits.view(np.int16)).view(torch.bfloat16).to(dev)
-        else:
-            d["logits"] = torch.from_numpy(w.logits).to(dev)
-        d["q"] = torch.from_numpy(w.q).to(dev) if w.q is not None else None
-        d["ids"] = torch.from_numpy(w.draft_ids).to(dev)
-        d["u"] = torch.from_numpy(w.uniforms).to(dev) if w.uniforms is not None else None
-        d["cu"] = torch.from_numpy(w.cu_gamma).to(dev)
-        sets.append((w, d))
+    n_sets = args.sets or auto_sets(args.config)
+    log(f"[bench] generating {n_sets} input set(s) of {args.config}")
+    sets = load_sets(torch, args.config, n_sets, dev, args.batch)
     w0 = sets[0][0]
     ragged = w0.uniform_gamma is None
     code = sv.SV_BF16 if w0.dtype == "bf16" else sv.SV_F32
     ver = sv.Verifier(w0.V, code, w0.B, max(w.draft_rows for w, _ in sets), 16)
     ver.set_path({"auto": sv.SV_PATH_AUTO, "two": sv.SV_PATH_TWO_LAUNCH, "one": sv.SV_PATH_ONE_LAUNCH}[args.plan])
-
-    outs = []
-    for w, d in sets:
-        outs.append(sv.VerifyOutputs(
-            torch.empty(w.B, dtype=torch.int32, device=dev),
-            torch.empty(w.target_rows, dtype=torch.int32, device=dev),
-            torch.empty(w.B, dtype=torch.float32, device=dev), None))
-
-    def step(k):
-        w, d = sets[k % len(sets)]
-        if ragged:
-            ver.run(d["logits"], d["ids"], temperature=w.T, q=d["q"], uniforms=d["u"],
-                    cu_gamma=d["cu"], total_draft_rows=w.draft_rows, out=outs[k % len(sets)])
-        else:
-            ver.run(d["logits"], d["ids"], temperature=w.T, q=d["q"], uniforms=d["u"],
-                    gamma=w.uniform_gamma, out=outs[k % len(sets)])
+    step = Steps(sv, torch, ver, sets, dev)
 
     # untimed: outputs of each set fix the algorithmic bytes of its steps
     nb = []
@@ -484,31 +612,16 @@ def main():
         step(k)
         torch.cuda.synchronize()
         assert ver.status() == sv.SV_OK, ver.last_error()
-        nb.append(outs[k].accepted_count.cpu().numpy())
+        nb.append(step.outs[k].accepted_count.cpu().numpy())
     one_launch = ver.last_path() == sv.SV_PATH_ONE_LAUNCH  # stops reading rows at the first rejection
     method_per_set = [method_bytes(w, n) for (w, _), n in zip(sets, nb)]
     needed_per_set = [needed_bytes(w, n, one_launch) for (w, _), n in zip(sets, nb)]
 
-    for k in range(args.warmup):
-        step(k)
-    torch.cuda.synchronize()
-
-    # timed loop: per-kernel HIP events (start and stop of the dispatch itself, on the
-    # launch stream) for one step in every TIMING_STRIDE, which keeps their cost out of
-    # the wall clock
-    ver.set_timing((args.steps + TIMING_STRIDE - 1) // TIMING_STRIDE, TIMING_STRIDE)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(k)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ktimes, kruns = ver.kernel_times()
-    ver.set_timing(0)
-    assert ver.status() == sv.SV_OK, ver.last_error()
-    assert kruns == (args.steps + TIMING_STRIDE - 1) // TIMING_STRIDE
-
-    ms = (t1 - t0) * 1e3 / args.steps
+    # timed loop: exactly args.steps steps between two device synchronizations; per-kernel
+    # HIP events (start and stop of the dispatch itself, on the launch stream) on one step
+    # in every TIMING_STRIDE, which keeps their cost out of the wall clock
+    sec, ktimes = timed_steps(sv, torch, ver, step, args.steps, args.warmup, TIMING_STRIDE)
+    ms = sec * 1e3
     pos_per_step = np.mean([w.draft_rows for w, _ in sets])
     value = pos_per_step / (ms * 1e-3)
     path_bytes = float(np.mean([method_per_set[k % len(sets)] for k in range(args.steps)]))
@@ -527,40 +640,34 @@ def main():
     else:
         k1_bytes = float(np.mean([w.draft_rows * (w.V * sl + 8) for w, _ in sets]))
         k1_needed = k1_bytes
-    k1_gbps = k1_bytes / (kt[k1] * 1e-3) / 1e9
+    k1_s = kt[k1] * 1e-3
+    k1_gbps = k1_bytes / k1_s / 1e9
+    traffic = counter_traffic(k1, traffic_tag(args.config, one_launch))
 
     # the same steps with p(x) requested for every draft: the one-launch plan then reads
     # every draft row, as the two-launch plan always does
     all_rows = None
     if one_launch and not w0.T == 0.0 and not args.no_every_row:
-        outs_p = [sv.VerifyOutputs(o.accepted_count, o.emitted_tokens, o.residual_sum,
-                                   torch.empty(w.draft_rows, dtype=torch.float32, device=dev))
-                  for o, (w, _) in zip(outs, sets)]
-        saved = list(outs)
-        outs[:] = outs_p
-        for k in range(args.warmup):
-            step(k)
-        torch.cuda.synchronize()
-        ver.set_timing((args.steps + TIMING_STRIDE - 1) // TIMING_STRIDE, TIMING_STRIDE)
-        t2 = time.perf_counter()
-        for k in range(args.steps):
-            step(k)
-        torch.cuda.synchronize()
-        t3 = time.perf_counter()
-        kt_all, _ = ver.kernel_times()
-        ver.set_timing(0)
-        assert ver.status() == sv.SV_OK, ver.last_error()
-        outs[:] = saved
-        ms_all = (t3 - t2) * 1e3 / args.steps
+        step_p = Steps(sv, torch, ver, sets, dev, want_p=True)
+        sec_all, kt_all = timed_steps(sv, torch, ver, step_p, args.steps, args.warmup, TIMING_STRIDE)
+        ms_all = sec_all * 1e3
         all_rows = {"ms_per_step": ms_all, "value": pos_per_step / (ms_all * 1e-3),
                     "kernel_us": {nm: t * 1e3 for nm, t in kt_all},
-                    "achieved_GBps": path_bytes / (kt_all[0][1] * 1e-3) / 1e9}
+                    "achieved_GBps": path_bytes / (kt_all[-1][1] * 1e-3) / 1e9,
+                    "frac_of_peak": path_bytes / (kt_all[-1][1] * 1e-3) / 1e9 / HBM_PEAK_GBPS}
         log(f"[bench] every row read (p(x) requested): {ms_all * 1e3:.2f} us/step, "
-            f"{all_rows['value'] / 1e6:.2f} M positions/s")
+            f"{all_rows['value'] / 1e6:.2f} M positions/s, kernel {kt_all[-1][1] * 1e3:.2f} us "
+            f"({all_rows['frac_of_peak']:.1%} of peak over the method's bytes, all of which it reads)")
 
-    # follow-on F1: one token per row from a given distribution, on this workload's rows
+    # the other workloads, each on its own rotated inputs, then the follow-on rows
     next_rows = {}
     if not args.no_next and w0.T > 0:
+        cfgs = {}
+        for cname, n, stride in (("C1", 2000, 1), ("C2", 400, 4), ("C4", 100, 4), ("C5", 60, 2)):
+            if cname != args.config:
+                cfgs[cname] = bench_config(sv, torch, dev, cname, n, 20, stride)
+                torch.cuda.empty_cache()
+        next_rows["configs"] = cfgs
         next_rows["F1_sample"] = bench_sampling(sv, torch, sets, dev, code, args)
         next_rows["per_gpu_share"] = bench_shares(sv, torch, sets, dev, code)
         next_rows["F2_adaptive_gamma"] = bench_adaptive(sv, torch, dev)
@@ -576,6 +683,9 @@ def main():
         f"{path_bytes / 1e6:.1f} MB/step; this plan reads {needed / 1e6:.1f} MB/step")
     for name, t in ktimes:
         log(f"[bench]   {name:20s} {t * 1e3:8.2f} us")
+    log(f"[bench] {k1}: frac {k1_gbps / HBM_PEAK_GBPS:.3f} (method bytes), "
+        f"frac_read {k1_needed / k1_s / 1e9 / HBM_PEAK_GBPS:.3f} (bytes read), frac_traffic "
+        + (f"{traffic / k1_s / 1e9 / HBM_PEAK_GBPS:.3f} (counter bytes)" if traffic else "n/a (no counters for these sources)"))
     log(f"[bench] acceptance: alpha_hat={alpha_hat:.4f} tokens/round={np.mean(acc + 1):.4f} "
         f"accepted/drafted={acc.sum() / gam.sum():.4f}")
 
@@ -598,6 +708,7 @@ def main():
                          + (", fp32 q" if w0.T > 0 else ", greedy") + f", T={w0.T:g}"),
             "B": w0.B, "gamma": cfgd["gamma"] if not ragged else "ragged 1..8", "V": w0.V,
             "logits": w0.dtype, "T": w0.T, "input_sets": len(sets),
+            "rotated_MB": len(sets) * input_bytes(w0) / 1e6,
         },
         "roofline": {
             "bound": "hbm",
@@ -606,12 +717,15 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": k1_gbps / HBM_PEAK_GBPS,
-            "traffic": counter_traffic(k1, f"{args.config}-{'one' if one_launch else 'two'}"),
+            "traffic": traffic,
             "bytes_per_launch": k1_bytes,
             "bytes_basis": ("the two-pass method's bytes per sequence (every draft row, the drawn row, "
                             "q of the rejected row, ids, uniforms, outputs) from this run's accepted counts"),
             "needed_bytes_per_launch": k1_needed,
-            "needed_GBps": k1_needed / (kt[k1] * 1e-3) / 1e9,
+            "needed_GBps": k1_needed / k1_s / 1e9,
+            "frac_read": k1_needed / k1_s / 1e9 / HBM_PEAK_GBPS,
+            "frac_traffic": traffic / k1_s / 1e9 / HBM_PEAK_GBPS if traffic else None,
+            "kernel_us": kt[k1] * 1e3,
         },
         "path": {
             "plan": "one launch, stops reading rows at the first rejection" if one_launch else "two launches",

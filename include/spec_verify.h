@@ -56,6 +56,12 @@
  *   - a judged or sampled row whose softmax normaliser is not finite or not
  *     positive (NaN / +inf logits, or a row of -inf): flagged; outputs for that
  *     sequence are unspecified but in range;
+ *   - greedy mode (T == 0): a NaN logit in a judged row (a draft row up to the
+ *     first mismatch, or the bonus row when it is read) raises the same flag
+ *     (SV_DATA_NONFINITE); outputs for that sequence are unspecified but in range.
+ *     -inf logits are values (a row of -inf has its argmax at index 0). A NaN in a
+ *     row after the first mismatch is examined by the two-launch plan (which judges
+ *     every draft row) and may or may not be by the one-launch plan;
  *   - malformed cu_gamma (decreasing, gamma_b > max_gamma, cu_gamma[B] !=
  *     total_draft_rows): flagged; that sequence's accepted_count is -1 and its
  *     other outputs are not written.

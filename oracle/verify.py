@@ -103,13 +103,13 @@ def inverse_cdf(weights: np.ndarray, u: float):
 
 
 def first_argmax(row) -> int:
-    """Greedy target token: argmax with the lowest index on ties.
-
-    A NaN logit is not a value of the target and never wins (reading: the pages define
-    greedy as taking the target's most likely token and say nothing of NaN); a row with
-    nothing above -inf gives index 0."""
-    x = np.asarray(row, dtype=np.float64)
-    return int(np.argmax(np.where(np.isnan(x), -np.inf, x)))
+    """Greedy target token: the most likely target token, argmax of the logits with the
+    lowest index on ties ([P1] ch.3 greedy paragraph; [P4] "출력이 변하지 않는다는 것이
+    핵심이다"). Defined for the input domain of finite logits (-inf allowed); a row of
+    -inf gives index 0. A NaN logit is outside the domain: the library reports it as a
+    data error and its outputs for that sequence are unspecified, so the oracle gives
+    no answer of its own for such rows."""
+    return int(np.argmax(np.asarray(row, dtype=np.float64)))
 
 
 @dataclasses.dataclass

@@ -162,6 +162,24 @@ def spec_verify_run(ctx: int, stream, batch: int, gamma: int, cu_gamma, total_dr
         raise SpecVerifyError(rc, _msg(ctx))
 
 
+def spec_verify_run_bound(ctx: int, stream, batch: int, gamma: int, cu_gamma, total_draft_rows: int,
+                          temperature: float, logits, q, draft_ids, uniforms, accepted_count,
+                          emitted_tokens, residual_sum, p_draft=None):
+    """spec_verify_run with its arguments marshalled once. Returns a function of no
+    arguments that enqueues the same step (same buffers, same stream) each time it is
+    called, so a loop of steps pays one foreign call per step and no conversions."""
+    fn = load_library().spec_verify_run
+    args = (ctx, _stream(stream), batch, gamma, _ptr(cu_gamma), total_draft_rows, float(temperature),
+            _ptr(logits), _ptr(q), _ptr(draft_ids), _ptr(uniforms), _ptr(accepted_count),
+            _ptr(emitted_tokens), _ptr(residual_sum), _ptr(p_draft))
+
+    def go():
+        rc = fn(*args)
+        if rc != SV_OK:
+            raise SpecVerifyError(rc, _msg(ctx))
+    return go
+
+
 def spec_verify_run_onehot(ctx: int, stream, batch: int, gamma: int, cu_gamma, total_draft_rows: int,
                            temperature: float, logits, draft_ids, uniforms, accepted_count,
                            emitted_tokens, residual_sum, p_draft=None) -> None:

@@ -257,11 +257,13 @@ __device__ __forceinline__ void block_row_lse(const T* row, int lo, int hi, floa
 }
 
 // Max raw logit of entries [lo, hi) of one row and its lowest index, over a kThreads
-// block; thread 0 returns them. A range of -inf (or NaN) entries yields its first index.
+// block; thread 0 returns them. A range of -inf entries yields its first index. A NaN
+// entry raises SV_DATA_NONFINITE in *err (the argmax is then unspecified).
 template <typename T, bool ALIGNED>
 __device__ __forceinline__ void block_row_argmax(const T* row, int lo, int hi, float* s_v, int* s_i, float& Vout,
-                                                 int& Iout) {
+                                                 int& Iout, int* err) {
   float bv = -INFINITY;
+  float nw = -INFINITY;  // NaN watch
   int bi = INT_MAX;
   if (ALIGNED) {
     const int g1 = hi >> 3;
@@ -272,17 +274,20 @@ __device__ __forceinline__ void block_row_argmax(const T* row, int lo, int hi, f
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) load_group(row, static_cast<size_t>(g + u * kThreads) * kGroup, xv[u]);
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u)
+      for (int u = 0; u < kUnroll; ++u) {
+        nw = nan_watch(nw, xv[u]);
 #pragma unroll
         for (int j = 0; j < kGroup; ++j)
           if (xv[u][j] > bv) {
             bv = xv[u][j];
             bi = (g + u * kThreads) * kGroup + j;
           }
+      }
     }
     for (; g < g1; g += kThreads) {
       float xv[kGroup];
       load_group(row, static_cast<size_t>(g) * kGroup, xv);
+      nw = nan_watch(nw, xv);
 #pragma unroll
       for (int j = 0; j < kGroup; ++j)
         if (xv[j] > bv) {
@@ -295,12 +300,14 @@ __device__ __forceinline__ void block_row_argmax(const T* row, int lo, int hi, f
     if (e < hi) bi = e;
     for (; e < hi; e += kThreads) {
       const float xv = load_one(row, e);
+      nw = nan_watch1(nw, xv);
       if (xv > bv) {
         bv = xv;
         bi = e;
       }
     }
   }
+  flag_nan(nw, err, SV_DATA_NONFINITE);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const float v2 = __shfl_xor(bv, o);
@@ -367,7 +374,7 @@ __global__ __launch_bounds__(kThreads) void k_rowargmax(Args a) {
   const int lo = k * a.span, hi = min(a.V, lo + a.span);
   float V;
   int I;
-  block_row_argmax<T, ALIGNED>(row, lo, hi, s_v, s_i, V, I);
+  block_row_argmax<T, ALIGNED>(row, lo, hi, s_v, s_i, V, I, a.err);
   if (threadIdx.x == 0) {
     a.p1[blockIdx.x] = RowStat{V, __int_as_float(I)};
     if (ACCEPT) {
@@ -1581,7 +1588,7 @@ __global__ __launch_bounds__(kThreads) void k_vs_rows(Args a, VShard vs) {
   if constexpr (GREEDY) {
     float V;
     int I;
-    block_row_argmax<T, ALIGNED>(row, 0, a.V, s_c, s_i, V, I);
+    block_row_argmax<T, ALIGNED>(row, 0, a.V, s_c, s_i, V, I, a.err);
     if (threadIdx.x == 0) vs.rec[r] = ShardRec{V, __int_as_float(I == INT_MAX ? INT_MAX : I + v0), 0.f, 0.f};
   } else {
     float lx = 0.f, qx = 0.f;
@@ -2252,11 +2259,13 @@ __global__ __launch_bounds__(kSeqThreads) void k_greedy_seq1(Args a) {
     return wide ? (k < nsp - 1 ? k * kSpan : V - kSpan) + lane_off : min(lane_off, V - kGroup);
   };
   float bv = -INFINITY;
-  int bi = entry0(0);  // a row of -inf (or NaN) still yields its lowest index
+  float nw = -INFINITY;  // NaN watch of the row
+  int bi = entry0(0);  // a row of -inf still yields its lowest index
   int n = g, tok = -1;
   auto step = [&](const Raw<T>& lr, int k) {
     float xv[kGroup];
     unpack(lr, xv);
+    nw = nan_watch(nw, xv);
     const int e = entry0(k);
 #pragma unroll
     for (int j = 0; j < kGroup; ++j)
@@ -2266,6 +2275,9 @@ __global__ __launch_bounds__(kSeqThreads) void k_greedy_seq1(Args a) {
       }
   };
   auto row_end = [&](int i) -> bool {
+    // a NaN in a judged row is a data error; the argmax is then unspecified
+    flag_nan(nw, a.err, SV_DATA_NONFINITE);
+    nw = -INFINITY;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
       const float v2 = __shfl_xor(bv, o);
@@ -2346,10 +2358,12 @@ __device__ __forceinline__ void greedy_participate(const Args& a, int b, int bas
     return L0 + static_cast<size_t>(r) * V;
   };
   float bv = -INFINITY;
+  float nw = -INFINITY;  // NaN watch of the row
   int bi = entry0(0);
   auto step = [&](const Raw<T>& lr, int k) {
     float xv[kGroup];
     unpack(lr, xv);
+    nw = nan_watch(nw, xv);
     const int e = entry0(k);
 #pragma unroll
     for (int q = 0; q < kGroup; ++q)
@@ -2360,6 +2374,8 @@ __device__ __forceinline__ void greedy_participate(const Args& a, int b, int bas
   };
   auto row_end = [&](int t) -> bool {
     const int i = rc;  // the row just read
+    flag_nan(nw, a.err, SV_DATA_NONFINITE);  // a NaN in a row this participant judged
+    nw = -INFINITY;
     // the next claim and the published minimum, loaded now so the merge hides them
     unsigned long long nc = 0, nb = ~0ull;
     if (threadIdx.x == 0) {
@@ -2651,6 +2667,7 @@ __global__ __launch_bounds__(kSeqThreads) void k_greedy_seq(Args a) {
   if (n == g) {  // the bonus row is read only when every draft was accepted
     const T* row = static_cast<const T*>(a.logits) + static_cast<size_t>(base + b + g) * a.V;
     float bv = -INFINITY;
+    float nw = -INFINITY;  // NaN watch of the bonus row
     int bi = INT_MAX;
     if (ALIGNED) {
       const int g1 = a.V >> 3;
@@ -2661,17 +2678,20 @@ __global__ __launch_bounds__(kSeqThreads) void k_greedy_seq(Args a) {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) load_group(row, static_cast<size_t>(gi + u * kSeqThreads) * kGroup, xv[u]);
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
+        for (int u = 0; u < kUnroll; ++u) {
+          nw = nan_watch(nw, xv[u]);
 #pragma unroll
           for (int j = 0; j < kGroup; ++j)
             if (xv[u][j] > bv) {
               bv = xv[u][j];
               bi = (gi + u * kSeqThreads) * kGroup + j;
             }
+        }
       }
       for (; gi < g1; gi += kSeqThreads) {
         float xv[kGroup];
         load_group(row, static_cast<size_t>(gi) * kGroup, xv);
+        nw = nan_watch(nw, xv);
 #pragma unroll
         for (int j = 0; j < kGroup; ++j)
           if (xv[j] > bv) {
@@ -2684,12 +2704,14 @@ __global__ __launch_bounds__(kSeqThreads) void k_greedy_seq(Args a) {
       if (e < a.V) bi = e;
       for (; e < a.V; e += kSeqThreads) {
         const float xv = load_one(row, e);
+        nw = nan_watch1(nw, xv);
         if (xv > bv) {
           bv = xv;
           bi = e;
         }
       }
     }
+    flag_nan(nw, a.err, SV_DATA_NONFINITE);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
       const float v2 = __shfl_xor(bv, o);

@@ -294,6 +294,22 @@ __device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2)
   if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
 }
 
+// NaN watch of the greedy rows: a NaN-propagating running max (IEEE maximum, one
+// v_maximum3_f32 per two entries) of every entry a lane reads, NaN afterwards iff one
+// of the entries was NaN. Start it at -inf.
+__device__ __forceinline__ float nan_watch(float t, const float (&x)[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; j += 2)
+    t = __builtin_elementwise_maximum(t, __builtin_elementwise_maximum(x[j], x[j + 1]));
+  return t;
+}
+__device__ __forceinline__ float nan_watch1(float t, float x) { return __builtin_elementwise_maximum(t, x); }
+// Raises `bit` in *err (once per wave) when a lane's watch holds NaN. Every lane of the
+// wave calls it.
+__device__ __forceinline__ void flag_nan(float t, int* err, int bit) {
+  if (__ballot(t != t) != 0 && (threadIdx.x & 63) == 0) atomicOr(err, bit);
+}
+
 // Largest b in [0, B) with cu[b] <= d, for a non-decreasing cu with cu[0] = 0
 // (B <= 65536). Every thread of the block calls it; result valid in all threads.
 __device__ __forceinline__ int seq_of_row(const int32_t* __restrict__ cu, int B, int d) {

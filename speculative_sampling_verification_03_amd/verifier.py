@@ -9,7 +9,7 @@ from typing import NamedTuple, Optional
 
 from .binding import (SV_BF16, SV_EDATA, SV_F32, spec_verify_create, spec_verify_destroy,
                       spec_verify_kernel_times, spec_verify_last_error, spec_verify_last_path,
-                      spec_verify_run, spec_verify_set_path, spec_verify_set_timing,
+                      spec_verify_run, spec_verify_run_bound, spec_verify_set_path, spec_verify_set_timing,
                       spec_verify_set_timing_stride, spec_verify_status, spec_sample_run,
                       spec_verify_run_onehot, spec_ngram_propose, spec_adapt_gamma,
                       SV_SAMPLE_LOGITS, SV_SAMPLE_WEIGHTS, spec_vshard_rows, spec_vshard_decide,
@@ -114,6 +114,28 @@ class Verifier:
                             None if greedy else q, draft_ids, None if greedy else uniforms,
                             out.accepted_count, out.emitted_tokens, out.residual_sum, out.p_draft)
         return out
+
+    def bind(self, logits, draft_ids, *, temperature: float, q=None, uniforms=None,
+             gamma: Optional[int] = None, cu_gamma=None, total_draft_rows: Optional[int] = None,
+             out: VerifyOutputs, stream=None):
+        """The checks of run() once, then a function of no arguments that enqueues that
+        same step (same tensors, same stream) each time it is called. The tensors must stay
+        alive and in place while the function is used."""
+        import torch
+        self.run(logits, draft_ids, temperature=temperature, q=q, uniforms=uniforms, gamma=gamma,
+                 cu_gamma=cu_gamma, total_draft_rows=total_draft_rows, out=out, stream=stream)
+        st = stream if stream is not None else torch.cuda.current_stream(self.device)
+        greedy = float(temperature) == 0.0
+        if cu_gamma is not None:
+            B = cu_gamma.numel() - 1
+            R = int(total_draft_rows if total_draft_rows is not None else draft_ids.numel())
+            g_arg = -1
+        else:
+            B = logits.numel() // ((gamma + 1) * self.vocab)
+            R, g_arg = B * gamma, gamma
+        return spec_verify_run_bound(self.ctx, st, B, g_arg, cu_gamma, R, float(temperature), logits,
+                                     None if greedy else q, draft_ids, None if greedy else uniforms,
+                                     out.accepted_count, out.emitted_tokens, out.residual_sum, out.p_draft)
 
     def sample(self, x, *, uniforms=None, temperature: float = 1.0, tokens=None, stream=None):
         """One token per row of logits `x` ([rows, V], the context's dtype): p = softmax(l / T),

@@ -75,3 +75,15 @@ def test_counter_traffic_needs_matching_sources(tmp_path, monkeypatch):
     assert bench.counter_traffic("k_greedy_seq1", "C3-one") is None
     (csrc / "spec_verify.hip").write_text("kernel sources B\n")  # the kernel changed
     assert bench.counter_traffic("k_verify_seq", "C3-one") is None
+
+
+def test_rotated_inputs_exceed_the_last_level_cache():
+    """Each workload rotates enough input sets to hold over 1 GiB (four times the 256 MB
+    last-level cache): C2's 90 MB sets need at least 8 of them."""
+    import synth
+    for cfg in ("C1", "C2", "C3", "C4", "C5"):
+        n = bench.auto_sets(cfg)
+        per = bench.input_bytes(synth.make_config(cfg, seed=0))
+        assert n * per >= bench.SET_BYTES_TARGET or n == bench.MAX_SETS, cfg
+        assert n >= 2 or per >= bench.SET_BYTES_TARGET, cfg
+    assert bench.auto_sets("C2") >= 8

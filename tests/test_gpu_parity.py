@@ -4,6 +4,7 @@ Every case prints what it runs before touching the GPU. Inputs come from the
 seeded generator in `synth`; nothing here reads from the HIP path to build an
 expected value.
 """
+import copy
 import math
 import sys
 
@@ -302,12 +303,24 @@ def test_greedy_one_launch(lib, dtype, V):
     v = verifier(lib, w.V, w.dtype, w.B, max(w.draft_rows, 1))
     _say("greedy one launch", f"{dtype} V={V} B={w.B}")
     ora = oracle_batch(w)
+    nan_seq = 1  # its row 0 (always judged) holds NaN: a data error, outputs unspecified but in range
+    cu = w.cu_gamma
+    g1, s1 = int(cu[nan_seq + 1] - cu[nan_seq]), int(cu[nan_seq]) + nan_seq
     for plan in (lib.SV_PATH_ONE_LAUNCH, lib.SV_PATH_TWO_LAUNCH):
         v.set_path(plan)
         gpu = run_gpu(v, w, ragged=True)
         assert v.last_path() == plan
-        assert gpu["status"] == lib.SV_EDATA and "draft-id" in v.last_error()
-        rep = compare(w, gpu, ora)
+        assert gpu["status"] == lib.SV_EDATA
+        assert "draft-id" in v.last_error() and "non-finite" in v.last_error(), v.last_error()
+        n1 = int(gpu["accepted_count"][nan_seq])
+        em1 = gpu["emitted_tokens"][s1:s1 + g1 + 1]
+        assert 0 <= n1 <= g1 and 0 <= em1[n1] < V and np.all(em1[n1 + 1:] == -1)
+        assert np.array_equal(em1[:n1], w.draft_ids[int(cu[nan_seq]):int(cu[nan_seq]) + n1])
+        # every other sequence: exact parity (the NaN sequence's outputs are copied over)
+        ora_c = copy.deepcopy(ora)
+        ora_c.accepted_count[nan_seq] = n1
+        ora_c.emitted_tokens[s1:s1 + g1 + 1] = em1
+        rep = compare(w, gpu, ora_c)
         _say("greedy one launch", f"plan={plan}", rep.summary())
         assert rep.ok(), rep.summary()
     v.set_path(lib.SV_PATH_AUTO)
