@@ -147,6 +147,43 @@ int spec_verify_run(spec_verify_ctx *ctx, void *hip_stream, int batch, int gamma
                     float *residual_sum, float *p_draft);
 
 /*
+ * spec_verify_run for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. It takes no context and
+ * allocates nothing (no hipMalloc, hipFree or allocating library call). Its workspace is
+ * a static device array inside the library, SV_STATIC_SCRATCH_MAX_BYTES at most, of which
+ * every GPU the library runs on holds one copy until the process ends; its address is
+ * looked up once per device, on the first call there, which also enqueues a small kernel
+ * on `hip_stream` that clears the workspace's counters.
+ *   device        the HIP device of every pointer; the calling thread's current device
+ *                 is left as it was.
+ *   vocab, logits_dtype  as for spec_verify_create.
+ *   batch .. p_draft     as for spec_verify_run, within the static workspace's limits:
+ *                 batch <= SV_STATIC_MAX_BATCH, total_draft_rows <= SV_STATIC_MAX_ROWS,
+ *                 gamma (or every gamma_b of a ragged run) <= SV_STATIC_MAX_GAMMA.
+ *   data_flags    device int32 [1], caller-owned: the data-error bits (SV_DATA_*) found
+ *                 by the kernels are OR-ed into it, never cleared (start it at 0).
+ * The kernels and outputs are those of spec_verify_run under SV_PATH_AUTO, except that a
+ * greedy batch never takes the helper plan (it runs one workgroup per sequence instead).
+ * Every call on one GPU shares that GPU's workspace, which keeps the last call's contents:
+ * calls that overlap on one GPU (two streams, two threads) race and give undefined
+ * results; calls in stream order are safe.
+ * Errors: SV_EINVAL (a size beyond the static limits, the checks of spec_verify_run, a
+ * NULL data_flags, no such device), SV_EHIP. The message of the calling thread's last
+ * call is spec_verify_last_error(NULL).
+ */
+enum {
+  SV_STATIC_MAX_BATCH = 1024,
+  SV_STATIC_MAX_ROWS = 16384,
+  SV_STATIC_MAX_GAMMA = 64,
+  SV_STATIC_SCRATCH_MAX_BYTES = 4 << 20
+};
+int spec_verify_run_static(int device, void *hip_stream, int vocab, int logits_dtype, int batch, int gamma,
+                           const int32_t *cu_gamma, int total_draft_rows, float temperature,
+                           const void *logits, const float *q, const int32_t *draft_ids,
+                           const float *uniforms, int32_t *accepted_count, int32_t *emitted_tokens,
+                           float *residual_sum, float *p_draft, int32_t *data_flags);
+
+/*
  * The same step for deterministic drafts, such as prompt-lookup (n-gram) proposals
  * ("Speculative Decoding", atonlee.tistory.com/330, ch.5; the pages do not say how such
  * drafts are verified, and this entry point takes the plain reading that the draft
@@ -353,7 +390,8 @@ int spec_adapt_gamma(spec_verify_ctx *ctx, void *hip_stream, int batch, const in
  */
 int spec_verify_status(spec_verify_ctx *ctx);
 
-/* Text of the last error on this context ("" if none). Owned by the context. */
+/* Text of the last error on this context ("" if none). Owned by the context. With ctx NULL:
+ * the message of the calling thread's last spec_verify_run_static call. */
 const char *spec_verify_last_error(const spec_verify_ctx *ctx);
 
 /* Free the workspace and the context. NULL-safe. Synchronizes the device first. */

@@ -18,5 +18,6 @@ from .binding import (  # noqa: F401
     spec_verify_status, spec_sample_run, spec_verify_run_onehot, spec_ngram_propose, spec_adapt_gamma,
     spec_vshard_rows, spec_vshard_decide, spec_vshard_finish, vshard_desc, VShardDesc,
     VSHARD_REC_BYTES, VSHARD_PART_DOUBLES, VSHARD_LOCAL_DOUBLES,
+    spec_verify_run_static, spec_verify_run_bound, SV_STATIC_MAX_BATCH, SV_STATIC_MAX_ROWS, SV_STATIC_MAX_GAMMA,
 )
 from .verifier import VocabShard, Verifier, VerifyOutputs  # noqa: F401

@@ -32,7 +32,9 @@ EXPORTED = (
     "spec_verify_kernel_times", "spec_verify_check_args", "spec_verify_set_path", "spec_verify_set_timing_stride",
     "spec_verify_last_path", "spec_sample_run", "spec_verify_run_onehot", "spec_ngram_propose",
     "spec_adapt_gamma", "spec_vshard_rows", "spec_vshard_decide", "spec_vshard_finish",
+    "spec_verify_run_static",
 )
+SV_STATIC_MAX_BATCH, SV_STATIC_MAX_ROWS, SV_STATIC_MAX_GAMMA = 1024, 16384, 64
 
 
 class SpecVerifyError(RuntimeError):
@@ -90,6 +92,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.spec_verify_kernel_times.restype = i32
     lib.spec_verify_check_args.argtypes = [i32] * 9 + [f32] + [i32] * 7 + [ctypes.c_char_p, i32]
     lib.spec_verify_check_args.restype = i32
+    lib.spec_verify_run_static.argtypes = [i32, vp, i32, i32, i32, i32, vp, i32, f32, vp, vp, vp, vp, vp, vp, vp,
+                                           vp, vp]
+    lib.spec_verify_run_static.restype = i32
     lib.spec_verify_run_onehot.argtypes = [vp, vp, i32, i32, vp, i32, f32, vp, vp, vp, vp, vp, vp, vp]
     lib.spec_verify_run_onehot.restype = i32
     lib.spec_ngram_propose.argtypes = [vp, vp, i32, vp, vp, i32, i32, i32, i32, vp, vp]
@@ -160,6 +165,20 @@ def spec_verify_run(ctx: int, stream, batch: int, gamma: int, cu_gamma, total_dr
         _ptr(emitted_tokens), _ptr(residual_sum), _ptr(p_draft))
     if rc != SV_OK:
         raise SpecVerifyError(rc, _msg(ctx))
+
+
+def spec_verify_run_static(device: int, stream, vocab: int, logits_dtype: int, batch: int, gamma: int, cu_gamma,
+                           total_draft_rows: int, temperature: float, logits, q, draft_ids, uniforms,
+                           accepted_count, emitted_tokens, residual_sum, p_draft, data_flags) -> None:
+    """Enqueue one verification step with no context and no allocation (the library's
+    static workspace); data-error bits are OR-ed into data_flags. Raises SpecVerifyError."""
+    lib = load_library()
+    rc = lib.spec_verify_run_static(
+        device, _stream(stream), vocab, logits_dtype, batch, gamma, _ptr(cu_gamma), total_draft_rows,
+        float(temperature), _ptr(logits), _ptr(q), _ptr(draft_ids), _ptr(uniforms), _ptr(accepted_count),
+        _ptr(emitted_tokens), _ptr(residual_sum), _ptr(p_draft), _ptr(data_flags))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, (lib.spec_verify_last_error(None) or b"").decode())
 
 
 def spec_verify_run_bound(ctx: int, stream, batch: int, gamma: int, cu_gamma, total_draft_rows: int,

@@ -48,6 +48,7 @@
 #include <string.h>
 
 #include <climits>
+#include <mutex>
 #include <new>
 
 #include "spec_verify.h"
@@ -2768,6 +2769,8 @@ struct spec_verify_ctx {
   int device = 0, V = 0, dtype = 0, max_batch = 0, max_rows = 0, max_gamma = 0, cus = 0;
   void* ws = nullptr;
   RowStat* p1 = nullptr;
+  size_t p1_cap = 0;         // entries of p1
+  bool no_helpers = false;   // greedy runs never take the helper plan (its counters carry host epochs)
   int32_t* accept = nullptr;
   float2* lxq = nullptr;     // split rows: the draft's logit and q entry
   int32_t* s_acc = nullptr;  // sampling: accepted counts (all 0) of the verify launch
@@ -2875,7 +2878,7 @@ hipError_t launch_fused_greedy(spec_verify_ctx* ctx, const Args& a, hipStream_t 
   ao.order = ordered ? ctx->order : nullptr;
   // helpers while the batch is at most four times the compute units (the longest
   // sequences then set the time)
-  const bool help = SV_GREEDY_HELP && a.B >= ctx->cus && a.B <= 4 * ctx->cus;
+  const bool help = SV_GREEDY_HELP && !ctx->no_helpers && a.B >= ctx->cus && a.B <= 4 * ctx->cus;
   if (help) {
     ao.gclaim = ctx->gclaim;
     ao.gpart = ctx->gpart;
@@ -3071,6 +3074,10 @@ int run_impl(spec_verify_ctx* ctx, void* hip_stream, int batch, int gamma, const
   a.R = total_draft_rows;
   a.max_gamma = ctx->max_gamma;
   choose_split(a.R, a.V, a.split, a.span);
+  if (static_cast<size_t>(a.R) * a.split > ctx->p1_cap) {  // cannot happen within the max_* sizes
+    set_msg(ctx->msg, sizeof(ctx->msg), "row statistics exceed the workspace");
+    return SV_EINVAL;
+  }
   const unsigned long long max_threads = 1ull << 32;
   if (static_cast<unsigned long long>(a.R) * a.split * kThreads >= max_threads ||
       static_cast<unsigned long long>(a.B) * kSeqThreads >= max_threads) {
@@ -3199,6 +3206,118 @@ template <typename T, bool A, bool R, bool G> struct VsRows { static constexpr a
 template <typename T, bool A, bool R, bool G> struct VsDecide { static constexpr auto fn = &k_vs_decide<T, A, R, G>; };
 template <typename T, bool A, bool R, bool G> struct VsFinish { static constexpr auto fn = &k_vs_finish<T, A, R>; };
 
+// ---------------------------------------------------------------- workspace layout
+// Byte offsets of a context's device arrays in one block, each 256-byte aligned: the
+// row statistics (p1_cap entries), per draft row the decision and the draft's logit and
+// q entry, per sequence the sampling-mode scratch outputs, the ordering and the three
+// greedy-helper counters, the split draw's sums and counts (split_cap sequences), and
+// the error word.
+struct WsLayout {
+  size_t p1, accept, lxq, s_acc, s_rsum, order, gclaim, gpart, gbest, dsum, dcnt, err, total;
+  size_t p1_cap;
+  int split_cap;
+};
+constexpr size_t ws_up(size_t x) { return (x + 255) / 256 * 256; }
+constexpr WsLayout ws_layout(size_t p1_cap, int max_rows, int max_batch, int split_cap) {
+  const size_t rows = static_cast<size_t>(max_rows > 0 ? max_rows : 1);
+  const size_t seqs = static_cast<size_t>(max_batch > 0 ? max_batch : 1);
+  const size_t cap = static_cast<size_t>(split_cap > 0 ? split_cap : 0);
+  WsLayout L{};
+  size_t o = 0;
+  L.p1 = o;      o += ws_up(sizeof(RowStat) * (p1_cap > 0 ? p1_cap : 1));
+  L.accept = o;  o += ws_up(sizeof(int32_t) * rows);
+  L.lxq = o;     o += ws_up(sizeof(float2) * rows);
+  L.s_acc = o;   o += ws_up(sizeof(int32_t) * seqs);
+  L.s_rsum = o;  o += ws_up(sizeof(float) * seqs);
+  L.order = o;   o += ws_up(sizeof(int32_t) * seqs);
+  L.gclaim = o;  o += ws_up(sizeof(unsigned long long) * seqs);
+  L.gpart = o;   o += ws_up(sizeof(unsigned long long) * seqs);
+  L.gbest = o;   o += ws_up(sizeof(unsigned long long) * seqs);
+  L.dsum = o;    o += ws_up(sizeof(double) * 3 * kMaxSub * cap);
+  L.dcnt = o;    o += ws_up(sizeof(int) * (cap > 0 ? cap : 1));
+  L.err = o;     o += 256;
+  L.total = o;
+  L.p1_cap = p1_cap;
+  L.split_cap = split_cap;
+  return L;
+}
+void ws_assign(spec_verify_ctx* ctx, const WsLayout& L, char* base) {
+  ctx->p1 = reinterpret_cast<RowStat*>(base + L.p1);
+  ctx->p1_cap = L.p1_cap;
+  ctx->accept = reinterpret_cast<int32_t*>(base + L.accept);
+  ctx->lxq = reinterpret_cast<float2*>(base + L.lxq);
+  ctx->s_acc = reinterpret_cast<int32_t*>(base + L.s_acc);
+  ctx->s_rsum = reinterpret_cast<float*>(base + L.s_rsum);
+  ctx->order = reinterpret_cast<int*>(base + L.order);
+  ctx->gclaim = reinterpret_cast<unsigned long long*>(base + L.gclaim);
+  ctx->gpart = reinterpret_cast<unsigned long long*>(base + L.gpart);
+  ctx->gbest = reinterpret_cast<unsigned long long*>(base + L.gbest);
+  ctx->split_cap = L.split_cap;
+  ctx->dsum = L.split_cap > 0 ? reinterpret_cast<double*>(base + L.dsum) : nullptr;
+  ctx->dcnt = L.split_cap > 0 ? reinterpret_cast<int*>(base + L.dcnt) : nullptr;
+  ctx->err = reinterpret_cast<int*>(base + L.err);
+}
+
+// The no-allocation entry point's workspace: a static device array of the layout above
+// for at most kStaticMaxBatch sequences and kStaticMaxRows draft rows (row statistics
+// for R x split <= R + SV_SPLIT_TARGET entries, the split draw for 128 sequences).
+constexpr int kStaticMaxBatch = SV_STATIC_MAX_BATCH;
+constexpr int kStaticMaxRows = SV_STATIC_MAX_ROWS;
+constexpr int kStaticSplitCap = 128;
+constexpr WsLayout kStaticLayout =
+    ws_layout(kStaticMaxRows + SV_SPLIT_TARGET, kStaticMaxRows, kStaticMaxBatch, kStaticSplitCap);
+constexpr int kStaticMaxDevices = 64;
+static_assert(kStaticLayout.total <= static_cast<size_t>(SV_STATIC_SCRATCH_MAX_BYTES), "static workspace size");
+static_assert(SV_STATIC_MAX_GAMMA == kFuseMaxGamma, "the static entry point's gamma limit");
+
+__global__ void k_zero_words(int* p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
+}
+
+}  // namespace
+
+// One copy per device, held until the process ends. In host code this name is a stand-in,
+// not a device address: kernels get the address hipGetSymbolAddress returns for the device.
+static __device__ __align__(256) unsigned char scratch[kStaticLayout.total];
+
+namespace {
+struct StaticDevice {
+  char* ptr = nullptr;  // this device's copy of `scratch`
+  int cus = 0;
+};
+StaticDevice g_static[kStaticMaxDevices];
+std::mutex g_static_mu;
+thread_local char g_static_msg[512];
+
+// Once per device, with the device current: the address of its copy of `scratch` and its
+// compute-unit count; the split draw's counts are cleared on `st` (a small kernel, so the
+// set-up can also be captured into a graph). Returns SV_OK or SV_EHIP.
+int static_device(int device, hipStream_t st, StaticDevice& out) {
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  StaticDevice& d = g_static[device];
+  if (!d.ptr) {
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      snprintf(g_static_msg, sizeof(g_static_msg), "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+      return SV_EHIP;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) cus = 256;
+    hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(256), 0, st, reinterpret_cast<int*>(static_cast<char*>(p) +
+                       kStaticLayout.dcnt), kStaticSplitCap);
+    e = hipGetLastError();
+    if (e != hipSuccess) {
+      snprintf(g_static_msg, sizeof(g_static_msg), "kernel launch: %s", hipGetErrorString(e));
+      return SV_EHIP;
+    }
+    d.cus = cus;
+    d.ptr = static_cast<char*>(p);
+  }
+  out = d;
+  return SV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -3262,46 +3381,16 @@ int spec_verify_create(spec_verify_ctx** out, int device, int vocab, int logits_
   ctx->max_rows = max_draft_rows;
   ctx->max_gamma = max_gamma;
   if (hipDeviceGetAttribute(&ctx->cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) ctx->cus = 256;
-  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   const int by_len = (vocab + SV_SPLIT_MIN_SPAN - 1) / SV_SPLIT_MIN_SPAN;
   const int max_split = by_len < kMaxSplit ? by_len : kMaxSplit;
-  const size_t n_p1 =
-      up(sizeof(RowStat) * static_cast<size_t>(max_draft_rows > 0 ? max_draft_rows : 1) * max_split);
-  const size_t n_ac = up(sizeof(int32_t) * static_cast<size_t>(max_draft_rows > 0 ? max_draft_rows : 1));
-  const size_t n_lq = up(sizeof(float2) * static_cast<size_t>(max_draft_rows > 0 ? max_draft_rows : 1));
-  const size_t n_g = up(sizeof(unsigned long long) * static_cast<size_t>(max_batch > 0 ? max_batch : 1));
-  const size_t n_sb = up(sizeof(int32_t) * static_cast<size_t>(max_batch > 0 ? max_batch : 1));
-  const size_t n_er = 256;
-  // split draw: sub-region sums and a count of finished slices per sequence
-  ctx->split_cap = max_batch < kSplitMaxB ? max_batch : kSplitMaxB;
-  const size_t cap = static_cast<size_t>(ctx->split_cap);
-  const size_t n_ds = up(sizeof(double) * 3 * kMaxSub * cap), n_dc = up(sizeof(int) * cap);
-  if (hipMalloc(&ctx->ws, n_p1 + n_ac + 3 * n_sb + n_er + n_ds + n_dc + n_lq + 3 * n_g) != hipSuccess) {
+  const WsLayout L = ws_layout(static_cast<size_t>(max_draft_rows > 0 ? max_draft_rows : 1) * max_split,
+                               max_draft_rows, max_batch, max_batch < kSplitMaxB ? max_batch : kSplitMaxB);
+  if (hipMalloc(&ctx->ws, L.total) != hipSuccess) {
     delete ctx;
     return SV_ENOMEM;
   }
-  char* p = static_cast<char*>(ctx->ws);
-  ctx->p1 = reinterpret_cast<RowStat*>(p);
-  ctx->accept = reinterpret_cast<int32_t*>(p + n_p1);
-  ctx->s_acc = reinterpret_cast<int32_t*>(p + n_p1 + n_ac);
-  ctx->s_rsum = reinterpret_cast<float*>(p + n_p1 + n_ac + n_sb);
-  ctx->err = reinterpret_cast<int*>(p + n_p1 + n_ac + 2 * n_sb);
-  if (cap > 0) {
-    char* c = p + n_p1 + n_ac + 2 * n_sb + n_er;
-    ctx->dsum = reinterpret_cast<double*>(c);
-    ctx->dcnt = reinterpret_cast<int*>(c + n_ds);
-  }
-  ctx->order = reinterpret_cast<int*>(p + n_p1 + n_ac + 2 * n_sb + n_er + n_ds + n_dc);
-  ctx->lxq = reinterpret_cast<float2*>(p + n_p1 + n_ac + 3 * n_sb + n_er + n_ds + n_dc);
-  {
-    char* gq = p + n_p1 + n_ac + 3 * n_sb + n_er + n_ds + n_dc + n_lq;
-    ctx->gclaim = reinterpret_cast<unsigned long long*>(gq);
-    ctx->gpart = reinterpret_cast<unsigned long long*>(gq + n_g);
-    ctx->gbest = reinterpret_cast<unsigned long long*>(gq + 2 * n_g);
-  }
-  if (hipMemset(ctx->err, 0, n_er) != hipSuccess ||
-      (ctx->dcnt && hipMemset(ctx->dcnt, 0, n_dc) != hipSuccess) || hipMemset(ctx->gclaim, 0, 3 * n_g) != hipSuccess ||
-      hipDeviceSynchronize() != hipSuccess) {
+  ws_assign(ctx, L, static_cast<char*>(ctx->ws));
+  if (hipMemset(ctx->ws, 0, L.total) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
     (void)hipFree(ctx->ws);
     delete ctx;
     return SV_EHIP;
@@ -3316,6 +3405,54 @@ int spec_verify_run(spec_verify_ctx* ctx, void* hip_stream, int batch, int gamma
                     int32_t* emitted_tokens, float* residual_sum, float* p_draft) {
   return run_impl(ctx, hip_stream, batch, gamma, cu_gamma, total_draft_rows, temperature, logits, q, false,
                   draft_ids, uniforms, accepted_count, emitted_tokens, residual_sum, p_draft);
+}
+
+int spec_verify_run_static(int device, void* hip_stream, int vocab, int logits_dtype, int batch, int gamma,
+                           const int32_t* cu_gamma, int total_draft_rows, float temperature, const void* logits,
+                           const float* q, const int32_t* draft_ids, const float* uniforms,
+                           int32_t* accepted_count, int32_t* emitted_tokens, float* residual_sum, float* p_draft,
+                           int32_t* data_flags) {
+  auto bad = [&](const char* m) {
+    set_msg(g_static_msg, sizeof(g_static_msg), m);
+    return SV_EINVAL;
+  };
+  if (vocab < 1 || vocab > kMaxVocab) return bad("vocab must be in [1, 2^24]");
+  if (logits_dtype != SV_F32 && logits_dtype != SV_BF16) return bad("logits_dtype must be SV_F32 or SV_BF16");
+  if (batch > kStaticMaxBatch) return bad("batch exceeds SV_STATIC_MAX_BATCH (1024) of the static workspace");
+  if (total_draft_rows > kStaticMaxRows)
+    return bad("total_draft_rows exceeds SV_STATIC_MAX_ROWS (16384) of the static workspace");
+  if (batch > 0 && !data_flags) return bad("data_flags is NULL");
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || device < 0 || device >= ndev || device >= kStaticMaxDevices)
+    return bad("no such device");
+  if (batch <= 0) {  // checked like spec_verify_run; nothing to enqueue
+    const int rc = spec_verify_check_args(vocab, logits_dtype, kStaticMaxBatch, kStaticMaxRows, kFuseMaxGamma,
+                                          batch, gamma, cu_gamma != nullptr, total_draft_rows, temperature, 1, 1,
+                                          1, 1, 1, 1, 1, g_static_msg, sizeof(g_static_msg));
+    return rc;
+  }
+  DeviceGuard guard(device);
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  StaticDevice dv;
+  const int rc0 = static_device(device, st, dv);
+  if (rc0 != SV_OK) return rc0;
+  // a context on the stack that describes the static workspace: the same checks, plans
+  // and kernels as spec_verify_run, minus the greedy helpers
+  spec_verify_ctx c;
+  c.device = device;
+  c.V = vocab;
+  c.dtype = logits_dtype;
+  c.max_batch = kStaticMaxBatch;
+  c.max_rows = kStaticMaxRows;
+  c.max_gamma = SV_STATIC_MAX_GAMMA;
+  c.cus = dv.cus;
+  c.no_helpers = true;
+  ws_assign(&c, kStaticLayout, dv.ptr);
+  c.err = data_flags;
+  const int rc = run_impl(&c, hip_stream, batch, gamma, cu_gamma, total_draft_rows, temperature, logits, q, false,
+                          draft_ids, uniforms, accepted_count, emitted_tokens, residual_sum, p_draft);
+  set_msg(g_static_msg, sizeof(g_static_msg), c.msg);
+  return rc;
 }
 
 int spec_verify_run_onehot(spec_verify_ctx* ctx, void* hip_stream, int batch, int gamma, const int32_t* cu_gamma,
@@ -3565,7 +3702,7 @@ int spec_verify_status(spec_verify_ctx* ctx) {
   return SV_EDATA;
 }
 
-const char* spec_verify_last_error(const spec_verify_ctx* ctx) { return ctx ? ctx->msg : ""; }
+const char* spec_verify_last_error(const spec_verify_ctx* ctx) { return ctx ? ctx->msg : g_static_msg; }
 
 void spec_verify_destroy(spec_verify_ctx* ctx) {
   if (!ctx) return;

@@ -1,0 +1,102 @@
+"""spec_verify_run_static, the entry point that allocates nothing, against spec_verify_run.
+
+Both run the same inputs; the static entry point must give the same outputs bit for bit
+(the same kernels, except that greedy batches never take the helper plan, whose outputs
+are the same by construction) and pass the oracle's bar. Each case makes two static calls
+in a row, the second with a smaller input, so that what the first call leaves in the
+static workspace cannot leak into the second.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+from _parity import compare, oracle_batch, run_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+def _say(*a):
+    print("[gpu-case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import speculative_sampling_verification_03_amd as sv
+    sv.load_library()
+    return sv
+
+
+def _static(sv, w, dev, flags):
+    ragged = w.uniform_gamma is None
+    code = sv.SV_BF16 if w.dtype == "bf16" else sv.SV_F32
+    acc = torch.empty(w.B, dtype=torch.int32, device="cuda")
+    em = torch.empty(w.target_rows, dtype=torch.int32, device="cuda")
+    S = torch.empty(w.B, dtype=torch.float32, device="cuda")
+    pd = torch.empty(w.draft_rows, dtype=torch.float32, device="cuda") if w.T > 0 else None
+    greedy = w.T == 0
+    sv.spec_verify_run_static(0, torch.cuda.current_stream(), w.V, code, w.B, -1 if ragged else w.uniform_gamma,
+                              dev["cu_gamma"] if ragged else None, w.draft_rows, w.T, dev["logits"],
+                              None if greedy else dev["q"], dev["draft_ids"], None if greedy else dev["uniforms"],
+                              acc, em, S, pd, flags)
+    torch.cuda.synchronize()
+    return dict(accepted_count=acc.cpu().numpy(), emitted_tokens=em.cpu().numpy(), residual_sum=S.cpu().numpy(),
+                p_draft=pd.cpu().numpy() if pd is not None else None)
+
+
+def _check(sv, w, label):
+    _say(label, f"B={w.B} V={w.V} {w.dtype} T={w.T} rows={w.draft_rows}")
+    dev = to_device(w)
+    code = sv.SV_BF16 if w.dtype == "bf16" else sv.SV_F32
+    with sv.Verifier(w.V, code, w.B, max(w.draft_rows, 1), 16) as v:
+        ref = run_gpu(v, w, dev=dev)
+        assert ref["status"] == sv.SV_OK, v.last_error()
+    flags = torch.zeros(1, dtype=torch.int32, device="cuda")
+    got = _static(sv, w, dev, flags)
+    assert int(flags.item()) == 0
+    for k in ("accepted_count", "emitted_tokens", "residual_sum"):
+        assert np.array_equal(got[k], ref[k]), (label, k)
+    if w.T > 0:
+        assert np.array_equal(got["p_draft"], ref["p_draft"], equal_nan=True), label
+    rep = compare(w, dict(got, status=sv.SV_OK), oracle_batch(w))
+    _say(label, rep.summary())
+    assert rep.ok(), rep.summary()
+
+
+@pytest.mark.parametrize("cfg,big,small", [("C3", 256, 64), ("C2", 64, 24), ("C4", 512, 100), ("C5", 1024, 200)])
+def test_static_entry_point_matches_context(lib, cfg, big, small):
+    """Two static calls in a row, the second smaller (C3: one launch, then the split draw
+    of a small batch; C4: greedy without helpers; C5: the ordered ragged launch)."""
+    _check(lib, synth.make_config(cfg, seed=40, batch=big), f"static {cfg} B={big}")
+    _check(lib, synth.make_config(cfg, seed=41, batch=small), f"static {cfg} B={small}")
+
+
+def test_static_data_flags_and_limits(lib):
+    sv = lib
+    w = synth.make_config("C3", seed=42, batch=16, vocab=4096)
+    w.draft_ids = w.draft_ids.copy()
+    w.draft_ids[5] = w.V + 7
+    dev = to_device(w)
+    flags = torch.zeros(1, dtype=torch.int32, device="cuda")
+    _say("static data flags", f"B={w.B}")
+    _static(sv, w, dev, flags)
+    assert int(flags.item()) & sv.SV_DATA_DRAFT_ID
+    code = sv.SV_BF16
+    with pytest.raises(sv.SpecVerifyError) as e:  # beyond the static workspace: nothing launched
+        sv.spec_verify_run_static(0, None, w.V, code, sv.SV_STATIC_MAX_BATCH + 1, 4, None,
+                                  4 * (sv.SV_STATIC_MAX_BATCH + 1), 1.0, dev["logits"], dev["q"], dev["draft_ids"],
+                                  dev["uniforms"], flags, flags, flags, None, flags)
+    assert e.value.code == sv.SV_EINVAL and "SV_STATIC_MAX_BATCH" in str(e.value)
+    with pytest.raises(sv.SpecVerifyError) as e:
+        sv.spec_verify_run_static(0, None, w.V, code, 1000, 17, None, 17000, 1.0, dev["logits"], dev["q"],
+                                  dev["draft_ids"], dev["uniforms"], flags, flags, flags, None, flags)
+    assert e.value.code == sv.SV_EINVAL and "SV_STATIC_MAX_ROWS" in str(e.value)
+    with pytest.raises(sv.SpecVerifyError) as e:
+        sv.spec_verify_run_static(0, None, w.V, code, 16, 4, None, 64, 1.0, dev["logits"], dev["q"],
+                                  dev["draft_ids"], dev["uniforms"], flags, flags, flags, None, None)
+    assert e.value.code == sv.SV_EINVAL and "data_flags" in str(e.value)
