@@ -490,12 +490,23 @@ def timed_steps(sv, torch, ver, steps, n, warmup, stride):
     return (t1 - t0) / n, ktimes
 
 
+def PLANS(sv):
+    return {"auto": sv.SV_PATH_AUTO, "two": sv.SV_PATH_TWO_LAUNCH, "one": sv.SV_PATH_ONE_LAUNCH,
+            "pooled": sv.SV_PATH_POOLED}
+
+
 def plan_name(sv, ver):
-    return {sv.SV_PATH_ONE_LAUNCH: "one launch", sv.SV_PATH_TWO_LAUNCH: "two launches"}.get(ver.last_path())
+    return {sv.SV_PATH_ONE_LAUNCH: "one launch", sv.SV_PATH_TWO_LAUNCH: "two launches",
+            sv.SV_PATH_POOLED: "small-batch pooled launch"}.get(ver.last_path())
 
 
-def traffic_tag(config, one_launch):
-    return f"{config}-{'one' if one_launch else 'two'}"
+def plan_key(sv, ver):
+    """'one', 'two' or 'pool': the plan the last call ran, as profiles name it."""
+    return {sv.SV_PATH_ONE_LAUNCH: "one", sv.SV_PATH_TWO_LAUNCH: "two", sv.SV_PATH_POOLED: "pool"}[ver.last_path()]
+
+
+def traffic_tag(config, key):
+    return f"{config}-{key}"
 
 
 def bench_config(sv, torch, dev, config, n_steps, warmup, stride, plan="auto", batch=None, n_sets=None):
@@ -508,7 +519,7 @@ def bench_config(sv, torch, dev, config, n_steps, warmup, stride, plan="auto", b
     w0 = sets[0][0]
     code = sv.SV_BF16 if w0.dtype == "bf16" else sv.SV_F32
     ver = sv.Verifier(w0.V, code, w0.B, max(w.draft_rows for w, _ in sets), 16)
-    ver.set_path({"auto": sv.SV_PATH_AUTO, "two": sv.SV_PATH_TWO_LAUNCH, "one": sv.SV_PATH_ONE_LAUNCH}[plan])
+    ver.set_path(PLANS(sv)[plan])
     steps = Steps(sv, torch, ver, sets, dev)
     acc = []
     for k in range(len(sets)):
@@ -516,7 +527,8 @@ def bench_config(sv, torch, dev, config, n_steps, warmup, stride, plan="auto", b
         torch.cuda.synchronize()
         assert ver.status() == sv.SV_OK, ver.last_error()
         acc.append(steps.outs[k].accepted_count.cpu().numpy())
-    one = ver.last_path() == sv.SV_PATH_ONE_LAUNCH
+    one = ver.last_path() == sv.SV_PATH_ONE_LAUNCH  # stops reading rows at the first rejection
+    key = plan_key(sv, ver)
     plan_txt = plan_name(sv, ver)
     dt, kt = timed_steps(sv, torch, ver, steps, n_steps, warmup, stride)
     ver.close()
@@ -536,7 +548,7 @@ def bench_config(sv, torch, dev, config, n_steps, warmup, stride, plan="auto", b
         "frac_read": needed / (k_us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
     }
     # counter bytes of every kernel of the step, where profiles of these sources exist
-    trs = [0.0 if nm == "k_order_by_gamma" else counter_traffic(nm, traffic_tag(config, one)) for nm, _ in kt]
+    trs = [0.0 if nm == "k_order_by_gamma" else counter_traffic(nm, traffic_tag(config, key)) for nm, _ in kt]
     tr = sum(trs) if all(t is not None for t in trs) else None
     res["traffic_MB"] = tr / 1e6 if tr else None
     res["frac_traffic"] = tr / (k_us * 1e-6) / 1e9 / HBM_PEAK_GBPS if tr else None
@@ -560,8 +572,9 @@ def main():
                     help="skip the other workloads and the follow-on measurements")
     ap.add_argument("--no-every-row", action="store_true",
                     help="skip the second timing with p(x) requested (every draft row read)")
-    ap.add_argument("--plan", choices=("auto", "two", "one"), default="auto",
-                    help="launch plan (auto: the library's choice by batch size)")
+    ap.add_argument("--plan", choices=("auto", "two", "one", "pooled"), default="auto",
+                    help="launch plan (auto: the library's choice by batch size; pooled: the small-batch "
+                         "one-launch plan, rows read in chunks and draws shared)")
     ap.add_argument("--batch", type=int, default=None, help="sequences per step (default: the workload's)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run plain device copies of MIB MiB (calibrates the HBM byte counters)")
@@ -603,7 +616,7 @@ def main():
     ragged = w0.uniform_gamma is None
     code = sv.SV_BF16 if w0.dtype == "bf16" else sv.SV_F32
     ver = sv.Verifier(w0.V, code, w0.B, max(w.draft_rows for w, _ in sets), 16)
-    ver.set_path({"auto": sv.SV_PATH_AUTO, "two": sv.SV_PATH_TWO_LAUNCH, "one": sv.SV_PATH_ONE_LAUNCH}[args.plan])
+    ver.set_path(PLANS(sv)[args.plan])
     step = Steps(sv, torch, ver, sets, dev)
 
     # untimed: outputs of each set fix the algorithmic bytes of its steps
@@ -613,9 +626,12 @@ def main():
         torch.cuda.synchronize()
         assert ver.status() == sv.SV_OK, ver.last_error()
         nb.append(step.outs[k].accepted_count.cpu().numpy())
-    one_launch = ver.last_path() == sv.SV_PATH_ONE_LAUNCH  # stops reading rows at the first rejection
+    stop = ver.last_path() == sv.SV_PATH_ONE_LAUNCH  # stops reading rows at the first rejection
+    one_launch = ver.last_path() in (sv.SV_PATH_ONE_LAUNCH, sv.SV_PATH_POOLED)
+    key = plan_key(sv, ver)
+    plan_txt = plan_name(sv, ver)
     method_per_set = [method_bytes(w, n) for (w, _), n in zip(sets, nb)]
-    needed_per_set = [needed_bytes(w, n, one_launch) for (w, _), n in zip(sets, nb)]
+    needed_per_set = [needed_bytes(w, n, stop) for (w, _), n in zip(sets, nb)]
 
     # timed loop: exactly args.steps steps between two device synchronizations; per-kernel
     # HIP events (start and stop of the dispatch itself, on the launch stream) on one step
@@ -642,12 +658,12 @@ def main():
         k1_needed = k1_bytes
     k1_s = kt[k1] * 1e-3
     k1_gbps = k1_bytes / k1_s / 1e9
-    traffic = counter_traffic(k1, traffic_tag(args.config, one_launch))
+    traffic = counter_traffic(k1, traffic_tag(args.config, key))
 
     # the same steps with p(x) requested for every draft: the one-launch plan then reads
     # every draft row, as the two-launch plan always does
     all_rows = None
-    if one_launch and not w0.T == 0.0 and not args.no_every_row:
+    if stop and not w0.T == 0.0 and not args.no_every_row:
         step_p = Steps(sv, torch, ver, sets, dev, want_p=True)
         sec_all, kt_all = timed_steps(sv, torch, ver, step_p, args.steps, args.warmup, TIMING_STRIDE)
         ms_all = sec_all * 1e3
@@ -728,7 +744,7 @@ def main():
             "kernel_us": kt[k1] * 1e3,
         },
         "path": {
-            "plan": "one launch, stops reading rows at the first rejection" if one_launch else "two launches",
+            "plan": "one launch, stops reading rows at the first rejection" if stop else plan_txt,
             "method_bytes_per_step": path_bytes,
             "needed_bytes_per_step": needed,
             "achieved_GBps": path_gbps,

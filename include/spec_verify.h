@@ -95,7 +95,8 @@ enum {
   SV_DATA_CU_GAMMA = 8,   /* malformed cu_gamma */
   SV_DATA_CONTEXT = 16,   /* malformed cu_ctx (spec_ngram_propose) */
   SV_DATA_STATE = 32,     /* adaptive draft-length state out of range (spec_adapt_gamma) */
-  SV_DATA_STALL = 64      /* a wait between the waves of one workgroup reached its bound: the
+  SV_DATA_STALL = 64      /* a wait between waves (of one workgroup, or of the workgroups of
+                             one sequence in the small-batch plan) reached its bound: the
                              outputs of that call are not valid (not expected in use) */
 };
 
@@ -221,17 +222,27 @@ int spec_verify_run_onehot(spec_verify_ctx *ctx, void *hip_stream, int batch, in
  * in that order, so the short ones are dispatched last. A greedy one-launch run with
  * one to four times as many sequences as compute units adds two waves of one helper
  * workgroup per sequence, dispatched as slots free up, which take rows of a sequence
- * still being judged; the outputs are the same. Both plans return the same
- * outputs, except that a draft id after the first rejection is not examined by the
- * one-launch plan (so it cannot raise SV_DATA_DRAFT_ID there).
- *   spec_verify_set_path(ctx, mode): SV_PATH_AUTO (default), SV_PATH_TWO_LAUNCH, or
- *     SV_PATH_ONE_LAUNCH (taken whenever the run allows it, whatever B). Returns
- *     SV_OK or SV_EINVAL (NULL ctx, unknown mode).
+ * still being judged; the outputs are the same.
+ * A third plan, one launch for small sampling batches (SV_PATH_POOLED): uniform gamma
+ * <= 64, T > 0, V a multiple of 8 and 16-byte aligned logits and q, B x gamma x split
+ * workgroups (split >= 1 chunks per draft row) no more than the device holds at once
+ * (about 512 on MI355X), B <= 2048 and the context's max_batch. Every draft row is read
+ * in parallel, in chunks; the workgroups of a sequence wait (boundedly) for each other's
+ * pass-1 records, all reach the same first rejection, and then sweep the drawn row
+ * together, the last to finish completing the draw. It reads every draft row (as the
+ * two-launch plan does) and gives the same outputs as the other plans. Under
+ * SV_PATH_AUTO it is taken when it applies and B is below the compute-unit count.
+ * All plans return the same outputs, except that a draft id after the first rejection
+ * is not examined by the one-launch plan (so it cannot raise SV_DATA_DRAFT_ID there).
+ *   spec_verify_set_path(ctx, mode): SV_PATH_AUTO (default), SV_PATH_TWO_LAUNCH,
+ *     SV_PATH_ONE_LAUNCH (taken whenever the run allows it, whatever B) or
+ *     SV_PATH_POOLED (taken whenever the run allows it; else the two-launch plan).
+ *     Returns SV_OK or SV_EINVAL (NULL ctx, unknown mode).
  *   spec_verify_last_path(ctx): the plan of the last successful run
- *     (SV_PATH_TWO_LAUNCH or SV_PATH_ONE_LAUNCH), SV_PATH_AUTO if none yet, or
- *     -SV_EINVAL for a NULL ctx.
+ *     (SV_PATH_TWO_LAUNCH, SV_PATH_ONE_LAUNCH or SV_PATH_POOLED), SV_PATH_AUTO if none
+ *     yet, or -SV_EINVAL for a NULL ctx.
  */
-enum { SV_PATH_AUTO = 0, SV_PATH_TWO_LAUNCH = 1, SV_PATH_ONE_LAUNCH = 2 };
+enum { SV_PATH_AUTO = 0, SV_PATH_TWO_LAUNCH = 1, SV_PATH_ONE_LAUNCH = 2, SV_PATH_POOLED = 3 };
 int spec_verify_set_path(spec_verify_ctx *ctx, int mode);
 int spec_verify_last_path(const spec_verify_ctx *ctx);
 

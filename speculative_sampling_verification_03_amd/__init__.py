@@ -11,7 +11,7 @@ from .binding import (  # noqa: F401
     SV_DATA_CONTEXT, SV_DATA_CU_GAMMA, SV_DATA_STATE, SV_DATA_DRAFT_ID, SV_DATA_NONFINITE, SV_DATA_UNIFORM,
     SV_DATA_STALL,
     SV_NGRAM_MAX_N,
-    SV_PATH_AUTO, SV_PATH_ONE_LAUNCH, SV_PATH_TWO_LAUNCH, SV_SAMPLE_LOGITS, SV_SAMPLE_WEIGHTS,
+    SV_PATH_AUTO, SV_PATH_ONE_LAUNCH, SV_PATH_TWO_LAUNCH, SV_PATH_POOLED, SV_SAMPLE_LOGITS, SV_SAMPLE_WEIGHTS,
     SpecVerifyError, load_library, spec_verify_check_args, spec_verify_create,
     spec_verify_destroy, spec_verify_kernel_times, spec_verify_last_error, spec_verify_last_path,
     spec_verify_run, spec_verify_set_path, spec_verify_set_timing, spec_verify_set_timing_stride,

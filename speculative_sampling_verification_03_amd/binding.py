@@ -21,7 +21,7 @@ SV_DATA_DRAFT_ID, SV_DATA_NONFINITE, SV_DATA_UNIFORM, SV_DATA_CU_GAMMA, SV_DATA_
     1, 2, 4, 8, 16, 32
 SV_DATA_STALL = 64
 SV_NGRAM_MAX_N = 64
-SV_PATH_AUTO, SV_PATH_TWO_LAUNCH, SV_PATH_ONE_LAUNCH = 0, 1, 2
+SV_PATH_AUTO, SV_PATH_TWO_LAUNCH, SV_PATH_ONE_LAUNCH, SV_PATH_POOLED = 0, 1, 2, 3
 SV_SAMPLE_LOGITS, SV_SAMPLE_WEIGHTS = 0, 1
 _CODE_NAMES = {SV_OK: "SV_OK", SV_EINVAL: "SV_EINVAL", SV_ENOMEM: "SV_ENOMEM",
                SV_EHIP: "SV_EHIP", SV_EDATA: "SV_EDATA"}

@@ -24,6 +24,11 @@
 //     the first rejection and draw; with at most half as many sequences as compute units
 //     k_draw_part shares each draw over two or four workgroups, the last to finish
 //     completing it.
+//   * one launch for small sampling batches (k_verify_group), B below the compute units:
+//     B x gamma x split 512-thread workgroups, all resident at once, read every draft row
+//     in parallel chunks; the workgroups of a sequence wait for each other's pass-1
+//     records, reach the same first rejection and sweep the drawn row together, the
+//     last to finish completing the draw.
 //   * rows with no drafts (k_sample_rows, k_sample_weights): one token per row.
 //   * vocabulary shards (k_vs_rows, k_vs_decide, k_vs_finish): one device's part when
 //     the columns are split over devices.
@@ -36,9 +41,10 @@
 // t = u S is re-swept with an fp64 block scan and the first token whose inclusive
 // prefix exceeds t is emitted. The bonus sweep keeps a running region max instead.
 //
-// Work is handed between workgroups of one launch only where no workgroup waits for
-// another: the per-XCD L2 caches are not coherent for plain stores, so such hand-offs
-// are stored and loaded at system scope, past the L2s.
+// Work handed between workgroups of one launch is stored and loaded at system scope,
+// past the per-XCD L2 caches, which are not coherent for plain stores. A workgroup waits
+// for another only in the small-batch plan, whose grid is resident at once, and every
+// such wait is bounded.
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
 
@@ -122,6 +128,11 @@ struct Args {
   unsigned long long* gpart;   // [B]
   unsigned long long* gbest;   // [B]
   unsigned int gepoch;
+  // small-batch one-launch plan
+  unsigned long long* pchunk;  // [workgroups][4] pass-1 records of the row chunks, tagged
+  unsigned long long* psum;    // [B][64][6] unit sums of the drawn rows, tagged
+  int uw, nunits;              // unit width (entries) and units of a drawn row
+  unsigned ptag;               // this call's tag (nonzero)
 };
 
 __device__ __forceinline__ bool finite_pos(float z) { return z > 0.f && z <= FLT_MAX; }
@@ -186,7 +197,7 @@ __device__ __forceinline__ bool accept_test(int x, float lx, float qx, float uu,
 // scaled max (max(l) * k2, clamped to the fp32 range) and z = sum 2^(l k2 - c), kept per
 // thread with a running max, merged over the wave and then the block. Thread 0 returns
 // the block's (C, Z); s_c, s_z are kWaves-entry LDS scratch.
-template <typename T, bool ALIGNED>
+template <typename T, bool ALIGNED, int NT = kThreads>
 __device__ __forceinline__ void block_row_lse(const T* row, int lo, int hi, float k2, float* s_c, float* s_z,
                                               float& C, float& Z) {
   float m = -FLT_MAX, c = -FLT_MAX;  // running max of l and its scaled value
@@ -206,10 +217,10 @@ __device__ __forceinline__ void block_row_lse(const T* row, int lo, int hi, floa
   if (ALIGNED) {
     const int g1 = hi >> 3;
     int g = (lo >> 3) + threadIdx.x;
-    for (; g + (kUnroll - 1) * kThreads < g1; g += kUnroll * kThreads) {
+    for (; g + (kUnroll - 1) * NT < g1; g += kUnroll * NT) {
       float xv[kUnroll][kGroup];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) load_group(row, static_cast<size_t>(g + u * kThreads) * kGroup, xv[u]);
+      for (int u = 0; u < kUnroll; ++u) load_group(row, static_cast<size_t>(g + u * NT) * kGroup, xv[u]);
       float bm = xv[0][0];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u)
@@ -221,7 +232,7 @@ __device__ __forceinline__ void block_row_lse(const T* row, int lo, int hi, floa
 #pragma unroll
         for (int j = 0; j < kGroup; ++j) s[j] += fast_exp2(fmaf(xv[u][j], k2, -c));
     }
-    for (; g < g1; g += kThreads) {
+    for (; g < g1; g += NT) {
       float xv[kGroup];
       load_group(row, static_cast<size_t>(g) * kGroup, xv);
       float bm = xv[0];
@@ -232,7 +243,7 @@ __device__ __forceinline__ void block_row_lse(const T* row, int lo, int hi, floa
       for (int j = 0; j < kGroup; ++j) s[j] += fast_exp2(fmaf(xv[j], k2, -c));
     }
   } else {
-    for (int e = lo + threadIdx.x; e < hi; e += kThreads) {
+    for (int e = lo + threadIdx.x; e < hi; e += NT) {
       const float xv = load_one(row, e);
       rebase(xv);
       s[0] += fast_exp2(fmaf(xv, k2, -c));
@@ -253,7 +264,7 @@ __device__ __forceinline__ void block_row_lse(const T* row, int lo, int hi, floa
   if (threadIdx.x == 0) {
     C = s_c[0];
     Z = s_z[0];
-    for (int i = 1; i < kWaves; ++i) lse2_merge(C, Z, s_c[i], s_z[i]);
+    for (int i = 1; i < NT / 64; ++i) lse2_merge(C, Z, s_c[i], s_z[i]);
   }
 }
 
@@ -1036,34 +1047,36 @@ __device__ __forceinline__ double tab_lookup(uint32_t mag, uint32_t sgn, const d
   return sT[2 * med3_0(static_cast<int>(mag) - tlo, tsent) + sgn];
 }
 // Fills sT. Within a binade the 128 values of x form an arithmetic sequence, so their
-// 2^(x k2) form a geometric one: each of 768 threads takes the 16 entries m = j, j + 8,
+// 2^(x k2) form a geometric one: each of 768 pieces holds the 16 entries m = j, j + 8,
 // ..., j + 120 of one (binade, sign), computes the first with exp2 and steps by
 // R = 2^(8 dx k2) (relative error under 16 * 2^-52 + the exp2 error). Threads j = 0..7
 // of the two signs of a binade write 16 adjacent entries per step, so the stores meet
-// no LDS bank conflict. The caller syncs before the first lookup.
+// no LDS bank conflict. Workgroups of fewer than 770 threads take several pieces per
+// thread. The caller syncs before the first lookup.
 constexpr int kTabPiece = 16;
 constexpr int kTabThreadsPerSign = 128 / kTabPiece;
-static_assert(2 * kTabBinades * kTabThreadsPerSign <= kSeqThreads, "one table piece per thread");
+static_assert(2 * kTabBinades * kTabThreadsPerSign + 2 <= 2 * kSeqThreads, "table pieces per thread");
 __device__ __forceinline__ void tab_build(double* sT, const Args& a) {
-  const int t = threadIdx.x;
-  const int h = t / kTabThreadsPerSign, j = t % kTabThreadsPerSign;
   const int be_lo = a.tlo >> 7, nb = ((a.thi + 1) >> 7) - be_lo;
-  if (h < 2 * nb) {
-    const int be = be_lo + (h >> 1);
-    const double sgn = (h & 1) ? -1.0 : 1.0;
-    // x = 2^(be - 127) (1 + m / 128) for be >= 1; subnormal binade: x = m 2^-133
-    const double x0 = be >= 1 ? ldexp(1.0, be - 127) : 0.0;
-    const double dx = ldexp(1.0, (be >= 1 ? be : 1) - 127 - 7);
-    double v = exp2(sgn * (x0 + j * dx) * a.k2d);
-    const double R = exp2(sgn * (kTabThreadsPerSign * dx) * a.k2d);
-    double* dst = sT + 2 * (be * 128 + j - a.tlo) + (h & 1);
+  for (int t = threadIdx.x; t < 2 * kTabBinades * kTabThreadsPerSign + 2; t += blockDim.x) {
+    const int h = t / kTabThreadsPerSign, j = t % kTabThreadsPerSign;
+    if (h < 2 * nb) {
+      const int be = be_lo + (h >> 1);
+      const double sgn = (h & 1) ? -1.0 : 1.0;
+      // x = 2^(be - 127) (1 + m / 128) for be >= 1; subnormal binade: x = m 2^-133
+      const double x0 = be >= 1 ? ldexp(1.0, be - 127) : 0.0;
+      const double dx = ldexp(1.0, (be >= 1 ? be : 1) - 127 - 7);
+      double v = exp2(sgn * (x0 + j * dx) * a.k2d);
+      const double R = exp2(sgn * (kTabThreadsPerSign * dx) * a.k2d);
+      double* dst = sT + 2 * (be * 128 + j - a.tlo) + (h & 1);
 #pragma unroll
-    for (int k = 0; k < kTabPiece; ++k) {
-      dst[2 * kTabThreadsPerSign * k] = v;
-      v *= R;
+      for (int k = 0; k < kTabPiece; ++k) {
+        dst[2 * kTabThreadsPerSign * k] = v;
+        v *= R;
+      }
+    } else if (h == 2 * kTabBinades && j < 2) {  // two idle threads: the sentinel pair
+      sT[2 * (a.thi + 1 - a.tlo) + j] = __builtin_inf();
     }
-  } else if (h == 2 * kTabBinades && j < 2) {  // two idle threads: the sentinel pair
-    sT[2 * (a.thi + 1 - a.tlo) + j] = __builtin_inf();
   }
 }
 
@@ -1967,6 +1980,339 @@ __global__ __launch_bounds__(kOrderThreads) void k_order_by_gamma(Args a) {
     a.order[atomicAdd(&s_bin[bin(b)], 1)] = b;
 }
 
+// ============================================================== small batches, one launch
+// With fewer sequences than compute units one launch of B x gamma x split workgroups
+// reads every draft row in parallel. Workgroup w = b * W + j (W = gamma * split per
+// sequence, j = i * split + k) takes chunk k of draft row i of sequence b: it computes the
+// chunk's base-2 softmax state (the chunk holding the draft also the draft's logit and q
+// entry) and stores it as a record of four 64-bit words, the value in the high half and
+// the call's tag in the low half. Wave 0 of every workgroup of the sequence then waits
+// until the sequence's W records carry the tag, merges each row's records in chunk order
+// and runs the fp64 accept tests of all rows ([P1] ch.3; [P3] 단계 3); every workgroup
+// of the sequence reaches the same first rejection n (same records, same order). The
+// drawn row (the residual of row n, or the bonus row when every draft is accepted; [P1]
+// ch.2) is cut into up to 64 units, unit u swept by wave u of the sequence's workgroups,
+// so the whole group sweeps it at once; each wave stores its unit's fp64 sums as six
+// tagged words (each 32-bit half of a sum beside the tag). The wave of unit 0 then waits
+// until every unit's words carry the tag and finishes the draw: the search over the unit
+// sums, the re-sweep of the selected unit, the sequence's outputs. With gamma = 0 a
+// sequence has one workgroup, which draws from its bonus row directly.
+//
+// Hand-offs between workgroups: the words handed over are stored and loaded with relaxed
+// atomics at system scope, which gfx950 executes as global stores and loads with sc0 sc1:
+// they bypass the per-XCD L2 caches (not coherent with each other) and are performed at
+// memory, each 64-bit word at once. A reader takes a value only from a word that carries
+// this call's tag, and every word of a value carries it, so it never mixes words of two
+// calls and needs no other signal; no word is reset between calls (an older call's words
+// carry an older tag; the tag is a 32-bit count of the context's calls). Every wait is
+// bounded; one that runs out raises SV_DATA_STALL (that call's outputs are then not
+// valid). The host sizes the grid so that every workgroup is resident at once, and a wait
+// then lasts only until the other workgroups of the group have stored their part.
+constexpr int kGrpThreads = 512;
+constexpr int kGrpWaves = kGrpThreads / 64;
+constexpr int kGrpMaxW = 64;            // workgroups of one sequence (records of one lane each)
+constexpr int kGrpMaxUnits = 64;        // units of a drawn row (unit sums of one lane each)
+constexpr int kGrpMaxItems = 2048;      // workgroups of one launch (records in the workspace)
+constexpr int kGrpSpinCap = 1 << 20;    // polls of a wait before it gives up (SV_DATA_STALL)
+constexpr int kSumWords = 6;            // words of a unit's three fp64 sums, each half tagged
+
+__device__ __forceinline__ void store_sys(unsigned long long* p, unsigned long long v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ unsigned long long load_sys(const unsigned long long* p) {
+  return __hip_atomic_load(const_cast<unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+// The stores this wave issued are acknowledged before its next memory instruction.
+__device__ __forceinline__ void stores_complete() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ unsigned long long rec_word(float v, unsigned tag) {
+  return (static_cast<unsigned long long>(__float_as_uint(v)) << 32) | tag;
+}
+__device__ __forceinline__ float rec_value(unsigned long long w) { return __uint_as_float(static_cast<uint32_t>(w >> 32)); }
+__device__ __forceinline__ bool rec_tagged(unsigned long long w, unsigned tag) { return static_cast<uint32_t>(w) == tag; }
+
+// A sequence's draw: pass-1 statistics of the drawn row (z, c; 0 for a bonus draw), n, g,
+// the row base, the rejected draft (the excluded token of one-hot drafts), the sequence,
+// the uniform.
+struct GroupDraw {
+  double zr, cr;
+  int n, g, base, xn, b;
+  float uf;
+};
+
+__device__ __forceinline__ double uniform_d(double v) {
+  return __hiloint2double(__builtin_amdgcn_readfirstlane(__double2hiint(v)),
+                          __builtin_amdgcn_readfirstlane(__double2loint(v)));
+}
+// The same values, held in scalar registers (they are the same in every lane).
+__device__ __forceinline__ GroupDraw uniform_draw(const GroupDraw& d) {
+  GroupDraw u;
+  u.zr = uniform_d(d.zr);
+  u.cr = uniform_d(d.cr);
+  u.n = __builtin_amdgcn_readfirstlane(d.n);
+  u.g = __builtin_amdgcn_readfirstlane(d.g);
+  u.base = __builtin_amdgcn_readfirstlane(d.base);
+  u.xn = __builtin_amdgcn_readfirstlane(d.xn);
+  u.b = __builtin_amdgcn_readfirstlane(d.b);
+  u.uf = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(d.uf)));
+  return u;
+}
+
+// The drawn row of d and, for a residual draw with drafts of real probabilities, the
+// draft row's q.
+template <typename T>
+__device__ __forceinline__ const T* drawn_row(const Args& a, const GroupDraw& d) {
+  return static_cast<const T*>(a.logits) + static_cast<size_t>(d.base + d.b + d.n) * a.V;
+}
+__device__ __forceinline__ const float* drawn_q(const Args& a, const GroupDraw& d) {
+  return d.n < d.g && !a.onehot ? a.q + static_cast<size_t>(d.base + d.n) * a.V : nullptr;
+}
+
+// One wave's re-sweep of entries [R0, R1) of a drawn row (R0 and R1 multiples of kGroup)
+// through a ring of four iterations (three for fp32 logits): the first entry whose inclusive prefix (from sel.P)
+// exceeds sel.t, else the last entry of positive weight, -1 if none. e = 2^(l k2 - ref)
+// by exp2_tab, weighted as draw_select's kind says.
+template <typename T>
+__device__ __forceinline__ int wave_resweep(const T* lrow, const float* qrow, int R0, int R1, const DrawSel& sel,
+                                            double Zq, double KN, const double* s_tab) {
+  const int lane = threadIdx.x & 63;
+  const int kind = sel.kind, excl = sel.excl;
+  const bool take_last = sel.take_last != 0;
+  const double t = sel.t, delta = sel.delta, ref = sel.ref;
+  const double invZ = 1.0 / sel.Z64;
+  const int nit = (R1 - R0 + kIter - 1) / kIter;
+  double run = sel.P;
+  int lastpos = -1;
+  constexpr int kR = sizeof(T) == 2 ? 4 : 3;  // iterations held in registers (all but one in flight)
+  Raw<T> Lb[kR];
+  Raw<float> Qb[kR];
+  auto issue = [&](int it, int slot) {
+    const int e = min(R0 + min(it, nit - 1) * kIter + lane * kGroup, R1 - kGroup);
+    load_raw_in(lrow, e, Lb[slot]);
+    if (kind == 0) load_raw_in(qrow, e, Qb[slot]);
+  };
+#pragma unroll
+  for (int k = 0; k < kR - 1; ++k) {
+    issue(k, k);
+    issue_order_fence();
+  }
+  for (int it0 = 0; it0 < nit; it0 += kR) {
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+      const int it = it0 + r;
+      issue(it + kR - 1, (r + kR - 1) % kR);
+      if (it >= nit) continue;
+      const int e = R0 + it * kIter + lane * kGroup;
+      const bool in = e < R1;
+      float x[kGroup];
+      unpack(Lb[r], x);
+      float qv[kGroup];
+      if (kind == 0) unpack(Qb[r], qv);
+      double rv[kGroup];
+      double tot = 0.0;
+#pragma unroll
+      for (int j = 0; j < kGroup; ++j) {
+        const double ev = exp2_tab(fma(static_cast<double>(x[j]), KN, -ref), s_tab);
+        double wv = ev;
+        if (kind == 0) {
+          const double w = fma(-static_cast<double>(qv[j]), Zq, ev);
+          wv = w > 0.0 ? w * invZ - static_cast<double>(qv[j]) * delta : 0.0;
+        }
+        rv[j] = (in && e + j != excl) ? wv : 0.0;
+        tot += rv[j];
+      }
+      const double inc = wave_incl_scan_dpp(tot);
+      double acc = run + (inc - tot);
+      int c2 = INT_MAX, lp = -1;
+#pragma unroll
+      for (int j = 0; j < kGroup; ++j) {
+        acc += rv[j];
+        if (!take_last && c2 == INT_MAX && acc > t) c2 = e + j;
+        if (rv[j] > 0.0) lp = e + j;
+      }
+      c2 = wave_min_int_dpp(c2);
+      lp = wave_max_int_dpp(lp);
+      run += readlane_d(inc, 63);
+      lastpos = max(lastpos, lp);
+      if (c2 != INT_MAX) return c2;
+    }
+  }
+  return lastpos;
+}
+
+// The finish of a sequence's draw by one wave, unit u's sums in lane u: the search, the
+// re-sweep of the selected unit, and the sequence's outputs (accepted count, the accepted
+// drafts, the drawn token, the -1 padding, residual_sum).
+template <typename T>
+__device__ __forceinline__ void group_finish(const Args& a, const GroupDraw& d, double v0, double v1, double v2,
+                                             const double* s_tab) {
+  const int lane = threadIdx.x & 63;
+  const int V = a.V;
+  const bool residual = d.n < d.g;
+  const bool oh = residual && a.onehot;
+  const bool qres = residual && !oh;
+  const T* lrow = drawn_row<T>(a, d);
+  const float* qrow = drawn_q(a, d);
+  const bool excl_ok = oh && d.xn >= 0 && d.xn < V;  // an invalid id removes nothing
+  const float lxn = excl_ok ? load_one(lrow, d.xn) : 0.f;
+  const DrawSel sel = draw_select(a, qres, oh, excl_ok, d.xn, lxn, a.nunits, a.uw, v0, v1, v2,
+                                  residual ? d.cr : 0.0, residual ? d.zr : 0.0, d.uf, s_tab);
+  int tok = -1;
+  if (sel.rs >= 0) {
+    const int R0 = min(V, sel.rs * a.uw), R1 = min(V, R0 + a.uw);
+    tok = wave_resweep<T>(lrow, qrow, R0, R1, sel, residual ? d.zr : 0.0, kExpScale * a.k2d, s_tab);
+  }
+  if (tok < 0) tok = V - 1;
+  const int out = d.base + d.b;
+  for (int i = lane; i < d.n; i += 64) a.emitted[out + i] = a.ids[d.base + i];
+  for (int i = d.n + 1 + lane; i <= d.g; i += 64) a.emitted[out + i] = -1;
+  if (lane == 0) {
+    a.emitted[out + d.n] = tok;
+    a.acc[d.b] = d.n;
+    a.rsum[d.b] = residual ? static_cast<float>(sel.S) : 0.f;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kGrpThreads, 4) void k_verify_group(Args a) {
+  __shared__ double s_tab[kExpN];
+  __shared__ float s_c[kGrpWaves], s_z[kGrpWaves];
+  __shared__ GroupDraw s_d;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int V = a.V, g = a.gamma, S = a.split;
+  const int W = g > 0 ? g * S : 1;  // workgroups of a sequence
+  const int b = static_cast<int>(blockIdx.x) / W, j = static_cast<int>(blockIdx.x) - b * W;
+  const int base = b * g;
+  exp_table_init(s_tab);
+  if (g > 0) {
+    const int i = j / S, k = j - i * S;  // chunk k of draft row i
+    const int d = base + i;
+    const T* row = static_cast<const T*>(a.logits) + static_cast<size_t>(d + b) * V;
+    const int lo = k * a.span, hi = min(V, lo + a.span);
+    // wave 0: the sequence's drafts and uniforms (lane i: row i), loaded ahead of pass 1
+    const int ii = min(lane, g - 1);
+    int xv = 0;
+    float uu = 0.f, uf = 0.f;
+    float lx = 0.f, qx = 0.f;
+    if (wave == 0) {
+      xv = a.ids[base + ii];
+      uu = a.u[base + ii + b];
+      uf = a.u[base + b + g];
+      if (lane == 0) {  // the accept operands of this chunk
+        const int x = a.ids[d];
+        if (x >= lo && x < hi) {
+          lx = load_one(row, x);
+          qx = a.onehot ? 1.f : a.q[static_cast<size_t>(d) * V + x];
+        }
+      }
+    }
+    float C, Z;
+    block_row_lse<T, true, kGrpThreads>(row, lo, hi, a.k2, s_c, s_z, C, Z);
+    if (wave == 0) {
+      if (lane == 0) {
+        unsigned long long* rec = a.pchunk + static_cast<size_t>(blockIdx.x) * 4;
+        store_sys(rec + 0, rec_word(C, a.ptag));
+        store_sys(rec + 1, rec_word(Z, a.ptag));
+        store_sys(rec + 2, rec_word(lx, a.ptag));
+        store_sys(rec + 3, rec_word(qx, a.ptag));
+      }
+      // the sequence's records, record l in lane l; then lane i merges row i's chunks
+      const unsigned long long* rb = a.pchunk + static_cast<size_t>(b) * W * 4;
+      const bool live = lane < W;
+      unsigned long long r0 = 0, r1 = 0, r2 = 0, r3 = 0;
+      for (int polls = 0;; ++polls) {
+        if (live) {
+          r0 = load_sys(rb + lane * 4);
+          r1 = load_sys(rb + lane * 4 + 1);
+          r2 = load_sys(rb + lane * 4 + 2);
+          r3 = load_sys(rb + lane * 4 + 3);
+        }
+        const bool ok = !live || (rec_tagged(r0, a.ptag) && rec_tagged(r1, a.ptag) && rec_tagged(r2, a.ptag) &&
+                                  rec_tagged(r3, a.ptag));
+        if (__ballot(!ok) == 0) break;
+        if (polls >= kGrpSpinCap) {
+          if (lane == 0) atomicOr(a.err, SV_DATA_STALL);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      const float Cl = rec_value(r0), Zl = rec_value(r1), lxl = rec_value(r2), qxl = rec_value(r3);
+      float Cm = -FLT_MAX, Zm = 0.f;
+      for (int kk = 0; kk < S; ++kk) {  // chunk order, the same in every workgroup and call
+        const float c2 = __shfl(Cl, ii * S + kk), z2 = __shfl(Zl, ii * S + kk);
+        lse2_merge(Cm, Zm, c2, z2);
+      }
+      const int kx = xv >= 0 && xv < V ? min(xv / a.span, S - 1) : 0;
+      const float lxv = __shfl(lxl, ii * S + kx), qxv = __shfl(qxl, ii * S + kx);
+      bool acc = true;
+      if (lane < g) {
+        double px;
+        const bool mine = lane == i && k == 0;  // one workgroup flags and reports row i
+        acc = accept_decision(xv, lxv, qxv, uu, Cm, Zm, a, px, mine);
+        if (mine && a.pdraft) a.pdraft[base + lane] = static_cast<float>(px);
+      }
+      const unsigned long long rej = __ballot(lane < g && !acc);
+      const int n = rej ? __ffsll(rej) - 1 : g;
+      const int src = n < g ? n : 0;
+      const float cr = __shfl(Cm, src), zr = __shfl(Zm, src);
+      const int xn = __shfl(xv, src);
+      if (lane == 0)
+        s_d = GroupDraw{n < g ? static_cast<double>(zr) : 0.0, n < g ? static_cast<double>(cr) : 0.0, n, g, base,
+                        n < g ? xn : -1, b, uf};
+    }
+  } else if (threadIdx.x == 0) {
+    s_d = GroupDraw{0.0, 0.0, 0, 0, 0, -1, b, a.u[b]};
+  }
+  __syncthreads();  // s_d, s_tab
+  const GroupDraw dd = uniform_draw(s_d);
+  const int unit = j * kGrpWaves + wave;
+  if (unit >= a.nunits) return;
+  const T* lrow = drawn_row<T>(a, dd);
+  const float* qrow = drawn_q(a, dd);
+  const bool residual = dd.n < dd.g;
+  const int r0 = unit * a.uw, r1 = min(V, r0 + a.uw);
+  double D, Q, Zs;
+  draw_sweep<T, true>(lrow, qrow, r0, r1, kExpScale * a.k2d, kExpScale * (residual ? dd.cr : 0.0),
+                      residual ? dd.zr : 0.0, s_tab, D, Q, Zs);
+  // the unit's three sums as six tagged words (each 32-bit half with the call's tag)
+  unsigned long long* sums = a.psum + static_cast<size_t>(b) * kGrpMaxUnits * kSumWords;
+  if (lane == 0) {
+    unsigned long long* dst = sums + static_cast<size_t>(unit) * kSumWords;
+    const double v[3] = {D, Q, Zs};
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+      const unsigned long long x = static_cast<unsigned long long>(__double_as_longlong(v[t]));
+      store_sys(dst + 2 * t, (x & 0xFFFFFFFF00000000ull) | a.ptag);
+      store_sys(dst + 2 * t + 1, (x << 32) | a.ptag);
+    }
+  }
+  if (unit != 0) return;
+  // the finisher (unit 0's wave): every unit's sums, unit u in lane u
+  const bool live = lane < a.nunits;
+  const unsigned long long* src = sums + static_cast<size_t>(live ? lane : 0) * kSumWords;
+  unsigned long long w[kSumWords];
+  for (int polls = 0;; ++polls) {
+    bool ok = true;
+#pragma unroll
+    for (int t = 0; t < kSumWords; ++t) {
+      w[t] = live ? load_sys(src + t) : 0ull;
+      ok = ok && (!live || rec_tagged(w[t], a.ptag));
+    }
+    if (__ballot(!ok) == 0) break;
+    if (polls >= kGrpSpinCap) {
+      if (lane == 0) atomicOr(a.err, SV_DATA_STALL);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  double v[3];
+#pragma unroll
+  for (int t = 0; t < 3; ++t)
+    v[t] = live ? __longlong_as_double(static_cast<long long>((w[2 * t] & 0xFFFFFFFF00000000ull) | (w[2 * t + 1] >> 32)))
+                : 0.0;
+  group_finish<T>(a, dd, v[0], v[1], v[2], s_tab);
+}
+
 // NT1: the judged rows are read with nontemporal loads. Measured on MI355X this helps
 // when every sequence has its own compute unit (B <= CUs: C3, 4.6% faster) and costs
 // when workgroups run in several rounds (C5, 1.6% slower), so the host picks it by B.
@@ -2744,7 +3090,7 @@ constexpr int kEventsPerRun = 2 * kKernels;
 // The launch sequences a call can take.
 enum Path {
   kPathSample2 = 0, kPathGreedy2 = 1, kPathSample1 = 2, kPathGreedy1 = 3, kPathSample3 = 4, kPathRows = 5,
-  kPathSample1R = 6, kPathGreedy1R = 7, kPathGreedyH = 8, kPathGreedyHR = 9, kPaths = 10
+  kPathSample1R = 6, kPathGreedy1R = 7, kPathGreedyH = 8, kPathGreedyHR = 9, kPathGroup = 10, kPaths = 11
 };
 struct PathInfo {
   int nk;
@@ -2761,6 +3107,7 @@ const PathInfo kPathInfo[kPaths] = {
     {2, {"k_order_by_gamma", "k_greedy_seq1"}},
     {1, {"k_greedy_help", nullptr}},
     {2, {"k_order_by_gamma", "k_greedy_help"}},
+    {1, {"k_verify_group", nullptr}},
 };
 
 }  // namespace
@@ -2795,6 +3142,12 @@ struct spec_verify_ctx {
   unsigned long long* gpart = nullptr;
   unsigned long long* gbest = nullptr;
   unsigned int gepoch = 0;  // the last call's epoch (0 is never used: the arrays start at 0)
+  // small-batch one-launch plan (up to grp_cap sequences)
+  unsigned long long* pchunk = nullptr;
+  unsigned long long* psum = nullptr;
+  int grp_cap = 0;
+  int grp_slots = 0;     // workgroups of k_verify_group resident at once (0: not yet known)
+  unsigned ptag = 0;     // the last call's tag
   char msg[512] = {0};
 };
 
@@ -2910,6 +3263,69 @@ hipError_t launch_fused_greedy(spec_verify_ctx* ctx, const Args& a, hipStream_t 
   const void* fn = a.B <= ctx->cus ? reinterpret_cast<const void*>(&k_greedy_seq1<T, RG, true>)
                                    : reinterpret_cast<const void*>(&k_greedy_seq1<T, RG, false>);
   const hipError_t e = launch_one(fn, dim3(a.B), dim3(kSeqThreads), ao, st, ev, k);
+  if (e != hipSuccess) return e;
+  if (ev) ++ctx->timing_runs;
+  return hipGetLastError();
+}
+
+// Workgroups of k_verify_group resident on the device at once.
+template <typename T>
+int group_slots(int cus) {
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(&k_verify_group<T>),
+                                                   kGrpThreads, 0) != hipSuccess || occ < 1)
+    occ = 1;
+  return cus * occ;
+}
+
+// The small-batch plan's geometry: chunks per draft row (split) and their width (span),
+// so that all B x gamma x split workgroups are resident at once, at most kGrpMaxW per
+// sequence; the drawn row's unit width and count. False when the rows alone are more
+// workgroups than that, or the workspace does not hold the batch.
+bool group_grid(spec_verify_ctx* ctx, Args& a, int& grid) {
+  if (!ctx->pchunk || a.B > ctx->grp_cap || a.gamma < 0 || a.gamma > kGrpMaxW) return false;
+  if (ctx->grp_slots == 0)
+    ctx->grp_slots = ctx->dtype == SV_BF16 ? group_slots<uint16_t>(ctx->cus) : group_slots<float>(ctx->cus);
+  const int cap = min(ctx->grp_slots, kGrpMaxItems);
+  int W;
+  if (a.gamma == 0) {
+    a.split = 1;
+    a.span = a.V;
+    W = 1;
+  } else {
+    const long long R = static_cast<long long>(a.B) * a.gamma;
+    if (R > cap) return false;
+    int s = static_cast<int>(min(static_cast<long long>(kMaxSplit), cap / R));
+    s = min(s, kGrpMaxW / a.gamma);
+    s = max(1, min(s, a.V / SV_SPLIT_MIN_SPAN));
+    int span = (a.V + s - 1) / s;
+    span = (span + kGroup - 1) / kGroup * kGroup;
+    a.span = span;
+    a.split = (a.V + span - 1) / span;
+    W = a.gamma * a.split;
+  }
+  if (static_cast<long long>(a.B) * W > cap) return false;
+  grid = a.B * W;
+  // units of the drawn row: at most one per wave of the sequence's workgroups and 64 in
+  // all, whole sweep iterations (a unit's loads are then issued together, without a
+  // masked tail)
+  const int units = min(kGrpMaxUnits, W * kGrpWaves);
+  const int per = (a.V + units - 1) / units;
+  a.uw = (per + kIter - 1) / kIter * kIter;
+  a.nunits = (a.V + a.uw - 1) / a.uw;
+  return true;
+}
+
+template <typename T>
+hipError_t launch_group(spec_verify_ctx* ctx, const Args& a0, hipStream_t st, int grid) {
+  hipEvent_t* ev = timing_slot(ctx, kPathGroup);
+  Args a = a0;
+  a.pchunk = ctx->pchunk;
+  a.psum = ctx->psum;
+  if (++ctx->ptag == 0) ctx->ptag = 1;
+  a.ptag = ctx->ptag;
+  const hipError_t e = launch_one(reinterpret_cast<const void*>(&k_verify_group<T>), dim3(grid), dim3(kGrpThreads),
+                                  a, st, ev, 0);
   if (e != hipSuccess) return e;
   if (ev) ++ctx->timing_runs;
   return hipGetLastError();
@@ -3105,11 +3521,20 @@ int run_impl(spec_verify_ctx* ctx, void* hip_stream, int batch, int gamma, const
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   // one launch per call when there are enough sequences to give every compute unit one
   const int gmax = cu_gamma ? ctx->max_gamma : gamma;
-  const bool fused = ctx->path_mode != SV_PATH_TWO_LAUNCH && aligned && gmax <= kFuseMaxGamma &&
-                     (ctx->path_mode == SV_PATH_ONE_LAUNCH || batch >= ctx->cus);
   const bool rg = cu_gamma != nullptr;
+  // small batches of sampling rows, uniform gamma: one launch with the rows read in
+  // parallel and the draws pooled (AUTO below the compute-unit count, or when asked)
+  Args ga = a;
+  int ggrid = 0;
+  const bool grp_ok = !greedy && !rg && aligned && group_grid(ctx, ga, ggrid);
+  const bool pooled = grp_ok && (ctx->path_mode == SV_PATH_POOLED ||
+                                 (ctx->path_mode == SV_PATH_AUTO && batch < ctx->cus));
+  const bool fused = !pooled && ctx->path_mode != SV_PATH_TWO_LAUNCH && ctx->path_mode != SV_PATH_POOLED && aligned &&
+                     gmax <= kFuseMaxGamma && (ctx->path_mode == SV_PATH_ONE_LAUNCH || batch >= ctx->cus);
   hipError_t e;
-  if (fused && greedy)
+  if (pooled)
+    e = ctx->dtype == SV_BF16 ? launch_group<uint16_t>(ctx, ga, st, ggrid) : launch_group<float>(ctx, ga, st, ggrid);
+  else if (fused && greedy)
     e = ctx->dtype == SV_BF16
             ? (rg ? launch_fused_greedy<uint16_t, true>(ctx, a, st) : launch_fused_greedy<uint16_t, false>(ctx, a, st))
             : (rg ? launch_fused_greedy<float, true>(ctx, a, st) : launch_fused_greedy<float, false>(ctx, a, st));
@@ -3122,7 +3547,7 @@ int run_impl(spec_verify_ctx* ctx, void* hip_stream, int batch, int gamma, const
   if (e != hipSuccess) return hip_fail(ctx, "kernel launch", e);
   ctx->last_stream = st;
   ctx->ran = true;
-  ctx->last_path = fused ? SV_PATH_ONE_LAUNCH : SV_PATH_TWO_LAUNCH;
+  ctx->last_path = pooled ? SV_PATH_POOLED : fused ? SV_PATH_ONE_LAUNCH : SV_PATH_TWO_LAUNCH;
   return SV_OK;
 }
 
@@ -3213,12 +3638,13 @@ template <typename T, bool A, bool R, bool G> struct VsFinish { static constexpr
 // greedy-helper counters, the split draw's sums and counts (split_cap sequences), and
 // the error word.
 struct WsLayout {
-  size_t p1, accept, lxq, s_acc, s_rsum, order, gclaim, gpart, gbest, dsum, dcnt, err, total;
+  size_t p1, accept, lxq, s_acc, s_rsum, order, gclaim, gpart, gbest, dsum, dcnt, err;
+  size_t pchunk, psum, total;
   size_t p1_cap;
-  int split_cap;
+  int split_cap, grp_cap;
 };
 constexpr size_t ws_up(size_t x) { return (x + 255) / 256 * 256; }
-constexpr WsLayout ws_layout(size_t p1_cap, int max_rows, int max_batch, int split_cap) {
+constexpr WsLayout ws_layout(size_t p1_cap, int max_rows, int max_batch, int split_cap, int grp_cap) {
   const size_t rows = static_cast<size_t>(max_rows > 0 ? max_rows : 1);
   const size_t seqs = static_cast<size_t>(max_batch > 0 ? max_batch : 1);
   const size_t cap = static_cast<size_t>(split_cap > 0 ? split_cap : 0);
@@ -3236,9 +3662,13 @@ constexpr WsLayout ws_layout(size_t p1_cap, int max_rows, int max_batch, int spl
   L.dsum = o;    o += ws_up(sizeof(double) * 3 * kMaxSub * cap);
   L.dcnt = o;    o += ws_up(sizeof(int) * (cap > 0 ? cap : 1));
   L.err = o;     o += 256;
+  const size_t gc = static_cast<size_t>(grp_cap > 0 ? grp_cap : 0);
+  L.pchunk = o;  o += gc > 0 ? ws_up(sizeof(unsigned long long) * 4 * kGrpMaxItems) : 0;
+  L.psum = o;    o += ws_up(sizeof(unsigned long long) * kSumWords * kGrpMaxUnits * gc);
   L.total = o;
   L.p1_cap = p1_cap;
   L.split_cap = split_cap;
+  L.grp_cap = grp_cap;
   return L;
 }
 void ws_assign(spec_verify_ctx* ctx, const WsLayout& L, char* base) {
@@ -3256,6 +3686,9 @@ void ws_assign(spec_verify_ctx* ctx, const WsLayout& L, char* base) {
   ctx->dsum = L.split_cap > 0 ? reinterpret_cast<double*>(base + L.dsum) : nullptr;
   ctx->dcnt = L.split_cap > 0 ? reinterpret_cast<int*>(base + L.dcnt) : nullptr;
   ctx->err = reinterpret_cast<int*>(base + L.err);
+  ctx->grp_cap = L.grp_cap;
+  ctx->pchunk = L.grp_cap > 0 ? reinterpret_cast<unsigned long long*>(base + L.pchunk) : nullptr;
+  ctx->psum = L.grp_cap > 0 ? reinterpret_cast<unsigned long long*>(base + L.psum) : nullptr;
 }
 
 // The no-allocation entry point's workspace: a static device array of the layout above
@@ -3265,13 +3698,19 @@ constexpr int kStaticMaxBatch = SV_STATIC_MAX_BATCH;
 constexpr int kStaticMaxRows = SV_STATIC_MAX_ROWS;
 constexpr int kStaticSplitCap = 128;
 constexpr WsLayout kStaticLayout =
-    ws_layout(kStaticMaxRows + SV_SPLIT_TARGET, kStaticMaxRows, kStaticMaxBatch, kStaticSplitCap);
+    ws_layout(kStaticMaxRows + SV_SPLIT_TARGET, kStaticMaxRows, kStaticMaxBatch, kStaticSplitCap, kStaticMaxBatch);
 constexpr int kStaticMaxDevices = 64;
 static_assert(kStaticLayout.total <= static_cast<size_t>(SV_STATIC_SCRATCH_MAX_BYTES), "static workspace size");
 static_assert(SV_STATIC_MAX_GAMMA == kFuseMaxGamma, "the static entry point's gamma limit");
 
-__global__ void k_zero_words(int* p, int n) {
-  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
+// Set-up of the static workspace: the split draw's counts to 0 and the small-batch
+// plan's records and unit sums to tag 0, which no call uses.
+__global__ void k_static_setup(char* ws) {
+  int* dcnt = reinterpret_cast<int*>(ws + kStaticLayout.dcnt);
+  for (int i = threadIdx.x; i < kStaticSplitCap; i += blockDim.x) dcnt[i] = 0;
+  unsigned long long* tail = reinterpret_cast<unsigned long long*>(ws + kStaticLayout.pchunk);
+  const size_t words = (kStaticLayout.total - kStaticLayout.pchunk) / sizeof(unsigned long long);
+  for (size_t i = threadIdx.x; i < words; i += blockDim.x) tail[i] = 0ull;
 }
 
 }  // namespace
@@ -3284,6 +3723,8 @@ namespace {
 struct StaticDevice {
   char* ptr = nullptr;  // this device's copy of `scratch`
   int cus = 0;
+  int grp_slots[2] = {0, 0};  // workgroups of k_verify_group resident at once: fp32, bf16 logits
+  unsigned ptag = 0;          // the small-batch plan's call tag, advanced by every call
 };
 StaticDevice g_static[kStaticMaxDevices];
 std::mutex g_static_mu;
@@ -3304,16 +3745,19 @@ int static_device(int device, hipStream_t st, StaticDevice& out) {
     }
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) cus = 256;
-    hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(256), 0, st, reinterpret_cast<int*>(static_cast<char*>(p) +
-                       kStaticLayout.dcnt), kStaticSplitCap);
+    hipLaunchKernelGGL(k_static_setup, dim3(1), dim3(256), 0, st, static_cast<char*>(p));
     e = hipGetLastError();
     if (e != hipSuccess) {
       snprintf(g_static_msg, sizeof(g_static_msg), "kernel launch: %s", hipGetErrorString(e));
       return SV_EHIP;
     }
+    d.grp_slots[0] = group_slots<float>(cus);
+    d.grp_slots[1] = group_slots<uint16_t>(cus);
     d.cus = cus;
     d.ptr = static_cast<char*>(p);
   }
+  d.ptag += 2;  // launch_group takes the next one
+  if (d.ptag == 0) d.ptag = 2;
   out = d;
   return SV_OK;
 }
@@ -3384,7 +3828,8 @@ int spec_verify_create(spec_verify_ctx** out, int device, int vocab, int logits_
   const int by_len = (vocab + SV_SPLIT_MIN_SPAN - 1) / SV_SPLIT_MIN_SPAN;
   const int max_split = by_len < kMaxSplit ? by_len : kMaxSplit;
   const WsLayout L = ws_layout(static_cast<size_t>(max_draft_rows > 0 ? max_draft_rows : 1) * max_split,
-                               max_draft_rows, max_batch, max_batch < kSplitMaxB ? max_batch : kSplitMaxB);
+                               max_draft_rows, max_batch, max_batch < kSplitMaxB ? max_batch : kSplitMaxB,
+                               max_batch < kGrpMaxItems ? max_batch : kGrpMaxItems);
   if (hipMalloc(&ctx->ws, L.total) != hipSuccess) {
     delete ctx;
     return SV_ENOMEM;
@@ -3447,6 +3892,8 @@ int spec_verify_run_static(int device, void* hip_stream, int vocab, int logits_d
   c.max_gamma = SV_STATIC_MAX_GAMMA;
   c.cus = dv.cus;
   c.no_helpers = true;
+  c.grp_slots = dv.grp_slots[logits_dtype == SV_BF16 ? 1 : 0];
+  c.ptag = dv.ptag;
   ws_assign(&c, kStaticLayout, dv.ptr);
   c.err = data_flags;
   const int rc = run_impl(&c, hip_stream, batch, gamma, cu_gamma, total_draft_rows, temperature, logits, q, false,
@@ -3672,7 +4119,9 @@ int spec_adapt_gamma(spec_verify_ctx* ctx, void* hip_stream, int batch, const in
 }
 
 int spec_verify_set_path(spec_verify_ctx* ctx, int mode) {
-  if (!ctx || (mode != SV_PATH_AUTO && mode != SV_PATH_TWO_LAUNCH && mode != SV_PATH_ONE_LAUNCH)) return SV_EINVAL;
+  if (!ctx || (mode != SV_PATH_AUTO && mode != SV_PATH_TWO_LAUNCH && mode != SV_PATH_ONE_LAUNCH &&
+               mode != SV_PATH_POOLED))
+    return SV_EINVAL;
   ctx->path_mode = mode;
   return SV_OK;
 }

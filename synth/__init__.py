@@ -357,11 +357,16 @@ def config_number(name: str) -> int:
 
 
 def make_config(name: str, seed: int = 0, batch: Optional[int] = None,
-                vocab: Optional[int] = None) -> Workload:
-    """Build workload `name` (C1..C5). batch / vocab override B / V (same recipe)."""
+                vocab: Optional[int] = None, gamma: Optional[int] = None) -> Workload:
+    """Build workload `name` (C1..C5). batch / vocab override B / V, gamma the draft
+    length of the uniform-gamma configurations (same recipe)."""
     c = CONFIGS[name]
     B = int(batch if batch is not None else c["B"])
     V = int(vocab if vocab is not None else c["V"])
+    if gamma is not None:
+        if name == "C5":
+            raise ValueError("C5 draws its per-sequence draft lengths; gamma applies to C1..C4")
+        c = dict(c, gamma=int(gamma))
     base = 0x5EED0000 + config_number(name) + 1000 * int(seed)
     if name == "C4":
         return make_greedy(name, np.full(B, c["gamma"]), V, c["dtype"], c["sigma_logit"],

@@ -18,7 +18,8 @@ torch = pytest.importorskip("torch")
 
 PLANS = (("two-launch", "SV_PATH_TWO_LAUNCH", True),
          ("one-launch", "SV_PATH_ONE_LAUNCH", True),
-         ("one-launch, stop at rejection", "SV_PATH_ONE_LAUNCH", False))
+         ("one-launch, stop at rejection", "SV_PATH_ONE_LAUNCH", False),
+         ("small-batch pooled", "SV_PATH_POOLED", False))
 
 
 def _say(*a):

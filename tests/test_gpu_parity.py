@@ -49,10 +49,12 @@ def verifier(sv, V, dtype, max_batch, max_rows, max_gamma=16):
 
 
 # Every parity case runs both launch plans; the one-launch plan also without p(x), the
-# way it stops reading rows at the first rejection.
+# way it stops reading rows at the first rejection, and with every workgroup drawing its
+# own row instead of the pooled draw.
 PLANS = (("two-launch", "SV_PATH_TWO_LAUNCH", True),
          ("one-launch", "SV_PATH_ONE_LAUNCH", True),
-         ("one-launch, stop at rejection", "SV_PATH_ONE_LAUNCH", False))
+         ("one-launch, stop at rejection", "SV_PATH_ONE_LAUNCH", False),
+         ("small-batch pooled", "SV_PATH_POOLED", False))
 
 
 def check_parity(sv, w, label, ragged=None, max_gamma=16, plans=PLANS):
@@ -370,7 +372,7 @@ def test_host_errors_launch_nothing(lib):
     assert torch.all(acc == -7) and torch.all(em == -7) and torch.all(rs == -7.0)
 
 
-PLAN_IDS = ["SV_PATH_TWO_LAUNCH", "SV_PATH_ONE_LAUNCH"]
+PLAN_IDS = ["SV_PATH_TWO_LAUNCH", "SV_PATH_ONE_LAUNCH", "SV_PATH_POOLED"]
 
 
 @pytest.mark.parametrize("plan", PLAN_IDS)
@@ -622,6 +624,45 @@ def test_split_draw_repeated_calls(lib, cfg, batch):
     v.set_path(lib.SV_PATH_AUTO)
 
 
+@pytest.mark.parametrize("cfg,batch,gamma", [("C2", None, None), ("C3", 32, None), ("C3", 64, None),
+                                             ("C2", 16, 0), ("C1", 1, None)])
+def test_pooled_draw_repeated_calls(lib, cfg, batch, gamma):
+    """The small-batch plan (one launch: chunks of every draft row read in parallel, the
+    workgroups of a sequence waiting for each other's tagged pass-1 records, then sweeping
+    the drawn row together, the last to count finishing it) over 100 calls in a row,
+    alternating two input sets: its workspace is kept between calls (records tagged by
+    call, draw counters reset by the finisher), so every call must give the first
+    (oracle-checked) outputs of its set; a call's leftovers must never leak into the next."""
+    ws = [synth.make_config(cfg, seed=s, batch=batch, gamma=gamma) for s in (61, 62)]
+    w0 = ws[0]
+    v = verifier(lib, w0.V, w0.dtype, w0.B, max(w0.draft_rows, 1))
+    v.set_path(lib.SV_PATH_POOLED)
+    devs = [to_device(w) for w in ws]
+    _say("pooled draw x100", f"{cfg} B={w0.B} V={w0.V} gamma={w0.uniform_gamma}")
+    first = []
+    for w, d in zip(ws, devs):
+        gpu = run_gpu(v, w, dev=d, want_p_draft=False)
+        assert gpu["status"] == lib.SV_OK, v.last_error()
+        assert v.last_path() == lib.SV_PATH_POOLED
+        rep = compare(w, gpu, oracle_batch(w))
+        _say("pooled draw x100", "first call", rep.summary())
+        assert rep.ok(), rep.summary()
+        first.append(gpu)
+    outs = []
+    for k in range(100):
+        w, d = ws[k % 2], devs[k % 2]
+        outs.append(v.run(d["logits"], d["draft_ids"], temperature=w.T, q=d["q"], uniforms=d["uniforms"],
+                          want_p_draft=False, gamma=w.uniform_gamma))
+    torch.cuda.synchronize()
+    assert v.status() == lib.SV_OK, v.last_error()
+    for k, o in enumerate(outs):
+        f = first[k % 2]
+        assert np.array_equal(o.accepted_count.cpu().numpy(), f["accepted_count"]), k
+        assert np.array_equal(o.emitted_tokens.cpu().numpy(), f["emitted_tokens"]), k
+        assert np.array_equal(o.residual_sum.cpu().numpy(), f["residual_sum"]), k
+    v.set_path(lib.SV_PATH_AUTO)
+
+
 def test_greedy_helpers_repeated_calls(lib):
     """Greedy one-launch batches of CUs..4 x CUs sequences add helper workgroups that claim
     rows through per-sequence counters tagged with the call's epoch: 100 calls in a row on
@@ -661,9 +702,14 @@ def test_greedy_helpers_repeated_calls(lib):
     v.close()
 
 
-def test_side_stream_and_timing(lib):
+@pytest.mark.parametrize("plan", ["SV_PATH_AUTO", "SV_PATH_TWO_LAUNCH"])
+def test_side_stream_and_timing(lib, plan):
+    """Calls on a side stream, timed per kernel: 32 sequences (fewer than compute units)
+    take the small-batch pooled launch by default; the two-launch plan splits the draw
+    when there are at most half as many sequences as compute units."""
     w = synth.make_config("C3", seed=16, batch=32)
     v = verifier(lib, w.V, w.dtype, w.B, w.draft_rows)
+    v.set_path(getattr(lib, plan))
     dev = to_device(w)
     s = torch.cuda.Stream()
     v.set_timing(3)
@@ -677,14 +723,19 @@ def test_side_stream_and_timing(lib):
         v.set_timing(0)
     s.synchronize()
     assert runs == 3
-    # 32 sequences: at most half as many as compute units, so the draw is split
-    split = w.B * 2 <= torch.cuda.get_device_properties(0).multi_processor_count
-    assert [n for n, _ in times] == (["k_rowstats", "k_draw_part"] if split else ["k_rowstats", "k_sample_seq"])
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if plan == "SV_PATH_AUTO":
+        assert v.last_path() == lib.SV_PATH_POOLED
+        assert [n for n, _ in times] == ["k_verify_group"]
+    else:
+        split = w.B * 2 <= cus
+        assert [n for n, _ in times] == (["k_rowstats", "k_draw_part"] if split else ["k_rowstats", "k_sample_seq"])
     assert all(t > 0 for _, t in times)
     gpu = dict(accepted_count=out.accepted_count.cpu().numpy(), emitted_tokens=out.emitted_tokens.cpu().numpy(),
                residual_sum=out.residual_sum.cpu().numpy(), p_draft=out.p_draft.cpu().numpy())
     rep = compare(w, gpu, oracle_batch(w))
     assert rep.ok(), rep.summary()
+    v.set_path(lib.SV_PATH_AUTO)
 
 
 def test_one_launch_plan_chosen_and_timed(lib):
