@@ -226,12 +226,14 @@ int spec_verify_run_onehot(spec_verify_ctx *ctx, void *hip_stream, int batch, in
  * A third plan, one launch for small sampling batches (SV_PATH_POOLED): uniform gamma
  * <= 64, T > 0, V a multiple of 8 and 16-byte aligned logits and q, B x gamma x split
  * workgroups (split >= 1 chunks per draft row) no more than the device holds at once
- * (about 512 on MI355X), B <= 2048 and the context's max_batch. Every draft row is read
+ * (about 1024 on MI355X), B <= 2048 and the context's max_batch. Every draft row is read
  * in parallel, in chunks; the workgroups of a sequence wait (boundedly) for each other's
  * pass-1 records, all reach the same first rejection, and then sweep the drawn row
- * together, the last to finish completing the draw. It reads every draft row (as the
- * two-launch plan does) and gives the same outputs as the other plans. Under
- * SV_PATH_AUTO it is taken when it applies and B is below the compute-unit count.
+ * together, the wave of the first unit completing the draw. Rows of at most 4096
+ * entries instead take one workgroup per sequence (any B), whose waves hand over through
+ * LDS. The plan reads every draft row (as the two-launch plan does) and gives the same
+ * outputs as the other plans. Under SV_PATH_AUTO it is taken when it applies and B is
+ * below the compute-unit count, or V <= 4096.
  * All plans return the same outputs, except that a draft id after the first rejection
  * is not examined by the one-launch plan (so it cannot raise SV_DATA_DRAFT_ID there).
  *   spec_verify_set_path(ctx, mode): SV_PATH_AUTO (default), SV_PATH_TWO_LAUNCH,

@@ -25,10 +25,11 @@
 //     k_draw_part shares each draw over two or four workgroups, the last to finish
 //     completing it.
 //   * one launch for small sampling batches (k_verify_group), B below the compute units:
-//     B x gamma x split 512-thread workgroups, all resident at once, read every draft row
+//     B x gamma x split 256-thread workgroups, all resident at once, read every draft row
 //     in parallel chunks; the workgroups of a sequence wait for each other's pass-1
 //     records, reach the same first rejection and sweep the drawn row together, the
-//     last to finish completing the draw.
+//     wave of the first unit completing the draw. Rows of at most 4096 entries take one
+//     workgroup per sequence instead (k_verify_tiny), its waves handing over through LDS.
 //   * rows with no drafts (k_sample_rows, k_sample_weights): one token per row.
 //   * vocabulary shards (k_vs_rows, k_vs_decide, k_vs_finish): one device's part when
 //     the columns are split over devices.
@@ -193,13 +194,13 @@ __device__ __forceinline__ bool accept_test(int x, float lx, float qx, float uu,
 }
 
 // ============================================================== step 1
-// Base-2 softmax state of entries [lo, hi) of one row over a kThreads block: c = the
-// scaled max (max(l) * k2, clamped to the fp32 range) and z = sum 2^(l k2 - c), kept per
-// thread with a running max, merged over the wave and then the block. Thread 0 returns
-// the block's (C, Z); s_c, s_z are kWaves-entry LDS scratch.
-template <typename T, bool ALIGNED, int NT = kThreads>
-__device__ __forceinline__ void block_row_lse(const T* row, int lo, int hi, float k2, float* s_c, float* s_z,
-                                              float& C, float& Z) {
+// Base-2 softmax state of entries [lo, hi) of one row: c = the scaled max (max(l) * k2,
+// clamped to the fp32 range) and z = sum 2^(l k2 - c), kept per thread with a running max
+// (thread tid of NT taking every NT-th group) and merged over the wave; every lane of the
+// wave returns the wave's (c, z).
+template <typename T, bool ALIGNED, int NT>
+__device__ __forceinline__ void wave_row_lse(const T* row, int lo, int hi, float k2, int tid, float& c_out,
+                                             float& z_out) {
   float m = -FLT_MAX, c = -FLT_MAX;  // running max of l and its scaled value
   float s[kGroup];
 #pragma unroll
@@ -216,7 +217,7 @@ __device__ __forceinline__ void block_row_lse(const T* row, int lo, int hi, floa
   };
   if (ALIGNED) {
     const int g1 = hi >> 3;
-    int g = (lo >> 3) + threadIdx.x;
+    int g = (lo >> 3) + tid;
     for (; g + (kUnroll - 1) * NT < g1; g += kUnroll * NT) {
       float xv[kUnroll][kGroup];
 #pragma unroll
@@ -243,7 +244,7 @@ __device__ __forceinline__ void block_row_lse(const T* row, int lo, int hi, floa
       for (int j = 0; j < kGroup; ++j) s[j] += fast_exp2(fmaf(xv[j], k2, -c));
     }
   } else {
-    for (int e = lo + threadIdx.x; e < hi; e += NT) {
+    for (int e = lo + tid; e < hi; e += NT) {
       const float xv = load_one(row, e);
       rebase(xv);
       s[0] += fast_exp2(fmaf(xv, k2, -c));
@@ -255,6 +256,17 @@ __device__ __forceinline__ void block_row_lse(const T* row, int lo, int hi, floa
     const float c2 = __shfl_xor(c, o), z2 = __shfl_xor(z, o);
     lse2_merge(c, z, c2, z2);
   }
+  c_out = c;
+  z_out = z;
+}
+
+// The same over an NT-thread block (kThreads by default): thread 0 returns the block's
+// (C, Z); s_c, s_z are NT / 64-entry LDS scratch.
+template <typename T, bool ALIGNED, int NT = kThreads>
+__device__ __forceinline__ void block_row_lse(const T* row, int lo, int hi, float k2, float* s_c, float* s_z,
+                                              float& C, float& Z) {
+  float c, z;
+  wave_row_lse<T, ALIGNED, NT>(row, lo, hi, k2, threadIdx.x, c, z);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   if (lane == 0) {
     s_c[w] = c;
@@ -2008,7 +2020,10 @@ __global__ __launch_bounds__(kOrderThreads) void k_order_by_gamma(Args a) {
 // bounded; one that runs out raises SV_DATA_STALL (that call's outputs are then not
 // valid). The host sizes the grid so that every workgroup is resident at once, and a wait
 // then lasts only until the other workgroups of the group have stored their part.
-constexpr int kGrpThreads = 512;
+#ifndef SV_GRP_THREADS
+#define SV_GRP_THREADS 256
+#endif
+constexpr int kGrpThreads = SV_GRP_THREADS;
 constexpr int kGrpWaves = kGrpThreads / 64;
 constexpr int kGrpMaxW = 64;            // workgroups of one sequence (records of one lane each)
 constexpr int kGrpMaxUnits = 64;        // units of a drawn row (unit sums of one lane each)
@@ -2141,10 +2156,11 @@ __device__ __forceinline__ int wave_resweep(const T* lrow, const float* qrow, in
 
 // The finish of a sequence's draw by one wave, unit u's sums in lane u: the search, the
 // re-sweep of the selected unit, and the sequence's outputs (accepted count, the accepted
-// drafts, the drawn token, the -1 padding, residual_sum).
+// drafts, the drawn token, the -1 padding, residual_sum). Lane i holds draft i's id
+// (gamma <= 64).
 template <typename T>
 __device__ __forceinline__ void group_finish(const Args& a, const GroupDraw& d, double v0, double v1, double v2,
-                                             const double* s_tab) {
+                                             const double* s_tab, int myid) {
   const int lane = threadIdx.x & 63;
   const int V = a.V;
   const bool residual = d.n < d.g;
@@ -2163,7 +2179,7 @@ __device__ __forceinline__ void group_finish(const Args& a, const GroupDraw& d, 
   }
   if (tok < 0) tok = V - 1;
   const int out = d.base + d.b;
-  for (int i = lane; i < d.n; i += 64) a.emitted[out + i] = a.ids[d.base + i];
+  if (lane < d.n) a.emitted[out + lane] = myid;
   for (int i = d.n + 1 + lane; i <= d.g; i += 64) a.emitted[out + i] = -1;
   if (lane == 0) {
     a.emitted[out + d.n] = tok;
@@ -2184,6 +2200,7 @@ __global__ __launch_bounds__(kGrpThreads, 4) void k_verify_group(Args a) {
   const int b = static_cast<int>(blockIdx.x) / W, j = static_cast<int>(blockIdx.x) - b * W;
   const int base = b * g;
   exp_table_init(s_tab);
+  int xv = 0;  // wave 0, lane i: draft i's id
   if (g > 0) {
     const int i = j / S, k = j - i * S;  // chunk k of draft row i
     const int d = base + i;
@@ -2191,7 +2208,6 @@ __global__ __launch_bounds__(kGrpThreads, 4) void k_verify_group(Args a) {
     const int lo = k * a.span, hi = min(V, lo + a.span);
     // wave 0: the sequence's drafts and uniforms (lane i: row i), loaded ahead of pass 1
     const int ii = min(lane, g - 1);
-    int xv = 0;
     float uu = 0.f, uf = 0.f;
     float lx = 0.f, qx = 0.f;
     if (wave == 0) {
@@ -2310,7 +2326,96 @@ __global__ __launch_bounds__(kGrpThreads, 4) void k_verify_group(Args a) {
   for (int t = 0; t < 3; ++t)
     v[t] = live ? __longlong_as_double(static_cast<long long>((w[2 * t] & 0xFFFFFFFF00000000ull) | (w[2 * t + 1] >> 32)))
                 : 0.0;
-  group_finish<T>(a, dd, v[0], v[1], v[2], s_tab);
+  group_finish<T>(a, dd, v[0], v[1], v[2], s_tab, xv);
+}
+
+// ---- short rows: one workgroup per sequence
+// With rows of at most kTinyMaxV entries one workgroup takes a whole sequence and every
+// hand-off goes through LDS: wave w computes the softmax state of draft rows w, w + 8, ...
+// (the draft's logit and q entry loaded ahead of the row), wave 0 runs the accept tests of
+// all rows, the waves sweep one unit each of the drawn row, and wave 0 finishes the draw.
+constexpr int kTinyMaxV = 4096;
+
+template <typename T>
+__global__ __launch_bounds__(kGrpThreads) void k_verify_tiny(Args a) {
+  __shared__ double s_tab[kExpN];
+  __shared__ float s_rc[kFuseMaxGamma], s_rz[kFuseMaxGamma], s_lx[kFuseMaxGamma], s_qx[kFuseMaxGamma];
+  __shared__ double s_us[kGrpWaves][3];
+  __shared__ GroupDraw s_d;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int V = a.V, g = a.gamma, b = static_cast<int>(blockIdx.x), base = b * g;
+  exp_table_init(s_tab);
+  int xv = 0;
+  float uu = 0.f, uf = 0.f;
+  if (wave == 0) {  // drafts and uniforms of the sequence (lane i: row i)
+    if (g > 0) {
+      const int ii = min(lane, g - 1);
+      xv = a.ids[base + ii];
+      uu = a.u[base + ii + b];
+    }
+    uf = a.u[base + b + g];
+  }
+  for (int i = wave; i < g; i += kGrpWaves) {
+    const int d = base + i;
+    const T* row = static_cast<const T*>(a.logits) + static_cast<size_t>(d + b) * V;
+    float lx = 0.f, qx = 0.f;
+    if (lane == 0) {
+      const int x = a.ids[d];
+      if (x >= 0 && x < V) {
+        lx = load_one(row, x);
+        qx = a.onehot ? 1.f : a.q[static_cast<size_t>(d) * V + x];
+      }
+    }
+    float c, z;
+    wave_row_lse<T, true, 64>(row, 0, V, a.k2, lane, c, z);
+    if (lane == 0) {
+      s_rc[i] = c;
+      s_rz[i] = z;
+      s_lx[i] = lx;
+      s_qx[i] = qx;
+    }
+  }
+  __syncthreads();  // s_rc, s_rz, s_lx, s_qx, s_tab
+  if (wave == 0) {
+    bool acc = true;
+    float Cm = 0.f, Zm = 0.f;
+    if (lane < g) {
+      double px;
+      Cm = s_rc[lane];
+      Zm = s_rz[lane];
+      acc = accept_decision(xv, s_lx[lane], s_qx[lane], uu, Cm, Zm, a, px, true);
+      if (a.pdraft) a.pdraft[base + lane] = static_cast<float>(px);
+    }
+    const unsigned long long rej = __ballot(lane < g && !acc);
+    const int n = rej ? __ffsll(rej) - 1 : g;
+    const int src = n < g ? n : 0;
+    const float cr = __shfl(Cm, src), zr = __shfl(Zm, src);
+    const int xn = __shfl(xv, src);
+    if (lane == 0)
+      s_d = GroupDraw{n < g ? static_cast<double>(zr) : 0.0, n < g ? static_cast<double>(cr) : 0.0, n, g, base,
+                      n < g ? xn : -1, b, uf};
+  }
+  __syncthreads();  // s_d
+  const GroupDraw dd = uniform_draw(s_d);
+  if (wave < a.nunits) {
+    const bool residual = dd.n < dd.g;
+    const int r0 = wave * a.uw, r1 = min(V, r0 + a.uw);
+    double D, Q, Zs;
+    draw_sweep<T, true>(drawn_row<T>(a, dd), drawn_q(a, dd), r0, r1, kExpScale * a.k2d,
+                        kExpScale * (residual ? dd.cr : 0.0), residual ? dd.zr : 0.0, s_tab, D, Q, Zs);
+    if (lane == 0) {
+      s_us[wave][0] = D;
+      s_us[wave][1] = Q;
+      s_us[wave][2] = Zs;
+    }
+  }
+  __syncthreads();  // s_us
+  if (wave == 0) {
+    const bool live = lane < a.nunits;
+    group_finish<T>(a, dd, live ? s_us[lane][0] : 0.0, live ? s_us[lane][1] : 0.0, live ? s_us[lane][2] : 0.0,
+                    s_tab, xv);
+  }
 }
 
 // NT1: the judged rows are read with nontemporal loads. Measured on MI355X this helps
@@ -3090,7 +3195,8 @@ constexpr int kEventsPerRun = 2 * kKernels;
 // The launch sequences a call can take.
 enum Path {
   kPathSample2 = 0, kPathGreedy2 = 1, kPathSample1 = 2, kPathGreedy1 = 3, kPathSample3 = 4, kPathRows = 5,
-  kPathSample1R = 6, kPathGreedy1R = 7, kPathGreedyH = 8, kPathGreedyHR = 9, kPathGroup = 10, kPaths = 11
+  kPathSample1R = 6, kPathGreedy1R = 7, kPathGreedyH = 8, kPathGreedyHR = 9, kPathGroup = 10, kPathTiny = 11,
+  kPaths = 12
 };
 struct PathInfo {
   int nk;
@@ -3108,6 +3214,7 @@ const PathInfo kPathInfo[kPaths] = {
     {1, {"k_greedy_help", nullptr}},
     {2, {"k_order_by_gamma", "k_greedy_help"}},
     {1, {"k_verify_group", nullptr}},
+    {1, {"k_verify_tiny", nullptr}},
 };
 
 }  // namespace
@@ -3280,10 +3387,23 @@ int group_slots(int cus) {
 
 // The small-batch plan's geometry: chunks per draft row (split) and their width (span),
 // so that all B x gamma x split workgroups are resident at once, at most kGrpMaxW per
-// sequence; the drawn row's unit width and count. False when the rows alone are more
-// workgroups than that, or the workspace does not hold the batch.
-bool group_grid(spec_verify_ctx* ctx, Args& a, int& grid) {
-  if (!ctx->pchunk || a.B > ctx->grp_cap || a.gamma < 0 || a.gamma > kGrpMaxW) return false;
+// sequence; the drawn row's unit width and count. Rows of at most kTinyMaxV entries take
+// one workgroup per sequence (k_verify_tiny, any B; *tiny set). False when the rows alone
+// are more workgroups than that, or the workspace does not hold the batch.
+bool group_grid(spec_verify_ctx* ctx, Args& a, int& grid, bool* tiny) {
+  *tiny = false;
+  if (a.gamma < 0 || a.gamma > kGrpMaxW) return false;
+  if (a.V <= kTinyMaxV) {
+    *tiny = true;
+    grid = a.B;
+    a.split = 1;
+    a.span = a.V;
+    const int per = (a.V + kGrpWaves - 1) / kGrpWaves;  // one unit per wave
+    a.uw = (per + kGroup - 1) / kGroup * kGroup;
+    a.nunits = (a.V + a.uw - 1) / a.uw;
+    return true;
+  }
+  if (!ctx->pchunk || a.B > ctx->grp_cap) return false;
   if (ctx->grp_slots == 0)
     ctx->grp_slots = ctx->dtype == SV_BF16 ? group_slots<uint16_t>(ctx->cus) : group_slots<float>(ctx->cus);
   const int cap = min(ctx->grp_slots, kGrpMaxItems);
@@ -3317,15 +3437,16 @@ bool group_grid(spec_verify_ctx* ctx, Args& a, int& grid) {
 }
 
 template <typename T>
-hipError_t launch_group(spec_verify_ctx* ctx, const Args& a0, hipStream_t st, int grid) {
-  hipEvent_t* ev = timing_slot(ctx, kPathGroup);
+hipError_t launch_group(spec_verify_ctx* ctx, const Args& a0, hipStream_t st, int grid, bool tiny) {
+  hipEvent_t* ev = timing_slot(ctx, tiny ? kPathTiny : kPathGroup);
   Args a = a0;
   a.pchunk = ctx->pchunk;
   a.psum = ctx->psum;
-  if (++ctx->ptag == 0) ctx->ptag = 1;
+  if (!tiny && ++ctx->ptag == 0) ctx->ptag = 1;
   a.ptag = ctx->ptag;
-  const hipError_t e = launch_one(reinterpret_cast<const void*>(&k_verify_group<T>), dim3(grid), dim3(kGrpThreads),
-                                  a, st, ev, 0);
+  const void* fn = tiny ? reinterpret_cast<const void*>(&k_verify_tiny<T>)
+                        : reinterpret_cast<const void*>(&k_verify_group<T>);
+  const hipError_t e = launch_one(fn, dim3(grid), dim3(kGrpThreads), a, st, ev, 0);
   if (e != hipSuccess) return e;
   if (ev) ++ctx->timing_runs;
   return hipGetLastError();
@@ -3526,14 +3647,16 @@ int run_impl(spec_verify_ctx* ctx, void* hip_stream, int batch, int gamma, const
   // parallel and the draws pooled (AUTO below the compute-unit count, or when asked)
   Args ga = a;
   int ggrid = 0;
-  const bool grp_ok = !greedy && !rg && aligned && group_grid(ctx, ga, ggrid);
+  bool tiny = false;
+  const bool grp_ok = !greedy && !rg && aligned && group_grid(ctx, ga, ggrid, &tiny);
   const bool pooled = grp_ok && (ctx->path_mode == SV_PATH_POOLED ||
-                                 (ctx->path_mode == SV_PATH_AUTO && batch < ctx->cus));
+                                 (ctx->path_mode == SV_PATH_AUTO && (tiny || batch < ctx->cus)));
   const bool fused = !pooled && ctx->path_mode != SV_PATH_TWO_LAUNCH && ctx->path_mode != SV_PATH_POOLED && aligned &&
                      gmax <= kFuseMaxGamma && (ctx->path_mode == SV_PATH_ONE_LAUNCH || batch >= ctx->cus);
   hipError_t e;
   if (pooled)
-    e = ctx->dtype == SV_BF16 ? launch_group<uint16_t>(ctx, ga, st, ggrid) : launch_group<float>(ctx, ga, st, ggrid);
+    e = ctx->dtype == SV_BF16 ? launch_group<uint16_t>(ctx, ga, st, ggrid, tiny)
+                              : launch_group<float>(ctx, ga, st, ggrid, tiny);
   else if (fused && greedy)
     e = ctx->dtype == SV_BF16
             ? (rg ? launch_fused_greedy<uint16_t, true>(ctx, a, st) : launch_fused_greedy<uint16_t, false>(ctx, a, st))

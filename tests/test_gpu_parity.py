@@ -624,26 +624,35 @@ def test_split_draw_repeated_calls(lib, cfg, batch):
     v.set_path(lib.SV_PATH_AUTO)
 
 
-@pytest.mark.parametrize("cfg,batch,gamma", [("C2", None, None), ("C3", 32, None), ("C3", 64, None),
-                                             ("C2", 16, 0), ("C1", 1, None)])
-def test_pooled_draw_repeated_calls(lib, cfg, batch, gamma):
+@pytest.mark.parametrize("cfg,batch,gamma,vocab", [("C2", None, None, None), ("C3", 32, None, None),
+                                                   ("C3", 64, None, None), ("C2", 16, 0, None),
+                                                   ("C1", 1, None, None), ("C2", 40, 12, 4096),
+                                                   ("C3", 30, 3, 4104), ("C3", 700, 2, 2048)])
+def test_pooled_draw_repeated_calls(lib, cfg, batch, gamma, vocab):
     """The small-batch plan (one launch: chunks of every draft row read in parallel, the
     workgroups of a sequence waiting for each other's tagged pass-1 records, then sweeping
-    the drawn row together, the last to count finishing it) over 100 calls in a row,
-    alternating two input sets: its workspace is kept between calls (records tagged by
-    call, draw counters reset by the finisher), so every call must give the first
-    (oracle-checked) outputs of its set; a call's leftovers must never leak into the next."""
-    ws = [synth.make_config(cfg, seed=s, batch=batch, gamma=gamma) for s in (61, 62)]
+    the drawn row together, the wave of unit 0 finishing it) over 100 calls in a row,
+    alternating two input sets: its workspace is kept between calls (records and unit sums
+    tagged by call), so every call must give the first (oracle-checked) outputs of its set;
+    a call's leftovers must never leak into the next. Rows of at most 4096 entries take one
+    workgroup per sequence (k_verify_tiny, any batch size); 4104 entries is the shortest
+    row of the chunked kernel."""
+    ws = [synth.make_config(cfg, seed=s, batch=batch, gamma=gamma, vocab=vocab) for s in (61, 62)]
     w0 = ws[0]
     v = verifier(lib, w0.V, w0.dtype, w0.B, max(w0.draft_rows, 1))
     v.set_path(lib.SV_PATH_POOLED)
     devs = [to_device(w) for w in ws]
     _say("pooled draw x100", f"{cfg} B={w0.B} V={w0.V} gamma={w0.uniform_gamma}")
     first = []
+    want = "k_verify_tiny" if w0.V <= 4096 else "k_verify_group"
     for w, d in zip(ws, devs):
+        v.set_timing(1)
         gpu = run_gpu(v, w, dev=d, want_p_draft=False)
+        times, _ = v.kernel_times()
+        v.set_timing(0)
         assert gpu["status"] == lib.SV_OK, v.last_error()
         assert v.last_path() == lib.SV_PATH_POOLED
+        assert [n for n, _ in times] == [want], times
         rep = compare(w, gpu, oracle_batch(w))
         _say("pooled draw x100", "first call", rep.summary())
         assert rep.ok(), rep.summary()
