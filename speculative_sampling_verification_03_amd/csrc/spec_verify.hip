@@ -1684,8 +1684,7 @@ __global__ __launch_bounds__(kSeqThreads) void k_vs_decide(Args a, VShard vs) {
       a.rsum[b] = 0.f;
     }
   } else {
-    exp_table_init(s_tab);
-    __syncthreads();
+    __syncthreads();  // s_n (the table is built after the accept tests, which do not use it)
     for (int i = threadIdx.x; i < g; i += kSeqThreads) {
       const int d = base + i;
       const int x = a.ids[d];
@@ -1705,7 +1704,8 @@ __global__ __launch_bounds__(kSeqThreads) void k_vs_decide(Args a, VShard vs) {
       if (a.pdraft) a.pdraft[d] = static_cast<float>(px);
       if (!acc) atomicMin(&s_n, i);
     }
-    __syncthreads();
+    exp_table_init(s_tab);
+    __syncthreads();  // s_n, s_cz, s_tab
     const int n = s_n;
     for (int i = threadIdx.x; i < n; i += kSeqThreads) a.emitted[base + b + i] = a.ids[base + i];
     if (threadIdx.x == 0) a.acc[b] = n;
@@ -1768,30 +1768,38 @@ __global__ __launch_bounds__(kSeqThreads) void k_vs_finish(Args a, VShard vs) {
   int base, g;
   if (!seq_geom<RAGGED>(a, b, base, g)) return;  // flagged by k_vs_decide
   const double* loc = vs.loc + static_cast<size_t>(b) * kLocStride;
-  exp_table_init(s_tab);
-  const float uf = a.u[base + b + g];
-  const double cr = loc[0], Zq = loc[1];
-  const int n = static_cast<int>(loc[2]);
-  __syncthreads();  // s_tab
-  if (n < 0) return;
-  const bool residual = n < g;
-  const double KN = kExpScale * a.k2d;
+  // every operand of the selection, loaded at once ahead of the table: the shards'
+  // totals (lane k: shard k), this shard's region sums (lane w: region w), cr, Zq, n, u
+  double v0 = 0.0, v1 = 0.0, v2 = 0.0, g0 = 0.0, g1 = 0.0, g2 = 0.0;
   if (wave == 0) {
-    const bool live = lane < vs.G;
-    double v0 = 0.0, v1 = 0.0, v2 = 0.0;
-    if (live) {
+    if (lane < vs.G) {
       const double* p = vs.part_all + (static_cast<size_t>(lane) * a.B + b) * 3;
       v0 = p[0];
       v1 = p[1];
       v2 = p[2];
     }
+    if (lane < kSeqWaves) {
+      const double* lr = loc + 4 + 3 * lane;
+      g0 = lr[0];
+      g1 = lr[1];
+      g2 = lr[2];
+    }
+  }
+  const float uf = a.u[base + b + g];
+  const double cr = loc[0], Zq = loc[1];
+  const int n = static_cast<int>(loc[2]);
+  exp_table_init(s_tab);
+  __syncthreads();  // s_tab
+  if (n < 0) return;
+  const bool residual = n < g;
+  const double KN = kExpScale * a.k2d;
+  if (wave == 0) {
     // shards as regions: the one whose columns the prefix crosses t in
     DrawSel d = draw_select(a, residual, false, false, -1, 0.f, vs.G, 1, v0, v1, v2, cr, Zq, uf, s_tab);
     int own = d.rs < 0 ? (vs.me == vs.G - 1 ? 2 : 0) : d.rs == vs.me ? 1 : 0;
     if (own == 1) {  // this shard's regions, from the prefix before the shard
       const bool l2 = lane < kSeqWaves;
-      const double* lr = loc + 4 + 3 * (l2 ? lane : 0);
-      const double w = l2 ? region_weight(d.kind, lr[0], lr[1], lr[2], d.Z64, d.delta, d.ref, KN, s_tab) : 0.0;
+      const double w = l2 ? region_weight(d.kind, g0, g1, g2, d.Z64, d.delta, d.ref, KN, s_tab) : 0.0;
       double P;
       int tl;
       d.rs = find_crossing(w, l2, d.t, d.P, d.take_last != 0, P, tl);
