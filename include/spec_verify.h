@@ -232,8 +232,9 @@ int spec_verify_run_onehot(spec_verify_ctx *ctx, void *hip_stream, int batch, in
  * together, the wave of the first unit completing the draw. Rows of at most 4096
  * entries instead take one workgroup per sequence (any B), whose waves hand over through
  * LDS. The plan reads every draft row (as the two-launch plan does) and gives the same
- * outputs as the other plans. Under SV_PATH_AUTO it is taken when it applies and B is
- * below the compute-unit count, or V <= 4096.
+ * outputs as the other plans. Under SV_PATH_AUTO it is taken when it applies and either
+ * V <= 4096, or B is below the compute-unit count with fp32 logits (bf16 logits whose
+ * values the draw's table covers take the two-launch plan, which measured faster there).
  * All plans return the same outputs, except that a draft id after the first rejection
  * is not examined by the one-launch plan (so it cannot raise SV_DATA_DRAFT_ID there).
  *   spec_verify_set_path(ctx, mode): SV_PATH_AUTO (default), SV_PATH_TWO_LAUNCH,

@@ -3657,8 +3657,12 @@ int run_impl(spec_verify_ctx* ctx, void* hip_stream, int batch, int gamma, const
   int ggrid = 0;
   bool tiny = false;
   const bool grp_ok = !greedy && !rg && aligned && group_grid(ctx, ga, ggrid, &tiny);
+  // AUTO: short rows, or fewer sequences than compute units with fp32 logits (bf16 rows
+  // drawn through the value table measured faster in two launches: C3 rows at B = 32 and
+  // 64, 26.5 and 32.7 us against 29.5 and 34.2 us)
+  const bool table = ctx->dtype == SV_BF16 && a.tlo <= a.thi;
   const bool pooled = grp_ok && (ctx->path_mode == SV_PATH_POOLED ||
-                                 (ctx->path_mode == SV_PATH_AUTO && (tiny || batch < ctx->cus)));
+                                 (ctx->path_mode == SV_PATH_AUTO && (tiny || (batch < ctx->cus && !table))));
   const bool fused = !pooled && ctx->path_mode != SV_PATH_TWO_LAUNCH && ctx->path_mode != SV_PATH_POOLED && aligned &&
                      gmax <= kFuseMaxGamma && (ctx->path_mode == SV_PATH_ONE_LAUNCH || batch >= ctx->cus);
   hipError_t e;

@@ -711,11 +711,12 @@ def test_greedy_helpers_repeated_calls(lib):
     v.close()
 
 
-@pytest.mark.parametrize("plan", ["SV_PATH_AUTO", "SV_PATH_TWO_LAUNCH"])
+@pytest.mark.parametrize("plan", ["SV_PATH_AUTO", "SV_PATH_POOLED"])
 def test_side_stream_and_timing(lib, plan):
-    """Calls on a side stream, timed per kernel: 32 sequences (fewer than compute units)
-    take the small-batch pooled launch by default; the two-launch plan splits the draw
-    when there are at most half as many sequences as compute units."""
+    """Calls on a side stream, timed per kernel: 32 sequences of bf16 rows (fewer than
+    compute units, values inside the draw's table) take two launches by default, the draw
+    split since there are at most half as many sequences as compute units; asked for, the
+    small-batch plan runs in one launch."""
     w = synth.make_config("C3", seed=16, batch=32)
     v = verifier(lib, w.V, w.dtype, w.B, w.draft_rows)
     v.set_path(getattr(lib, plan))
@@ -733,10 +734,11 @@ def test_side_stream_and_timing(lib, plan):
     s.synchronize()
     assert runs == 3
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    if plan == "SV_PATH_AUTO":
+    if plan == "SV_PATH_POOLED":
         assert v.last_path() == lib.SV_PATH_POOLED
         assert [n for n, _ in times] == ["k_verify_group"]
     else:
+        assert v.last_path() == lib.SV_PATH_TWO_LAUNCH
         split = w.B * 2 <= cus
         assert [n for n, _ in times] == (["k_rowstats", "k_draw_part"] if split else ["k_rowstats", "k_sample_seq"])
     assert all(t > 0 for _, t in times)
