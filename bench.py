@@ -679,7 +679,7 @@ def main():
     next_rows = {}
     if not args.no_next and w0.T > 0:
         cfgs = {}
-        for cname, n, stride in (("C1", 2000, 1), ("C2", 400, 4), ("C4", 100, 4), ("C5", 60, 2)):
+        for cname, n, stride in (("C1", 2000, 8), ("C2", 400, 4), ("C4", 100, 4), ("C5", 60, 2)):
             if cname != args.config:
                 cfgs[cname] = bench_config(sv, torch, dev, cname, n, 20, stride)
                 torch.cuda.empty_cache()
