@@ -2024,10 +2024,13 @@ __global__ __launch_bounds__(kOrderThreads) void k_order_by_gamma(Args a) {
 // memory, each 64-bit word at once. A reader takes a value only from a word that carries
 // this call's tag, and every word of a value carries it, so it never mixes words of two
 // calls and needs no other signal; no word is reset between calls (an older call's words
-// carry an older tag; the tag is a 32-bit count of the context's calls). Every wait is
-// bounded; one that runs out raises SV_DATA_STALL (that call's outputs are then not
-// valid). The host sizes the grid so that every workgroup is resident at once, and a wait
-// then lasts only until the other workgroups of the group have stored their part.
+// carry an older tag; the tag is a 32-bit count of the context's launches of this plan).
+// Every wait is bounded; one that runs out raises SV_DATA_STALL (that call's outputs are
+// then not valid). The host sizes the grid so that every workgroup is resident at once,
+// and a wait then lasts only until the other workgroups of the group have stored their
+// part. With fewer resident (other work on the device) the groups still finish: a group's
+// workgroups are contiguous in dispatch order, so the earliest unfinished group has all
+// of its workgroups dispatched, and it never waits on a later one.
 #ifndef SV_GRP_THREADS
 #define SV_GRP_THREADS 256
 #endif
@@ -2045,8 +2048,6 @@ __device__ __forceinline__ void store_sys(unsigned long long* p, unsigned long l
 __device__ __forceinline__ unsigned long long load_sys(const unsigned long long* p) {
   return __hip_atomic_load(const_cast<unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
-// The stores this wave issued are acknowledged before its next memory instruction.
-__device__ __forceinline__ void stores_complete() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ unsigned long long rec_word(float v, unsigned tag) {
   return (static_cast<unsigned long long>(__float_as_uint(v)) << 32) | tag;
 }

@@ -333,6 +333,18 @@ def test_large_gamma(lib):
     check_parity(lib, w, "gamma=40", max_gamma=64)
 
 
+@pytest.mark.parametrize("B,gamma,V,dtype", [(2, 64, 8192, "f32"), (3, 64, 4096, "bf16"), (1, 1, 40960, "bf16"),
+                                            (300, 1, 8192, "f32"), (5, 7, 4104, "f32")])
+def test_small_batch_plan_shapes(lib, B, gamma, V, dtype):
+    """The small-batch plan at the corners of its geometry, under every plan: 64 draft
+    rows of one sequence (64 records, 64 units), the short-row kernel with 64 rows per
+    workgroup, a single draft row split 16 ways, more sequences than compute units, and
+    a row length just past the short-row limit whose units end mid-iteration."""
+    w = synth.make_sampling(f"small-batch B={B} g={gamma} V={V}", np.full(B, gamma), V, dtype, 0.9, 2.5, 0.6,
+                            seed=77 + B + gamma)
+    check_parity(lib, w, f"small-batch shapes B={B} gamma={gamma} V={V} {dtype}", max_gamma=64)
+
+
 def test_empty_batch(lib):
     v = verifier(lib, 100, "f32", 4, 16)
     e = torch.empty(0, device="cuda")
