@@ -4311,11 +4311,13 @@ int spec_verify_set_timing(spec_verify_ctx* ctx, int runs) {
   if (!ctx->ev) return SV_ENOMEM;
   ctx->timing_cap = runs;
   ctx->timing_seen = 0;
+  // The events only carry timestamps, read after the stream has finished: recording them
+  // needs no system-scope release (an L2 write-back between the kernels they bracket).
   for (size_t i = 0; i < n; ++i) {
-    const hipError_t e = hipEventCreate(&ctx->ev[i]);
+    const hipError_t e = hipEventCreateWithFlags(&ctx->ev[i], hipEventDisableSystemFence);
     if (e != hipSuccess) {
       free_events(ctx);
-      return hip_fail(ctx, "hipEventCreate", e);
+      return hip_fail(ctx, "hipEventCreateWithFlags", e);
     }
   }
   ctx->timing_runs = 0;
