@@ -78,12 +78,20 @@ def test_counter_traffic_needs_matching_sources(tmp_path, monkeypatch):
 
 
 def test_rotated_inputs_exceed_the_last_level_cache():
-    """Each workload rotates enough input sets to hold over 1 GiB (four times the 256 MB
-    last-level cache): C2's 90 MB sets need at least 8 of them."""
+    """Each workload rotates enough input sets that, between two uses of one set, the
+    other sets' calls read over 1 GiB (four times the 256 MB last-level cache), by the
+    most bytes a call can read: C3 needs 4 sets, C2's 57 MB calls 20."""
+    import numpy as np
     import synth
     for cfg in ("C1", "C2", "C3", "C4", "C5"):
+        w = synth.make_config(cfg, seed=0)
         n = bench.auto_sets(cfg)
-        per = bench.input_bytes(synth.make_config(cfg, seed=0))
-        assert n * per >= bench.SET_BYTES_TARGET or n == bench.MAX_SETS, cfg
-        assert n >= 2 or per >= bench.SET_BYTES_TARGET, cfg
-    assert bench.auto_sets("C2") >= 8
+        per = bench.max_call_bytes(w)
+        assert (n - 1) * per >= bench.SET_BYTES_TARGET or n == bench.MAX_SETS, cfg
+        assert n >= 2, cfg
+        # the bound is the larger of the two extreme acceptances
+        g = w.gammas.astype(np.int64)
+        for acc in (np.zeros_like(g), g, g // 2):
+            assert bench.method_bytes(w, acc) <= per, (cfg, acc[:4])
+    assert bench.auto_sets("C3") == 4
+    assert bench.auto_sets("C2") == 20
