@@ -215,7 +215,9 @@ int spec_verify_run_onehot(spec_verify_ctx *ctx, void *hip_stream, int batch, in
  * the first mismatching row, or of the bonus row, is the token). The one-launch plan
  * needs V a multiple of 8, 16-byte aligned logits (and q when T > 0), gamma_b <= 64
  * (for ragged runs: the context's max_gamma <= 64) and, under SV_PATH_AUTO, at least
- * as many sequences as the device has compute units. With p_draft requested (T > 0)
+ * 0.55 times as many sequences as the device has compute units (greedy: 0.8 times;
+ * below that the two launches, which spread the rows over every compute unit, measured
+ * faster on MI355X). With p_draft requested (T > 0)
  * it still reads every row. A ragged run with more sequences than compute units
  * first launches a one-workgroup kernel that orders the sequences by gamma_b,
  * longest first (the workspace holds the order); workgroups then take the sequences

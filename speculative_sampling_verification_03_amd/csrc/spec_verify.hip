@@ -12,10 +12,11 @@
 //        변하지 않는다는 것이 핵심이다" (greedy reduces to argmax equality).
 //
 // Launch plans (all on the caller's stream, no host sync):
-//   * one launch (k_verify_seq; greedy: k_greedy_seq1), B >= compute units: one
-//     1024-thread workgroup per sequence judges its draft rows left to right in one
-//     read each (base-2 online max and sum in fp32, the accept test in fp64), stops at
-//     the first rejection and draws from the one row it needs. A ragged batch first
+//   * one launch (k_verify_seq; greedy: k_greedy_seq1), B >= 0.55 (greedy: 0.8) times
+//     the compute units: one 1024-thread workgroup per sequence judges its draft rows
+//     left to right in one read each (base-2 online max and sum in fp32, the accept
+//     test in fp64), stops at the first rejection and draws from the one row it
+//     needs. A ragged batch first
 //     orders its sequences longest first (k_order_by_gamma). Greedy batches of up to
 //     four times the compute units add helper workgroups (k_greedy_help).
 //   * two launches, smaller batches: k_rowstats / k_rowargmax, grid = (draft rows) x
@@ -2427,10 +2428,10 @@ __global__ __launch_bounds__(kGrpThreads) void k_verify_tiny(Args a) {
   }
 }
 
-// NT1: the judged rows are read with nontemporal loads. Measured on MI355X this helps
-// when every sequence has its own compute unit (B <= CUs: C3, 4.6% faster) and costs
-// when workgroups run in several rounds (C5, 1.6% slower), so the host picks it by B.
-template <typename T, bool RAGGED, bool NT1>
+// The judged rows are read with ordinary loads: nontemporal ones measured slower on
+// MI355X with inputs rotated past the last-level cache (B = 256, gamma = 4, V = 128256
+// bf16: 70.1 against 69.5 us; B = 160: 59.4 against 59.1 us).
+template <typename T, bool RAGGED>
 __global__ __launch_bounds__(kSeqThreads) void k_verify_seq(Args a) {
   __shared__ double s_tab[kExpN];
   __shared__ float2 s_cz[kFuseMaxGamma];
@@ -2453,8 +2454,8 @@ __global__ __launch_bounds__(kSeqThreads) void k_verify_seq(Args a) {
       if (tab) tab_build(sT, a);
     };
     const int n = g == 0 ? 0
-                  : a.V >= kSeqWaves * kIter ? judge_rows_exact<T, true, NT1>(a, b, base, g, s_cz, &s_xn, hook)
-                                             : judge_rows_exact<T, false, NT1>(a, b, base, g, s_cz, &s_xn, hook);
+                  : a.V >= kSeqWaves * kIter ? judge_rows_exact<T, true, false>(a, b, base, g, s_cz, &s_xn, hook)
+                                             : judge_rows_exact<T, false, false>(a, b, base, g, s_cz, &s_xn, hook);
     if (g == 0) {
       if (tab) tab_build(sT, a);
       if (threadIdx.x == 0) a.acc[b] = 0;
@@ -2473,8 +2474,8 @@ __global__ __launch_bounds__(kSeqThreads) void k_verify_seq(Args a) {
   } else {
     exp_table_init(s_tab);
     const int n = g == 0 ? 0
-                  : a.V >= kSeqWaves * kIter ? judge_rows_exact<T, true, NT1>(a, b, base, g, s_cz, &s_xn, [] {})
-                                             : judge_rows_exact<T, false, NT1>(a, b, base, g, s_cz, &s_xn, [] {});
+                  : a.V >= kSeqWaves * kIter ? judge_rows_exact<T, true, false>(a, b, base, g, s_cz, &s_xn, [] {})
+                                             : judge_rows_exact<T, false, false>(a, b, base, g, s_cz, &s_xn, [] {});
     if (g == 0 && threadIdx.x == 0) a.acc[b] = 0;
     __syncthreads();  // s_cz of row n, s_tab
     final_draw<T, true>(a, b, base, g, n, n < g ? static_cast<double>(s_cz[n].x) : 0.0,
@@ -3332,8 +3333,7 @@ hipError_t launch_fused(spec_verify_ctx* ctx, const Args& a, hipStream_t st) {
                                     dim3(kOrderThreads), ao, st, ev, k++);
     if (e != hipSuccess) return e;
   }
-  const void* fn = a.B <= ctx->cus ? reinterpret_cast<const void*>(&k_verify_seq<T, RG, true>)
-                                   : reinterpret_cast<const void*>(&k_verify_seq<T, RG, false>);
+  const void* fn = reinterpret_cast<const void*>(&k_verify_seq<T, RG>);
   const hipError_t e = launch_one(fn, dim3(a.B), dim3(kSeqThreads), ao, st, ev, k);
   if (e != hipSuccess) return e;
   if (ev) ++ctx->timing_runs;
@@ -3375,7 +3375,9 @@ hipError_t launch_fused_greedy(spec_verify_ctx* ctx, const Args& a, hipStream_t 
                                     dim3(kOrderThreads), ao, st, ev, k++);
     if (e != hipSuccess) return e;
   }
-  // nontemporal row loads when every sequence has its own compute unit, as for sampling
+  // nontemporal row loads when every sequence has its own compute unit (measured with
+  // inputs rotated past the last-level cache, gamma = 8, V = 152064 bf16: B = 255, 103.4
+  // against 106.0 us with ordinary loads; B = 224, 101.5 against 103.5 us)
   const void* fn = a.B <= ctx->cus ? reinterpret_cast<const void*>(&k_greedy_seq1<T, RG, true>)
                                    : reinterpret_cast<const void*>(&k_greedy_seq1<T, RG, false>);
   const hipError_t e = launch_one(fn, dim3(a.B), dim3(kSeqThreads), ao, st, ev, k);
@@ -3649,7 +3651,6 @@ int run_impl(spec_verify_ctx* ctx, void* hip_stream, int batch, int gamma, const
   }
   DeviceGuard guard(ctx->device);
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
-  // one launch per call when there are enough sequences to give every compute unit one
   const int gmax = cu_gamma ? ctx->max_gamma : gamma;
   const bool rg = cu_gamma != nullptr;
   // small batches of sampling rows, uniform gamma: one launch with the rows read in
@@ -3664,8 +3665,15 @@ int run_impl(spec_verify_ctx* ctx, void* hip_stream, int batch, int gamma, const
   const bool table = ctx->dtype == SV_BF16 && a.tlo <= a.thi;
   const bool pooled = grp_ok && (ctx->path_mode == SV_PATH_POOLED ||
                                  (ctx->path_mode == SV_PATH_AUTO && (tiny || (batch < ctx->cus && !table))));
+  // AUTO takes one launch from a fraction of the compute-unit count on: below it the two
+  // launches spread the rows over every compute unit and finish first, above it one
+  // workgroup per sequence does. Measured on MI355X with inputs rotated past the
+  // last-level cache (us per call, one / two launches): sampling, gamma = 4, V = 128256
+  // bf16: B = 128 57.7 / 51.3, B = 144 58.8 / 59.8, B = 192 62.4 / 68.7; greedy,
+  // gamma = 8, V = 152064 bf16: B = 192 100.7 / 95.8, B = 208 101.4 / 103.2.
+  const int one_min = greedy ? (4 * ctx->cus + 4) / 5 : (11 * ctx->cus + 19) / 20;
   const bool fused = !pooled && ctx->path_mode != SV_PATH_TWO_LAUNCH && ctx->path_mode != SV_PATH_POOLED && aligned &&
-                     gmax <= kFuseMaxGamma && (ctx->path_mode == SV_PATH_ONE_LAUNCH || batch >= ctx->cus);
+                     gmax <= kFuseMaxGamma && (ctx->path_mode == SV_PATH_ONE_LAUNCH || batch >= one_min);
   hipError_t e;
   if (pooled)
     e = ctx->dtype == SV_BF16 ? launch_group<uint16_t>(ctx, ga, st, ggrid, tiny)
