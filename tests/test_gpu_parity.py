@@ -474,6 +474,41 @@ def test_ordered_one_launch_ragged(lib, dtype, T):
     assert rep.ok(), rep.summary()
 
 
+@pytest.mark.parametrize("dtype,ragged", [("bf16", False), ("f32", True), ("bf16", True)])
+def test_one_launch_more_sequences_than_cus_repeated_calls(lib, dtype, ragged):
+    """More sequences than compute units in one launch (workgroups in several rounds; a
+    ragged batch ordered first): 40 calls in a row on two input sets of different batch
+    sizes must each give the first call's (oracle-checked) outputs for that set."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    ws = []
+    for k, B in enumerate((2 * cus + 37, cus + 5)):
+        rng = np.random.default_rng([71, k])
+        gammas = rng.integers(0, 9, B) if ragged else np.full(B, 4)
+        ws.append(synth.make_sampling("more than CUs", gammas, 3000, dtype, 1.0, 2.0, 1.0, seed=72 + k))
+    devs = [to_device(w) for w in ws]
+    v = verifier(lib, ws[0].V, dtype, max(w.B for w in ws), max(w.draft_rows for w in ws))
+    v.set_path(lib.SV_PATH_ONE_LAUNCH)
+    first = []
+    for w, d in zip(ws, devs):
+        _say("one launch, B > CUs", dtype, f"ragged={ragged} B={w.B}")
+        v.set_timing(1)
+        gpu = run_gpu(v, w, dev=d, ragged=ragged, want_p_draft=False)
+        times, _ = v.kernel_times()
+        v.set_timing(0)
+        assert gpu["status"] == lib.SV_OK, v.last_error()
+        assert [n for n, _ in times][-1] == "k_verify_seq", times
+        rep = compare(w, gpu, oracle_batch(w))
+        assert rep.ok(), rep.summary()
+        first.append(gpu)
+    for k in range(40):
+        i = k % 2
+        gpu = run_gpu(v, ws[i], dev=devs[i], ragged=ragged, want_p_draft=False)
+        for key in ("accepted_count", "emitted_tokens", "residual_sum"):
+            assert np.array_equal(gpu[key], first[i][key]), (k, key)
+    assert v.status() == lib.SV_OK, v.last_error()
+    v.set_path(lib.SV_PATH_AUTO)
+
+
 def test_ordered_one_launch_many_sequences(lib):
     """More sequences than the ordering kernel keeps in registers (8 per thread of 1024):
     its loop over the rest; V = 96 keeps the oracle quick."""
