@@ -121,3 +121,21 @@ def test_create_rejects_bad_arguments_before_touching_a_device():
     assert lib.spec_verify_create(ctypes.byref(out), 0, 10, 5, 1, 1, 1) == sv.SV_EINVAL
     assert lib.spec_verify_create(ctypes.byref(out), 0, 10, sv.SV_F32, 1, 1, 2000) == sv.SV_EINVAL
     assert lib.spec_verify_create(ctypes.byref(out), 0, (1 << 24) + 1, sv.SV_F32, 1, 1, 1) == sv.SV_EINVAL
+
+
+def test_build_refuses_scratch_kernels():
+    """The build reads the compiler's per-kernel resource remarks and names every kernel
+    that reports scratch (such kernels ran markedly slower on MI355X)."""
+    from speculative_sampling_verification_03_amd import build as B
+    remarks = "\n".join([
+        "a.hip:2:1: remark: Function Name: k_one [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:2:1: remark:     VGPRs: 116 [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:2:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:9:1: remark: Function Name: k_two [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:9:1: remark:     ScratchSize [bytes/lane]: 48 [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:20:1: remark: Function Name: k_three [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:20:1: remark:     ScratchSize [bytes/lane]: 8 [-Rpass-analysis=kernel-resource-usage]",
+    ])
+    assert B.scratch_kernels(remarks) == [("k_two", 48), ("k_three", 8)]
+    assert B.scratch_kernels("") == []
+    assert B.RESOURCE_REMARKS == "-Rpass-analysis=kernel-resource-usage"
