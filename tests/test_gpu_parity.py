@@ -855,3 +855,28 @@ def test_gpu_chi_square_million_sequences(lib):
         reach = int(np.sum(n >= i))
         acc = int(np.sum(n > i))
         assert stats.binomtest(acc, reach, a).pvalue * g > 1e-4
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_auto_plan_random_shapes(lib, seed):
+    """Seeded random shapes around AUTO's switch points (0.55 and 0.8 times the compute
+    units, the compute-unit count, the small-batch plan's limits): B up to 1.6x the CUs,
+    gamma 0..8 uniform or ragged, V a multiple of 8 or not, bf16 or fp32, sampling or
+    greedy; AUTO's choice and, with p(x) requested, every plan match the oracle."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    rng = np.random.default_rng([90, seed])
+    B = int(rng.choice([int(0.55 * cus) + rng.integers(-4, 5), int(0.8 * cus) + rng.integers(-4, 5),
+                        cus + rng.integers(-3, 4), rng.integers(1, 40), rng.integers(int(1.2 * cus), int(1.6 * cus))]))
+    B = max(B, 1)
+    ragged = bool(rng.integers(0, 2))
+    gammas = rng.integers(0, 9, B) if ragged else np.full(B, int(rng.integers(1, 9)))
+    V = int(rng.choice([8 * int(rng.integers(1, 160)), int(rng.integers(2, 1300))]))
+    dtype = str(rng.choice(["bf16", "f32"]))
+    greedy = rng.random() < 0.3
+    if greedy:
+        w = synth.make_greedy("auto random", gammas, V, dtype, 3.0, 0.8, seed=91 + seed)
+    else:
+        T = float(rng.choice([1.0, 0.7, 1.6]))
+        w = synth.make_sampling("auto random", gammas, V, dtype, T, 2.0, 1.0, seed=91 + seed)
+    plans = (("auto", "SV_PATH_AUTO", False), ("auto, p(x)", "SV_PATH_AUTO", not greedy)) + PLANS
+    check_parity(lib, w, f"auto random {seed}", ragged=ragged, plans=plans)
