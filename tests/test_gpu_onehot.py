@@ -73,6 +73,7 @@ def check_onehot(sv, w, label, ragged=None, expect=None):
     ("C3", 1.0, 3.0, 0.8, 64),
     ("C3", 0.5, 4.0, 0.9, 64),
     ("C2", 0.8, 3.0, 0.7, 64),
+    ("C1", 1.0, 2.0, 0.6, 64),   # short rows (the short-row kernel), no q rows
 ])
 def test_onehot_parity(lib, cfg, T, sigma, agree, batch):
     c = synth.CONFIGS[cfg]
