@@ -187,3 +187,29 @@ def test_parity_at_1e5_sequences(lib, cfg, base_batch, per_call):
     assert total >= 10 ** 5
     assert not unflagged, unflagged[:5]
     assert flagged <= math.floor(FLAGGED_RATE_MAX * total)
+
+
+@pytest.mark.parametrize("dtype,ragged,plan", [("bf16", False, "SV_PATH_ONE_LAUNCH"),
+                                               ("bf16", True, "SV_PATH_TWO_LAUNCH"),
+                                               ("f32", False, "SV_PATH_ONE_LAUNCH"),
+                                               ("f32", True, "SV_PATH_AUTO")])
+def test_parity_distinct_rows(lib, dtype, ragged, plan):
+    """The replicated-batch tests above reuse a few hundred target rows; here every one of
+    4096 sequences has rows of its own (about 20000 distinct target rows per case, V = 8192,
+    gamma 4 or ragged 1..8), verified in one call and compared with the oracle sequence by
+    sequence under the flag rule."""
+    from _parity import oracle_batch, run_gpu, to_device
+    B, V = 4096, 8192
+    rng = np.random.default_rng([35, int(ragged), len(dtype)])
+    gammas = rng.integers(1, 9, B) if ragged else np.full(B, 4)
+    w = synth.make_sampling("distinct rows", gammas, V, dtype, 1.0, 2.5, 0.8, seed=36 + int(ragged))
+    _say("distinct rows", dtype, f"ragged={ragged} B={B} V={V} rows={w.draft_rows + B} plan={plan}")
+    code = lib.SV_BF16 if dtype == "bf16" else lib.SV_F32
+    v = lib.Verifier(V, code, B, w.draft_rows, 16)
+    v.set_path(getattr(lib, plan))
+    gpu = run_gpu(v, w, dev=to_device(w), ragged=ragged, want_p_draft=True)
+    assert gpu["status"] == lib.SV_OK, v.last_error()
+    rep = compare(w, gpu, oracle_batch(w))
+    _say("distinct rows", rep.summary())
+    v.close()
+    assert rep.ok(), rep.summary()
