@@ -880,3 +880,14 @@ def test_auto_plan_random_shapes(lib, seed):
         w = synth.make_sampling("auto random", gammas, V, dtype, T, 2.0, 1.0, seed=91 + seed)
     plans = (("auto", "SV_PATH_AUTO", False), ("auto, p(x)", "SV_PATH_AUTO", not greedy)) + PLANS
     check_parity(lib, w, f"auto random {seed}", ragged=ragged, plans=plans)
+
+
+@pytest.mark.parametrize("V,dtype,B", [(262144, "bf16", 6), (262152, "f32", 5), (300000, "bf16", 300),
+                                       (152064, "bf16", 3)])
+def test_large_vocabularies(lib, V, dtype, B):
+    """Vocabularies past the headline's 128256: 2^18 entries, one group past it, a
+    300000-entry row with more sequences than compute units, and C4's 152064 in sampling
+    mode; every plan against the oracle."""
+    gammas = np.random.default_rng([95, V % 1000]).integers(1, 6, B)
+    w = synth.make_sampling(f"large V={V}", gammas, V, dtype, 1.0, 3.0, 0.8, seed=96 + B)
+    check_parity(lib, w, f"large vocabulary V={V} {dtype} B={B}", ragged=True)
