@@ -164,7 +164,13 @@ int spec_verify_run(spec_verify_ctx *ctx, void *hip_stream, int batch, int gamma
  *   data_flags    device int32 [1], caller-owned: the data-error bits (SV_DATA_*) found
  *                 by the kernels are OR-ed into it, never cleared (start it at 0).
  * The kernels and outputs are those of spec_verify_run under SV_PATH_AUTO, except that a
- * greedy batch never takes the helper plan (it runs one workgroup per sequence instead).
+ * greedy batch never takes the helper plan (it runs one workgroup per sequence instead)
+ * and a sampling batch never takes the small-batch plan's several workgroups per
+ * sequence (short rows keep their one workgroup per sequence): both hand data between
+ * workgroups under a per-call number kept on the host, and such a batch takes the
+ * other plans. Nothing the kernels leave in the workspace is told apart by a host-side
+ * number (its counters return to zero within each call), so calls captured into a HIP
+ * graph can be replayed, also with new contents in the captured buffers.
  * Every call on one GPU shares that GPU's workspace, which keeps the last call's contents:
  * calls that overlap on one GPU (two streams, two threads) race and give undefined
  * results; calls in stream order are safe.

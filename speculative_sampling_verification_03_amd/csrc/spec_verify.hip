@@ -3235,6 +3235,7 @@ struct spec_verify_ctx {
   RowStat* p1 = nullptr;
   size_t p1_cap = 0;         // entries of p1
   bool no_helpers = false;   // greedy runs never take the helper plan (its counters carry host epochs)
+  bool no_tagged = false;    // nor the small-batch plan's workgroups, whose records carry a host call tag
   int32_t* accept = nullptr;
   float2* lxq = nullptr;     // split rows: the draft's logit and q entry
   int32_t* s_acc = nullptr;  // sampling: accepted counts (all 0) of the verify launch
@@ -3658,7 +3659,7 @@ int run_impl(spec_verify_ctx* ctx, void* hip_stream, int batch, int gamma, const
   Args ga = a;
   int ggrid = 0;
   bool tiny = false;
-  const bool grp_ok = !greedy && !rg && aligned && group_grid(ctx, ga, ggrid, &tiny);
+  const bool grp_ok = !greedy && !rg && aligned && group_grid(ctx, ga, ggrid, &tiny) && (tiny || !ctx->no_tagged);
   // AUTO: short rows, or fewer sequences than compute units with fp32 logits (bf16 rows
   // drawn through the value table measured faster in two launches: C3 rows at B = 32 and
   // 64, 26.5 and 32.7 us against 29.5 and 34.2 us)
@@ -3868,7 +3869,6 @@ struct StaticDevice {
   char* ptr = nullptr;  // this device's copy of `scratch`
   int cus = 0;
   int grp_slots[2] = {0, 0};  // workgroups of k_verify_group resident at once: fp32, bf16 logits
-  unsigned ptag = 0;          // the small-batch plan's call tag, advanced by every call
 };
 StaticDevice g_static[kStaticMaxDevices];
 std::mutex g_static_mu;
@@ -3900,8 +3900,6 @@ int static_device(int device, hipStream_t st, StaticDevice& out) {
     d.cus = cus;
     d.ptr = static_cast<char*>(p);
   }
-  d.ptag += 2;  // launch_group takes the next one
-  if (d.ptag == 0) d.ptag = 2;
   out = d;
   return SV_OK;
 }
@@ -4036,8 +4034,8 @@ int spec_verify_run_static(int device, void* hip_stream, int vocab, int logits_d
   c.max_gamma = SV_STATIC_MAX_GAMMA;
   c.cus = dv.cus;
   c.no_helpers = true;
+  c.no_tagged = true;
   c.grp_slots = dv.grp_slots[logits_dtype == SV_BF16 ? 1 : 0];
-  c.ptag = dv.ptag;
   ws_assign(&c, kStaticLayout, dv.ptr);
   c.err = data_flags;
   const int rc = run_impl(&c, hip_stream, batch, gamma, cu_gamma, total_draft_rows, temperature, logits, q, false,
