@@ -245,6 +245,9 @@ int spec_verify_run_onehot(spec_verify_ctx *ctx, void *hip_stream, int batch, in
  * values the draw's table covers take the two-launch plan, which measured faster there).
  * All plans return the same outputs, except that a draft id after the first rejection
  * is not examined by the one-launch plan (so it cannot raise SV_DATA_DRAFT_ID there).
+ * Calls through a context are not meant to be captured into a HIP graph and replayed:
+ * the greedy helper plan and the small-batch plan number their calls on the host, and a
+ * replay would reuse the number. spec_verify_run_static takes neither and replays.
  *   spec_verify_set_path(ctx, mode): SV_PATH_AUTO (default), SV_PATH_TWO_LAUNCH,
  *     SV_PATH_ONE_LAUNCH (taken whenever the run allows it, whatever B) or
  *     SV_PATH_POOLED (taken whenever the run allows it; else the two-launch plan).
