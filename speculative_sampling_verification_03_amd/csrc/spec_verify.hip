@@ -16,9 +16,9 @@
 //     the compute units: one 1024-thread workgroup per sequence judges its draft rows
 //     left to right in one read each (base-2 online max and sum in fp32, the accept
 //     test in fp64), stops at the first rejection and draws from the one row it
-//     needs. A ragged batch first
-//     orders its sequences longest first (k_order_by_gamma). Greedy batches of up to
-//     four times the compute units add helper workgroups (k_greedy_help).
+//     needs. A ragged batch first orders its sequences longest first
+//     (k_order_by_gamma). Greedy batches of up to four times the compute units add
+//     helper workgroups (k_greedy_help).
 //   * two launches, smaller batches: k_rowstats / k_rowargmax, grid = (draft rows) x
 //     split, 256 threads, one read of every draft row, keep each split's (c, z) or
 //     (max, index); then k_sample_seq / k_greedy_seq, one workgroup per sequence, find
