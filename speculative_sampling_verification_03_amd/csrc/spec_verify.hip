@@ -161,10 +161,19 @@ __device__ __forceinline__ bool seq_geom(const Args& a, int b, int& base, int& g
   return ok;
 }
 
-// Merge (c, z) partial softmax states kept in base 2.
+// Merge (c, z) partial softmax states kept in base 2; a state stands for z 2^c. A partial
+// taken against a reference below its largest entry (a wave's first chunk, at a low
+// temperature) can hold z near the top of the fp32 range, and scaling such a z by
+// 2^(c - C) would underflow the factor and drop the partial. So each z is split as
+// m 2^e (m in [0.5, 1)) and e goes into the power of two: the merged reference is the
+// larger c + e, the merged z lies in [0.5, 2), and a term that underflows is below 2^-126
+// of the merged z. Only the differences c - C are rounded, never the references.
 __device__ __forceinline__ void lse2_merge(float& c, float& z, float c2, float z2) {
-  const float C = fmaxf(c, c2);
-  z = z * fast_exp2(c - C) + z2 * fast_exp2(c2 - C);
+  const float e1 = static_cast<float>(__builtin_amdgcn_frexp_expf(z));
+  const float e2 = static_cast<float>(__builtin_amdgcn_frexp_expf(z2));
+  const float C = fmaxf(c + e1, c2 + e2);
+  z = __builtin_amdgcn_frexp_mantf(z) * fast_exp2((c - C) + e1) +
+      __builtin_amdgcn_frexp_mantf(z2) * fast_exp2((c2 - C) + e2);
   c = C;
 }
 
@@ -1835,9 +1844,10 @@ __global__ __launch_bounds__(kSeqThreads) void k_vs_finish(Args a, VShard vs) {
 // Pass 1: per row, z = sum 2^(l k2 - c) in fp32. Each wave takes its reference c from
 // the first chunk it reads of the row (the chunk's max times k2; the row max can only be
 // larger, so no entry underflows the sum's precision) and adds plain exp2 terms after
-// that, with no running max. A wave whose sum overflows (a value more than ~100 octaves
+// that, with no running max. A wave whose sum overflows (a value 128 or more octaves
 // above that first chunk's max) or is not finite redoes its chunks of the row with the
-// running max. Returns n; s_cz[i] = (c, z) of each judged row.
+// running max; a sum that stays finite can still lie near 2^128, which the merge of the
+// waves' partials takes in its stride. Returns n; s_cz[i] = (c, z) of each judged row.
 template <typename T, bool WIDE, bool NT, typename Hook>
 __device__ __forceinline__ int judge_rows_exact(const Args& a, int b, int base, int g, float2* s_cz, int* s_xn,
                                                 Hook&& hook) {

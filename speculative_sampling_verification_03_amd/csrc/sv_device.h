@@ -53,13 +53,6 @@ __device__ __forceinline__ float load_one(const float* __restrict__ p, size_t e)
 // ---------------------------------------------------------------- math
 __device__ __forceinline__ float fast_exp2(float y) { return __builtin_amdgcn_exp2f(y); }
 
-// Merge two (max, sum exp2((x - max) * k)) partial states.
-__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2, float k2) {
-  const float M = fmaxf(m, m2);
-  s = s * fast_exp2((m - M) * k2) + s2 * fast_exp2((m2 - M) * k2);
-  m = M;
-}
-
 // 2^(Z/N) in float64 for Z in units of 1/N octave, N = 2^SV_EXP_LOG2N table entries.
 // With n = rint(Z) = N k + j (0 <= j < N) and f = Z - n (exact, |f| <= 1/2):
 // 2^(Z/N) = 2^k * 2^(j/N) * e^(f c), c = ln2/N, e^(f c) from a short Taylor

@@ -891,3 +891,43 @@ def test_large_vocabularies(lib, V, dtype, B):
     gammas = np.random.default_rng([95, V % 1000]).integers(1, 6, B)
     w = synth.make_sampling(f"large V={V}", gammas, V, dtype, 1.0, 3.0, 0.8, seed=96 + B)
     check_parity(lib, w, f"large vocabulary V={V} {dtype} B={B}", ragged=True)
+
+
+def _low_temperature_rows(dtype, case):
+    """N(0, 1) logits, V = 128256, six sequences of four drafts, with entries planted in
+    every target row; half of the drafts point at a planted 12."""
+    if case == "overlap":
+        marks, spike, octaves = [(5127, 8.0), (120164, 12.0)], 120164, 126.8
+    else:
+        marks = [(5127, 8.0), (5639, 8.0), (6151, 8.0), (46180, 12.0), (46692, 12.0), (47204, 12.0)]
+        spike, octaves = 46180, 127.4
+    T = 4.0 * math.log2(math.e) / octaves  # 12 - 8 = 4 logits is `octaves` octaves
+    w = synth.make_sampling(f"low T {case}", np.full(6, 4), 128256, dtype, T, 1.0, 0.8, seed=97)
+    for r in range(w.target_rows):
+        row = w.logits_f32(slice(r, r + 1))[0].copy()
+        for col, val in marks:
+            row[col] = val
+        w.logits[r] = synth.bf16_round(row) if dtype == "bf16" else row
+    w.draft_ids[::2] = spike
+    return w
+
+
+@pytest.mark.parametrize("case", ["overlap", "three"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_low_temperature_partials_near_fp32_top(lib, dtype, case):
+    """The one-launch plan walks a row in spans of 16 chunks of 512 entries (wave w reads
+    chunk w of each span; the last span starts at V - 8192 and gives weight 0 to what the
+    span before it covered), and each wave sums 2^(l k2 - c) against its first chunk's
+    maximum. At a low temperature a later entry 4 logits above that maximum is 126 to 128
+    octaves up: the wave's partial stays finite but lies near the top of the fp32 range.
+      * overlap: wave 10's first chunk tops at 8 and a 12 sits where the last span
+        overlaps the one before, so wave 0 meets the 12 with weight 0 and takes it as its
+        reference; wave 10's partial (about 2^126.8) must survive the scale 2^-126.8;
+      * three: waves 10, 11 and 12 each meet a 12 after a first chunk topping at 8; their
+        three partials (about 2^127.4 each) must not add up past the fp32 range.
+    Every plan against the oracle, p(x) included."""
+    w = _low_temperature_rows(dtype, case)
+    runs, ora = check_parity(lib, w, f"low temperature, {case}, {dtype}")
+    spike_rows = np.flatnonzero(w.draft_ids == w.draft_ids[0])
+    expect = 1.0 if case == "overlap" else 1.0 / 3.0
+    assert np.allclose(ora.p_draft[spike_rows], expect, rtol=1e-6), ora.p_draft[spike_rows]
