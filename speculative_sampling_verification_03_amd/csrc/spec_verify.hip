@@ -177,6 +177,26 @@ __device__ __forceinline__ void lse2_merge(float& c, float& z, float c2, float z
   c = C;
 }
 
+// The same merge over the states (c, z) of the 16 lanes of each row of the wave, by DPP
+// steps inside the row (a max of c + e, then a sum of m 2^(c - C + e)): one exp2 per lane
+// and no LDS permutes. Returns row 0's (C, Z), wave-uniform; every wave that runs it on
+// the same states gets the same bits.
+__device__ __forceinline__ void merge_row16(float c, float z, float& C, float& Z) {
+  const float e = static_cast<float>(__builtin_amdgcn_frexp_expf(z));
+  int r = __float_as_int(c + e);
+  r = __float_as_int(fmaxf(__int_as_float(r), __int_as_float(__builtin_amdgcn_update_dpp(r, r, 0xB1, 0xF, 0xF, false))));
+  r = __float_as_int(fmaxf(__int_as_float(r), __int_as_float(__builtin_amdgcn_update_dpp(r, r, 0x4E, 0xF, 0xF, false))));
+  r = __float_as_int(fmaxf(__int_as_float(r), __int_as_float(__builtin_amdgcn_update_dpp(r, r, 0x141, 0xF, 0xF, false))));
+  r = __float_as_int(fmaxf(__int_as_float(r), __int_as_float(__builtin_amdgcn_update_dpp(r, r, 0x140, 0xF, 0xF, false))));
+  C = __int_as_float(__builtin_amdgcn_readlane(r, 0));
+  int t = __float_as_int(__builtin_amdgcn_frexp_mantf(z) * fast_exp2((c - C) + e));
+  t = __float_as_int(__int_as_float(t) + __int_as_float(__builtin_amdgcn_update_dpp(t, t, 0xB1, 0xF, 0xF, false)));
+  t = __float_as_int(__int_as_float(t) + __int_as_float(__builtin_amdgcn_update_dpp(t, t, 0x4E, 0xF, 0xF, false)));
+  t = __float_as_int(__int_as_float(t) + __int_as_float(__builtin_amdgcn_update_dpp(t, t, 0x141, 0xF, 0xF, false)));
+  t = __float_as_int(__int_as_float(t) + __int_as_float(__builtin_amdgcn_update_dpp(t, t, 0x140, 0xF, 0xF, false)));
+  Z = __int_as_float(__builtin_amdgcn_readlane(t, 0));
+}
+
 // Accept test of one draft position ([P1] ch.3; [P2] "품질은 rejection sampling이
 // 지킨다"; [P3] 단계 3): p(x) = 2^(l_x k2 - c) / z in fp64 (the same normaliser as
 // the row statistics), thr = 1 if p(x) >= q(x) else p(x) / q(x), accept iff u < thr.
@@ -1925,19 +1945,10 @@ __device__ __forceinline__ int judge_rows_exact(const Args& a, int b, int base, 
         for (int j = 0; j < kGroup; ++j) sacc[j] = 0.f;
         __syncthreads();
         // every wave merges the partials in the same order and takes the same decision
-        float C = -FLT_MAX, Z = 0.f;
-        if (lane < kSeqWaves) {
-          const float2 pz = s_part[lane];
-          C = pz.x;
-          Z = pz.y;
-        }
-#pragma unroll
-        for (int o = kSeqWaves / 2; o > 0; o >>= 1) {
-          const float c2 = __shfl_xor(C, o), z2 = __shfl_xor(Z, o);
-          lse2_merge(C, Z, c2, z2);
-        }
-        C = __shfl(C, 0);
-        Z = __shfl(Z, 0);
+        static_assert(kSeqWaves == 16, "one DPP row holds the wave partials");
+        const float2 pz = s_part[lane & (kSeqWaves - 1)];
+        float C, Z;
+        merge_row16(pz.x, pz.y, C, Z);
         // lx, qx were loaded behind the ring's first loads: keep their uses here, inside
         // the row loop, so that waiting for them never drains the ring
         asm volatile("" : "+v"(lxb), "+v"(qx));
