@@ -161,26 +161,30 @@ __device__ __forceinline__ bool seq_geom(const Args& a, int b, int& base, int& g
   return ok;
 }
 
-// Merge (c, z) partial softmax states kept in base 2; a state stands for z 2^c. A partial
-// taken against a reference below its largest entry (a wave's first chunk, at a low
-// temperature) can hold z near the top of the fp32 range, and scaling such a z by
-// 2^(c - C) would underflow the factor and drop the partial. So each z is split as
-// m 2^e (m in [0.5, 1)) and e goes into the power of two: the merged reference is the
-// larger c + e, the merged z lies in [0.5, 2), and a term that underflows is below 2^-126
-// of the merged z. Only the differences c - C are rounded, never the references.
+// Merge (c, z) partial softmax states kept in base 2 (a state stands for z 2^c) that were
+// taken with a running max: c is the scaled max of the partial's entries, so z is at
+// most the number of terms, the result cannot overflow, and a term that underflows is
+// below 2^(C - 126), negligible beside the row's largest entry (which some partial
+// counts in full).
 __device__ __forceinline__ void lse2_merge(float& c, float& z, float c2, float z2) {
-  const float e1 = static_cast<float>(__builtin_amdgcn_frexp_expf(z));
-  const float e2 = static_cast<float>(__builtin_amdgcn_frexp_expf(z2));
-  const float C = fmaxf(c + e1, c2 + e2);
-  z = __builtin_amdgcn_frexp_mantf(z) * fast_exp2((c - C) + e1) +
-      __builtin_amdgcn_frexp_mantf(z2) * fast_exp2((c2 - C) + e2);
+  const float C = fmaxf(c, c2);
+  z = z * fast_exp2(c - C) + z2 * fast_exp2(c2 - C);
   c = C;
 }
 
-// The same merge over the states (c, z) of the 16 lanes of each row of the wave, by DPP
-// steps inside the row (a max of c + e, then a sum of m 2^(c - C + e)): one exp2 per lane
-// and no LDS permutes. Returns row 0's (C, Z), wave-uniform; every wave that runs it on
-// the same states gets the same bits.
+// Pass 1 of the one-launch plan moves a wave's exp2 reference up when an entry lies more
+// than this many octaves above it.
+constexpr float kRebaseOctaves = 8.f;
+
+// Merge of the states (c, z) held by the 16 lanes of each row of the wave (the wave
+// partials of one row). Each z is split as m 2^e (m in [0.5, 1)) and e goes into the
+// power of two: C is the largest c + e, Z = sum m 2^(c - C + e) is 0 or lies in
+// [0.5, 16], a term that underflows is below 2^-126 of Z, and only the differences
+// c - C are rounded, never the references. So the merge loses no partial whatever its
+// z: pass 1 keeps z below 2^21, but a partial held against a reference far below its
+// largest entry (z near 2^128) would merge as exactly. DPP steps inside the row (a max,
+// then a sum): one exp2 per lane and no LDS permutes. Returns row 0's (C, Z),
+// wave-uniform; every wave that runs it on the same states gets the same bits.
 __device__ __forceinline__ void merge_row16(float c, float z, float& C, float& Z) {
   const float e = static_cast<float>(__builtin_amdgcn_frexp_expf(z));
   int r = __float_as_int(c + e);
@@ -1861,13 +1865,16 @@ __global__ __launch_bounds__(kSeqThreads) void k_vs_finish(Args a, VShard vs) {
   for (int i = n + 1 + threadIdx.x; i <= g; i += kSeqThreads) a.emitted[base + b + i] = -1;
 }
 
-// Pass 1: per row, z = sum 2^(l k2 - c) in fp32. Each wave takes its reference c from
-// the first chunk it reads of the row (the chunk's max times k2; the row max can only be
-// larger, so no entry underflows the sum's precision) and adds plain exp2 terms after
-// that, with no running max. A wave whose sum overflows (a value 128 or more octaves
-// above that first chunk's max) or is not finite redoes its chunks of the row with the
-// running max; a sum that stays finite can still lie near 2^128, which the merge of the
-// waves' partials takes in its stride. Returns n; s_cz[i] = (c, z) of each judged row.
+// Pass 1: per row, z = sum 2^(l k2 - c) in fp32. Each wave keeps one reference c for its
+// chunks of the row: the first chunk's max times k2, raised to a later chunk's max
+// whenever an entry lies more than kRebaseOctaves above it (a wave-uniform branch: the
+// sums are scaled by 2^(c_old - c_new)). Every term then has an exponent argument of at
+// most kRebaseOctaves, whose rounding to fp32 is at most 2^-22 octave (1.7e-7 relative),
+// and z stays below 2^21. At T = 1 the first chunk's reference holds for the whole row
+// nearly always (8 octaves are 5.5 logits); low temperatures raise it a few times per
+// row. A wave whose sum is not finite (infinite or NaN logits) redoes its chunks of the
+// row with the running max, which raises the data flag. Returns n; s_cz[i] = (c, z) of
+// each judged row.
 template <typename T, bool WIDE, bool NT, typename Hook>
 __device__ __forceinline__ int judge_rows_exact(const Args& a, int b, int base, int g, float2* s_cz, int* s_xn,
                                                 Hook&& hook) {
@@ -1905,22 +1912,41 @@ __device__ __forceinline__ int judge_rows_exact(const Args& a, int b, int base, 
         hook();
       },
       [&](const Raw<T>& lr, int k) {
-        float xv[kGroup];
-        unpack(lr, xv);
-        if (k == 0) {  // the row's first chunk sets the reference
+        float t[kGroup];  // exponent arguments l k2 - c
+        {
+          float xv[kGroup];
+          unpack(lr, xv);
+#pragma unroll
+          for (int j = 0; j < kGroup; ++j) t[j] = fmaf(xv[j], k2, -c);
+        }
+        float tm = t[0];
+#pragma unroll
+        for (int j = 1; j < kGroup; ++j) tm = fmaxf(tm, t[j]);
+        // a new reference when an entry of the chunk lies more than kRebaseOctaves above
+        // the current one (at the row's first chunk c is -FLT_MAX: always)
+        if (__builtin_expect(__ballot(tm > kRebaseOctaves) != 0, 0)) {
+          float xv[kGroup];
+          unpack(lr, xv);
           float bm = xv[0];
 #pragma unroll
           for (int j = 1; j < kGroup; ++j) bm = fmaxf(bm, xv[j]);
-          c = fmaxf(wave_max_dpp(bm) * k2, -FLT_MAX);
+          const float cn = fmaxf(wave_max_dpp(bm) * k2, -FLT_MAX);
+          const float sc = fast_exp2(c - cn);
+#pragma unroll
+          for (int j = 0; j < kGroup; ++j) {
+            sacc[j] *= sc;
+            t[j] = fmaf(xv[j], k2, -cn);
+          }
+          c = cn;
         }
         const float wgt = k == nsp - 1 ? wlast : 1.f;
 #pragma unroll
-        for (int j = 0; j < kGroup; ++j) sacc[j] = fmaf(wgt, fast_exp2(fmaf(xv[j], k2, -c)), sacc[j]);
+        for (int j = 0; j < kGroup; ++j) sacc[j] = fmaf(wgt, fast_exp2(t[j]), sacc[j]);
       },
       [&](int i) {
         float z = wave_sum(((sacc[0] + sacc[1]) + (sacc[2] + sacc[3])) + ((sacc[4] + sacc[5]) + (sacc[6] + sacc[7])));
         float cw = c;
-        if (!(z <= FLT_MAX)) {  // overflow or not finite: this wave's chunks again, running max
+        if (!(z <= FLT_MAX)) {  // not finite (data errors): this wave's chunks again, running max
           const T* rowp = Lseq + static_cast<size_t>(i) * V;
           float m = -FLT_MAX;
           cw = -FLT_MAX;

@@ -915,17 +915,18 @@ def _low_temperature_rows(dtype, case):
 @pytest.mark.parametrize("case", ["overlap", "three"])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_low_temperature_partials_near_fp32_top(lib, dtype, case):
-    """The one-launch plan walks a row in spans of 16 chunks of 512 entries (wave w reads
-    chunk w of each span; the last span starts at V - 8192 and gives weight 0 to what the
-    span before it covered), and each wave sums 2^(l k2 - c) against its first chunk's
-    maximum. At a low temperature a later entry 4 logits above that maximum is 126 to 128
-    octaves up: the wave's partial stays finite but lies near the top of the fp32 range.
+    """Rows whose later entries lie far above each wave's first chunk at a low
+    temperature. The one-launch plan walks a row in spans of 16 chunks of 512 entries
+    (wave w reads chunk w of each span; the last span starts at V - 8192 and gives weight
+    0 to what the span before it covered) and sums 2^(l k2 - c) against a per-wave
+    reference c. Here an entry 4 logits above a wave's first chunk is 126 to 128 octaves
+    up, which a reference kept from the first chunk turns into partials near the top of
+    the fp32 range, and whose exponent arguments round at 2^-18 octave:
       * overlap: wave 10's first chunk tops at 8 and a 12 sits where the last span
-        overlaps the one before, so wave 0 meets the 12 with weight 0 and takes it as its
-        reference; wave 10's partial (about 2^126.8) must survive the scale 2^-126.8;
-      * three: waves 10, 11 and 12 each meet a 12 after a first chunk topping at 8; their
-        three partials (about 2^127.4 each) must not add up past the fp32 range.
-    Every plan against the oracle, p(x) included."""
+        overlaps the one before, so wave 0 meets the 12 with weight 0;
+      * three: waves 10, 11 and 12 each meet a 12 after a first chunk topping at 8.
+    Every plan against the oracle, p(x) included; p of the drafts at a 12 is 1 (one 12)
+    or 1/3 (three)."""
     w = _low_temperature_rows(dtype, case)
     runs, ora = check_parity(lib, w, f"low temperature, {case}, {dtype}")
     spike_rows = np.flatnonzero(w.draft_ids == w.draft_ids[0])
