@@ -912,6 +912,49 @@ def _low_temperature_rows(dtype, case):
     return w
 
 
+def _llm_like(w, seed):
+    """Rows shaped like a language model's output: in 70% of target rows one confident
+    token 8 to 25 logits above the row's maximum, in 30% a block of up to V/4 entries
+    masked to -inf, in 20% a second entry equal to the row's maximum (an exact tie).
+    Greedy drafts are then re-drawn: the lowest-index argmax in 80% of rows. Changes w
+    in place."""
+    rng = np.random.default_rng([777, seed])
+    V = w.V
+    for r in range(w.target_rows):
+        row = w.logits_f32(slice(r, r + 1))[0].copy()
+        if rng.random() < 0.7:
+            row[int(rng.integers(0, V))] = row.max() + np.float32(rng.uniform(8, 25))
+        if rng.random() < 0.3:
+            a = int(rng.integers(0, V))
+            row[a:a + int(rng.integers(1, max(2, V // 4)))] = -np.inf
+        if rng.random() < 0.2 and np.isfinite(row.max()):
+            row[int(rng.integers(0, V))] = row.max()
+        if not np.isfinite(row).any():
+            row[0] = 0.0
+        w.logits[r] = synth.bf16_round(row) if w.dtype == "bf16" else row
+    if w.T == 0.0 and w.draft_rows:
+        rows = np.concatenate([np.arange(int(w.cu_gamma[b]) + b, int(w.cu_gamma[b + 1]) + b) for b in range(w.B)])
+        top = np.argmax(w.logits_f32(rows), axis=1)
+        keep = rng.random(w.draft_rows) < 0.8
+        w.draft_ids[keep] = top[keep]
+    return w
+
+
+@pytest.mark.parametrize("dtype,greedy,T,V,B", [("bf16", False, 1.0, 128256, 40), ("f32", False, 0.7, 152064, 24),
+                                               ("bf16", False, 0.3, 32000, 300), ("bf16", True, 0.0, 152064, 40),
+                                               ("f32", True, 0.0, 50000, 270)])
+def test_llm_like_rows(lib, dtype, greedy, T, V, B):
+    """Confident tokens far above the rest of the row, masked -inf blocks and exact ties
+    together, ragged gamma_b in 0..8, every plan against the oracle."""
+    gammas = np.random.default_rng([98, V, B]).integers(0, 9, B)
+    if greedy:
+        w = synth.make_greedy("llm-like", gammas, V, dtype, 2.0, 0.8, seed=98 + B)
+    else:
+        w = synth.make_sampling("llm-like", gammas, V, dtype, T, 2.0, 0.8, seed=98 + B)
+    _llm_like(w, B)
+    check_parity(lib, w, f"llm-like rows {dtype} T={T} V={V} B={B}", ragged=True)
+
+
 @pytest.mark.parametrize("case", ["overlap", "three"])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_low_temperature_partials_near_fp32_top(lib, dtype, case):
