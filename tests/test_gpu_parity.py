@@ -957,7 +957,7 @@ def test_llm_like_rows(lib, dtype, greedy, T, V, B):
 
 @pytest.mark.parametrize("case", ["overlap", "three"])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_low_temperature_partials_near_fp32_top(lib, dtype, case):
+def test_low_temperature_entries_far_above_first_chunk(lib, dtype, case):
     """Rows whose later entries lie far above each wave's first chunk at a low
     temperature. The one-launch plan walks a row in spans of 16 chunks of 512 entries
     (wave w reads chunk w of each span; the last span starts at V - 8192 and gives weight
