@@ -55,7 +55,10 @@
  *     position with thr <= 1 and makes a draw take the last positive weight);
  *   - a judged or sampled row whose softmax normaliser is not finite or not
  *     positive (NaN / +inf logits, or a row of -inf): flagged; outputs for that
- *     sequence are unspecified but in range;
+ *     sequence are unspecified but in range. Row statistics are fp32 sums against a
+ *     reference l log2(e)/T rounded to fp32, whose rounding passes the fp32
+ *     exponent range once |l| log2(e)/T reaches about 2^30 (fp32 logits of 1e6 at
+ *     T = 1e-3): such a row's normaliser overflows and is flagged the same way;
  *   - greedy mode (T == 0): a NaN logit in a judged row (a draft row up to the
  *     first mismatch, or the bonus row when it is read) raises the same flag
  *     (SV_DATA_NONFINITE); outputs for that sequence are unspecified but in range.

@@ -112,6 +112,7 @@ struct Args {
   int B, gamma, V, R, split, span, max_gamma;
   float k2;        // log2(e) / T, fp32
   double k2d;      // log2(e) / T, fp64
+  double kr;       // k2d / k2: scales a pass-1 reference into the fp64 draws (draw_ref)
   // bf16 value table of the one-launch path: magnitudes (bit patterns without the sign)
   // tlo..thi, thi < 0x7F80; tlo > thi when the table is not used
   int tlo, thi;
@@ -226,6 +227,14 @@ __device__ __forceinline__ bool accept_test(int x, float lx, float qx, float uu,
                                             const Args& a, double& px) {
   return accept_decision(x, lx, qx, uu, c, z, a, px, true);
 }
+
+// A pass-1 reference c as the fp64 draws take it. Pass 1 sums 2^(l k2 - c) with k2 the
+// fp32 rounding of log2(e)/T, and the draws weigh entries by 2^(l k2d - c') with k2d =
+// log2(e)/T itself, dividing by pass 1's z. With c' = c, the two sums differ by
+// 2^(l (k2d - k2)) per term, an octave once |l k2| nears 2^24. With c' = c k2d / k2 (the
+// same reference logit c / k2, scaled by k2d) they differ by 2^((l - c/k2)(k2d - k2)):
+// within 3e-7 for every term within 30 octaves of the reference, at any |l k2|.
+__device__ __forceinline__ double draw_ref(const Args& a, float c) { return static_cast<double>(c) * a.kr; }
 
 // ============================================================== step 1
 // Base-2 softmax state of entries [lo, hi) of one row: c = the scaled max (max(l) * k2,
@@ -1484,15 +1493,15 @@ __global__ __launch_bounds__(kSeqThreads) void k_sample_seq(Args a) {
     for (int i = threadIdx.x; i < n; i += kSeqThreads) a.emitted[base + b + i] = a.ids[base + i];
     if (threadIdx.x == 0) a.acc[b] = n;
     __syncthreads();  // sT
-    const double Zq = n < g ? static_cast<double>(s_cz[n].y) * exp2(static_cast<double>(s_cz[n].x)) : 0.0;
+    const double Zq = n < g ? static_cast<double>(s_cz[n].y) * exp2(draw_ref(a, s_cz[n].x)) : 0.0;
     if (tab && final_draw_tab(a, b, base, g, n, Zq, sT)) return;
-    final_draw<T, ALIGNED>(a, b, base, g, n, n < g ? static_cast<double>(s_cz[n].x) : 0.0,
+    final_draw<T, ALIGNED>(a, b, base, g, n, n < g ? draw_ref(a, s_cz[n].x) : 0.0,
                            n < g ? static_cast<double>(s_cz[n].y) : 0.0, s_tab);
   } else {
     const int n = first_rejection<T, ACCEPT, false>(a, b, base, g, s_cz, nullptr, &s_n);
     for (int i = threadIdx.x; i < n; i += kSeqThreads) a.emitted[base + b + i] = a.ids[base + i];
     if (threadIdx.x == 0) a.acc[b] = n;
-    final_draw<T, ALIGNED>(a, b, base, g, n, n < g ? static_cast<double>(s_cz[n].x) : 0.0,
+    final_draw<T, ALIGNED>(a, b, base, g, n, n < g ? draw_ref(a, s_cz[n].x) : 0.0,
                            n < g ? static_cast<double>(s_cz[n].y) : 0.0, s_tab);
   }
 }
@@ -1536,7 +1545,7 @@ __global__ __launch_bounds__(kSeqThreads) void k_draw_part(Args a) {
     if (threadIdx.x == 0) a.acc[b] = n;
   }
   __syncthreads();  // sT / s_tab
-  const double cr = n < g ? static_cast<double>(s_cz[n].x) : 0.0;
+  const double cr = n < g ? draw_ref(a, s_cz[n].x) : 0.0;
   const double zr = n < g ? static_cast<double>(s_cz[n].y) : 0.0;
   const int ns = kSeqWaves * a.nslice;
   const int sw = kTab ? sub_width(a.V, ns) : iter_width(a.V, ns);
@@ -1748,7 +1757,7 @@ __global__ __launch_bounds__(kSeqThreads) void k_vs_decide(Args a, VShard vs) {
     const int Vs = vs.vb[vs.me + 1] - vs.vb[vs.me];
     const T* lrow = static_cast<const T*>(a.logits) + static_cast<size_t>(base + b + (residual ? n : g)) * Vs;
     const float* qrow = residual ? a.q + static_cast<size_t>(base + n) * Vs : nullptr;
-    const double cr = residual ? static_cast<double>(s_cz[n].x) : 0.0;
+    const double cr = residual ? draw_ref(a, s_cz[n].x) : 0.0;
     const double Zq = residual ? static_cast<double>(s_cz[n].y) : 0.0;
     const double KN = kExpScale * a.k2d;
     const int rw = iter_width(Vs, kSeqWaves);
@@ -2330,7 +2339,7 @@ __global__ __launch_bounds__(kGrpThreads, 4) void k_verify_group(Args a) {
       const float cr = __shfl(Cm, src), zr = __shfl(Zm, src);
       const int xn = __shfl(xv, src);
       if (lane == 0)
-        s_d = GroupDraw{n < g ? static_cast<double>(zr) : 0.0, n < g ? static_cast<double>(cr) : 0.0, n, g, base,
+        s_d = GroupDraw{n < g ? static_cast<double>(zr) : 0.0, n < g ? draw_ref(a, cr) : 0.0, n, g, base,
                         n < g ? xn : -1, b, uf};
     }
   } else if (threadIdx.x == 0) {
@@ -2450,7 +2459,7 @@ __global__ __launch_bounds__(kGrpThreads) void k_verify_tiny(Args a) {
     const float cr = __shfl(Cm, src), zr = __shfl(Zm, src);
     const int xn = __shfl(xv, src);
     if (lane == 0)
-      s_d = GroupDraw{n < g ? static_cast<double>(zr) : 0.0, n < g ? static_cast<double>(cr) : 0.0, n, g, base,
+      s_d = GroupDraw{n < g ? static_cast<double>(zr) : 0.0, n < g ? draw_ref(a, cr) : 0.0, n, g, base,
                       n < g ? xn : -1, b, uf};
   }
   __syncthreads();  // s_d
@@ -2508,7 +2517,7 @@ __global__ __launch_bounds__(kSeqThreads) void k_verify_seq(Args a) {
       if (threadIdx.x == 0) a.acc[b] = 0;
     }
     __syncthreads();  // s_cz of row n, sT (s_tab without the table)
-    const double cr = n < g ? static_cast<double>(s_cz[n].x) : 0.0;
+    const double cr = n < g ? draw_ref(a, s_cz[n].x) : 0.0;
     const double zr = n < g ? static_cast<double>(s_cz[n].y) : 0.0;
     // table scale: sum 2^(l k2) = z 2^c
     const int xn = n < g ? s_xn : -1;
@@ -2525,7 +2534,7 @@ __global__ __launch_bounds__(kSeqThreads) void k_verify_seq(Args a) {
                                              : judge_rows_exact<T, false, false>(a, b, base, g, s_cz, &s_xn, [] {});
     if (g == 0 && threadIdx.x == 0) a.acc[b] = 0;
     __syncthreads();  // s_cz of row n, s_tab
-    final_draw<T, true>(a, b, base, g, n, n < g ? static_cast<double>(s_cz[n].x) : 0.0,
+    final_draw<T, true>(a, b, base, g, n, n < g ? draw_ref(a, s_cz[n].x) : 0.0,
                         n < g ? static_cast<double>(s_cz[n].y) : 0.0, s_tab, n < g ? s_xn : -1);
   }
 }
@@ -3685,9 +3694,11 @@ int run_impl(spec_verify_ctx* ctx, void* hip_stream, int batch, int gamma, const
   if (greedy) {
     a.k2 = 0.f;
     a.k2d = 0.0;
+    a.kr = 1.0;
   } else {
     a.k2d = 1.4426950408889634 / static_cast<double>(temperature);
     a.k2 = static_cast<float>(a.k2d);
+    a.kr = a.k2d / static_cast<double>(a.k2);
     // bf16 value table window: magnitudes below 2^etop, |x k2| < 990, kTabBinades octaves
     const int etop = static_cast<int>(floor(log2(990.0 / a.k2d)));
     const int be_hi = etop + 127 > 255 ? 255 : etop + 127;  // biased exponent, exclusive
@@ -3789,6 +3800,7 @@ int vshard_prepare(spec_verify_ctx* ctx, const spec_vshard* sh, int batch, int g
   a.thi = 0;
   a.k2d = greedy ? 0.0 : 1.4426950408889634 / static_cast<double>(temperature);
   a.k2 = static_cast<float>(a.k2d);
+  a.kr = greedy ? 1.0 : a.k2d / static_cast<double>(a.k2);
   vs = VShard{};
   vs.G = G;
   vs.me = sh->shard;

@@ -912,6 +912,38 @@ def _low_temperature_rows(dtype, case):
     return w
 
 
+@pytest.mark.parametrize("dtype,scale,T,V", [("bf16", 1000.0, 1e-4, 33), ("f32", 30.0, 1e-4, 8191),
+                                             ("f32", 1e4, 1e-3, 4099), ("bf16", 1e4, 0.01, 128256)])
+def test_large_scaled_logits(lib, dtype, scale, T, V):
+    """Rows whose |l| log2(e) / T reaches 10^6 to 10^8 (N(0, 1) logits times `scale` at a
+    small T): pass 1 keeps its sums in fp32 against a reference rounded to fp32 with k2
+    rounded to fp32, the draws weigh entries in fp64 with log2(e)/T itself, so the
+    reference must be rescaled between the two (at |l k2| = 4e7 the unscaled one put the
+    residual's normaliser off by 2.5 times). Every plan against the oracle."""
+    B = 200 if V < 1000 else 24
+    gammas = np.random.default_rng([99, V]).integers(0, 9, B)
+    w = synth.make_sampling("large scaled logits", gammas, V, dtype, T, 1.0, 0.8, seed=99)
+    x = (w.logits_f32().astype(np.float64) * scale).astype(np.float32)
+    w.logits = synth.bf16_round(x) if dtype == "bf16" else x
+    check_parity(lib, w, f"large scaled logits {dtype} scale={scale} T={T} V={V}", ragged=True)
+
+
+@pytest.mark.parametrize("plan", ["SV_PATH_TWO_LAUNCH", "SV_PATH_ONE_LAUNCH", "SV_PATH_POOLED"])
+def test_scaled_logits_past_fp32_reference_flagged(lib, plan):
+    """Past |l| log2(e) / T of about 2^30 the fp32 reference's own rounding exceeds the
+    fp32 exponent range, and the row's normaliser overflows: flagged as a non-finite
+    normaliser, outputs in range (fp32 logits of 1e20 at T = 1)."""
+    w = synth.make_sampling("past fp32 reference", np.full(8, 4), 1000, "f32", 1.0, 1.0, 0.8, seed=100)
+    w.logits = (w.logits_f32().astype(np.float64) * 1e20).astype(np.float32)
+    v = verifier(lib, 1000, "f32", 8, 32)
+    v.set_path(getattr(lib, plan))
+    gpu = run_gpu(v, w)
+    assert gpu["status"] == lib.SV_EDATA
+    assert "non-finite" in v.last_error()
+    assert np.all((gpu["emitted_tokens"] >= -1) & (gpu["emitted_tokens"] < 1000))
+    assert np.all((gpu["accepted_count"] >= 0) & (gpu["accepted_count"] <= 4))
+
+
 def _llm_like(w, seed):
     """Rows shaped like a language model's output: in 70% of target rows one confident
     token 8 to 25 logits above the row's maximum, in 30% a block of up to V/4 entries
