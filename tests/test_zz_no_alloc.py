@@ -3,8 +3,8 @@
 Both run the same inputs; the static entry point must give the same outputs bit for bit
 (the same kernels, except that greedy batches never take the helper plan, whose outputs
 are the same by construction, and sampling batches never take the small-batch plan's
-several workgroups per sequence: there the context runs the two-launch plan for the
-comparison) and pass the oracle's bar. Each case makes two static calls in a row, the
+several workgroups per sequence: there the context runs the plan the static entry point
+takes instead, one launch from 0.55 x CUs sequences up and two launches below) and pass the oracle's bar. Each case makes two static calls in a row, the
 second with a smaller input, so that what the first call leaves in the static workspace
 cannot leak into the second. Captured into a HIP graph, static calls replay with new
 inputs and match the eager results.
@@ -52,6 +52,14 @@ def _static(sv, w, dev, flags):
                 p_draft=pd.cpu().numpy() if pd is not None else None)
 
 
+def _static_plan(sv, w):
+    """The plan the static entry point takes for a sampling batch that the context would
+    give to the small-batch plan: one launch from 0.55 x CUs sequences up (the AUTO rule's
+    crossover), else two launches."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return sv.SV_PATH_ONE_LAUNCH if w.B >= (11 * cus + 19) // 20 else sv.SV_PATH_TWO_LAUNCH
+
+
 def _check(sv, w, label):
     _say(label, f"B={w.B} V={w.V} {w.dtype} T={w.T} rows={w.draft_rows}")
     dev = to_device(w)
@@ -60,7 +68,7 @@ def _check(sv, w, label):
         ref = run_gpu(v, w, dev=dev)
         assert ref["status"] == sv.SV_OK, v.last_error()
         if v.last_path() == sv.SV_PATH_POOLED and w.V > 4096:  # not taken by the static entry point
-            v.set_path(sv.SV_PATH_TWO_LAUNCH)
+            v.set_path(_static_plan(sv, w))
             ref = run_gpu(v, w, dev=dev)
             assert ref["status"] == sv.SV_OK, v.last_error()
     flags = torch.zeros(1, dtype=torch.int32, device="cuda")
